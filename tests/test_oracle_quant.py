@@ -1,0 +1,253 @@
+"""Pins for the oracle's activation path: smoothing, low-rank down-projection
+and the int4 / NVFP4 group quantizers (first fused step of the layer: blog
+"Hugging Face integrates Nunchaku 4-bit diffusion inference into Diffusers",
+"SVDQuant and the Nunchaku engine").
+
+Pins: hand-worked golden examples, exact rational brute force of every
+rounding (nearest value, ties to even), closed-form invariants (codes never
+reach -8, the absmax element maps to +-7, round-trip error bounds), and a
+library matmul for the down-projection.
+"""
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from bit_w4a4_quantized_svdq_amd import synth
+from tests.test_oracle_codecs import E2M1_MAGS, _brute_bf16, _brute_e4m3, _nearest_even
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def load_examples():
+    ex = {}
+    with open(os.path.join(GOLDEN, "quant_examples.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, val = line.split(":", 1)
+            name, field = key.split(".")
+            ex.setdefault(name, {})[field] = val.split()
+    return ex
+
+
+EXAMPLES = load_examples()
+
+
+def _group(values, size):
+    v = np.zeros((1, size), np.float32)
+    v[0, :len(values)] = [float(t) for t in values]
+    return v
+
+
+def test_golden_int4_examples(oracle):
+    for name in ("int4_a", "int4_b"):
+        e = EXAMPLES[name]
+        codes, scales = oracle.quantize_int4(_group(e["values"], 64))
+        assert int(scales[0, 0]) == int(e["scale"][0], 16), name
+        want = [int(b, 16) for b in e["bytes"]]
+        assert codes[0, :len(want)].tolist() == want, name
+        assert not codes[0, len(want):].any()
+
+
+def test_golden_nvfp4_example(oracle):
+    e = EXAMPLES["nvfp4_a"]
+    codes, scales = oracle.quantize_nvfp4(_group(e["values"], 16))
+    assert int(scales[0, 0]) == int(e["scale"][0], 16)
+    want = [int(b, 16) for b in e["bytes"]]
+    assert codes[0].tolist() == want + [0] * (8 - len(want))
+
+
+def test_golden_awq_example(oracle):
+    e = EXAMPLES["awq_a"]
+    W = synth.to_bf16_bits(_group(e["values"], 64))
+    codes, scales, zeros = oracle.awq_quantize_weight(W)
+    assert int(scales[0, 0]) == int(e["scale"][0], 16)
+    assert int(zeros[0, 0]) == int(e["zero"][0], 16)
+    want = [int(b, 16) for b in e["bytes"]]
+    assert codes[0, :3].tolist() == want
+    assert (codes[0, 2:] == 0x55).all()
+
+
+def test_formats_table_group_sizes(oracle):
+    """The quantizers' group sizes are the table's: int4 64, nvfp4 16."""
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "formats_table.txt"))
+            if l.strip() and not l.startswith("#")]
+    table = {(m, p): int(g) for m, p, g in rows}
+    v = np.random.default_rng(0).standard_normal((2, 128)).astype(np.float32)
+    _, s4 = oracle.quantize_int4(v)
+    _, sf = oracle.quantize_nvfp4(v)
+    assert 128 // s4.shape[1] == table[("svdq_w4a4", "int4")] == 64
+    assert 128 // sf.shape[1] == table[("svdq_w4a4", "nvfp4")] == 16
+    W = synth.to_bf16_bits(v)
+    _, sa, _ = oracle.awq_quantize_weight(W)
+    assert 128 // sa.shape[1] == table[("awq_w4a16", "int4")] == 64
+
+
+# ----------------------------------------------------------------- helpers
+
+def _bf16_test_rows(rng, rows, K):
+    """bf16 test activations: normals with per-group magnitude spread, plus
+    exact ties, zero groups, constant groups, tiny and large groups."""
+    v = rng.standard_normal((rows, K)) * np.exp(rng.uniform(-3, 3, (rows, K // 64)).repeat(64, 1))
+    x = synth.to_bf16_bits(v)
+    xf = synth.bf16_bits_to_f32(x).copy()
+    xf[0, :64] = 0.0                                        # zero group
+    xf[0, 64:128] = -1.75                                   # constant group
+    xf[1, :64] = np.float32(2.0 ** -130) * rng.integers(-7, 8, 64)   # subnormal group
+    xf[1, 64:128] = synth.bf16_bits_to_f32(synth.to_bf16_bits(rng.standard_normal(64) * 1e30))
+    # ties: absmax 7 with scale exactly 1 and half-integer members
+    xf[2, :64] = rng.integers(-13, 14, 64) / 2.0
+    xf[2, 0] = 7.0
+    return synth.to_bf16_bits(xf)
+
+
+def _int4_brute(vals, scale_bits):
+    """Exact: scale = nearest bf16 to absmax/7; q = nearest integer to v/s in [-8,7], ties even."""
+    a = max(abs(Fraction(float(t))) for t in vals)
+    s_code = _brute_bf16(float(a / 7)) if a != 0 else 0
+    assert s_code == int(scale_bits)
+    s = Fraction(float(np.uint32(s_code << 16).view(np.float32)))
+    if s == 0:
+        return [0] * len(vals)
+    return [max(-8, min(7, round(Fraction(float(t)) / s))) for t in vals]
+
+
+# --------------------------------------------------------------- int4 pins
+
+def test_int4_quantizer_brute_force(oracle):
+    rng = np.random.default_rng(21)
+    x = _bf16_test_rows(rng, 6, 512)
+    xf = synth.bf16_bits_to_f32(x)
+    codes, scales = oracle.quantize_int4(xf)
+    q = oracle.unpack_int4(codes, 6, 512)
+    for m in range(6):
+        for g in range(8):
+            want = _int4_brute(xf[m, 64 * g:64 * g + 64], scales[m, g])
+            assert q[m, 64 * g:64 * g + 64].tolist() == want, (m, g)
+
+
+def test_int4_scale_is_exact_nearest_bf16_of_absmax_over_7(oracle):
+    """fp32 divide then bf16 rounding equals one rounding of the exact a/7
+    (1/7 has a period-3 binary expansion, so no double-rounding tie)."""
+    rng = np.random.default_rng(22)
+    a = synth.bf16_bits_to_f32(synth.to_bf16_bits(np.exp(rng.uniform(-80, 80, 3000))))
+    v = np.zeros((len(a), 64), np.float32)
+    v[:, 5] = a
+    _, scales = oracle.quantize_int4(v)
+    for ai, s in zip(a.tolist(), scales[:, 0].tolist()):
+        assert s == _brute_bf16(float(Fraction(ai) / 7))
+
+
+def test_int4_invariants(oracle):
+    rng = np.random.default_rng(23)
+    x = synth.to_bf16_bits(rng.standard_normal((64, 1024)) * 3)
+    xf = synth.bf16_bits_to_f32(x)
+    codes, scales = oracle.quantize_int4(xf)
+    q = oracle.unpack_int4(codes, 64, 1024).astype(np.float64)
+    s = synth.bf16_bits_to_f32(scales).astype(np.float64).repeat(64, 1)
+    assert q.min() >= -7 and q.max() <= 7                    # -8 never occurs
+    err = np.abs(xf.astype(np.float64) - q * s)
+    assert (err <= s / 2).all()                             # round trip <= scale/2
+    g = np.abs(xf).reshape(64, 16, 64)
+    amax_idx = g.argmax(-1)
+    qa = np.take_along_axis(q.reshape(64, 16, 64), amax_idx[..., None], -1)[..., 0]
+    assert (np.abs(qa) == 7).all()                           # absmax maps to +-7
+
+
+def test_int4_zero_group(oracle):
+    codes, scales = oracle.quantize_int4(np.zeros((3, 128), np.float32))
+    assert not codes.any() and not scales.any()
+
+
+# -------------------------------------------------------------- NVFP4 pins
+
+def test_nvfp4_quantizer_brute_force(oracle):
+    rng = np.random.default_rng(24)
+    x = _bf16_test_rows(rng, 4, 256)
+    xf = synth.bf16_bits_to_f32(x)
+    codes, scales = oracle.quantize_nvfp4(xf)
+    c = oracle.unpack_u4(codes, 4, 256)
+    for m in range(4):
+        for g in range(16):
+            vals = xf[m, 16 * g:16 * g + 16]
+            a = max(abs(Fraction(float(t))) for t in vals)
+            s_code = _brute_e4m3(float(a / 6))
+            assert int(scales[m, g]) == s_code, (m, g)
+            d = Fraction(float(oracle.e4m3_to_f32(np.uint8([s_code]))[0]))
+            for k, t in enumerate(vals.tolist()):
+                q = Fraction(t) / d if d != 0 else Fraction(0)
+                sign = 8 if (d != 0 and np.signbit(t)) else 0
+                want = sign | _nearest_even(E2M1_MAGS, list(range(8)), abs(q))
+                assert int(c[m, 16 * g + k]) == want, (m, g, k, t)
+
+
+def test_nvfp4_round_trip_bound(oracle):
+    """|x - dec(c)*d| <= half the E2M1 spacing at |x/d| times d, plus the
+    saturation excess above 6*d."""
+    rng = np.random.default_rng(25)
+    xf = synth.bf16_bits_to_f32(synth.to_bf16_bits(rng.standard_normal((32, 512))))
+    codes, scales = oracle.quantize_nvfp4(xf)
+    c = oracle.e2m1_to_f32(oracle.unpack_u4(codes, 32, 512)).astype(np.float64)
+    d = oracle.e4m3_to_f32(scales).astype(np.float64).repeat(16, 1)
+    v = np.abs(xf / d)
+    half_spacing = np.where(v < 2, 0.25, np.where(v < 4, 0.5, 1.0))
+    bound = half_spacing * d + np.maximum(0.0, np.abs(xf) - 6 * d)
+    assert (np.abs(xf - c * d) <= bound * (1 + 1e-12)).all()
+
+
+# ---------------------------------------------------- smoothing / low rank
+
+def test_smoothing_is_exact_nearest_bf16_of_quotient(oracle):
+    rng = np.random.default_rng(26)
+    x = synth.to_bf16_bits(rng.standard_normal((8, 192)) * 10)
+    s = synth.to_bf16_bits(np.exp(rng.uniform(-4, 4, 192)))
+    xh = oracle.smooth_act(x, s)
+    xf, sf = synth.bf16_bits_to_f32(x), synth.bf16_bits_to_f32(s)
+    for m in range(8):
+        for k in range(192):
+            assert int(xh[m, k]) == _brute_bf16(float(Fraction(float(xf[m, k])) / Fraction(float(sf[k]))))
+    # direction: dividing x by s and multiplying W by s keeps x W^T
+    W = synth.to_bf16_bits(rng.standard_normal((16, 192)) * 0.02)
+    R = oracle.svdq_residual(W, s, None, None)             # rank 0: R = W*s
+    lhs = synth.bf16_bits_to_f32(xh).astype(np.float64) @ R.astype(np.float64).T
+    rhs = xf.astype(np.float64) @ synth.bf16_bits_to_f32(W).astype(np.float64).T
+    assert np.linalg.norm(lhs - rhs) <= 2 ** -7 * np.linalg.norm(rhs)
+
+
+def test_smooth_factors_closed_form(oracle):
+    x = synth.to_bf16_bits(np.array([[1.0, -8.0, 0.0, 2.0], [-4.0, 2.0, 0.0, 0.5]]))
+    W = synth.to_bf16_bits(np.array([[1.0, 0.5, 3.0, 0.0], [-0.25, 2.0, 1.0, 0.0]]))
+    s = synth.bf16_bits_to_f32(oracle.smooth_factors(x, W))
+    # sqrt(4/1)=2, sqrt(8/2)=2, ax=0 -> 1, aw=0 -> 1
+    assert s.tolist() == [2.0, 2.0, 1.0, 1.0]
+
+
+def test_lowrank_down_matches_library_matmul(oracle):
+    rng = np.random.default_rng(27)
+    xh = synth.to_bf16_bits(rng.standard_normal((40, 320)))
+    L1 = synth.to_bf16_bits(rng.standard_normal((16, 320)) * 0.1)
+    t = oracle.lowrank_down(xh, L1)
+    ref = (synth.bf16_bits_to_f32(xh).astype(np.float64) @
+           synth.bf16_bits_to_f32(L1).astype(np.float64).T).astype(np.float32)
+    ulp = np.abs(t.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
+    assert ulp.max() <= 1 and (ulp == 0).mean() > 0.99
+
+
+def test_quantize_act_composes_the_steps(oracle):
+    rng = np.random.default_rng(28)
+    x = synth.to_bf16_bits(rng.standard_normal((8, 256)))
+    s = synth.to_bf16_bits(np.exp(rng.uniform(-1, 1, 256)))
+    L1 = synth.to_bf16_bits(rng.standard_normal((16, 256)) * 0.1)
+    xh = oracle.smooth_act(x, s)
+    for prec, qfn in ((oracle.INT4, oracle.quantize_int4), (oracle.NVFP4, oracle.quantize_nvfp4)):
+        codes, scales, t = oracle.quantize_act(prec, x, s, L1)
+        c2, s2 = qfn(synth.bf16_bits_to_f32(xh))
+        assert np.array_equal(codes, c2) and np.array_equal(scales, s2)
+        assert np.array_equal(t, oracle.lowrank_down(xh, L1))
+    # smooth=None means s = 1
+    c_none, _, _ = oracle.quantize_act(oracle.INT4, x, None, L1)
+    c_one, _, _ = oracle.quantize_act(oracle.INT4, x, np.full(256, 0x3F80, np.uint16), L1)
+    assert np.array_equal(c_none, c_one)
