@@ -1,0 +1,259 @@
+#!/usr/bin/env python3
+"""Benchmark of the SVDQuant W4A4 / AWQ W4A16 hot path on one MI355X.
+
+One step = the quantized linear layers of one DiT block at 1024x1024
+(4096 tokens, hidden 3072), each layer a full pass of the hot path:
+  qkv       int4  W4A4  4096 x 3072 -> 9216   (quantize_act + gemm)
+  mlp_up    int4  W4A4  4096 x 3072 -> 12288  (quantize_act + gemm)
+  mlp_down  int4  W4A4  4096 x 12288 -> 3072  (quantize_act + gemm)
+  attn_out  nvfp4 W4A4  4096 x 3072 -> 3072   (quantize_act + gemm)
+  adaln     AWQ   W4A16 1 x 3072 -> 18432     (gemv)
+All inputs are seeded synthetic tensors already resident in HBM (weights are
+random already-quantized tensors of the right shapes and value ranges).
+
+Printed JSON line: ``value`` is the step's effective W4A4 throughput, the sum
+of 2*M*N*K over the four W4A4 layers divided by the step time (quantize
+kernels and the GEMV included in the time).  ``kernels`` gives per-kernel
+average durations measured with HIP events on the launch stream inside the
+timed region; ``roofline`` is for the dominant kernel (the int4 GEMM of
+mlp_up, int8 matrix-core peak); ``gemv`` reports the W4A16 GEMV alone for
+M in {1, 2, 8} streaming 16 rotating weight copies (more than the 256 MB
+Infinity Cache); ``cpu_baseline`` times the CPU oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0        # MI355X dense int8 matrix peak, TOPS
+PEAK_BF16_TFLOPS = 2500.0      # dense bf16
+PEAK_HBM_GBPS = 8000.0         # HBM3E
+
+TOKENS, HIDDEN = 4096, 3072
+LAYERS = [  # name, precision, M, K, N, rank, seed
+    ("qkv", "int4", TOKENS, HIDDEN, 3 * HIDDEN, 32, 11),
+    ("mlp_up", "int4", TOKENS, HIDDEN, 4 * HIDDEN, 32, 12),
+    ("mlp_down", "int4", TOKENS, 4 * HIDDEN, HIDDEN, 32, 13),
+    ("attn_out", "nvfp4", TOKENS, HIDDEN, HIDDEN, 32, 14),
+]
+ADALN = ("adaln", HIDDEN, 6 * HIDDEN, 15)   # name, K, N, seed
+
+
+def algorithmic_bytes_quantize(M, K, rank, prec):
+    """x read + smooth + lora_down read + codes/scales/lora_act written."""
+    sc = M * (K // 64) * 2 if prec == "int4" else M * (K // 16)
+    return M * K * 2 + K * 2 + rank * K * 2 + M * K // 2 + sc + M * rank * 4
+
+
+def algorithmic_bytes_gemm(M, N, K, rank, prec):
+    """act codes/scales + weight codes/scales + lora_act/lora_up + out."""
+    if prec == "int4":
+        sc = (M + N) * (K // 64) * 2
+    else:
+        sc = (M + N) * (K // 16)
+    return (M + N) * K // 2 + sc + M * rank * 4 + N * rank * 2 + M * N * 2
+
+
+def algorithmic_bytes_gemv(M, N, K):
+    return N * K // 2 + 2 * N * (K // 64) * 2 + M * K * 2 + M * N * 2
+
+
+def build_inputs(torch, synth):
+    from bit_w4a4_quantized_svdq_amd.layer import AWQW4A16Linear, SVDQW4A4Linear
+    layers, xs = {}, {}
+    for name, prec, M, K, N, rank, seed in LAYERS:
+        w = synth.synthetic_w4a4_weights(seed, N, K, rank, prec)
+        layers[name] = SVDQW4A4Linear(prec, w["wgt_codes"], w["wgt_scales"], w["lora_down"], w["lora_up"],
+                                      w["smooth"], None)
+        rng = np.random.default_rng(seed + 1000)
+        if name == "mlp_down":
+            x = synth.gelu_tanh(rng.standard_normal((M, K)) * 5.7)
+        else:
+            x, _ = synth.draw_activations(rng, M, K, max(1, K // 100), 50.0)
+        xs[name] = torch.from_numpy(synth.to_bf16_bits(x).view(np.int16)).view(torch.bfloat16).cuda()
+        layers[name].buffers(M)
+    name, K, N, seed = ADALN
+    aw = synth.synthetic_awq_weights(seed, N, K)
+    layers[name] = AWQW4A16Linear(aw["wgt_codes"], aw["wgt_scales"], aw["wgt_zeros"], None)
+    rng = np.random.default_rng(seed + 1000)
+    xs[name] = torch.from_numpy(synth.to_bf16_bits(rng.standard_normal((8, K))).view(np.int16)) \
+        .view(torch.bfloat16).cuda()
+    return layers, xs
+
+
+def run_step(layers, xs, events=None):
+    """One pass of the hot path.  With ``events`` (dict name -> list of
+    (start, end) pairs) every kernel is bracketed by HIP events."""
+    import torch
+
+    def timed(key, fn):
+        if events is None:
+            fn()
+            return
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        events.setdefault(key, []).append((s, e))
+
+    for name, *_ in LAYERS:
+        L = layers[name]
+        b = L.buffers(xs[name].shape[0])
+        timed(f"{name}.quantize_act", lambda: L.quantize(xs[name], b))
+        timed(f"{name}.gemm_w4a4", lambda: L.gemm(b))
+    timed("adaln.awq_gemv", lambda: layers["adaln"](xs["adaln"][:1]))
+
+
+def gemv_sweep(torch, synth, reps=50):
+    """W4A16 GEMV alone, M in {1,2,8}, rotating 16 weight copies (512 MB)."""
+    from bit_w4a4_quantized_svdq_amd import capi
+    name, K, N, seed = ADALN
+    copies = []
+    for c in range(16):
+        aw = synth.synthetic_awq_weights(seed + 100 + c, N, K)
+        copies.append([torch.from_numpy(aw["wgt_codes"]).cuda(),
+                       torch.from_numpy(aw["wgt_scales"].view(np.int16)).view(torch.bfloat16).cuda(),
+                       torch.from_numpy(aw["wgt_zeros"].view(np.int16)).view(torch.bfloat16).cuda()])
+    rng = np.random.default_rng(seed)
+    x = torch.from_numpy(synth.to_bf16_bits(rng.standard_normal((8, K))).view(np.int16)).view(torch.bfloat16).cuda()
+    out = {}
+    for M in (1, 2, 8):
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        for i in range(20):
+            c = copies[i % 16]
+            capi.awq_gemv_w4a16(x[:M], c[0], c[1], c[2], None, y)
+        torch.cuda.synchronize()
+        ev = []
+        for i in range(reps):
+            c = copies[i % 16]
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            capi.awq_gemv_w4a16(x[:M], c[0], c[1], c[2], None, y)
+            e.record()
+            ev.append((s, e))
+        torch.cuda.synchronize()
+        us = float(np.median([s.elapsed_time(e) for s, e in ev])) * 1e3
+        gbps = algorithmic_bytes_gemv(M, N, K) / (us * 1e-6) / 1e9
+        out[f"M={M}"] = {"us": round(us, 3), "GB/s": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4)}
+    return out
+
+
+def cpu_baseline(synth, budget_rows=32):
+    """The CPU oracle (single-threaded C, as it stands) on a bounded sample of
+    the same step: the first ``budget_rows`` rows of each W4A4 layer
+    (quantize + GEMM) and the M=1 GEMV."""
+    import oracle
+    ops, t_total = 0.0, 0.0
+    for name, prec, M, K, N, rank, seed in LAYERS:
+        w = synth.synthetic_w4a4_weights(seed, N, K, rank, prec)
+        rng = np.random.default_rng(seed + 1000)
+        x, _ = synth.draw_activations(rng, budget_rows, K, max(1, K // 100), 50.0)
+        xb = synth.to_bf16_bits(x)
+        p = oracle.INT4 if prec == "int4" else oracle.NVFP4
+        t0 = time.perf_counter()
+        ac, asc, t = oracle.quantize_act(p, xb, w["smooth"], w["lora_down"])
+        oracle.gemm_w4a4(p, ac, asc, w["wgt_codes"], w["wgt_scales"], t, w["lora_up"], None)
+        t_total += time.perf_counter() - t0
+        ops += 2.0 * budget_rows * N * K
+    name, K, N, seed = ADALN
+    aw = synth.synthetic_awq_weights(seed, N, K)
+    xg = synth.to_bf16_bits(np.random.default_rng(seed).standard_normal((1, K)))
+    t0 = time.perf_counter()
+    oracle.awq_gemv(xg, aw["wgt_codes"], aw["wgt_scales"], aw["wgt_zeros"], None)
+    t_total += time.perf_counter() - t0
+    return {"value": round(ops / t_total / 1e12, 6), "unit": "TOPS", "cores": 1, "kind": "oracle",
+            "sample": f"first {budget_rows} rows of each W4A4 layer (quantize + GEMM) and the M=1 GEMV; "
+                      f"{t_total:.1f} s on one host thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gemv-sweep", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build measures the single-GPU hot path "
+              f"(--gpus {args.gpus} was requested)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from bit_w4a4_quantized_svdq_amd import capi, synth
+    capi.lib()                                    # fail loudly if libsvdq.so is missing
+    torch.cuda.set_device(0)
+    print(f"[bench] building inputs", file=sys.stderr, flush=True)
+    layers, xs = build_inputs(torch, synth)
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        run_step(layers, xs)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    events = {}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        run_step(layers, xs, events)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    kernels = {}
+    for key, lst in events.items():
+        us = float(np.mean([s.elapsed_time(e) for s, e in lst])) * 1e3
+        kernels[key] = {"us": round(us, 3)}
+    w4a4_ops = 0.0
+    for name, prec, M, K, N, rank, seed in LAYERS:
+        ops = 2.0 * M * N * K
+        w4a4_ops += ops
+        g = kernels[f"{name}.gemm_w4a4"]
+        g["TOPS"] = round(ops / (g["us"] * 1e-6) / 1e12, 2)
+        peak = PEAK_INT8_TOPS if prec == "int4" else PEAK_BF16_TFLOPS
+        g["frac_peak"] = round(g["TOPS"] / peak, 4)
+        g["peak"] = "int8 5000 TOPS" if prec == "int4" else "bf16 2500 TFLOP/s (exact NVFP4 path)"
+        q = kernels[f"{name}.quantize_act"]
+        qb = algorithmic_bytes_quantize(M, K, rank, prec)
+        q["GB/s"] = round(qb / (q["us"] * 1e-6) / 1e9, 1)
+        q["frac_hbm"] = round(q["GB/s"] / PEAK_HBM_GBPS, 4)
+    name, K, N, seed = ADALN
+    a = kernels["adaln.awq_gemv"]
+    a["GB/s"] = round(algorithmic_bytes_gemv(1, N, K) / (a["us"] * 1e-6) / 1e9, 1)
+    a["frac_hbm"] = round(a["GB/s"] / PEAK_HBM_GBPS, 4)
+
+    value = w4a4_ops / (ms_per_step * 1e-3) / 1e12
+    dom = kernels["mlp_up.gemm_w4a4"]
+    roofline = {"bound": "mfma", "kernel": "svdq_gemm_w4a4 int4 (mlp_up 4096x3072->12288)",
+                "achieved": dom["TOPS"], "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
+                "frac": round(dom["TOPS"] / PEAK_INT8_TOPS, 4), "traffic": None,
+                "algorithmic_bytes": algorithmic_bytes_gemm(TOKENS, 4 * HIDDEN, HIDDEN, 32, "int4"),
+                "avg_launch_us": dom["us"]}
+
+    gemv = None if args.no_gemv_sweep else gemv_sweep(torch, synth)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(synth)
+
+    rec = {"metric": "W4A4 GEMM effective TOPS + % MFMA peak; W4A16 GEMV GB/s + % HBM peak",
+           "value": round(value, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+           "config": {"workload": "dit_block_1024px_quantized_linears", "tokens": TOKENS,
+                      "hidden": HIDDEN,
+                      "layers": {n: f"{p} {M}x{K}->{N} rank {r}" for n, p, M, K, N, r, _ in LAYERS} |
+                                {"adaln": f"awq_w4a16 1x{K}->{N} g64"}},
+           "roofline": roofline, "kernels": kernels, "gemv": gemv, "cpu_baseline": cpu}
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

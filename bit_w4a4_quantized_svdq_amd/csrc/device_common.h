@@ -1,0 +1,74 @@
+// device_common.h -- small gfx950 device helpers shared by the HIP kernels of
+// libsvdq (bf16 / E4M3 bit manipulation, MFMA operand vector types, wave
+// reductions).  Internal to the HIP library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace svdq {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN -> quiet NaN with the sign kept.
+// Overflow rounds to infinity and subnormals round on the same grid as
+// normals because bf16 shares binary32's exponent field.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x0040u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// Largest-magnitude reduction across lanes xor-distance `mask` (wave64).
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) {
+    return __shfl_xor(v, mask, kWave);
+}
+
+// E4M3 ("FN") encode of a non-negative finite fp32, round to nearest even,
+// saturating at 448 (the format has no infinity).
+__device__ __forceinline__ uint32_t e4m3_encode_nonneg(float v) {
+    if (!(v < 448.0f)) return 0x7Eu;                 // also catches +inf
+    if (v < 0.015625f) {                              // below 2^-6: spacing 2^-9
+        return (uint32_t)__builtin_rintf(v * 512.0f); // exact scaling; 8 -> 0x08
+    }
+    uint32_t u = __float_as_uint(v);
+    uint32_t e = (u >> 23) - 127u + 7u;               // biased E4M3 exponent, >= 1
+    uint32_t mant = u & 0x7FFFFFu;
+    uint32_t m = mant >> 20;
+    uint32_t rem = mant & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (m & 1u))) ++m;
+    if (m == 8u) { m = 0u; ++e; }
+    uint32_t code = (e << 3) | m;
+    return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// E4M3 ("FN") decode of a non-NaN code with the sign bit clear.
+__device__ __forceinline__ float e4m3_decode_nonneg(uint32_t c) {
+    uint32_t f = (c >> 3) & 15u, m = c & 7u;
+    if (f == 0u) return (float)m * 0.001953125f;      // m * 2^-9, exact
+    return __uint_as_float(((f + 120u) << 23) | (m << 20));
+}
+
+// E4M3 ("FN") decode with the sign bit.
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+    const float v = e4m3_decode_nonneg(c & 0x7Fu);
+    return (c & 0x80u) ? -v : v;
+}
+
+}  // namespace svdq

@@ -1,0 +1,282 @@
+// quantize_act.hip -- first fused step of the SVDQuant W4A4 layer on gfx950:
+// smoothing, 16-bit low-rank down-projection and per-group 4-bit
+// quantization in one pass over the activations (blog "Hugging Face
+// integrates Nunchaku 4-bit diffusion inference into Diffusers", section
+// "SVDQuant and the Nunchaku engine": the low-rank down-projection is fused
+// into the quantize kernel so the 16-bit branch adds no extra pass over x).
+//
+// Work split: a block owns 16 rows; its 8 waves take the K-groups of 64 in
+// turn (wave w: groups w, w+8, ...).  Lane l of a wave holds row l%16 and the
+// 8-element slices 8*(l/16) and 32+8*(l/16) of the group -- exactly the
+// A-operand layout of v_mfma_f32_16x16x32_bf16, so the smoothed bf16 values
+// feed the matrix core for x_hat . L1^T straight from registers, and the same
+// registers give the group absmax (a max over the 4 lanes of a row).  x is
+// read from HBM once.
+//
+// Exactness (codes and scales must equal the reference rule bit for bit):
+//  * x_hat = RNE_bf16(fl32(x / s)) is computed as RNE_bf16(x * fl32(1/s)).
+//    Both operands are bf16 (8-bit significands), so a quotient that is not
+//    itself a bf16 midpoint lies at least 2^-17 (relative) from every
+//    midpoint, far beyond the 2^-23 error of the product; a quotient can only
+//    BE a midpoint when the result is below 2^-126 (a bf16 subnormal), and
+//    such lanes (fp32-subnormal products) are recomputed with IEEE division,
+//    as are channels whose 1/s would leave fp32's normal range.
+//  * int4: q = RNE(x_hat / scale).  The quotient is formed as one Newton
+//    step on the reciprocal (qe = x*inv; r = fma(-qe, scale, x) is exact;
+//    q = fma(r, inv, qe)), which returns the exact value whenever the exact
+//    quotient is a half-integer, and is within 2^-20 otherwise, while a
+//    non-tie quotient of two bf16 values is at least 2^-10 from a
+//    half-integer.  Rounding is then the fp32 add of 2^23 + 16 (ties to
+//    even), whose low 4 mantissa bits are the two's-complement nibble.
+//  * NVFP4: the E2M1 code of v = x_hat/d is rint(min(2|v|, |v|+2, |v|/2+4))
+//    clamped to 7 -- the piecewise-linear map that sends the E2M1 grid
+//    {0,.5,1,1.5,2,3,4,6} onto 0..7, so round-to-nearest-even on it gives the
+//    nearest value with ties to the even code.  v comes from the same Newton
+//    step; ties are exact and non-ties stay 2^-11 (relative) away.
+#include "device_common.h"
+#include "launch.h"
+
+namespace svdq {
+
+constexpr int QA_ROWS = 16;          // rows per block (one MFMA row tile)
+constexpr int QA_WAVES = 8;          // waves per block
+constexpr int QA_CHUNK = 64;         // K-groups whose 1/s is staged in LDS at a time
+
+__device__ __forceinline__ float v4u_elem(const v4u &v, int e) {
+    // element e (0..7) of 8 packed bf16
+    uint32_t w = v[e >> 1];
+    return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+}
+
+template <int PREC, int RT>
+__global__ __launch_bounds__(QA_WAVES * 64)
+void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
+                         const uint16_t *__restrict__ smooth,
+                         const uint16_t *__restrict__ lora_down,
+                         uint8_t *__restrict__ codes, void *__restrict__ scales,
+                         float *__restrict__ lora_act)
+{
+    __shared__ float s_inv[QA_CHUNK * 64];
+    __shared__ float s_part[RT > 0 ? QA_WAVES * QA_ROWS * RT * 16 : 1];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int r = lane & 15;
+    const int kq = lane >> 4;
+    const int row = blockIdx.x * QA_ROWS + r;
+    const bool row_ok = row < M;
+    const int NG = K >> 6;
+    const size_t xrow_off = (size_t)(row_ok ? row : 0) * (size_t)K;
+
+    v4f acc[RT > 0 ? RT : 1];
+#pragma unroll
+    for (int t = 0; t < (RT > 0 ? RT : 1); ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    for (int c0 = 0; c0 < NG; c0 += QA_CHUNK) {
+        const int cg = min(QA_CHUNK, NG - c0);
+        int unsafe = 0;
+        for (int i = threadIdx.x; i < cg * 64; i += blockDim.x) {
+            float s = smooth ? bf16_to_f32(smooth[c0 * 64 + i]) : 1.0f;
+            float as = fabsf(s);
+            bool ok = (as >= 0x1p-64f) && (as <= 0x1p64f);
+            s_inv[i] = ok ? 1.0f / s : 0.0f;
+            unsafe |= ok ? 0 : 1;
+        }
+        unsafe = __syncthreads_or(unsafe);
+
+        for (int g = c0 + wave; g < c0 + cg; g += QA_WAVES) {
+            const int kbase = g * 64 + 8 * kq;
+            // ---- loads: x slices and the low-rank factor slices
+            v4u xr[2];
+            xr[0] = row_ok ? *(const v4u *)(x + xrow_off + kbase) : v4u{0u, 0u, 0u, 0u};
+            xr[1] = row_ok ? *(const v4u *)(x + xrow_off + kbase + 32) : v4u{0u, 0u, 0u, 0u};
+            v4u lr[RT > 0 ? RT : 1][2];
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+                const uint16_t *lp = lora_down + (size_t)(t * 16 + r) * (size_t)K + kbase;
+                lr[t][0] = *(const v4u *)lp;
+                lr[t][1] = *(const v4u *)(lp + 32);
+            }
+            const float *inv = s_inv + (g - c0) * 64 + 8 * kq;
+
+            // ---- smoothing: v = x * (1/s), then RNE to bf16
+            float xh[16];
+            int bad = 0;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                float xv = v4u_elem(xr[e >> 3], e & 7);
+                float v = xv * inv[(e >> 3) * 32 + (e & 7)];
+                bad |= __builtin_amdgcn_class(v, 0x90) ? 1 : 0;   // fp32 subnormal
+                xh[e] = v;
+            }
+            if (__builtin_expect(unsafe | __any(bad), 0)) {
+                // exact path: IEEE fp32 division
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    float xv = v4u_elem(xr[e >> 3], e & 7);
+                    int k = kbase + (e >> 3) * 32 + (e & 7);
+                    float s = smooth ? bf16_to_f32(smooth[k]) : 1.0f;
+                    xh[e] = xv / s;
+                }
+            }
+            v4u ah[2];
+            float amax = 0.0f;
+            float amax_j[2] = {0.0f, 0.0f};
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    uint32_t lo = f32_to_bf16_rne(xh[8 * j + 2 * p]);
+                    uint32_t hi = f32_to_bf16_rne(xh[8 * j + 2 * p + 1]);
+                    ah[j][p] = lo | (hi << 16);
+                    xh[8 * j + 2 * p] = __uint_as_float(lo << 16);
+                    xh[8 * j + 2 * p + 1] = __uint_as_float(hi << 16);
+                    amax_j[j] = fmaxf(amax_j[j], fmaxf(fabsf(xh[8 * j + 2 * p]),
+                                                       fabsf(xh[8 * j + 2 * p + 1])));
+                }
+            }
+
+            // ---- low-rank down-projection on the matrix cores
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(v8bf, ah[j]), __builtin_bit_cast(v8bf, lr[t][j]),
+                        acc[t], 0, 0, 0);
+                }
+            }
+
+            if constexpr (PREC == 0) {
+                // ---- int4, group 64: absmax over the row's 4 lanes
+                amax = fmaxf(amax_j[0], amax_j[1]);
+                amax = fmaxf(amax, shfl_xor_f(amax, 16));
+                amax = fmaxf(amax, shfl_xor_f(amax, 32));
+                const float s_f = amax / 7.0f;
+                const uint32_t sbits = f32_to_bf16_rne(s_f);
+                const float sb = __uint_as_float(sbits << 16);
+                uint32_t word[2] = {0u, 0u};
+                if (__builtin_expect(__any(sb < 0x1p-100f), 0)) {
+                    // tiny or zero scales: IEEE division (zero scale -> zero codes)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        float q = sb == 0.0f ? 0.0f
+                                             : __builtin_amdgcn_fmed3f(__builtin_rintf(xh[e] / sb), -8.0f, 7.0f);
+                        uint32_t nib = __float_as_uint(q + 8388624.0f) & 15u;
+                        word[e >> 3] |= nib << (4 * (e & 7));
+                    }
+                } else {
+                    const float inv_s = 1.0f / sb;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        float qe = xh[e] * inv_s;
+                        float rr = __builtin_fmaf(-qe, sb, xh[e]);
+                        float qc = __builtin_fmaf(rr, inv_s, qe);
+                        qc = __builtin_amdgcn_fmed3f(qc, -8.0f, 7.0f);
+                        uint32_t nib = __float_as_uint(qc + 8388624.0f) & 15u;   // + 2^23 + 16
+                        word[e >> 3] |= nib << (4 * (e & 7));
+                    }
+                }
+                if (row_ok) {
+                    uint8_t *cp = codes + (size_t)row * (size_t)(K >> 1) + g * 32 + 4 * kq;
+                    *(uint32_t *)cp = word[0];
+                    *(uint32_t *)(cp + 16) = word[1];
+                    if (kq == 0) ((uint16_t *)scales)[(size_t)row * NG + g] = (uint16_t)sbits;
+                }
+            } else {
+                // ---- NVFP4, group 16: lanes kq and kq^1 share a group within step j
+                uint32_t word[2] = {0u, 0u};
+                uint32_t sc[2];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    float a = fmaxf(amax_j[j], shfl_xor_f(amax_j[j], 16));
+                    const float s_f = a / 6.0f;
+                    const uint32_t se = e4m3_encode_nonneg(s_f);
+                    const float d = e4m3_decode_nonneg(se);
+                    sc[j] = se;
+                    if (d != 0.0f) {
+                        const float inv_d = 1.0f / d;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            float xv = xh[8 * j + e];
+                            float qe = xv * inv_d;
+                            float rr = __builtin_fmaf(-qe, d, xv);
+                            float v = fabsf(__builtin_fmaf(rr, inv_d, qe));
+                            float f = fminf(fminf(2.0f * v, v + 2.0f), __builtin_fmaf(v, 0.5f, 4.0f));
+                            f = fminf(f, 7.0f);
+                            uint32_t m = __float_as_uint(f + 8388608.0f) & 7u;      // + 2^23
+                            uint32_t sgn = (__float_as_uint(xv) >> 28) & 8u;
+                            word[j] |= (m | sgn) << (4 * e);
+                        }
+                    }
+                }
+                if (row_ok) {
+                    uint8_t *cp = codes + (size_t)row * (size_t)(K >> 1) + g * 32 + 4 * kq;
+                    *(uint32_t *)cp = word[0];
+                    *(uint32_t *)(cp + 16) = word[1];
+                    if ((kq & 1) == 0) {
+                        uint8_t *sp = (uint8_t *)scales + (size_t)row * (size_t)(K >> 4) + g * 4 + (kq >> 1);
+                        sp[0] = (uint8_t)sc[0];
+                        sp[2] = (uint8_t)sc[1];
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    if constexpr (RT > 0) {
+        // ---- reduce the low-rank partials of the 8 waves and write fp32
+        // MFMA 16x16 output layout: lane l holds column l%16, rows 4*(l/16)+i.
+        float *mine = s_part + wave * (QA_ROWS * RT * 16);
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                mine[(4 * kq + i) * (RT * 16) + t * 16 + r] = acc[t][i];
+        __syncthreads();
+        const int total = QA_ROWS * RT * 16;
+        for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
+            float s = 0.0f;
+#pragma unroll
+            for (int w = 0; w < QA_WAVES; ++w) s += s_part[w * total + idx];
+            const int rr = idx / (RT * 16);
+            const int orow = blockIdx.x * QA_ROWS + rr;
+            if (orow < M) lora_act[(size_t)orow * (RT * 16) + (idx % (RT * 16))] = s;
+        }
+    }
+}
+
+template <int PREC>
+static hipError_t launch_prec(int M, int K, int rank, const void *x, const void *smooth,
+                              const void *lora_down, void *codes, void *scales, float *lora_act,
+                              hipStream_t st)
+{
+    dim3 grid((M + QA_ROWS - 1) / QA_ROWS), block(QA_WAVES * 64);
+    const uint16_t *xp = (const uint16_t *)x, *sp = (const uint16_t *)smooth,
+                   *lp = (const uint16_t *)lora_down;
+    uint8_t *cp = (uint8_t *)codes;
+#define QA_CASE(RTV)                                                                            \
+    case RTV:                                                                                   \
+        hipLaunchKernelGGL((quantize_act_kernel<PREC, RTV>), grid, block, 0, st, M, K, xp, sp, lp, \
+                           cp, scales, lora_act);                                               \
+        break;
+    switch (rank / 16) {
+        QA_CASE(0) QA_CASE(1) QA_CASE(2) QA_CASE(3) QA_CASE(4)
+        QA_CASE(5) QA_CASE(6) QA_CASE(7) QA_CASE(8)
+        default: return hipErrorInvalidValue;
+    }
+#undef QA_CASE
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_act(int precision, int M, int K, int rank, const void *x,
+                               const void *smooth, const void *lora_down, void *act_codes,
+                               void *act_scales, float *lora_act, hipStream_t stream)
+{
+    if (precision == 0)
+        return launch_prec<0>(M, K, rank, x, smooth, lora_down, act_codes, act_scales, lora_act, stream);
+    return launch_prec<1>(M, K, rank, x, smooth, lora_down, act_codes, act_scales, lora_act, stream);
+}
+
+}  // namespace svdq

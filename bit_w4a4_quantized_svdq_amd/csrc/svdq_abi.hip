@@ -1,0 +1,189 @@
+// svdq_abi.hip -- the C ABI of libsvdq (declared in include/svdq.h): host-side
+// argument checks, a per-device architecture check, and dispatch to the
+// gfx950 kernels.  Every check runs before anything is enqueued.
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <cstdint>
+
+#include "../../include/svdq.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+svdq_status fail(svdq_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+constexpr int64_t kMaxMN = int64_t(1) << 24;
+constexpr int64_t kMaxK = int64_t(1) << 16;
+
+// 0 = unknown, 1 = gfx950, 2 = other; one slot per device ordinal.
+std::atomic<int> g_arch_ok[64];
+
+svdq_status check_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(SVDQ_ERR_HIP, "hipGetDevice failed");
+    if (dev < 0 || dev >= 64) return fail(SVDQ_ERR_UNSUPPORTED, "device ordinal %d out of range", dev);
+    int v = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+            return fail(SVDQ_ERR_HIP, "hipGetDeviceProperties failed");
+        v = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_arch_ok[dev].store(v, std::memory_order_relaxed);
+    }
+    if (v != 1) return fail(SVDQ_ERR_UNSUPPORTED, "libsvdq runs on gfx950 (MI355X) only");
+    return SVDQ_OK;
+}
+
+svdq_status check_shape(int64_t M, int64_t N, int64_t K, int32_t rank) {
+    if (M < 0 || N < 0 || M > kMaxMN || N > kMaxMN)
+        return fail(SVDQ_ERR_INVALID_ARG, "M and N must be in [0, 2^24] (M=%lld N=%lld)",
+                    (long long)M, (long long)N);
+    if (K <= 0 || K % 64 != 0 || K > kMaxK)
+        return fail(SVDQ_ERR_INVALID_ARG, "K must be a positive multiple of 64 up to 2^16 (K=%lld)",
+                    (long long)K);
+    if (rank < 0 || rank > 128 || rank % 16 != 0)
+        return fail(SVDQ_ERR_INVALID_ARG, "rank must be a multiple of 16 in [0, 128] (rank=%d)", rank);
+    return SVDQ_OK;
+}
+
+svdq_status check_ptr(const void *p, const char *name, bool may_be_null) {
+    if (!p) return may_be_null ? SVDQ_OK : fail(SVDQ_ERR_INVALID_ARG, "%s must not be NULL", name);
+    if (!aligned16(p)) return fail(SVDQ_ERR_INVALID_ARG, "%s must be 16-byte aligned", name);
+    return SVDQ_OK;
+}
+
+// The kernels use one-dimensional grids of (M/tm) * (N/tn) blocks.
+svdq_status check_grid(int64_t M, int64_t N, int64_t tm, int64_t tn) {
+    const int64_t blocks = ((M + tm - 1) / tm) * ((N + tn - 1) / tn);
+    if (blocks > INT32_MAX)
+        return fail(SVDQ_ERR_INVALID_ARG, "problem too large: %lld thread blocks", (long long)blocks);
+    return SVDQ_OK;
+}
+
+#define SVDQ_TRY(expr)                      \
+    do {                                    \
+        svdq_status _st = (expr);           \
+        if (_st != SVDQ_OK) return _st;     \
+    } while (0)
+
+svdq_status launched(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+    g_last_error[0] = '\0';
+    return SVDQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+svdq_status svdq_quantize_act(int32_t precision, int64_t M, int64_t K, int32_t rank,
+                              const void *x, const void *smooth, const void *lora_down,
+                              void *act_codes, void *act_scales, float *lora_act, void *stream)
+{
+    if (precision != SVDQ_INT4 && precision != SVDQ_NVFP4)
+        return fail(SVDQ_ERR_UNSUPPORTED, "precision must be SVDQ_INT4 or SVDQ_NVFP4 (got %d)", precision);
+    SVDQ_TRY(check_shape(M, 1, K, rank));
+    SVDQ_TRY(check_ptr(x, "x", false));
+    SVDQ_TRY(check_ptr(smooth, "smooth", true));
+    SVDQ_TRY(check_ptr(lora_down, "lora_down", rank == 0));
+    SVDQ_TRY(check_ptr(act_codes, "act_codes", false));
+    SVDQ_TRY(check_ptr(act_scales, "act_scales", false));
+    SVDQ_TRY(check_ptr(lora_act, "lora_act", rank == 0));
+    if (M == 0) return SVDQ_OK;
+    SVDQ_TRY(check_device());
+    return launched(svdq::launch_quantize_act(precision, (int)M, (int)K, rank, x, smooth, lora_down,
+                                              act_codes, act_scales, lora_act, (hipStream_t)stream),
+                    "svdq_quantize_act");
+}
+
+svdq_status svdq_gemm_w4a4(int32_t precision, int64_t M, int64_t N, int64_t K, int32_t rank,
+                           const void *act_codes, const void *act_scales, const void *wgt_codes,
+                           const void *wgt_scales, float alpha, const float *lora_act,
+                           const void *lora_up, const void *bias, void *out, void *stream)
+{
+    if (precision != SVDQ_INT4 && precision != SVDQ_NVFP4)
+        return fail(SVDQ_ERR_UNSUPPORTED, "precision must be SVDQ_INT4 or SVDQ_NVFP4 (got %d)", precision);
+    SVDQ_TRY(check_shape(M, N, K, rank));
+    SVDQ_TRY(check_ptr(act_codes, "act_codes", false));
+    SVDQ_TRY(check_ptr(act_scales, "act_scales", false));
+    SVDQ_TRY(check_ptr(wgt_codes, "wgt_codes", false));
+    SVDQ_TRY(check_ptr(wgt_scales, "wgt_scales", false));
+    SVDQ_TRY(check_ptr(lora_act, "lora_act", rank == 0));
+    SVDQ_TRY(check_ptr(lora_up, "lora_up", rank == 0));
+    SVDQ_TRY(check_ptr(bias, "bias", true));
+    SVDQ_TRY(check_ptr(out, "out", false));
+    if (M == 0 || N == 0) return SVDQ_OK;
+    SVDQ_TRY(check_grid(M, N, 128, 128));
+    SVDQ_TRY(check_device());
+    hipError_t e = precision == SVDQ_INT4
+        ? svdq::launch_gemm_w4a4_int4((int)M, (int)N, (int)K, rank, act_codes, act_scales, wgt_codes,
+                                      wgt_scales, alpha, lora_act, lora_up, bias, out, (hipStream_t)stream)
+        : svdq::launch_gemm_w4a4_nvfp4((int)M, (int)N, (int)K, rank, act_codes, act_scales, wgt_codes,
+                                       wgt_scales, alpha, lora_act, lora_up, bias, out, (hipStream_t)stream);
+    return launched(e, "svdq_gemm_w4a4");
+}
+
+svdq_status awq_gemv_w4a16(int64_t M, int64_t N, int64_t K, int32_t group_size, const void *x,
+                           const void *wgt_codes, const void *wgt_scales, const void *wgt_zeros,
+                           const void *bias, void *out, void *stream)
+{
+    if (group_size != 64)
+        return fail(SVDQ_ERR_UNSUPPORTED, "awq_w4a16 supports group_size 64 only (got %d)", group_size);
+    SVDQ_TRY(check_shape(M, N, K, 0));
+    SVDQ_TRY(check_ptr(x, "x", false));
+    SVDQ_TRY(check_ptr(wgt_codes, "wgt_codes", false));
+    SVDQ_TRY(check_ptr(wgt_scales, "wgt_scales", false));
+    SVDQ_TRY(check_ptr(wgt_zeros, "wgt_zeros", false));
+    SVDQ_TRY(check_ptr(bias, "bias", true));
+    SVDQ_TRY(check_ptr(out, "out", false));
+    if (M == 0 || N == 0) return SVDQ_OK;
+    SVDQ_TRY(check_grid(M, N, 64, 16));
+    SVDQ_TRY(check_device());
+    return launched(svdq::launch_awq_gemv((int)M, (int)N, (int)K, x, wgt_codes, wgt_scales, wgt_zeros,
+                                          bias, out, (hipStream_t)stream),
+                    "awq_gemv_w4a16");
+}
+
+svdq_status svdq_debug_group_sums(int64_t M, int64_t N, int64_t K, const void *act_codes,
+                                  const void *wgt_codes, int32_t *G, void *stream)
+{
+    SVDQ_TRY(check_shape(M, N, K, 0));
+    SVDQ_TRY(check_ptr(act_codes, "act_codes", false));
+    SVDQ_TRY(check_ptr(wgt_codes, "wgt_codes", false));
+    SVDQ_TRY(check_ptr(G, "G", false));
+    if (M == 0 || N == 0) return SVDQ_OK;
+    SVDQ_TRY(check_grid(M, N, 128, 128));
+    SVDQ_TRY(check_device());
+    return launched(svdq::launch_group_sums_int4((int)M, (int)N, (int)K, act_codes, wgt_codes, G,
+                                                 (hipStream_t)stream),
+                    "svdq_debug_group_sums");
+}
+
+const char *svdq_status_string(svdq_status s)
+{
+    switch (s) {
+        case SVDQ_OK: return "SVDQ_OK";
+        case SVDQ_ERR_INVALID_ARG: return "SVDQ_ERR_INVALID_ARG: an argument failed the host-side checks";
+        case SVDQ_ERR_UNSUPPORTED: return "SVDQ_ERR_UNSUPPORTED: precision, group size or device not supported";
+        case SVDQ_ERR_HIP: return "SVDQ_ERR_HIP: a HIP runtime call or kernel launch failed";
+    }
+    return "unknown svdq_status";
+}
+
+const char *svdq_last_error(void) { return g_last_error; }
+
+int32_t svdq_abi_version(void) { return 1; }
+
+}  // extern "C"

@@ -1,0 +1,148 @@
+/*
+ * svdq.h -- C ABI of the MI355X (gfx950) SVDQuant W4A4 / AWQ W4A16 layer
+ * library (libsvdq.so).
+ *
+ * The layer ("Nunchaku Lite" Diffusers docs, table "Supported quantization
+ * types"; blog "Hugging Face integrates Nunchaku 4-bit diffusion inference
+ * into Diffusers", section "SVDQuant and the Nunchaku engine"):
+ *   W4A4:  y = alpha * Q(x / s) . Q(R)^T  +  (x/s . L1^T) . L2^T  +  bias
+ *          where s migrates activation outliers into the weights, L1 / L2
+ *          are the 16-bit low-rank branch (rank r) and R is the 4-bit
+ *          residual.  The computation is two calls: svdq_quantize_act
+ *          (smooth, low-rank down-projection, group quantization: one pass
+ *          over x) and svdq_gemm_w4a4 (4-bit GEMM with the low-rank
+ *          up-projection and bias in its epilogue).
+ *   W4A16: y = x . dequant(q, s, z)^T + bias, int4 weights in groups of 64
+ *          with bf16 scales and zero points (awq_gemv_w4a16).
+ *
+ * Conventions for every call
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the
+ *    library never allocates, frees or synchronizes.  Work is enqueued on
+ *    `stream` (a hipStream_t; NULL is the null stream) and is asynchronous.
+ *  - Layouts are row-major and dense.  bf16 values are IEEE binary16-brain
+ *    bit patterns.  "codes" are packed 4-bit values: [rows, K/2] bytes,
+ *    element k of a row in byte k/2, even k in the low nibble.
+ *  - int4 codes are two's complement in [-8, 7]; int4 group size 64 with
+ *    bf16 scales.  NVFP4 codes are E2M1 (bit 3 = sign), group size 16 with
+ *    E4M3 ("FN" variant) scales.  AWQ codes are unsigned in [0, 15].
+ *  - Argument checks run on the host before anything is enqueued; a failed
+ *    check returns SVDQ_ERR_INVALID_ARG or SVDQ_ERR_UNSUPPORTED and
+ *    enqueues nothing.  Requirements: pointers 16-byte aligned; K a
+ *    positive multiple of 64; M >= 0 and N >= 0 (zero-sized calls return
+ *    SVDQ_OK and enqueue nothing); rank a multiple of 16 in [0, 128];
+ *    M, N <= 2^24 and K <= 2^16; the current device is gfx950.
+ *  - A launch failure returns SVDQ_ERR_HIP.  Faults inside a kernel surface
+ *    at the caller's next synchronization.  Outputs must not alias inputs.
+ *    Calls keep no state besides a per-device architecture check; they may
+ *    be made from several threads.  Non-finite inputs give unspecified
+ *    (but memory-safe) outputs.
+ */
+#ifndef SVDQ_H
+#define SVDQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum svdq_status {
+    SVDQ_OK = 0,
+    SVDQ_ERR_INVALID_ARG = 1,
+    SVDQ_ERR_UNSUPPORTED = 2,
+    SVDQ_ERR_HIP = 3
+} svdq_status;
+
+/* precision of the W4A4 layer ("Supported quantization types" table) */
+enum { SVDQ_INT4 = 0 /* group 64, bf16 scales */, SVDQ_NVFP4 = 1 /* group 16, E4M3 scales */ };
+
+/*
+ * svdq_quantize_act -- first step of the W4A4 layer: one pass over x.
+ *   x_hat[m,k]  = RNE_bf16( x[m,k] / smooth[k] )        (fp32 quotient)
+ *   lora_act    = x_hat . lora_down^T                    (fp32, [M, rank])
+ *   int4 : per row and group of 64, scale = RNE_bf16(absmax/7),
+ *          code = RNE(x_hat/scale) (ties to even), zero scale -> zero codes
+ *   nvfp4: per row and group of 16, scale = E4M3_RNE_sat(absmax/6),
+ *          code = E2M1_RNE_sat(x_hat/scale), zero scale -> zero codes
+ * The method fuses the low-rank down-projection into the quantize kernel
+ * ("SVDQuant and the Nunchaku engine").  Codes and scales are bit-exact
+ * against the rule above; lora_act is an fp32 sum in unspecified order.
+ *
+ *   precision  SVDQ_INT4 or SVDQ_NVFP4
+ *   x          bf16 [M, K]
+ *   smooth     bf16 [K] smoothing factors; NULL means 1
+ *   lora_down  bf16 [rank, K]; ignored (may be NULL) when rank == 0
+ *   act_codes  out: u8 [M, K/2]
+ *   act_scales out: int4 bf16 [M, K/64]; nvfp4 u8 (E4M3) [M, K/16]
+ *   lora_act   out: fp32 [M, rank]; ignored (may be NULL) when rank == 0
+ */
+svdq_status svdq_quantize_act(int32_t precision, int64_t M, int64_t K, int32_t rank,
+                              const void *x, const void *smooth, const void *lora_down,
+                              void *act_codes, void *act_scales, float *lora_act,
+                              void *stream);
+
+/*
+ * svdq_gemm_w4a4 -- second step: 4-bit GEMM with the fused low-rank
+ * up-projection and bias ("SVDQuant and the Nunchaku engine": the
+ * up-projection is fused into the 4-bit compute kernel).
+ *   y[m,n] = RNE_bf16( alpha * sum_k deq(act)[m,k] * deq(wgt)[n,k]
+ *                      + sum_j lora_act[m,j] * lora_up[n,j] + bias[n] )
+ * deq is code * group scale.  The sum is fp32 in unspecified order.
+ *
+ *   act_codes, act_scales  as written by svdq_quantize_act ([M, ...])
+ *   wgt_codes  u8 [N, K/2] (int4 or E2M1 codes of the 4-bit residual)
+ *   wgt_scales int4 bf16 [N, K/64]; nvfp4 u8 (E4M3) [N, K/16]
+ *   alpha      scale of the 4-bit term (per-tensor; 1.0f for int4)
+ *   lora_act   fp32 [M, rank]; lora_up bf16 [N, rank]; ignored when rank == 0
+ *   bias       bf16 [N] or NULL
+ *   out        out: bf16 [M, N]
+ */
+svdq_status svdq_gemm_w4a4(int32_t precision, int64_t M, int64_t N, int64_t K, int32_t rank,
+                           const void *act_codes, const void *act_scales,
+                           const void *wgt_codes, const void *wgt_scales, float alpha,
+                           const float *lora_act, const void *lora_up, const void *bias,
+                           void *out, void *stream);
+
+/*
+ * awq_gemv_w4a16 -- int4 weight-only layer with bf16 activations, for the
+ * memory-bound, precision-sensitive layers (adaptive-norm modulation;
+ * "Nunchaku Lite" docs, awq_w4a16 int4 group 64).
+ *   y[m,n] = RNE_bf16( sum_k x[m,k] * (q[n,k] - z[n,k/64]) * s[n,k/64] + bias[n] )
+ * The sum is fp32 in unspecified order.  Tuned for M <= 16; any M works.
+ *
+ *   group_size must be 64
+ *   x          bf16 [M, K]
+ *   wgt_codes  u8 [N, K/2], unsigned codes 0..15
+ *   wgt_scales bf16 [N, K/64]
+ *   wgt_zeros  bf16 [N, K/64], integer values 0..15
+ *   bias       bf16 [N] or NULL
+ *   out        out: bf16 [M, N]
+ */
+svdq_status awq_gemv_w4a16(int64_t M, int64_t N, int64_t K, int32_t group_size,
+                           const void *x, const void *wgt_codes, const void *wgt_scales,
+                           const void *wgt_zeros, const void *bias, void *out, void *stream);
+
+/*
+ * svdq_debug_group_sums -- test hook on the int4 GEMM's own device code
+ * path (operand unpacking and integer matrix-core products): writes the
+ * exact integer group sums
+ *   G[m,n,g] = sum_{k in group g} qa[m,k] * qw[n,k]      int32 [M, N, K/64]
+ * Not needed to run the layer.
+ */
+svdq_status svdq_debug_group_sums(int64_t M, int64_t N, int64_t K, const void *act_codes,
+                                  const void *wgt_codes, int32_t *G, void *stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char *svdq_status_string(svdq_status s);
+
+/* Text of the last argument-check failure on the calling thread ("" if none). */
+const char *svdq_last_error(void);
+
+/* ABI version of this header: 1. */
+int32_t svdq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVDQ_H */

@@ -1,0 +1,131 @@
+"""Helpers for the GPU parity tests: host<->device transfer of bf16 bit
+patterns, case builders (seeded inputs + the oracle's offline weight
+preparation), and the comparison rules.
+
+Pass bar (codes, scales and integer group sums bit-exact; bf16 outputs
+within 1e-2 relative Frobenius error and within 2 bf16 ulp for at least
+99.9% of elements) is the one stated for this layer; lora_act, an fp32
+intermediate summed in a different order on each side, is held to 1e-5
+relative Frobenius error."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from bit_w4a4_quantized_svdq_amd import synth
+
+DEV = "cuda"
+
+
+def announce(*parts):
+    """Name the case on stderr before a GPU step (bypasses pytest capture)."""
+    sys.__stderr__.write("[gpu case] " + " ".join(str(p) for p in parts) + "\n")
+    sys.__stderr__.flush()
+
+
+def to_dev(a, kind):
+    """numpy -> device tensor.  kind: 'bf16' (uint16 bits), 'u8', 'f32', 'i32'."""
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if kind == "bf16":
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(a).to(DEV)
+
+
+def to_host(t, kind):
+    t = t.detach().cpu().contiguous()
+    if kind == "bf16":
+        return t.view(torch.int16).numpy().view(np.uint16).copy()
+    return t.numpy().copy()
+
+
+def empty(shape, kind):
+    dt = {"bf16": torch.bfloat16, "u8": torch.uint8, "f32": torch.float32, "i32": torch.int32}[kind]
+    return torch.empty(shape, dtype=dt, device=DEV)
+
+
+def poison(t):
+    """Fill an output buffer with a NaN/0xFF pattern so unwritten elements show."""
+    t.view(torch.uint8).fill_(0xFF)
+    return t
+
+
+def ulp_dist(a, b):
+    def ordv(h):
+        h = np.asarray(h, np.int64)
+        return np.where(h & 0x8000, -(h & 0x7FFF), h)
+    return np.abs(ordv(a) - ordv(b))
+
+
+def bf16_f64(h):
+    return synth.bf16_bits_to_f32(h).astype(np.float64)
+
+
+def assert_bf16_close(got, ref, what=""):
+    """The output bar: rel. Frobenius <= 1e-2 and <= 2 ulp for >= 99.9%."""
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    g, r = bf16_f64(got), bf16_f64(ref)
+    assert np.isfinite(g).all(), f"{what}: non-finite output"
+    d = ulp_dist(got, ref)
+    frob = np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-300)
+    within = (d <= 2).mean()
+    assert frob <= 1e-2 and within >= 0.999, \
+        f"{what}: rel_frob={frob:.3e} within2ulp={within:.5f} max_ulp={d.max()}"
+    return {"rel_frob": frob, "within_2ulp": within, "max_ulp": int(d.max())}
+
+
+def assert_f32_close(got, ref, tol=1e-5, what=""):
+    frob = np.linalg.norm(got.astype(np.float64) - ref) / max(np.linalg.norm(ref), 1e-300)
+    assert frob <= tol, f"{what}: rel_frob={frob:.3e}"
+
+
+def svdq_case(cfg: synth.LinearConfig, with_bias=False, M=None, x=None):
+    """Seeded layer of a config, prepared offline by the oracle."""
+    prec = oracle.INT4 if cfg.precision == "int4" else oracle.NVFP4
+    case = synth.linear_case(cfg, M=M, with_bias=with_bias)
+    if x is not None:
+        case["x"] = x
+    prep = oracle.prepare_svdq_weight(prec, case["x"], case["W"], cfg.rank)
+    case.update(prep)
+    case["prec"] = prec
+    return case
+
+
+def gpu_quantize(prec, x, smooth, lora_down, K):
+    from bit_w4a4_quantized_svdq_amd import capi
+    M = x.shape[0]
+    rank = 0 if lora_down is None else lora_down.shape[0]
+    codes = poison(empty((M, K // 2), "u8"))
+    scales = poison(empty((M, K // 64), "bf16") if prec == 0 else empty((M, K // 16), "u8"))
+    lact = poison(empty((M, rank), "f32")) if rank else None
+    capi.svdq_quantize_act(prec, to_dev(x, "bf16"), to_dev(smooth, "bf16"), to_dev(lora_down, "bf16"),
+                           codes, scales, lact)
+    torch.cuda.synchronize()
+    return (to_host(codes, "u8"), to_host(scales, "bf16" if prec == 0 else "u8"),
+            None if lact is None else to_host(lact, "f32"))
+
+
+def gpu_gemm(prec, act_codes, act_scales, wgt_codes, wgt_scales, lora_act, lora_up, bias, alpha=1.0):
+    from bit_w4a4_quantized_svdq_amd import capi
+    M, N = act_codes.shape[0], wgt_codes.shape[0]
+    out = poison(empty((M, N), "bf16"))
+    skind = "bf16" if prec == 0 else "u8"
+    capi.svdq_gemm_w4a4(prec, to_dev(act_codes, "u8"), to_dev(act_scales, skind), to_dev(wgt_codes, "u8"),
+                        to_dev(wgt_scales, skind), alpha, to_dev(lora_act, "f32"), to_dev(lora_up, "bf16"),
+                        to_dev(bias, "bf16"), out)
+    torch.cuda.synchronize()
+    return to_host(out, "bf16")
+
+
+def gpu_gemv(x, codes, scales, zeros, bias):
+    from bit_w4a4_quantized_svdq_amd import capi
+    M, N = x.shape[0], codes.shape[0]
+    out = poison(empty((M, N), "bf16"))
+    capi.awq_gemv_w4a16(to_dev(x, "bf16"), to_dev(codes, "u8"), to_dev(scales, "bf16"),
+                        to_dev(zeros, "bf16"), to_dev(bias, "bf16"), out)
+    torch.cuda.synchronize()
+    return to_host(out, "bf16")

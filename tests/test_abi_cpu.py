@@ -1,0 +1,127 @@
+"""C ABI checks that need no GPU: libsvdq.so loads, exports every function
+declared in include/svdq.h, and rejects bad arguments on the host before any
+HIP call (so these run on a CPU-only machine)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_w4a4_quantized_svdq_amd import capi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "svdq.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(capi.LIB_PATH),
+                                reason="libsvdq.so not built (python -m bit_w4a4_quantized_svdq_amd.build)")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for f in ("svdq_quantize_act", "svdq_gemm_w4a4", "awq_gemv_w4a16"):
+        assert f in names
+    assert set(names) == set(capi.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(capi.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert capi.svdq_abi_version() == 1
+    for s in range(4):
+        assert capi.svdq_status_string(s).startswith(("SVDQ_OK", "SVDQ_ERR"))
+    assert "unknown" in capi.svdq_status_string(99)
+
+
+A = 1 << 20          # a 16-byte aligned fake device address (never dereferenced)
+MIS = A + 2          # misaligned
+
+
+def qa(prec=0, M=4, K=64, rank=16, x=A, smooth=A, down=A, codes=A, scales=A, lact=A):
+    return capi.lib().svdq_quantize_act(prec, M, K, rank, x, smooth, down, codes, scales, lact, None)
+
+
+def gm(prec=0, M=4, N=64, K=64, rank=16, ac=A, asc=A, wc=A, wsc=A, lact=A, up=A, bias=A, out=A):
+    return capi.lib().svdq_gemm_w4a4(prec, M, N, K, rank, ac, asc, wc, wsc, 1.0, lact, up, bias, out,
+                                     None)
+
+
+def gv(M=1, N=64, K=64, gs=64, x=A, c=A, s=A, z=A, bias=A, out=A):
+    return capi.lib().awq_gemv_w4a16(M, N, K, gs, x, c, s, z, bias, out, None)
+
+
+INV, UNS = capi.SVDQ_ERR_INVALID_ARG, capi.SVDQ_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,want,msg", [
+    (dict(prec=2), UNS, "precision"),
+    (dict(K=0), INV, "K must"), (dict(K=96), INV, "K must"), (dict(K=1 << 17), INV, "K must"),
+    (dict(M=-1), INV, "M and N"), (dict(M=(1 << 24) + 1), INV, "M and N"),
+    (dict(rank=8), INV, "rank"), (dict(rank=144), INV, "rank"), (dict(rank=-16), INV, "rank"),
+    (dict(x=None), INV, "x must not"), (dict(codes=None), INV, "act_codes"),
+    (dict(scales=None), INV, "act_scales"), (dict(down=None), INV, "lora_down"),
+    (dict(lact=None), INV, "lora_act"), (dict(x=MIS), INV, "aligned"),
+    (dict(smooth=MIS), INV, "smooth"),
+])
+def test_quantize_act_rejects(kw, want, msg):
+    assert qa(**kw) == want
+    assert msg in capi.svdq_last_error()
+
+
+def test_quantize_act_optional_pointers_and_empty():
+    # rank 0: lora pointers may be NULL; M = 0 is a no-op that succeeds
+    assert qa(M=0, rank=0, down=None, lact=None, smooth=None) == capi.SVDQ_OK
+
+
+@pytest.mark.parametrize("kw,want,msg", [
+    (dict(prec=-1), UNS, "precision"), (dict(N=-5), INV, "M and N"), (dict(K=32), INV, "K must"),
+    (dict(rank=20), INV, "rank"), (dict(ac=None), INV, "act_codes"), (dict(wc=None), INV, "wgt_codes"),
+    (dict(wsc=None), INV, "wgt_scales"), (dict(up=None), INV, "lora_up"), (dict(out=None), INV, "out"),
+    (dict(bias=MIS), INV, "bias"), (dict(wc=MIS), INV, "wgt_codes"),
+])
+def test_gemm_rejects(kw, want, msg):
+    assert gm(**kw) == want
+    assert msg in capi.svdq_last_error()
+
+
+def test_gemm_empty_is_noop():
+    assert gm(M=0) == capi.SVDQ_OK
+    assert gm(N=0, rank=0, lact=None, up=None, bias=None) == capi.SVDQ_OK
+
+
+@pytest.mark.parametrize("kw,want,msg", [
+    (dict(gs=128), UNS, "group_size"), (dict(gs=16), UNS, "group_size"), (dict(K=100), INV, "K must"),
+    (dict(x=None), INV, "x must not"), (dict(z=None), INV, "wgt_zeros"), (dict(s=MIS), INV, "wgt_scales"),
+])
+def test_gemv_rejects(kw, want, msg):
+    assert gv(**kw) == want
+    assert msg in capi.svdq_last_error()
+
+
+def test_gemv_empty_is_noop():
+    assert gv(M=0, bias=None) == capi.SVDQ_OK
+
+
+def test_group_sums_rejects():
+    L = capi.lib()
+    assert L.svdq_debug_group_sums(4, 4, 100, A, A, A, None) == INV
+    assert L.svdq_debug_group_sums(4, 4, 64, A, A, None, None) == INV
+    assert L.svdq_debug_group_sums(0, 4, 64, A, A, A, None) == capi.SVDQ_OK
+
+
+def test_python_binding_raises_on_bad_status():
+    import numpy as np
+    import torch
+    x = torch.zeros((4, 96), dtype=torch.bfloat16)       # K = 96: not a multiple of 64
+    codes = torch.zeros((4, 48), dtype=torch.uint8)
+    scales = torch.zeros((4, 2), dtype=torch.bfloat16)
+    with pytest.raises(capi.SvdqError) as ei:
+        capi.svdq_quantize_act(0, x, None, None, codes, scales, None, stream=0)
+    assert ei.value.status == INV
+    assert "K must" in str(ei.value)

@@ -1,0 +1,77 @@
+"""Parity at the full DiT-shaped sizes (the configurations the benchmark
+times, same kernels and launch shapes): codes and scales over the whole
+tensor, lora_act over the whole tensor, GEMM outputs on sampled rows that
+the oracle computes one by one, and the weight-only GEMV in full.
+
+Workloads (seeded, synthetic; weights prepared offline by the oracle):
+  QKV    M=4096 K=3072 N=9216  int4 g64 rank 32
+  MLP    up 4096x3072->12288, down 4096x12288->3072 (GELU-tanh input), int4, rank 32
+  NVFP4  attention out 4096x3072->3072, rank 32
+  AWQ    adaptive-norm modulation, M in {1,2,8}, K=3072, N=18432"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_w4a4_quantized_svdq_amd import synth
+from tests.gpu_helpers import announce, assert_bf16_close, assert_f32_close, gpu_gemm, gpu_gemv, gpu_quantize, svdq_case
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+SAMPLE_ROWS = 24
+
+
+def _rows(M, seed):
+    rng = np.random.default_rng(seed)
+    extra = rng.choice(np.arange(2, M - 1), SAMPLE_ROWS - 3, replace=False)
+    return np.concatenate([[0, 1, M - 1], np.sort(extra)])
+
+
+def _layer_parity(cfg, case, prec):
+    K = cfg.K
+    announce("fullsize quantize_act", cfg.name)
+    gc, gs, gt = gpu_quantize(prec, case["x"], case["smooth"], case["lora_down"], K)
+    oc, os_, ot = oracle.quantize_act(prec, case["x"], case["smooth"], case["lora_down"])
+    assert np.array_equal(gs, os_), f"{cfg.name}: scales differ ({int((gs != os_).sum())} elements)"
+    assert np.array_equal(gc, oc), f"{cfg.name}: codes differ ({int((gc != oc).sum())} bytes)"
+    assert_f32_close(gt, ot, 1e-5, cfg.name + " lora_act")
+    announce("fullsize gemm_w4a4", cfg.name)
+    y = gpu_gemm(prec, oc, os_, case["wgt_codes"], case["wgt_scales"], ot, case["lora_up"], case["bias"])
+    rows = _rows(cfg.M, cfg.seed)
+    ref = oracle.gemm_w4a4(prec, oc, os_, case["wgt_codes"], case["wgt_scales"], ot, case["lora_up"],
+                           case["bias"], rows=rows)
+    stats = assert_bf16_close(y[rows], ref, cfg.name)
+    assert np.isfinite(synth.bf16_bits_to_f32(y)).all()
+    return stats
+
+
+def test_fullsize_qkv_int4():
+    _layer_parity(synth.QKV, svdq_case(synth.QKV), oracle.INT4)
+
+
+def test_fullsize_mlp_up_int4():
+    _layer_parity(synth.MLP_UP, svdq_case(synth.MLP_UP), oracle.INT4)
+
+
+def test_fullsize_mlp_down_int4():
+    h = synth.gelu_activations(synth.MLP_UP, synth.MLP_DOWN)
+    case = {"x": h["x"], "W": h["W"], "bias": None}
+    case.update(oracle.prepare_svdq_weight(oracle.INT4, h["x"], h["W"], synth.MLP_DOWN.rank))
+    _layer_parity(synth.MLP_DOWN, case, oracle.INT4)
+
+
+def test_fullsize_attn_out_nvfp4():
+    _layer_parity(synth.ATTN_OUT_NVFP4, svdq_case(synth.ATTN_OUT_NVFP4), oracle.NVFP4)
+
+
+@pytest.mark.parametrize("M", [1, 2, 8])
+def test_fullsize_adaln_awq(M):
+    cfg = synth.ADALN_AWQ
+    case = synth.linear_case(cfg, M=8)
+    codes, scales, zeros = oracle.awq_quantize_weight(case["W"])
+    x = case["x"][:M]
+    announce("fullsize awq_gemv", cfg.name, "M", M)
+    y = gpu_gemv(x, codes, scales, zeros, None)
+    ref = oracle.awq_gemv(x, codes, scales, zeros, None)
+    assert_bf16_close(y, ref, f"{cfg.name} M={M}")

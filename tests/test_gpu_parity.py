@@ -1,0 +1,232 @@
+"""GPU parity of the HIP path against the CPU oracle, element by element, at
+sizes the oracle finishes in seconds (several tiles plus ragged tails) and
+at the degenerate and edge cases of the method.  All calls go through the
+C ABI (libsvdq.so) via its Python binding."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_w4a4_quantized_svdq_amd import capi, synth
+from tests.gpu_helpers import (announce, assert_bf16_close, assert_f32_close, gpu_gemm, gpu_gemv,
+                               gpu_quantize, svdq_case, to_dev, to_host, empty, poison)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def _heavy_x(rng, M, K, n_out=None, scale=50.0):
+    x = rng.standard_normal((M, K))
+    n_out = max(1, K // 100) if n_out is None else n_out
+    x[:, rng.choice(K, n_out, replace=False)] *= scale
+    return synth.to_bf16_bits(x)
+
+
+def _check_quantize(prec, x, smooth, down, what):
+    K = x.shape[1]
+    announce("quantize_act", what, "prec", prec, "shape", x.shape, "rank", 0 if down is None else down.shape[0])
+    gc, gs, gt = gpu_quantize(prec, x, smooth, down, K)
+    oc, os_, ot = oracle.quantize_act(prec, x, smooth, down)
+    assert np.array_equal(gs, os_), f"{what}: scales differ at {np.argwhere(gs != os_)[:5].tolist()}"
+    assert np.array_equal(gc, oc), f"{what}: codes differ at {np.argwhere(gc != oc)[:5].tolist()}"
+    if down is not None:
+        assert_f32_close(gt, ot, 1e-5, what)
+    return oc, os_, ot
+
+
+# ------------------------------------------------------------ quantize_act
+
+@pytest.mark.parametrize("prec", [0, 1])
+def test_quantize_act_tiny_config(prec):
+    cfg = synth.TINY if prec == 0 else synth.LinearConfig("tiny_nvfp4", 64, 256, 256, 16, "nvfp4", 0, 4, 30.0)
+    c = svdq_case(cfg)
+    _check_quantize(prec, c["x"], c["smooth"], c["lora_down"], cfg.name)
+
+
+@pytest.mark.parametrize("prec,M,K,rank", [
+    (0, 1, 64, 0), (0, 17, 192, 48), (0, 200, 512, 32), (0, 33, 4160, 16), (0, 40, 1024, 128),
+    (1, 1, 64, 0), (1, 17, 192, 16), (1, 200, 512, 32), (1, 33, 4160, 128), (1, 40, 1024, 64),
+])
+def test_quantize_act_shapes(prec, M, K, rank):
+    rng = np.random.default_rng(1000 + 7 * M + K + rank + prec)
+    x = _heavy_x(rng, M, K)
+    smooth = synth.to_bf16_bits(np.exp(rng.standard_normal(K) * 0.7))
+    down = synth.to_bf16_bits(rng.standard_normal((rank, K)) * 0.05) if rank else None
+    _check_quantize(prec, x, smooth, down, f"M{M}_K{K}_r{rank}")
+
+
+def _edge_rows(K):
+    """Rows that hit the method's degenerate and tie cases (bf16 bits)."""
+    rows = []
+    f = np.zeros(K)
+    rows.append(f.copy())                                   # all-zero row
+    rows.append(np.full(K, -1.75))                          # constant groups
+    t = np.tile(np.arange(-13, 14) / 2.0, K)[:K]            # int4 ties: absmax 7 -> scale 1
+    t[::64] = 7.0
+    rows.append(t)
+    e = np.tile([6.0, -0.25, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -5.0, -0.75, 0.0, -0.0, 3.0, 1.5, -6.0],
+                K // 16)                                    # nvfp4 ties: absmax 6 -> scale 1
+    rows.append(e)
+    rows.append(np.tile(np.arange(1, 17), K // 16) * 2.0 ** -133)   # bf16 subnormal inputs
+    rows.append(np.tile([5000.0, -3000.0, 1.0, 0.5], K // 4))       # E4M3 saturation (absmax/6 > 448)
+    rows.append(np.tile([1e-30, -3e-31, 2e-32, 0.0], K // 4))       # tiny groups
+    rows.append(np.linspace(-3.0e4, 3.0e4, K))
+    x = synth.to_bf16_bits(np.stack(rows))
+    x[1, 5] = 0x8000                                        # a -0
+    return x
+
+
+@pytest.mark.parametrize("prec", [0, 1])
+@pytest.mark.parametrize("smooth_kind", ["none", "ones", "twos_threes", "tiny_channels", "random"])
+def test_quantize_act_edge_values(prec, smooth_kind):
+    K = 256
+    x = _edge_rows(K)
+    rng = np.random.default_rng(77)
+    if smooth_kind == "none":
+        smooth = None
+    elif smooth_kind == "ones":
+        smooth = np.full(K, 0x3F80, np.uint16)
+    elif smooth_kind == "twos_threes":                      # halves subnormal inputs -> exact bf16 ties
+        smooth = synth.to_bf16_bits(np.where(np.arange(K) % 2 == 0, 2.0, 3.0))
+    elif smooth_kind == "tiny_channels":                    # 1/s outside fp32's normal range -> IEEE path
+        s = np.exp(rng.standard_normal(K) * 0.3)
+        s[::37] = 2.0 ** -70
+        smooth = synth.to_bf16_bits(s)
+        x = x.copy()
+        x[:, ::37] = synth.to_bf16_bits(np.full((x.shape[0], len(range(0, K, 37))), 2.0 ** -80))
+    else:
+        smooth = synth.to_bf16_bits(np.exp(rng.standard_normal(K)))
+    down = synth.to_bf16_bits(rng.standard_normal((16, K)) * 0.05)
+    _check_quantize(prec, x, smooth, down, f"edge_{smooth_kind}")
+
+
+def test_quantize_act_ragged_large_M():
+    rng = np.random.default_rng(5)
+    x = _heavy_x(rng, 4095, 256)
+    _check_quantize(0, x, None, synth.to_bf16_bits(rng.standard_normal((32, 256)) * 0.05), "M4095")
+
+
+# ------------------------------------------------------------------ GEMM
+
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_gemm_int4_tiny_config(with_bias):
+    cfg = synth.TINY
+    c = svdq_case(cfg, with_bias=with_bias)
+    ac, asc, t = oracle.quantize_act(0, c["x"], c["smooth"], c["lora_down"])
+    announce("gemm_w4a4 int4", cfg.name, "bias", with_bias)
+    y = gpu_gemm(0, ac, asc, c["wgt_codes"], c["wgt_scales"], t, c["lora_up"], c["bias"])
+    ref = oracle.gemm_w4a4(0, ac, asc, c["wgt_codes"], c["wgt_scales"], t, c["lora_up"], c["bias"])
+    assert_bf16_close(y, ref, cfg.name)
+
+
+def _random_gemm_case(prec, M, N, K, rank, with_bias, seed):
+    rng = np.random.default_rng(seed)
+    x = _heavy_x(rng, M, K)
+    smooth = synth.to_bf16_bits(np.exp(rng.standard_normal(K) * 0.5))
+    w = synth.synthetic_w4a4_weights(seed + 1, N, K, rank, "int4" if prec == 0 else "nvfp4")
+    ac, asc, t = oracle.quantize_act(prec, x, smooth, w["lora_down"])
+    bias = synth.to_bf16_bits(rng.standard_normal(N)) if with_bias else None
+    return ac, asc, t, w, bias
+
+
+@pytest.mark.parametrize("prec,M,N,K,rank,with_bias,alpha", [
+    (0, 200, 320, 512, 32, True, 1.0), (0, 1, 64, 64, 0, False, 1.0), (0, 130, 96, 4160, 16, True, 1.0),
+    (0, 257, 129, 192, 128, False, 0.5), (0, 64, 1000, 640, 48, True, 1.0),
+    (1, 200, 320, 512, 32, True, 1.0), (1, 1, 64, 64, 0, False, 1.0), (1, 130, 96, 4160, 16, True, 0.5),
+    (1, 257, 129, 192, 128, False, 2.0),
+])
+def test_gemm_shapes(prec, M, N, K, rank, with_bias, alpha):
+    ac, asc, t, w, bias = _random_gemm_case(prec, M, N, K, rank, with_bias, 2000 + M + N + K + prec)
+    announce("gemm_w4a4", "prec", prec, "M,N,K,r", M, N, K, rank, "alpha", alpha)
+    y = gpu_gemm(prec, ac, asc, w["wgt_codes"], w["wgt_scales"], t, w["lora_up"], bias, alpha)
+    ref = oracle.gemm_w4a4(prec, ac, asc, w["wgt_codes"], w["wgt_scales"], t, w["lora_up"], bias, alpha=alpha)
+    assert_bf16_close(y, ref, f"gemm p{prec} {M}x{N}x{K} r{rank}")
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 64, 64), (200, 320, 512), (33, 130, 4160), (1, 1, 128)])
+def test_debug_group_sums_exact(M, N, K):
+    rng = np.random.default_rng(3000 + M + N + K)
+    qa = rng.integers(-8, 8, (M, K))                        # includes foreign -8 codes
+    qw = rng.integers(-8, 8, (N, K))
+    qa[0, :64] = -8
+    qw[0, :64] = -8                                          # extreme group: 64 * 64 = 4096
+    ac, wc = synth.pack_nibbles(qa), synth.pack_nibbles(qw)
+    announce("debug_group_sums", M, N, K)
+    G = poison(empty((M, N, K // 64), "i32"))
+    capi.svdq_debug_group_sums(to_dev(ac, "u8"), to_dev(wc, "u8"), G)
+    torch.cuda.synchronize()
+    got = to_host(G, "i32")
+    ref = oracle.group_sums_int4(ac, wc, K)
+    assert np.array_equal(got, ref), f"group sums differ at {np.argwhere(got != ref)[:5].tolist()}"
+
+
+def test_zero_residual_layer_on_gpu():
+    """Weight == its low-rank branch: the 4-bit term vanishes and the GPU
+    output is the fp32 low-rank product plus bias."""
+    rng = np.random.default_rng(41)
+    M, N, K, r = 96, 192, 256, 16
+    x = synth.to_bf16_bits(rng.standard_normal((M, K)))
+    up = synth.to_bf16_bits(rng.standard_normal((N, r)) * 0.3)
+    down = synth.to_bf16_bits(rng.standard_normal((r, K)) * 0.3)
+    bias = synth.to_bf16_bits(rng.standard_normal(N))
+    zc = np.zeros((N, K // 2), np.uint8)
+    zs = np.zeros((N, K // 64), np.uint16)
+    announce("zero residual layer")
+    gc, gs, gt = gpu_quantize(0, x, None, down, K)
+    y = gpu_gemm(0, gc, gs, zc, zs, gt, up, bias)
+    ref_t = (synth.bf16_bits_to_f32(x).astype(np.float64) @ synth.bf16_bits_to_f32(down).astype(np.float64).T)
+    ref = oracle.f64_to_bf16(ref_t @ synth.bf16_bits_to_f32(up).astype(np.float64).T +
+                             synth.bf16_bits_to_f32(bias).astype(np.float64)[None, :])
+    assert_bf16_close(y, ref, "zero residual")
+
+
+def test_layer_end_to_end_and_determinism():
+    """GPU quantize -> GPU GEMM through the layer object equals the oracle's
+    chain within the bar, and two runs give identical bits."""
+    from bit_w4a4_quantized_svdq_amd.layer import SVDQW4A4Linear
+    cfg = synth.TINY
+    c = svdq_case(cfg, with_bias=True)
+    layer = SVDQW4A4Linear("int4", c["wgt_codes"], c["wgt_scales"], c["lora_down"], c["lora_up"],
+                           c["smooth"], c["bias"])
+    xd = to_dev(c["x"], "bf16")
+    announce("layer end to end", cfg.name)
+    y1 = to_host(layer(xd).clone(), "bf16")
+    y2 = to_host(layer(xd).clone(), "bf16")
+    torch.cuda.synchronize()
+    assert np.array_equal(y1, y2)
+    ac, asc, t = oracle.quantize_act(0, c["x"], c["smooth"], c["lora_down"])
+    ref = oracle.gemm_w4a4(0, ac, asc, c["wgt_codes"], c["wgt_scales"], t, c["lora_up"], c["bias"])
+    assert_bf16_close(y1, ref, "layer")
+
+
+# ------------------------------------------------------------------ GEMV
+
+@pytest.mark.parametrize("M,N,K,with_bias", [
+    (1, 1024, 3072, False), (2, 512, 3072, True), (8, 256, 3072, False), (17, 100, 128, True),
+    (70, 96, 64, True), (3, 5, 64, False), (16, 48, 4160, True),
+])
+def test_awq_gemv_shapes(M, N, K, with_bias):
+    rng = np.random.default_rng(4000 + M + N + K)
+    x = synth.to_bf16_bits(rng.standard_normal((M, K)))
+    W = synth.to_bf16_bits(rng.standard_normal((N, K)) * 0.02)
+    codes, scales, zeros = oracle.awq_quantize_weight(W)
+    bias = synth.to_bf16_bits(rng.standard_normal(N)) if with_bias else None
+    announce("awq_gemv", M, N, K, "bias", with_bias)
+    y = gpu_gemv(x, codes, scales, zeros, bias)
+    ref = oracle.awq_gemv(x, codes, scales, zeros, bias)
+    assert_bf16_close(y, ref, f"gemv {M}x{N}x{K}")
+
+
+def test_awq_gemv_extreme_codes():
+    """Codes 0 and 15 with zero points 0 and 15 (the (q - z) range ends)."""
+    rng = np.random.default_rng(43)
+    M, N, K = 4, 64, 256
+    x = synth.to_bf16_bits(rng.standard_normal((M, K)))
+    q = np.where(rng.random((N, K)) < 0.5, 0, 15)
+    codes = synth.pack_nibbles(q)
+    scales = synth.to_bf16_bits(rng.uniform(0.001, 0.01, (N, K // 64)))
+    zeros = synth.to_bf16_bits(np.where(rng.random((N, K // 64)) < 0.5, 0.0, 15.0))
+    announce("awq_gemv extreme codes")
+    y = gpu_gemv(x, codes, scales, zeros, None)
+    ref = oracle.awq_gemv(x, codes, scales, zeros, None)
+    assert_bf16_close(y, ref, "gemv extremes")
