@@ -7,30 +7,89 @@
 // (blog "Hugging Face integrates Nunchaku 4-bit diffusion inference into
 // Diffusers", "SVDQuant and the Nunchaku engine").
 //
-// Operands.  CDNA4 has no int4 matrix instruction, so a packed nibble is
-// placed in the high half of a byte: (d << 4) & 0xF0F0F0F0 gives the even
-// nibbles of a dword as int8 = 16*code, d & 0xF0F0F0F0 the odd ones.  Two
-// bit operations turn 8 codes into 8 int8 lanes, and v_mfma_i32_32x32x32_i8
-// then returns 256 * G exactly (|256 G| <= 2^20).  A dot product does not
-// depend on the order of k as long as both operands use the same order, so
-// the even/odd split is applied to A and B alike.
+// Integer products.  CDNA4 has no int4 matrix instruction, so a packed
+// nibble is placed in the high half of a byte: (d << 4) & 0xF0F0F0F0 gives
+// the even nibbles of a dword as int8 = 16*code, d & 0xF0F0F0F0 the odd
+// ones.  Two bit operations turn 8 codes into 8 int8 lanes, and two
+// v_mfma_i32_32x32x32_i8 return 256 * G_g exactly (|256 G| <= 2^20).  A dot
+// product does not depend on the order of k as long as both operands use the
+// same order, so the even/odd split is applied to A and B alike.
 //
-// Tiling: 256 threads, 128x128 output tile, 4 waves of 64x64 (2x2 tiles of
-// 32x32).  One K-step is one group of 64.  Fragments stream from global
-// memory straight into registers, one group ahead.  Group scales are staged
-// in LDS as fp32, 8 groups at a time, with 2^-8 * alpha folded into the
-// weight scale.  Per group and output: one cvt, one mul, one fma (VALU).
+// Group scales.  Every output needs acc += G_g * (sx_g * sw_g) once per
+// group, and on CDNA4 the vector ALU is the scarce unit (one 32x32 tile-group
+// of int8 matrix work is about as long as 16 vector instructions).  The
+// scale outer product P_g = sx_g (x) sw_g is therefore formed on the matrix
+// core as well: a bf16 v_mfma_f32_32x32x16 whose only non-zero k slot holds
+// sx (A) and sw (B).  bf16 x bf16 is exact in fp32, so P_g is exact and lands
+// in the same 32x32 accumulator layout as G_g.  The vector ALU then does one
+// int->float conversion and one fma per output and group.  The factor 2^-8
+// (from the 16*code operands) and alpha are applied once at the end.
+//
+// Data movement.  256 threads own a 128x128 output tile (4 waves of 64x64,
+// each 2x2 tiles of 32x32); one K-step is one group of 64.  A 4-stage ring in
+// LDS is filled with global_load_lds (global memory straight to LDS, no
+// registers): per group 4 KB of A codes, 4 KB of B codes and 2 x 512 B of
+// scales (one dword per row).  Codes sit in LDS as [half][row][16 B], so the 16-byte fragment
+// reads of a wave are contiguous and free of bank conflicts.  One barrier per
+// group separates the consumers of a stage from its next refill.  Blocks are
+// mapped to tiles so that each XCD (own L2) walks a contiguous band of tiles
+// in groups of 8 M-tiles, keeping the A and B tiles in flight L2-resident.
 #include "device_common.h"
 #include "launch.h"
 
 namespace svdq {
 
-constexpr int G4_BM = 128, G4_BN = 128, G4_THREADS = 256, G4_SCHUNK = 8;
+constexpr int G4_BM = 128, G4_BN = 128, G4_THREADS = 256, G4_STAGES = 4;
+constexpr int G4_CODES = G4_BM * 32;                   // bytes of A (or B) codes per group
+// Scales are copied with global_load_lds_ushort, which writes one dword per
+// lane (the 16-bit value zero-extended), so each row's scale takes 4 bytes.
+constexpr int G4_SA = 2 * G4_CODES;                    // offset of the A scales in a stage
+constexpr int G4_SB = G4_SA + 4 * G4_BM;               // offset of the B scales
+constexpr int G4_STAGE = G4_SB + 4 * G4_BN;            // 9216 bytes
+constexpr int G4_GROUP_M = 8;                          // M-tiles per raster group
 
 // 32x32 MFMA accumulator layout: lane l, register i -> row 8*(i/4) + 4*(l/32) + i%4, col l%32.
 
+typedef __attribute__((address_space(1))) const void *gptr_t;
+typedef __attribute__((address_space(3))) void *lptr_t;
+
+__device__ __forceinline__ void unpack_i8(const v4u &c, v4i &lo, v4i &hi) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        lo[i] = (int)((c[i] << 4) & 0xF0F0F0F0u);
+        hi[i] = (int)(c[i] & 0xF0F0F0F0u);
+    }
+}
+
+// Block -> (M-tile, N-tile).  Hardware dispatches block b to XCD b % 8; give
+// each XCD a contiguous range of tile ids, and order tile ids by groups of
+// G4_GROUP_M M-tiles so that neighbouring tiles share A rows and B rows.
+__device__ __forceinline__ void tile_of_block(int b, int nbm, int nbn, int &bm, int &bn) {
+    const int nb = nbm * nbn;
+    const int x = b & 7, local = b >> 3;
+    const int q = nb >> 3, r = nb & 7;
+    const int t = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + local;
+    const int per_group = G4_GROUP_M * nbn;
+    const int first_m = (t / per_group) * G4_GROUP_M;
+    const int gm = min(nbm - first_m, G4_GROUP_M);
+    const int within = t % per_group;
+    bm = first_m + within % gm;
+    bn = within / gm;
+}
+
+__device__ __forceinline__ void wait_vmcnt(int n) {
+    // s_waitcnt with vmcnt = n (n in {0, 2, 3, 4, 6}); expcnt and lgkmcnt left unconstrained
+    switch (n) {
+        case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+        case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+        case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+        case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+        default: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+    }
+}
+
 template <bool GROUP_SUMS>
-__global__ __launch_bounds__(G4_THREADS)
+__global__ __launch_bounds__(G4_THREADS, 2)
 void gemm_w4a4_int4_kernel(int M, int N, int K, int rank,
                            const uint8_t *__restrict__ act_codes,
                            const uint16_t *__restrict__ act_scales,
@@ -41,60 +100,43 @@ void gemm_w4a4_int4_kernel(int M, int N, int K, int rank,
                            const uint16_t *__restrict__ bias,
                            uint16_t *__restrict__ out, int32_t *__restrict__ gsum)
 {
-    __shared__ float s_sx[2][G4_SCHUNK][G4_BM];
-    __shared__ float s_sw[2][G4_SCHUNK][G4_BN];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[G4_STAGES * G4_STAGE];
+    constexpr int LOADS = GROUP_SUMS ? 2 : 3;             // global_load_lds per wave per group
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int l32 = lane & 31, h = lane >> 5;
-    const int nbn = (N + G4_BN - 1) / G4_BN;
-    const int m0 = (int)(blockIdx.x / nbn) * G4_BM, n0 = (int)(blockIdx.x % nbn) * G4_BN;
+    const int nbm = (M + G4_BM - 1) / G4_BM, nbn = (N + G4_BN - 1) / G4_BN;
+    int bm, bn;
+    tile_of_block((int)blockIdx.x, nbm, nbn, bm, bn);
+    const int m0 = bm * G4_BM, n0 = bn * G4_BN;
     const int NG = K >> 6;
     const size_t rowbytes = (size_t)(K >> 1);
 
-    // rows this lane loads fragments for (clamped; out-of-range rows are zeroed)
-    int arow[2], brow[2];
-    bool aok[2], bok[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        arow[t] = m0 + wm * 64 + t * 32 + l32;
-        brow[t] = n0 + wn * 64 + t * 32 + l32;
-        aok[t] = arow[t] < M;
-        bok[t] = brow[t] < N;
-        if (!aok[t]) arow[t] = 0;
-        if (!bok[t]) brow[t] = 0;
-    }
-    const uint8_t *ap[2], *bp[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        ap[t] = act_codes + (size_t)arow[t] * rowbytes + 16 * h;
-        bp[t] = wgt_codes + (size_t)brow[t] * rowbytes + 16 * h;
-    }
-
-    // scale staging: thread t < 128 loads A row m0+t, t >= 128 loads B row n0+t-128
-    const bool s_is_a = tid < G4_BM;
-    const int s_r = s_is_a ? tid : tid - G4_BM;
-    const int s_row = (s_is_a ? m0 : n0) + s_r;
-    const bool s_ok = s_row < (s_is_a ? M : N);
-    const uint16_t *s_src = (s_is_a ? act_scales : wgt_scales) + (size_t)(s_ok ? s_row : 0) * NG;
-    const float s_mul = s_is_a ? 1.0f : alpha * 0.00390625f;   // alpha * 2^-8 on the weight side
-    uint16_t s_reg[G4_SCHUNK];
-    auto load_scales = [&](int c) {
-#pragma unroll
-        for (int i = 0; i < G4_SCHUNK; ++i) {
-            int g = c * G4_SCHUNK + i;
-            s_reg[i] = (s_ok && g < NG) ? s_src[g] : (uint16_t)0;
-        }
-    };
-    auto store_scales = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < G4_SCHUNK; ++i) {
-            float v = bf16_to_f32(s_reg[i]) * s_mul;
-            if (s_is_a) s_sx[buf][i][s_r] = v;
-            else s_sw[buf][i][s_r] = v;
-        }
+    // Producer role.  Wave w copies LDS chunk w (1 KB) of the A codes and of the
+    // B codes of every group: chunk j = half (j/2), rows 64*(j%2) .. +63, lane l
+    // -> row 64*(j%2) + l.  Rows past M (columns past N) read a clamped, valid
+    // row: they only feed outputs that are never stored.  Waves 0,1 also copy
+    // the A scales of rows 64w .. 64w+63, waves 2,3 the B scales.
+    const int p_half = wave >> 1, p_row = 64 * (wave & 1) + lane;
+    const uint8_t *pa = act_codes + (size_t)min(m0 + p_row, M - 1) * rowbytes + 16 * p_half;
+    const uint8_t *pb = wgt_codes + (size_t)min(n0 + p_row, N - 1) * rowbytes + 16 * p_half;
+    const bool ps_is_a = wave < 2;
+    const int ps_row = 64 * (wave & 1) + lane;
+    const uint16_t *ps = nullptr;
+    if constexpr (!GROUP_SUMS)
+        ps = ps_is_a ? act_scales + (size_t)min(m0 + ps_row, M - 1) * NG
+                     : wgt_scales + (size_t)min(n0 + ps_row, N - 1) * NG;
+    auto issue = [&](int g) {
+        uint8_t *st = smem + (g % G4_STAGES) * G4_STAGE;
+        __builtin_amdgcn_global_load_lds((gptr_t)(pa + (size_t)g * 32), (lptr_t)(st + wave * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gptr_t)(pb + (size_t)g * 32), (lptr_t)(st + G4_CODES + wave * 1024),
+                                         16, 0, 0);
+        if constexpr (!GROUP_SUMS)
+            __builtin_amdgcn_global_load_lds((gptr_t)(ps + g),
+                                             (lptr_t)(st + (ps_is_a ? G4_SA : G4_SB) + 256 * (wave & 1)), 2, 0, 0);
     };
 
     v16f acc[2][2];
@@ -105,94 +147,99 @@ void gemm_w4a4_int4_kernel(int M, int N, int K, int rank,
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
 
-    v4u fa[2], fb[2];
-    auto load_frags = [&](int g) {
+    // consumer offsets inside a stage
+    int a_off[2], b_off[2];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            fa[t] = aok[t] ? *(const v4u *)(ap[t] + (size_t)g * 32) : v4u{0u, 0u, 0u, 0u};
-            fb[t] = bok[t] ? *(const v4u *)(bp[t] + (size_t)g * 32) : v4u{0u, 0u, 0u, 0u};
-        }
-    };
-
-    if (!GROUP_SUMS) {
-        load_scales(0);
-        store_scales(0);
-        if (NG > G4_SCHUNK) load_scales(1);
+    for (int t = 0; t < 2; ++t) {
+        a_off[t] = h * (G4_CODES / 2) + (wm * 64 + t * 32 + l32) * 16;
+        b_off[t] = G4_CODES + h * (G4_CODES / 2) + (wn * 64 + t * 32 + l32) * 16;
     }
-    load_frags(0);
-    __syncthreads();
+
+    for (int g = 0; g < G4_STAGES - 1 && g < NG; ++g) issue(g);
 
     for (int g = 0; g < NG; ++g) {
-        v4u ca[2] = {fa[0], fa[1]}, cb[2] = {fb[0], fb[1]};
-        if (g + 1 < NG) load_frags(g + 1);
+        // this wave's copies of group g have landed once at most the copies of
+        // the groups issued after it are still in flight
+        const int newer = min(G4_STAGES - 2, NG - 1 - g);
+        wait_vmcnt(newer * LOADS);
+        // Workgroup barrier without the full memory fence of __syncthreads()
+        // (which would also wait for the copies still in flight): every wave
+        // has waited for its own copies of g, so after the barrier all of g is
+        // in LDS, and every wave has finished reading the stage of g-1.  The
+        // empty asm statements keep the compiler from moving LDS accesses
+        // across the barrier.
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (g + G4_STAGES - 1 < NG) issue(g + G4_STAGES - 1);
 
+        const uint8_t *st = smem + (g % G4_STAGES) * G4_STAGE;
+        v4u fa[2], fb[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            fa[t] = *(const v4u *)(st + a_off[t]);
+            fb[t] = *(const v4u *)(st + b_off[t]);
+        }
         v4i alo[2], ahi[2], blo[2], bhi[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                alo[t][i] = (int)((ca[t][i] << 4) & 0xF0F0F0F0u);
-                ahi[t][i] = (int)(ca[t][i] & 0xF0F0F0F0u);
-                blo[t][i] = (int)((cb[t][i] << 4) & 0xF0F0F0F0u);
-                bhi[t][i] = (int)(cb[t][i] & 0xF0F0F0F0u);
-            }
+            unpack_i8(fa[t], alo[t], ahi[t]);
+            unpack_i8(fb[t], blo[t], bhi[t]);
         }
-        v16i G[2][2];
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                v16i z = {};
-                z = __builtin_amdgcn_mfma_i32_32x32x32_i8(alo[a], blo[b], z, 0, 0, 0);
-                G[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ahi[a], bhi[b], z, 0, 0, 0);
-            }
 
         if constexpr (GROUP_SUMS) {
 #pragma unroll
             for (int a = 0; a < 2; ++a)
 #pragma unroll
                 for (int b = 0; b < 2; ++b) {
+                    v16i G = {};
+                    G = __builtin_amdgcn_mfma_i32_32x32x32_i8(alo[a], blo[b], G, 0, 0, 0);
+                    G = __builtin_amdgcn_mfma_i32_32x32x32_i8(ahi[a], bhi[b], G, 0, 0, 0);
                     const int col = n0 + wn * 64 + b * 32 + l32;
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         const int rowi = m0 + wm * 64 + a * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-                        if (rowi < M && col < N)
-                            gsum[((size_t)rowi * N + col) * NG + g] = G[a][b][i] >> 8;
+                        if (rowi < M && col < N) gsum[((size_t)rowi * N + col) * NG + g] = G[i] >> 8;
                     }
                 }
         } else {
-            const int buf = (g / G4_SCHUNK) & 1, gi = g % G4_SCHUNK;
+            // P-MFMA operands: only k = 0 (lanes 0..31, slot 0) is non-zero
+            const uint32_t *sxs = (const uint32_t *)(st + G4_SA);
+            const uint32_t *sws = (const uint32_t *)(st + G4_SB);
+            v8bf pa_op[2], pb_op[2];
 #pragma unroll
-            for (int a = 0; a < 2; ++a) {
-                float sx[16];
-                const float *sxp = &s_sx[buf][gi][wm * 64 + a * 32 + 4 * h];
+            for (int t = 0; t < 2; ++t) {
+                const uint32_t sxa = sxs[wm * 64 + t * 32 + l32] & 0xFFFFu;
+                const uint32_t swb = sws[wn * 64 + t * 32 + l32] & 0xFFFFu;
+                pa_op[t] = __builtin_bit_cast(v8bf, v4u{h == 0 ? sxa : 0u, 0u, 0u, 0u});
+                pb_op[t] = __builtin_bit_cast(v8bf, v4u{h == 0 ? swb : 0u, 0u, 0u, 0u});
+            }
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    v4f v = *(const v4f *)(sxp + 8 * q);
-                    sx[4 * q + 0] = v[0];
-                    sx[4 * q + 1] = v[1];
-                    sx[4 * q + 2] = v[2];
-                    sx[4 * q + 3] = v[3];
-                }
+            for (int a = 0; a < 2; ++a)
 #pragma unroll
                 for (int b = 0; b < 2; ++b) {
-                    const float sw = s_sw[buf][gi][wn * 64 + b * 32 + l32];
+                    v16i G = {};
+                    G = __builtin_amdgcn_mfma_i32_32x32x32_i8(alo[a], blo[b], G, 0, 0, 0);
+                    G = __builtin_amdgcn_mfma_i32_32x32x32_i8(ahi[a], bhi[b], G, 0, 0, 0);
+                    v16f P = {};
+                    P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa_op[a], pb_op[b], P, 0, 0, 0);
 #pragma unroll
                     for (int i = 0; i < 16; ++i)
-                        acc[a][b][i] = __builtin_fmaf((float)G[a][b][i], sx[i] * sw, acc[a][b][i]);
+                        acc[a][b][i] = __builtin_fmaf((float)G[i], P[i], acc[a][b][i]);
+                    if (b == 1) __builtin_amdgcn_sched_barrier(0);   // at most 2 tiles of G, P live
                 }
-            }
-            // chunk boundary: publish the next chunk of scales
-            if (gi == G4_SCHUNK - 1 && g + 1 < NG) {
-                const int c_next = g / G4_SCHUNK + 1;
-                store_scales(c_next & 1);
-                __syncthreads();
-                if ((c_next + 1) * G4_SCHUNK < NG) load_scales(c_next + 1);
-            }
         }
     }
 
     if constexpr (!GROUP_SUMS) {
+        const float post = alpha * 0.00390625f;            // alpha * 2^-8
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[a][b][i] *= post;
+
         // ---- low-rank up-projection on the matrix cores: acc += t . up^T.
         // t (fp32) is split into bf16 hi + lo (t - hi is exact in fp32), the
         // up factor is bf16, products are exact in fp32.
@@ -201,7 +248,7 @@ void gemm_w4a4_int4_kernel(int M, int N, int K, int rank,
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const int rrow = m0 + wm * 64 + t * 32 + l32;
-                v4u hv, lv;
+                v4u hv = v4u{0u, 0u, 0u, 0u}, lv = hv;
                 if (rrow < M) {
                     const float *tp = lora_act + (size_t)rrow * rank + s + 8 * h;
                     v4f t0 = *(const v4f *)tp, t1 = *(const v4f *)(tp + 4);
@@ -214,9 +261,6 @@ void gemm_w4a4_int4_kernel(int M, int N, int K, int rank,
                         hv[p] = h0 | (h1 << 16);
                         lv[p] = l0 | (l1 << 16);
                     }
-                } else {
-                    hv = v4u{0u, 0u, 0u, 0u};
-                    lv = hv;
                 }
                 thi[t] = __builtin_bit_cast(v8bf, hv);
                 tlo[t] = __builtin_bit_cast(v8bf, lv);
