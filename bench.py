@@ -167,7 +167,7 @@ def cpu_baseline(synth, budget_rows=32):
     aw = synth.synthetic_awq_weights(seed, N, K)
     xg = synth.to_bf16_bits(np.random.default_rng(seed).standard_normal((1, K)))
     t0 = time.perf_counter()
-    oracle.awq_gemv(xg, aw["wgt_codes"], aw["wgt_scales"], aw["wgt_zeros"], None)
+    oracle.awq_gemv(xg, aw["wgt_codes"], aw["wgt_scales"].T, aw["wgt_zeros"].T, None)
     t_total += time.perf_counter() - t0
     return {"value": round(ops / t_total / 1e12, 6), "unit": "TOPS", "cores": 1, "kind": "oracle",
             "sample": f"first {budget_rows} rows of each W4A4 layer (quantize + GEMM) and the M=1 GEMV; "

@@ -33,6 +33,8 @@
 //    {0,.5,1,1.5,2,3,4,6} onto 0..7, so round-to-nearest-even on it gives the
 //    nearest value with ties to the even code.  v comes from the same Newton
 //    step; ties are exact and non-ties stay 2^-11 (relative) away.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -56,6 +58,7 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
                          uint8_t *__restrict__ codes, void *__restrict__ scales,
                          float *__restrict__ lora_act)
 {
+    constexpr int LSLOTS = RT <= 4 ? 3 : 1;   // low-rank slices prefetched unless the rank is large
     __shared__ float s_inv[QA_CHUNK * 64];
     __shared__ float s_part[RT > 0 ? QA_WAVES * QA_ROWS * RT * 16 : 1];
 
@@ -66,7 +69,7 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
     const int row = blockIdx.x * QA_ROWS + r;
     const bool row_ok = row < M;
     const int NG = K >> 6;
-    const size_t xrow_off = (size_t)(row_ok ? row : 0) * (size_t)K;
+    const size_t xrow_off = (size_t)min(row, M - 1) * (size_t)K;   // rows past M: clamped, results not stored
 
     v4f acc[RT > 0 ? RT : 1];
 #pragma unroll
@@ -84,19 +87,35 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
         }
         unsafe = __syncthreads_or(unsafe);
 
-        for (int g = c0 + wave; g < c0 + cg; g += QA_WAVES) {
-            const int kbase = g * 64 + 8 * kq;
-            // ---- loads: x slices and the low-rank factor slices
-            v4u xr[2];
-            xr[0] = row_ok ? *(const v4u *)(x + xrow_off + kbase) : v4u{0u, 0u, 0u, 0u};
-            xr[1] = row_ok ? *(const v4u *)(x + xrow_off + kbase + 32) : v4u{0u, 0u, 0u, 0u};
-            v4u lr[RT > 0 ? RT : 1][2];
+        // This wave's groups in the chunk: g_i = c0 + wave + i * QA_WAVES.  x
+        // slices stream two groups ahead and the low-rank factor slices (L2
+        // resident) one group ahead, in register rings with compile-time slots.
+        const int n_w = wave < cg ? (cg - wave + QA_WAVES - 1) / QA_WAVES : 0;
+        v4u xring[3][2];
+        v4u lring[LSLOTS][RT > 0 ? RT : 1][2];
+        auto load_x = [&](int i, auto slot_c) __attribute__((always_inline)) {
+            constexpr int S = decltype(slot_c)::value;
+            const int kb = (c0 + wave + i * QA_WAVES) * 64 + 8 * kq;
+            xring[S][0] = *(const v4u *)(x + xrow_off + kb);
+            xring[S][1] = *(const v4u *)(x + xrow_off + kb + 32);
+            asm volatile("" ::: "memory");   // keep the loads here, ahead of their use
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        auto load_l = [&](int i, auto slot_c) __attribute__((always_inline)) {
+            constexpr int S = decltype(slot_c)::value;
+            const int kb = (c0 + wave + i * QA_WAVES) * 64 + 8 * kq;
 #pragma unroll
             for (int t = 0; t < RT; ++t) {
-                const uint16_t *lp = lora_down + (size_t)(t * 16 + r) * (size_t)K + kbase;
-                lr[t][0] = *(const v4u *)lp;
-                lr[t][1] = *(const v4u *)(lp + 32);
+                const uint16_t *lp = lora_down + (size_t)(t * 16 + r) * (size_t)K + kb;
+                lring[S][t][0] = *(const v4u *)lp;
+                lring[S][t][1] = *(const v4u *)(lp + 32);
             }
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        auto process = [&](int i, const v4u (&xr)[2], const v4u (&lr)[RT > 0 ? RT : 1][2]) __attribute__((always_inline)) {
+            const int g = c0 + wave + i * QA_WAVES;
+            const int kbase = g * 64 + 8 * kq;
             const float *inv = s_inv + (g - c0) * 64 + 8 * kq;
 
             // ---- smoothing: v = x * (1/s), then RNE to bf16
@@ -221,6 +240,38 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
                     }
                 }
             }
+        };
+        // Loads are unconditional (the index is clamped to the wave's last
+        // group; surplus loads read valid memory and are never used) so that
+        // the compiler can count the loads in flight exactly.
+        const int i_last = n_w - 1;
+        auto step = [&](int i, auto xs_c, auto ls_c) __attribute__((always_inline)) {
+            constexpr int XS = decltype(xs_c)::value;
+            constexpr int LS = decltype(ls_c)::value;
+            load_x(min(i + 2, i_last), std::integral_constant<int, (XS + 2) % 3>{});
+            if constexpr (LSLOTS == 3) {
+                load_l(min(i + 1, i_last), std::integral_constant<int, (LS + 1) % 3>{});
+                process(i, xring[XS], lring[LS]);
+            } else {
+                load_l(i, std::integral_constant<int, 0>{});
+                process(i, xring[XS], lring[0]);
+            }
+        };
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        using I2 = std::integral_constant<int, 2>;
+        if (n_w > 0) {
+            load_x(0, I0{});
+            load_x(min(1, i_last), I1{});
+            if constexpr (LSLOTS == 3) load_l(0, I0{});
+            const int nfull = (n_w / 3) * 3;
+            for (int i = 0; i < nfull; i += 3) {
+                step(i, I0{}, I0{});
+                step(i + 1, I1{}, I1{});
+                step(i + 2, I2{}, I2{});
+            }
+            if (nfull < n_w) step(nfull, I0{}, I0{});
+            if (nfull + 1 < n_w) step(nfull + 1, I1{}, I1{});
         }
         __syncthreads();
     }
