@@ -23,6 +23,7 @@ Infinity Cache); ``cpu_baseline`` times the CPU oracle on a bounded sample.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -146,6 +147,59 @@ def gemv_sweep(torch, synth, reps=50):
     return out
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_int4_mlp_up_traffic.txt")
+GEMM_INT4_SOURCE = os.path.join(ROOT, "bit_w4a4_quantized_svdq_amd", "csrc", "gemm_w4a4_int4.hip")
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the dominant kernel from the recorded rocprofv3
+    counter runs (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel factor),
+    or None when the kernel source has changed since they were taken."""
+    try:
+        rec = {}
+        for line in open(TRAFFIC_FILE):
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
+        src = hashlib.sha256(open(GEMM_INT4_SOURCE, "rb").read()).hexdigest()
+        if rec.get("source_sha256") != src:
+            return None
+        return int(float(rec["hbm_bytes_per_launch"]))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def profile_kernel(torch, synth, name, reps):
+    """Run one hot-path kernel ``reps`` times on its full-size inputs (for
+    rocprofv3).  name: <layer>.quantize_act | <layer>.gemm_w4a4 | adaln.awq_gemv"""
+    layers, xs = build_inputs(torch, synth)
+    layer, kind = name.split(".")
+    L = layers[layer]
+    if kind == "awq_gemv":
+        fn = lambda: L(xs[layer][:1])
+    else:
+        b = L.buffers(xs[layer].shape[0])
+        L.quantize(xs[layer], b)
+        fn = (lambda: L.quantize(xs[layer], b)) if kind == "quantize_act" else (lambda: L.gemm(b))
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        fn()
+    torch.cuda.synchronize()
+    print(f"[bench] ran {name} x{reps}", file=sys.stderr, flush=True)
+
+
+def copy_calibration(torch, mb, reps):
+    """A plain device copy of ``mb`` MiB (torch's copy kernel), the reference for
+    scaling the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    n = mb * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(f"[bench] copied {mb} MiB x{reps}", file=sys.stderr, flush=True)
+
+
 def cpu_baseline(synth, budget_rows=32):
     """The CPU oracle (single-threaded C, as it stands) on a bounded sample of
     the same step: the first ``budget_rows`` rows of each W4A4 layer
@@ -167,7 +221,7 @@ def cpu_baseline(synth, budget_rows=32):
     aw = synth.synthetic_awq_weights(seed, N, K)
     xg = synth.to_bf16_bits(np.random.default_rng(seed).standard_normal((1, K)))
     t0 = time.perf_counter()
-    oracle.awq_gemv(xg, aw["wgt_codes"], aw["wgt_scales"].T, aw["wgt_zeros"].T, None)
+    oracle.awq_gemv(xg, aw["wgt_codes"], aw["wgt_scales"], aw["wgt_zeros"], None)
     t_total += time.perf_counter() - t0
     return {"value": round(ops / t_total / 1e12, 6), "unit": "TOPS", "cores": 1, "kind": "oracle",
             "sample": f"first {budget_rows} rows of each W4A4 layer (quantize + GEMM) and the M=1 GEMV; "
@@ -181,6 +235,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemv-sweep", action="store_true")
+    ap.add_argument("--profile-kernel", default=None,
+                    help="run only this kernel --steps times (e.g. mlp_up.gemm_w4a4), for rocprofv3")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="run only a plain copy of this many MiB --steps times (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build measures the single-GPU hot path "
@@ -191,6 +249,12 @@ def main():
     from bit_w4a4_quantized_svdq_amd import capi, synth
     capi.lib()                                    # fail loudly if libsvdq.so is missing
     torch.cuda.set_device(0)
+    if args.copy_mb:
+        copy_calibration(torch, args.copy_mb, args.steps)
+        return
+    if args.profile_kernel:
+        profile_kernel(torch, synth, args.profile_kernel, args.steps)
+        return
     print(f"[bench] building inputs", file=sys.stderr, flush=True)
     layers, xs = build_inputs(torch, synth)
     torch.cuda.synchronize()
@@ -236,7 +300,7 @@ def main():
     dom = kernels["mlp_up.gemm_w4a4"]
     roofline = {"bound": "mfma", "kernel": "svdq_gemm_w4a4 int4 (mlp_up 4096x3072->12288)",
                 "achieved": dom["TOPS"], "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
-                "frac": round(dom["TOPS"] / PEAK_INT8_TOPS, 4), "traffic": None,
+                "frac": round(dom["TOPS"] / PEAK_INT8_TOPS, 4), "traffic": recorded_traffic(),
                 "algorithmic_bytes": algorithmic_bytes_gemm(TOKENS, 4 * HIDDEN, HIDDEN, 32, "int4"),
                 "avg_launch_us": dom["us"]}
 

@@ -50,9 +50,6 @@ constexpr int G4_GROUP_M = 8;                          // M-tiles per raster gro
 
 // 32x32 MFMA accumulator layout: lane l, register i -> row 8*(i/4) + 4*(l/32) + i%4, col l%32.
 
-typedef __attribute__((address_space(1))) const void *gptr_t;
-typedef __attribute__((address_space(3))) void *lptr_t;
-
 __device__ __forceinline__ void unpack_i8(const v4u &c, v4i &lo, v4i &hi) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

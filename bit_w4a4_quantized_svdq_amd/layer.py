@@ -84,7 +84,7 @@ class SVDQW4A4Linear:
 class AWQW4A16Linear:
     """y = x . ((q - z) * s)^T + bias with int4 weights in groups of 64.
 
-    wgt_codes [N, K/2]; wgt_scales and wgt_zeros group-major [K/64, N]."""
+    wgt_codes [N, K/2]; wgt_scales and wgt_zeros [N, K/64]."""
 
     def __init__(self, wgt_codes, wgt_scales, wgt_zeros, bias=None, device="cuda"):
         self.wgt_codes = _dev(wgt_codes, torch.uint8, device)

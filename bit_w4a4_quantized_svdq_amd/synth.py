@@ -142,9 +142,9 @@ def synthetic_w4a4_weights(seed: int, N: int, K: int, rank: int, precision: str)
 def synthetic_awq_weights(seed: int, N: int, K: int):
     """Random AWQ weight tensors: unsigned codes uniform in [0,15], bf16
     scales 0.02*(2+|N(0,1)|)/15, bf16 integer zero points uniform in [4,11].
-    Scales and zero points are group-major [K/64, N], the library's layout."""
+    Scales and zero points are [N, K/64]."""
     rng = np.random.default_rng(seed)
     codes = pack_nibbles(rng.integers(0, 16, size=(N, K)))
-    scales = to_bf16_bits(0.02 * (2.0 + np.abs(rng.standard_normal((K // 64, N)))) / 15.0)
-    zeros = to_bf16_bits(rng.integers(4, 12, size=(K // 64, N)).astype(np.float64))
+    scales = to_bf16_bits(0.02 * (2.0 + np.abs(rng.standard_normal((N, K // 64)))) / 15.0)
+    zeros = to_bf16_bits(rng.integers(4, 12, size=(N, K // 64)).astype(np.float64))
     return {"wgt_codes": codes, "wgt_scales": scales, "wgt_zeros": zeros}

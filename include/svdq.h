@@ -107,16 +107,15 @@ svdq_status svdq_gemm_w4a4(int32_t precision, int64_t M, int64_t N, int64_t K, i
  * awq_gemv_w4a16 -- int4 weight-only layer with bf16 activations, for the
  * memory-bound, precision-sensitive layers (adaptive-norm modulation;
  * "Nunchaku Lite" docs, awq_w4a16 int4 group 64).
- *   y[m,n] = RNE_bf16( sum_k x[m,k] * (q[n,k] - z[k/64,n]) * s[k/64,n] + bias[n] )
- * The sum is fp32 in unspecified order.  Tuned for M <= 16; any M works.
- * Scales and zero points are group-major, so that the weight rows a GPU lane
- * accumulates side by side share one load.
+ *   y[m,n] = RNE_bf16( sum_k x[m,k] * (q[n,k] - z[n,k/64]) * s[n,k/64] + bias[n] )
+ * The sum is fp32 in unspecified order.  Tuned for M <= 32 (a GEMV); any M
+ * works, the weights being streamed once per 32 rows of x.
  *
  *   group_size must be 64
  *   x          bf16 [M, K]
  *   wgt_codes  u8 [N, K/2], unsigned codes 0..15
- *   wgt_scales bf16 [K/64, N]   (group-major)
- *   wgt_zeros  bf16 [K/64, N]   (group-major), integer values 0..15
+ *   wgt_scales bf16 [N, K/64]
+ *   wgt_zeros  bf16 [N, K/64], integer values 0..15
  *   bias       bf16 [N] or NULL
  *   out        out: bf16 [M, N]
  */

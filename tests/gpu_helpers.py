@@ -122,12 +122,11 @@ def gpu_gemm(prec, act_codes, act_scales, wgt_codes, wgt_scales, lora_act, lora_
 
 
 def gpu_gemv(x, codes, scales, zeros, bias):
-    """scales, zeros in the oracle's [N, K/64] layout; the library takes them
-    group-major ([K/64, N])."""
+    """scales, zeros [N, K/64], the oracle's and the library's layout."""
     from bit_w4a4_quantized_svdq_amd import capi
     M, N = x.shape[0], codes.shape[0]
     out = poison(empty((M, N), "bf16"))
-    capi.awq_gemv_w4a16(to_dev(x, "bf16"), to_dev(codes, "u8"), to_dev(np.ascontiguousarray(scales.T), "bf16"),
-                        to_dev(np.ascontiguousarray(zeros.T), "bf16"), to_dev(bias, "bf16"), out)
+    capi.awq_gemv_w4a16(to_dev(x, "bf16"), to_dev(codes, "u8"), to_dev(scales, "bf16"),
+                        to_dev(zeros, "bf16"), to_dev(bias, "bf16"), out)
     torch.cuda.synchronize()
     return to_host(out, "bf16")
