@@ -19,19 +19,23 @@
 // group, and on CDNA4 the vector ALU is the scarce unit (one 32x32 tile-group
 // of int8 matrix work is about as long as 16 vector instructions).  The
 // scale outer product P_g = sx_g (x) sw_g is therefore formed on the matrix
-// core as well: a bf16 v_mfma_f32_32x32x16 whose only non-zero k slot holds
-// sx (A) and sw (B).  bf16 x bf16 is exact in fp32, so P_g is exact and lands
-// in the same 32x32 accumulator layout as G_g.  The vector ALU then does one
-// int->float conversion and one fma per output and group.  The factor 2^-8
-// (from the 16*code operands) and alpha are applied once at the end.
+// core as well: an fp32 v_mfma_f32_32x32x2 with sx (A) and sw (B) in both k
+// slots, i.e. P_g = 2 sx_g (x) sw_g (each operand is one register, and
+// lanes 32..63 read the same scales as lanes 0..31).  A product of two bf16
+// values is exact in fp32 and doubling is exact, so P_g is exact and lands in
+// the same 32x32 accumulator layout as G_g.  The vector ALU then does one
+// int->float conversion and one fma per output and group.  The factor 2^-9
+// (2^-8 from the 16*code operands, 1/2 from P) and alpha are applied once at
+// the end.
 //
 // Data movement.  256 threads own a 128x128 output tile (4 waves of 64x64,
 // each 2x2 tiles of 32x32); one K-step is one group of 64.  A 4-stage ring in
 // LDS is filled with global_load_lds (global memory straight to LDS, no
-// registers): per group 4 KB of A codes, 4 KB of B codes and 2 x 512 B of
-// scales (one dword per row).  Codes sit in LDS as [half][row][16 B], so the 16-byte fragment
-// reads of a wave are contiguous and free of bank conflicts.  One barrier per
-// group separates the consumers of a stage from its next refill.  Blocks are
+// registers): per group 4 KB of A codes and 4 KB of B codes; the scales of 8
+// groups at a time into a two-slot ring.  Codes sit in LDS as
+// [half][row][16 B], so the 16-byte fragment reads of a wave are contiguous
+// and free of bank conflicts.  One barrier per group separates the consumers
+// of a stage from its next refill.  Blocks are
 // mapped to tiles so that each XCD (own L2) walks a contiguous band of tiles
 // in groups of 8 M-tiles, keeping the A and B tiles in flight L2-resident.
 #include "device_common.h"
@@ -41,11 +45,19 @@ namespace svdq {
 
 constexpr int G4_BM = 128, G4_BN = 128, G4_THREADS = 256, G4_STAGES = 4;
 constexpr int G4_CODES = G4_BM * 32;                   // bytes of A (or B) codes per group
-// Scales are copied with global_load_lds_ushort, which writes one dword per
-// lane (the 16-bit value zero-extended), so each row's scale takes 4 bytes.
-constexpr int G4_SA = 2 * G4_CODES;                    // offset of the A scales in a stage
-constexpr int G4_SB = G4_SA + 4 * G4_BM;               // offset of the B scales
-constexpr int G4_STAGE = G4_SB + 4 * G4_BN;            // 9216 bytes
+constexpr int G4_STAGE = 2 * G4_CODES;                 // one group of A and B codes: 8 KB
+// Scales travel 8 groups at a time: each row's 8 consecutive bf16 scales are
+// 16 contiguous bytes, so one 16-byte copy per lane moves 64 rows' scales for
+// 8 groups (a copy of one 2-byte scale per lane per group would touch 64
+// separate cache lines for 128 bytes).  Two 8-group slots alternate.
+// A slot holds [A rows | B rows][8 groups x 2 B] when the row length K/64 is
+// a multiple of 8 (16-byte aligned rows); otherwise each group's scales are
+// copied one 2-byte value per lane (zero-extended to a dword) into
+// [group][A rows | B rows][4 B].
+constexpr int G4_SC_GROUPS = 8;
+constexpr int G4_SC_SLOT = G4_SC_GROUPS * (G4_BM + G4_BN) * 4;   // 8 KB (the larger layout)
+constexpr int G4_SC = G4_STAGES * G4_STAGE;            // offset of the two scale slots
+constexpr int G4_SMEM = G4_SC + 2 * G4_SC_SLOT;        // 48 KB
 constexpr int G4_GROUP_M = 8;                          // M-tiles per raster group
 
 // 32x32 MFMA accumulator layout: lane l, register i -> row 8*(i/4) + 4*(l/32) + i%4, col l%32.
@@ -75,17 +87,21 @@ __device__ __forceinline__ void tile_of_block(int b, int nbm, int nbn, int &bm, 
 }
 
 __device__ __forceinline__ void wait_vmcnt(int n) {
-    // s_waitcnt with vmcnt = n (n in {0, 2, 3, 4, 6}); expcnt and lgkmcnt left unconstrained
+    // s_waitcnt with vmcnt = n (0 <= n <= 7); expcnt and lgkmcnt left unconstrained
     switch (n) {
         case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+        case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
         case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
         case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
         case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
-        default: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+        case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+        case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+        default: __builtin_amdgcn_s_waitcnt(0x0F77); break;
     }
 }
 
-template <bool GROUP_SUMS>
+// SC16: scales copied 8 groups per 16-byte copy (K/64 a multiple of 8)
+template <bool GROUP_SUMS, bool SC16>
 __global__ __launch_bounds__(G4_THREADS, 2)
 void gemm_w4a4_int4_kernel(int M, int N, int K, int rank,
                            const uint8_t *__restrict__ act_codes,
@@ -97,8 +113,10 @@ void gemm_w4a4_int4_kernel(int M, int N, int K, int rank,
                            const uint16_t *__restrict__ bias,
                            uint16_t *__restrict__ out, int32_t *__restrict__ gsum)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[G4_STAGES * G4_STAGE];
-    constexpr int LOADS = GROUP_SUMS ? 2 : 3;             // global_load_lds per wave per group
+    __shared__ __attribute__((aligned(16))) uint8_t smem[G4_SMEM];
+    // global_load_lds per wave for group g: 2 for the codes, plus the scales
+    // (every group, or the first group of each 8 with SC16)
+    auto loads_of = [](int g) { return GROUP_SUMS ? 2 : (SC16 ? 2 + ((g & 7) == 0) : 3); };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -116,7 +134,8 @@ void gemm_w4a4_int4_kernel(int M, int N, int K, int rank,
     // B codes of every group: chunk j = half (j/2), rows 64*(j%2) .. +63, lane l
     // -> row 64*(j%2) + l.  Rows past M (columns past N) read a clamped, valid
     // row: they only feed outputs that are never stored.  Waves 0,1 also copy
-    // the A scales of rows 64w .. 64w+63, waves 2,3 the B scales.
+    // the A scales of rows 64w .. 64w+63, waves 2,3 the B scales (8 groups
+    // per copy with SC16).
     const int p_half = wave >> 1, p_row = 64 * (wave & 1) + lane;
     const uint8_t *pa = act_codes + (size_t)min(m0 + p_row, M - 1) * rowbytes + 16 * p_half;
     const uint8_t *pb = wgt_codes + (size_t)min(n0 + p_row, N - 1) * rowbytes + 16 * p_half;
@@ -131,9 +150,18 @@ void gemm_w4a4_int4_kernel(int M, int N, int K, int rank,
         __builtin_amdgcn_global_load_lds((gptr_t)(pa + (size_t)g * 32), (lptr_t)(st + wave * 1024), 16, 0, 0);
         __builtin_amdgcn_global_load_lds((gptr_t)(pb + (size_t)g * 32), (lptr_t)(st + G4_CODES + wave * 1024),
                                          16, 0, 0);
-        if constexpr (!GROUP_SUMS)
-            __builtin_amdgcn_global_load_lds((gptr_t)(ps + g),
-                                             (lptr_t)(st + (ps_is_a ? G4_SA : G4_SB) + 256 * (wave & 1)), 2, 0, 0);
+        if constexpr (!GROUP_SUMS) {
+            uint8_t *slot = smem + G4_SC + ((g >> 3) & 1) * G4_SC_SLOT;
+            if constexpr (SC16) {
+                if ((g & 7) == 0)   // rows' scales of groups g .. g+7: [A rows | B rows][16 B]
+                    __builtin_amdgcn_global_load_lds((gptr_t)(ps + g),
+                        (lptr_t)(slot + (ps_is_a ? 0 : G4_BM * 16) + 1024 * (wave & 1)), 16, 0, 0);
+            } else {                // group g's scales: [g % 8][A rows | B rows][4 B]
+                __builtin_amdgcn_global_load_lds((gptr_t)(ps + g),
+                    (lptr_t)(slot + (g & 7) * (4 * (G4_BM + G4_BN)) + (ps_is_a ? 0 : 4 * G4_BM) + 256 * (wave & 1)),
+                    2, 0, 0);
+            }
+        }
     };
 
     v16f acc[2][2];
@@ -158,7 +186,9 @@ void gemm_w4a4_int4_kernel(int M, int N, int K, int rank,
         // this wave's copies of group g have landed once at most the copies of
         // the groups issued after it are still in flight
         const int newer = min(G4_STAGES - 2, NG - 1 - g);
-        wait_vmcnt(newer * LOADS);
+        int newer_loads = 0;
+        for (int j = 1; j <= newer; ++j) newer_loads += loads_of(g + j);
+        wait_vmcnt(newer_loads);
         // Workgroup barrier without the full memory fence of __syncthreads()
         // (which would also wait for the copies still in flight): every wave
         // has waited for its own copies of g, so after the barrier all of g is
@@ -200,16 +230,24 @@ void gemm_w4a4_int4_kernel(int M, int N, int K, int rank,
                     }
                 }
         } else {
-            // P-MFMA operands: only k = 0 (lanes 0..31, slot 0) is non-zero
-            const uint32_t *sxs = (const uint32_t *)(st + G4_SA);
-            const uint32_t *sws = (const uint32_t *)(st + G4_SB);
-            v8bf pa_op[2], pb_op[2];
+            // P-MFMA operands: this lane's row scale as fp32 (a bf16 is the top
+            // half of an fp32), the same value in both k slots
+            const uint8_t *slot = smem + G4_SC + ((g >> 3) & 1) * G4_SC_SLOT;
+            float pa_op[2], pb_op[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const uint32_t sxa = sxs[wm * 64 + t * 32 + l32] & 0xFFFFu;
-                const uint32_t swb = sws[wn * 64 + t * 32 + l32] & 0xFFFFu;
-                pa_op[t] = __builtin_bit_cast(v8bf, v4u{h == 0 ? sxa : 0u, 0u, 0u, 0u});
-                pb_op[t] = __builtin_bit_cast(v8bf, v4u{h == 0 ? swb : 0u, 0u, 0u, 0u});
+                const int ra = wm * 64 + t * 32 + l32, rb = wn * 64 + t * 32 + l32;
+                uint32_t sa, sb;
+                if constexpr (SC16) {
+                    sa = *(const uint16_t *)(slot + ra * 16 + (g & 7) * 2);
+                    sb = *(const uint16_t *)(slot + G4_BM * 16 + rb * 16 + (g & 7) * 2);
+                } else {
+                    const uint8_t *gs = slot + (g & 7) * (4 * (G4_BM + G4_BN));
+                    sa = *(const uint32_t *)(gs + ra * 4) & 0xFFFFu;
+                    sb = *(const uint32_t *)(gs + 4 * G4_BM + rb * 4) & 0xFFFFu;
+                }
+                pa_op[t] = __uint_as_float(sa << 16);
+                pb_op[t] = __uint_as_float(sb << 16);
             }
 #pragma unroll
             for (int a = 0; a < 2; ++a)
@@ -219,7 +257,7 @@ void gemm_w4a4_int4_kernel(int M, int N, int K, int rank,
                     G = __builtin_amdgcn_mfma_i32_32x32x32_i8(alo[a], blo[b], G, 0, 0, 0);
                     G = __builtin_amdgcn_mfma_i32_32x32x32_i8(ahi[a], bhi[b], G, 0, 0, 0);
                     v16f P = {};
-                    P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa_op[a], pb_op[b], P, 0, 0, 0);
+                    P = __builtin_amdgcn_mfma_f32_32x32x2f32(pa_op[a], pb_op[b], P, 0, 0, 0);   // 2 sx sw
 #pragma unroll
                     for (int i = 0; i < 16; ++i)
                         acc[a][b][i] = __builtin_fmaf((float)G[i], P[i], acc[a][b][i]);
@@ -229,7 +267,7 @@ void gemm_w4a4_int4_kernel(int M, int N, int K, int rank,
     }
 
     if constexpr (!GROUP_SUMS) {
-        const float post = alpha * 0.00390625f;            // alpha * 2^-8
+        const float post = alpha * 0.001953125f;           // alpha * 2^-9
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -300,11 +338,18 @@ hipError_t launch_gemm_w4a4_int4(int M, int N, int K, int rank, const void *act_
                                  hipStream_t stream)
 {
     dim3 grid(((N + G4_BN - 1) / G4_BN) * ((M + G4_BM - 1) / G4_BM)), block(G4_THREADS);
-    hipLaunchKernelGGL((gemm_w4a4_int4_kernel<false>), grid, block, 0, stream, M, N, K, rank,
-                       (const uint8_t *)act_codes, (const uint16_t *)act_scales,
-                       (const uint8_t *)wgt_codes, (const uint16_t *)wgt_scales, alpha, lora_act,
-                       (const uint16_t *)lora_up, (const uint16_t *)bias, (uint16_t *)out,
-                       (int32_t *)nullptr);
+    if ((K >> 6) % G4_SC_GROUPS == 0)
+        hipLaunchKernelGGL((gemm_w4a4_int4_kernel<false, true>), grid, block, 0, stream, M, N, K, rank,
+                           (const uint8_t *)act_codes, (const uint16_t *)act_scales,
+                           (const uint8_t *)wgt_codes, (const uint16_t *)wgt_scales, alpha, lora_act,
+                           (const uint16_t *)lora_up, (const uint16_t *)bias, (uint16_t *)out,
+                           (int32_t *)nullptr);
+    else
+        hipLaunchKernelGGL((gemm_w4a4_int4_kernel<false, false>), grid, block, 0, stream, M, N, K, rank,
+                           (const uint8_t *)act_codes, (const uint16_t *)act_scales,
+                           (const uint8_t *)wgt_codes, (const uint16_t *)wgt_scales, alpha, lora_act,
+                           (const uint16_t *)lora_up, (const uint16_t *)bias, (uint16_t *)out,
+                           (int32_t *)nullptr);
     return hipGetLastError();
 }
 
@@ -312,7 +357,7 @@ hipError_t launch_group_sums_int4(int M, int N, int K, const void *act_codes,
                                   const void *wgt_codes, int32_t *G, hipStream_t stream)
 {
     dim3 grid(((N + G4_BN - 1) / G4_BN) * ((M + G4_BM - 1) / G4_BM)), block(G4_THREADS);
-    hipLaunchKernelGGL((gemm_w4a4_int4_kernel<true>), grid, block, 0, stream, M, N, K, 0,
+    hipLaunchKernelGGL((gemm_w4a4_int4_kernel<true, false>), grid, block, 0, stream, M, N, K, 0,
                        (const uint8_t *)act_codes, (const uint16_t *)nullptr,
                        (const uint8_t *)wgt_codes, (const uint16_t *)nullptr, 1.0f,
                        (const float *)nullptr, (const uint16_t *)nullptr,
