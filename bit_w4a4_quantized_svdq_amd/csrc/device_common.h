@@ -39,6 +39,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
+// Two fp32 -> two bf16 (lo in bits 0..15), round to nearest even, with the
+// gfx950 conversion instruction (v_cvt_pk_bf16_f32, one vector instruction
+// for both values).  Finite results equal pack_bf16x2's; a NaN input gives a
+// quiet NaN of the same sign.
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{lo, hi}), v2bf));
+}
+
 // Largest-magnitude reduction across lanes xor-distance `mask` (wave64).
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) {
     return __shfl_xor(v, mask, kWave);
