@@ -47,6 +47,7 @@
 // conversion, and for a tile fully inside the output, 2-byte buffer stores
 // whose row offsets are scalar.
 #include "device_common.h"
+#include "gemm_epilogue.h"
 #include "launch.h"
 
 namespace svdq {
@@ -358,98 +359,8 @@ void gemm_w4a4_int4_kernel(int M, int N, int K, int rank,
     }
 
     if constexpr (!GROUP_SUMS) {
-        // acc = 2^8 * sum_g G_g sx_g sw_g (the codes entered as 16*code):
-        // y = alpha * 2^-8 * acc + bias + t . up^T
-        const float post = alpha * 0.00390625f;
-        const bool rows_full = m0 + G4_BM <= M;                       // block-uniform
-        const bool tile_full = rows_full && n0 + G4_BN <= N;
-        float bv[2];
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const int col = n0 + wn * 64 + b * 32 + l32;
-            bv[b] = (bias && col < N) ? bf16_to_f32(bias[col]) : 0.0f;
-        }
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) acc[a][b][i] = __builtin_fmaf(acc[a][b][i], post, bv[b]);
-
-        // ---- low-rank up-projection on the matrix cores: acc += t . up^T.
-        // t (fp32) is split into bf16 hi + lo (t - hi is exact in fp32), the
-        // up factor is bf16, products are exact in fp32.
-        for (int s = 0; s < rank; s += 16) {
-            v8bf thi[2], tlo[2], up[2];
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int rrow = m0 + wm * 64 + t * 32 + l32;
-                v4f t0 = v4f{0.f, 0.f, 0.f, 0.f}, t1 = t0;
-                if (rows_full || rrow < M) {
-                    const float *tp = lora_act + (size_t)rrow * rank + s + 8 * h;
-                    t0 = *(const v4f *)tp;
-                    t1 = *(const v4f *)(tp + 4);
-                }
-                const float tv[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
-                v4u hv, lv;
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const uint32_t hb = pack_bf16x2_rne(tv[2 * p], tv[2 * p + 1]);
-                    hv[p] = hb;
-                    lv[p] = pack_bf16x2_rne(tv[2 * p] - bf16_lo(hb), tv[2 * p + 1] - bf16_hi(hb));
-                }
-                thi[t] = __builtin_bit_cast(v8bf, hv);
-                tlo[t] = __builtin_bit_cast(v8bf, lv);
-                const int ucol = n0 + wn * 64 + t * 32 + l32;
-                v4u uv = ucol < N ? *(const v4u *)(lora_up + (size_t)ucol * rank + s + 8 * h)
-                                  : v4u{0u, 0u, 0u, 0u};
-                up[t] = __builtin_bit_cast(v8bf, uv);
-            }
-#pragma unroll
-            for (int a = 0; a < 2; ++a)
-#pragma unroll
-                for (int b = 0; b < 2; ++b) {
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(thi[a], up[b], acc[a][b], 0, 0, 0);
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tlo[a], up[b], acc[a][b], 0, 0, 0);
-                }
-        }
-
-        // ---- bf16 store.  Registers i, i+1 (i even) of a lane are rows r, r+1
-        // of one column: one packed conversion, two 2-byte stores.
-        if (tile_full && N <= (1 << 22)) {
-            // whole tile in range: buffer stores, the row offset of each store
-            // is block-uniform (scalar register), only the column part is per lane
-            const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(out + (size_t)m0 * N + n0), (short)0, G4_BM * N * 2, 0x00020000);
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                const int voff = (4 * h * N + wn * 64 + b * 32 + l32) * 2;
-#pragma unroll
-                for (int a = 0; a < 2; ++a)
-#pragma unroll
-                    for (int i = 0; i < 16; i += 2) {
-                        const int row = wm * 64 + a * 32 + 8 * (i >> 2) + (i & 3);
-                        const uint32_t pk = pack_bf16x2_rne(acc[a][b][i], acc[a][b][i + 1]);
-                        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)pk, ro, voff, row * N * 2, 0);
-                        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pk >> 16), ro, voff, (row + 1) * N * 2, 0);
-                    }
-            }
-        } else {
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                const int col = n0 + wn * 64 + b * 32 + l32;
-                if (col >= N) continue;
-#pragma unroll
-                for (int a = 0; a < 2; ++a)
-#pragma unroll
-                    for (int i = 0; i < 16; i += 2) {
-                        const int rowi = m0 + wm * 64 + a * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-                        const uint32_t pk = pack_bf16x2_rne(acc[a][b][i], acc[a][b][i + 1]);
-                        if (rowi < M) out[(size_t)rowi * N + col] = (uint16_t)pk;
-                        if (rowi + 1 < M) out[(size_t)(rowi + 1) * N + col] = (uint16_t)(pk >> 16);
-                    }
-            }
-        }
+        // acc = 2^8 * sum_g G_g sx_g sw_g (the codes entered as 16*code)
+        gemm_epilogue(acc, alpha * 0.00390625f, M, N, rank, m0, n0, wm, wn, lane, lora_act, lora_up, bias, out);
     }
 }
 
