@@ -1,5 +1,6 @@
-// gemm_epilogue.h -- shared epilogue of the two W4A4 GEMM kernels (int4 and
-// NVFP4): y = post * acc + bias + t . up^T, rounded to bf16 and stored.  The
+// gemm_common.h -- pieces shared by the two W4A4 GEMM kernels (int4 and
+// NVFP4): tile rasterization, copy/barrier helpers, and the epilogue
+// y = post * acc + bias + t . up^T, rounded to bf16 and stored.  The
 // low-rank up-projection is the second half of the 16-bit branch of the
 // SVDQuant layer, fused into the 4-bit GEMM (blog "Hugging Face integrates
 // Nunchaku 4-bit diffusion inference into Diffusers", "SVDQuant and the
@@ -14,6 +15,56 @@
 #include "device_common.h"
 
 namespace svdq {
+
+// Block -> (M-tile, N-tile).  Hardware dispatches block b to XCD b % 8; give
+// each XCD a contiguous range of tile ids, and order tile ids by groups of
+// group_m M-tiles so that neighbouring tiles share A rows and B rows.
+__device__ __forceinline__ void tile_of_block(int b, int nbm, int nbn, int group_m, int &bm, int &bn) {
+    const int nb = nbm * nbn;
+    const int x = b & 7, local = b >> 3;
+    const int q = nb >> 3, r = nb & 7;
+    const int t = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + local;
+    const int per_group = group_m * nbn;
+    const int first_m = (t / per_group) * group_m;
+    const int gm = min(nbm - first_m, group_m);
+    const int within = t % per_group;
+    bm = first_m + within % gm;
+    bn = within / gm;
+}
+
+// The optimizer forgets what x holds: x is (re)defined at this point, so
+// nothing computed from it can be hoisted above, and a value that reaches it
+// must be complete here.
+template <typename T>
+__device__ __forceinline__ void opaque(T &x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("" : "+v"(x));
+#endif
+}
+
+__device__ __forceinline__ void wait_vmcnt(int n) {
+    // s_waitcnt with vmcnt = n (0 <= n <= 7); expcnt and lgkmcnt left unconstrained
+    switch (n) {
+        case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+        case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+        case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+        case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+        case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+        case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+        case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+        default: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+    }
+}
+
+// Workgroup barrier without the full memory fence of __syncthreads() (which
+// would also wait for every copy still in flight).  Callers wait for the
+// copies they need with wait_vmcnt() first.  The empty asm statements keep
+// the compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 __device__ __forceinline__ void gemm_epilogue(v16f (&acc)[2][2], float post, int M, int N, int rank,
                                               int m0, int n0, int wm, int wn, int lane,

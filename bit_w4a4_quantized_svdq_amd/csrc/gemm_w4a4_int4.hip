@@ -47,7 +47,7 @@
 // conversion, and for a tile fully inside the output, 2-byte buffer stores
 // whose row offsets are scalar.
 #include "device_common.h"
-#include "gemm_epilogue.h"
+#include "gemm_common.h"
 #include "launch.h"
 
 namespace svdq {
@@ -84,46 +84,6 @@ __device__ __forceinline__ void unpack_i8(const v4u &c, v4i &lo, v4i &hi) {
     for (int i = 0; i < 4; ++i) hi[i] = (int)(c[i] & 0xF0F0F0F0u);
 }
 
-// Block -> (M-tile, N-tile).  Hardware dispatches block b to XCD b % 8; give
-// each XCD a contiguous range of tile ids, and order tile ids by groups of
-// G4_GROUP_M M-tiles so that neighbouring tiles share A rows and B rows.
-__device__ __forceinline__ void tile_of_block(int b, int nbm, int nbn, int &bm, int &bn) {
-    const int nb = nbm * nbn;
-    const int x = b & 7, local = b >> 3;
-    const int q = nb >> 3, r = nb & 7;
-    const int t = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + local;
-    const int per_group = G4_GROUP_M * nbn;
-    const int first_m = (t / per_group) * G4_GROUP_M;
-    const int gm = min(nbm - first_m, G4_GROUP_M);
-    const int within = t % per_group;
-    bm = first_m + within % gm;
-    bn = within / gm;
-}
-
-// The optimizer forgets what x holds: x is (re)defined at this point, so
-// nothing computed from it can be hoisted above, and a value that reaches it
-// must be complete here.
-template <typename T>
-__device__ __forceinline__ void opaque(T &x) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    asm volatile("" : "+v"(x));
-#endif
-}
-
-__device__ __forceinline__ void wait_vmcnt(int n) {
-    // s_waitcnt with vmcnt = n (0 <= n <= 7); expcnt and lgkmcnt left unconstrained
-    switch (n) {
-        case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-        case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
-        case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
-        case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
-        case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
-        case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
-        case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
-        default: __builtin_amdgcn_s_waitcnt(0x0F77); break;
-    }
-}
-
 // SC16: scales copied 8 groups per 16-byte copy (K/64 a multiple of 8)
 template <bool GROUP_SUMS, bool SC16>
 __global__ __launch_bounds__(G4_THREADS, GROUP_SUMS ? 2 : 3)
@@ -146,7 +106,7 @@ void gemm_w4a4_int4_kernel(int M, int N, int K, int rank,
     const int l32 = lane & 31, h = lane >> 5;
     const int nbm = (M + G4_BM - 1) / G4_BM, nbn = (N + G4_BN - 1) / G4_BN;
     int bm, bn;
-    tile_of_block((int)blockIdx.x, nbm, nbn, bm, bn);
+    tile_of_block((int)blockIdx.x, nbm, nbn, G4_GROUP_M, bm, bn);
     const int m0 = bm * G4_BM, n0 = bn * G4_BN;
     const int NG = K >> 6;
     const int rowbytes = K >> 1;
@@ -227,17 +187,9 @@ void gemm_w4a4_int4_kernel(int M, int N, int K, int rank,
         sb_off[t] = SC16 ? G4_BM * 16 + (wn * 64 + t * 32 + l32) * 16 : 4 * G4_BM + (wn * 64 + t * 32 + l32) * 4;
     }
 
-    // Workgroup barrier without the full memory fence of __syncthreads()
-    // (which would also wait for the copies still in flight): every wave has
-    // waited for its own copies of the group about to be read, so after the
-    // barrier all of it is in LDS, and every wave has finished reading the
-    // stage that the next copy overwrites.  The empty asm statements keep the
-    // compiler from moving LDS accesses across the barrier.
-    auto barrier = [] {
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-    };
+    // lds_barrier(): every wave has waited for its own copies of the group
+    // about to be read, so after it all of that group is in LDS, and every
+    // wave has finished reading the stage that the next copy overwrites.
 
     // One group: fragments from the stage at `st`, scales from `sc` (this
     // group's column of a scale slot), G_g on the integer matrix core.
@@ -323,7 +275,7 @@ void gemm_w4a4_int4_kernel(int M, int N, int K, int rank,
                 if (j < 6) wait_vmcnt(4);                   // groups c+j+1, c+j+2: codes only
                 else if (j == 6) { if (last) wait_vmcnt(2); else wait_vmcnt(5); }
                 else { if (last) wait_vmcnt(0); else wait_vmcnt(5); }
-                barrier();
+                lds_barrier();
                 if (j < 5) {
                     issue_codes(c + j + 3, (j + 3) & 3);
                 } else if (!last) {
@@ -351,7 +303,7 @@ void gemm_w4a4_int4_kernel(int M, int N, int K, int rank,
         for (int g = 0; g < NG; ++g) {
             const int newer = min(G4_STAGES - 2, NG - 1 - g);
             wait_vmcnt(newer * loads_of(g));
-            barrier();
+            lds_barrier();
             if (g + G4_STAGES - 1 < NG) issue(g + G4_STAGES - 1);
             compute(smem + (g % G4_STAGES) * G4_STAGE,
                     smem + G4_SC + ((g >> 3) & 1) * G4_SC_SLOT + (g & 7) * (4 * (G4_BM + G4_BN)), g);

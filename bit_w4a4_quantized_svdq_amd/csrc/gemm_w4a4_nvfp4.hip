@@ -13,23 +13,45 @@
 // turns one byte (two E2M1 codes) into two fp16 values (its scale operand
 // only contributes a power of two, so it is left at 1), and one packed fp16
 // multiply applies the group scale: one vector instruction per element.
-// The block dequantizes each 64-wide K slice of its A and B tiles once into
-// LDS, and the waves run v_mfma_f32_32x32x16_f16 on it with fp32
-// accumulation (products are exact; only the fp32 sum rounds).  alpha
-// multiplies the 4-bit term at the end.
+// v_cvt_scalef32_pk_f16_fp8 turns two E4M3 scale bytes into fp16 (exact for
+// all 256 codes).  The products in v_mfma_f32_32x32x16_f16 are exact; only
+// the fp32 accumulation rounds.  alpha multiplies the 4-bit term at the end.
+//
+// Data movement follows the int4 kernel: 256 threads own a 128x128 output
+// tile (4 waves of 64x64); one K-step is a 64-wide slice (4 scale groups).
+// A 4-stage LDS ring is filled with buffer loads that write LDS directly:
+// per slice 4 KB of A codes and 4 KB of B codes as [half][row][16 B], so a
+// lane's 16-byte fragment holds 32 consecutive k of one row.  Each wave
+// dequantizes its own fragments in registers (each element is converted by
+// the two waves that share its row or column) and feeds them to the matrix
+// core: per slice and wave 128 vector instructions against 16 MFMAs.  A
+// dot product does not depend on the order of k, so lane half h takes k =
+// 32h .. 32h+31 of the slice and MFMA step s its k = 32h + 8s .. +7, for A
+// and B alike.  When K is a multiple of 256 the scales travel 4 slices at a
+// time (16 bytes per row) and the loop runs in chunks of 4 slices with
+// compile-time wait counts; otherwise each slice's 4 scale bytes per row are
+// copied on their own.
 #include "device_common.h"
-#include "gemm_epilogue.h"
+#include "gemm_common.h"
 #include "launch.h"
 
 namespace svdq {
 
-constexpr int NV_BM = 128, NV_BN = 128, NV_BK = 64, NV_THREADS = 256;
-constexpr int NV_LDS_STRIDE = NV_BK + 8;   // fp16 elements per LDS row (+16 B against bank conflicts)
+constexpr int NV_BM = 128, NV_BN = 128, NV_THREADS = 256, NV_STAGES = 4;
+constexpr int NV_CODES = NV_BM * 32;                  // bytes of A (or B) codes per slice
+constexpr int NV_STAGE = 2 * NV_CODES;                // 8 KB
+constexpr int NV_SC_SLICES = 4;                       // slices per 16-byte scale copy
+constexpr int NV_SC_SLOT = (NV_BM + NV_BN) * 16;      // 4 KB: [A rows | B rows][16 B]
+constexpr int NV_SC = NV_STAGES * NV_STAGE;           // offset of the two scale slots
+constexpr int NV_SMEM = NV_SC + 2 * NV_SC_SLOT;       // 40 KB
+constexpr int NV_GROUP_M = 8;
 
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
-__global__ __launch_bounds__(NV_THREADS)
+// SC4: scales copied 4 slices (16 bytes per row) at a time (K a multiple of 256)
+template <bool SC4>
+__global__ __launch_bounds__(NV_THREADS, 2)
 void gemm_w4a4_nvfp4_kernel(int M, int N, int K, int rank,
                             const uint8_t *__restrict__ act_codes,
                             const uint8_t *__restrict__ act_scales,
@@ -39,55 +61,64 @@ void gemm_w4a4_nvfp4_kernel(int M, int N, int K, int rank,
                             const uint16_t *__restrict__ lora_up,
                             const uint16_t *__restrict__ bias, uint16_t *__restrict__ out)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t s_a[NV_BM * NV_LDS_STRIDE];   // fp16 bits
-    __shared__ __attribute__((aligned(16))) uint16_t s_b[NV_BN * NV_LDS_STRIDE];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[NV_SMEM];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int l32 = lane & 31, h = lane >> 5;
-    const int nbn = (N + NV_BN - 1) / NV_BN;
-    const int m0 = (int)(blockIdx.x / nbn) * NV_BM, n0 = (int)(blockIdx.x % nbn) * NV_BN;
-    const size_t rowbytes = (size_t)(K >> 1);
-    const int NG16 = K >> 4;
+    const int nbm = (M + NV_BM - 1) / NV_BM, nbn = (N + NV_BN - 1) / NV_BN;
+    int bm, bn;
+    tile_of_block((int)blockIdx.x, nbm, nbn, NV_GROUP_M, bm, bn);
+    const int m0 = bm * NV_BM, n0 = bn * NV_BN;
+    const int NS = K >> 6;                            // slices
+    const int rowbytes = K >> 1;
+    const int NG16 = K >> 4;                          // scale bytes per row
 
-    // dequant duty: thread t handles row t/2 of both tiles, K half (t%2)*32 .. +32
-    const int d_row = tid >> 1, d_half = tid & 1;
-    const int am = m0 + d_row, bn = n0 + d_row;
-    const bool a_ok = am < M, b_ok = bn < N;
-    const uint8_t *a_cp = act_codes + (size_t)(a_ok ? am : 0) * rowbytes + 16 * d_half;
-    const uint8_t *b_cp = wgt_codes + (size_t)(b_ok ? bn : 0) * rowbytes + 16 * d_half;
-    const uint8_t *a_sp = act_scales + (size_t)(a_ok ? am : 0) * NG16 + 2 * d_half;
-    const uint8_t *b_sp = wgt_scales + (size_t)(b_ok ? bn : 0) * NG16 + 2 * d_half;
-
-    v4u ra, rb;
-    uint32_t sa0, sa1, sb0, sb1;
-    auto gload = [&](int kb) {
-        const int kbyte = kb * (NV_BK / 2), kgrp = kb * (NV_BK / 16);
-        ra = a_ok ? *(const v4u *)(a_cp + kbyte) : v4u{0u, 0u, 0u, 0u};
-        rb = b_ok ? *(const v4u *)(b_cp + kbyte) : v4u{0u, 0u, 0u, 0u};
-        sa0 = a_ok ? a_sp[kgrp] : 0u;
-        sa1 = a_ok ? a_sp[kgrp + 1] : 0u;
-        sb0 = b_ok ? b_sp[kgrp] : 0u;
-        sb1 = b_ok ? b_sp[kgrp + 1] : 0u;
+    // Producer role (as in the int4 kernel): wave w copies LDS chunk w (1 KB)
+    // of the A and of the B codes of every slice, lane l -> row 64*(w%2) + l,
+    // half w/2; rows past M (columns past N) read a clamped valid row whose
+    // outputs are never stored.  Waves 0,1 copy the A scales of their 64
+    // rows, waves 2,3 the B scales.
+    const int p_half = wave >> 1, p_row = 64 * (wave & 1) + lane;
+    const uint8_t *pa_base = act_codes + (size_t)m0 * rowbytes;
+    const uint8_t *pb_base = wgt_codes + (size_t)n0 * rowbytes;
+    const uint32_t pa_off = (uint32_t)(min(p_row, M - 1 - m0) * rowbytes + 16 * p_half);
+    const uint32_t pb_off = (uint32_t)(min(p_row, N - 1 - n0) * rowbytes + 16 * p_half);
+    const bool ps_is_a = wave < 2;
+    const uint8_t *ps_base = ps_is_a ? act_scales + (size_t)m0 * NG16 : wgt_scales + (size_t)n0 * NG16;
+    const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)pa_base, (short)0, min(NV_BM, M - m0) * rowbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)pb_base, (short)0, min(NV_BN, N - n0) * rowbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rss = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)ps_base, (short)0, (ps_is_a ? min(NV_BM, M - m0) : min(NV_BN, N - n0)) * NG16, 0x00020000);
+    auto issue_codes = [&](int g, int stage) {
+        uint8_t *st = smem + stage * NV_STAGE + wave * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lptr_t)st, 16, pa_off, g * 32, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lptr_t)(st + NV_CODES), 16, pb_off, g * 32, 0, 0);
     };
-    auto dequant_store = [&](const v4u &codes, uint32_t s0, uint32_t s1, uint16_t *dst) {
-        // the two group scales as fp16 (every E4M3 value is an fp16 normal)
-        const _Float16 f0 = (_Float16)e4m3_decode(s0), f1 = (_Float16)e4m3_decode(s1);
-        v4u o[4];
-#pragma unroll
-        for (int wdx = 0; wdx < 4; ++wdx) {          // dword wdx holds k = 8*wdx .. 8*wdx+7
-            const v2h f = wdx < 2 ? v2h{f0, f0} : v2h{f1, f1};
-            // byte p: k = 8*wdx + 2p (low nibble), 8*wdx + 2p + 1 (high nibble)
-            o[wdx][0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes[wdx], 1.0f, 0) * f);
-            o[wdx][1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes[wdx], 1.0f, 1) * f);
-            o[wdx][2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes[wdx], 1.0f, 2) * f);
-            o[wdx][3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes[wdx], 1.0f, 3) * f);
-        }
-        uint16_t *d = dst + d_row * NV_LDS_STRIDE + 32 * d_half;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) *(v4u *)(d + 8 * q) = o[q];
+    // This lane's scale row starts at byte row * K/16 = (its code offset) / 8
+    // (waves 2,3 copy the second code half: subtract its 16 bytes first).
+    // Scales of slices g .. g+3 into slot `slot`: [A rows | B rows][16 B].
+    auto issue_scales4 = [&](int g, int slot) {
+        uint32_t oa = pa_off, ob = pb_off;
+        opaque(oa);
+        opaque(ob);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rss,
+            (lptr_t)(smem + NV_SC + slot * NV_SC_SLOT + (ps_is_a ? 0 : NV_BM * 16) + 1024 * (wave & 1)),
+            16, (ps_is_a ? oa : ob - 16) >> 3, g * 4, 0, 0);
+    };
+    // Scales of slice g alone into entry g % 4 of a ring of 1 KB entries,
+    // each [A rows | B rows][4 B] (one entry per code stage in flight).
+    auto issue_scales1 = [&](int g) {
+        uint32_t oa = pa_off, ob = pb_off;
+        opaque(oa);
+        opaque(ob);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rss,
+            (lptr_t)(smem + NV_SC + (g % NV_STAGES) * 1024 + (ps_is_a ? 0 : NV_BM * 4) + 256 * (wave & 1)),
+            4, (ps_is_a ? oa : ob - 16) >> 3, g * 4, 0, 0);
     };
 
     v16f acc[2][2];
@@ -98,27 +129,101 @@ void gemm_w4a4_nvfp4_kernel(int M, int N, int K, int rank,
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
 
-    const int KB = K / NV_BK;
-    gload(0);
-    for (int kb = 0; kb < KB; ++kb) {
-        __syncthreads();                              // previous slice fully consumed
-        dequant_store(ra, sa0, sa1, s_a);
-        dequant_store(rb, sb0, sb1, s_b);
-        __syncthreads();
-        if (kb + 1 < KB) gload(kb + 1);
+    // consumer offsets: fragments in a stage, scale pairs in a slot
+    int a_off[2], b_off[2], sa_off[2], sb_off[2];
 #pragma unroll
-        for (int ks = 0; ks < NV_BK / 16; ++ks) {
+    for (int t = 0; t < 2; ++t) {
+        const int ra = wm * 64 + t * 32 + l32, rb = wn * 64 + t * 32 + l32;
+        a_off[t] = h * (NV_CODES / 2) + ra * 16;
+        b_off[t] = NV_CODES + h * (NV_CODES / 2) + rb * 16;
+        // the lane's two groups of a slice are 2h, 2h+1: one 2-byte read
+        sa_off[t] = (SC4 ? ra * 16 : ra * 4) + 2 * h;
+        sb_off[t] = (SC4 ? (NV_BM + rb) * 16 : (NV_BM + rb) * 4) + 2 * h;
+    }
+
+    // one slice: dequantize this wave's fragments step by step and run the MFMAs
+    auto compute = [&](const uint8_t *st, const uint8_t *sc) {
+        v4u fa[2], fb[2];
+        v2h sa[2], sb[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            fa[t] = *(const v4u *)(st + a_off[t]);
+            fb[t] = *(const v4u *)(st + b_off[t]);
+            // two E4M3 scales -> fp16 {group 2h, group 2h+1}
+            sa[t] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(*(const uint16_t *)(sc + sa_off[t]), 1.0f, false);
+            sb[t] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(*(const uint16_t *)(sc + sb_off[t]), 1.0f, false);
+        }
+        // dword s of a fragment: k = 32h + 8s .. +7, group 2h + s/2
+        auto deq = [](uint32_t c, v2h sc2, int s) {
+            const v2h f = (s < 2) ? v2h{sc2[0], sc2[0]} : v2h{sc2[1], sc2[1]};
+            v4u o;
+            o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 0) * f);
+            o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 1) * f);
+            o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 2) * f);
+            o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 3) * f);
+            return __builtin_bit_cast(v8h, o);
+        };
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
             v8h av[2], bv[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                av[t] = *(const v8h *)(s_a + (wm * 64 + t * 32 + l32) * NV_LDS_STRIDE + 16 * ks + 8 * h);
-                bv[t] = *(const v8h *)(s_b + (wn * 64 + t * 32 + l32) * NV_LDS_STRIDE + 16 * ks + 8 * h);
+                av[t] = deq(fa[t][s], sa[t], s);
+                bv[t] = deq(fb[t][s], sb[t], s);
             }
 #pragma unroll
             for (int a = 0; a < 2; ++a)
 #pragma unroll
                 for (int b = 0; b < 2; ++b)
                     acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[a], bv[b], acc[a][b], 0, 0, 0);
+        }
+    };
+
+    if constexpr (SC4) {
+        // Per wave, slice g costs two copies (codes), plus one (scales) when
+        // g % 4 == 0; waiting until at most the copies of the two slices
+        // issued after g are in flight means that g has landed.
+        issue_codes(0, 0);
+        issue_scales4(0, 0);
+        issue_codes(1, 1);
+        issue_codes(2, 2);
+        for (int c = 0; c < NS; c += NV_SC_SLICES) {
+            const bool last = c + NV_SC_SLICES == NS;
+            const int par = (c >> 2) & 1;
+            const uint8_t *slot = smem + NV_SC + par * NV_SC_SLOT;
+#pragma unroll
+            for (int j = 0; j < NV_SC_SLICES; ++j) {
+                __builtin_amdgcn_sched_barrier(0);            // slices stay in program order
+                if (j < 2) wait_vmcnt(4);                     // slices c+j+1, c+j+2: codes only
+                else if (j == 2) { if (last) wait_vmcnt(2); else wait_vmcnt(5); }
+                else { if (last) wait_vmcnt(0); else wait_vmcnt(5); }
+                lds_barrier();
+                if (j == 0) {
+                    issue_codes(c + 3, 3);
+                } else if (!last) {
+                    issue_codes(c + j + 3, (j + 3) & 3);
+                    if (j == 1) issue_scales4(c + NV_SC_SLICES, par ^ 1);
+                }
+                compute(smem + j * NV_STAGE, slot + 4 * j);
+                // the slice's accumulation completes before the next barrier
+#pragma unroll
+                for (int a = 0; a < 2; ++a)
+#pragma unroll
+                    for (int b = 0; b < 2; ++b) opaque(acc[a][b]);
+            }
+        }
+    } else {
+        auto issue = [&](int g) {
+            issue_codes(g, g % NV_STAGES);
+            issue_scales1(g);
+        };
+        for (int g = 0; g < NV_STAGES - 1 && g < NS; ++g) issue(g);
+        for (int g = 0; g < NS; ++g) {
+            const int newer = min(NV_STAGES - 2, NS - 1 - g);
+            wait_vmcnt(3 * newer);
+            lds_barrier();
+            if (g + NV_STAGES - 1 < NS) issue(g + NV_STAGES - 1);
+            compute(smem + (g % NV_STAGES) * NV_STAGE, smem + NV_SC + (g % NV_STAGES) * 1024);
         }
     }
 
@@ -132,10 +237,16 @@ hipError_t launch_gemm_w4a4_nvfp4(int M, int N, int K, int rank, const void *act
                                   hipStream_t stream)
 {
     dim3 grid(((N + NV_BN - 1) / NV_BN) * ((M + NV_BM - 1) / NV_BM)), block(NV_THREADS);
-    hipLaunchKernelGGL(gemm_w4a4_nvfp4_kernel, grid, block, 0, stream, M, N, K, rank,
-                       (const uint8_t *)act_codes, (const uint8_t *)act_scales,
-                       (const uint8_t *)wgt_codes, (const uint8_t *)wgt_scales, alpha, lora_act,
-                       (const uint16_t *)lora_up, (const uint16_t *)bias, (uint16_t *)out);
+    if (K % 256 == 0)
+        hipLaunchKernelGGL((gemm_w4a4_nvfp4_kernel<true>), grid, block, 0, stream, M, N, K, rank,
+                           (const uint8_t *)act_codes, (const uint8_t *)act_scales,
+                           (const uint8_t *)wgt_codes, (const uint8_t *)wgt_scales, alpha, lora_act,
+                           (const uint16_t *)lora_up, (const uint16_t *)bias, (uint16_t *)out);
+    else
+        hipLaunchKernelGGL((gemm_w4a4_nvfp4_kernel<false>), grid, block, 0, stream, M, N, K, rank,
+                           (const uint8_t *)act_codes, (const uint8_t *)act_scales,
+                           (const uint8_t *)wgt_codes, (const uint8_t *)wgt_scales, alpha, lora_act,
+                           (const uint16_t *)lora_up, (const uint16_t *)bias, (uint16_t *)out);
     return hipGetLastError();
 }
 
