@@ -41,8 +41,12 @@
 namespace svdq {
 
 constexpr int QA_ROWS = 16;          // rows per block (one MFMA row tile)
-constexpr int QA_WAVES = 8;          // waves per block
+// waves per block: 16 (four per SIMD) for ranks up to 32, 8 above (the
+// low-rank partials of all waves are reduced in LDS)
+template <int RT> constexpr int qa_waves() { return RT <= 2 ? 16 : 8; }
 constexpr int QA_CHUNK = 64;         // K-groups whose 1/s is staged in LDS at a time
+constexpr int QA_XDEPTH = 2;         // x slices in flight per wave (groups ahead)
+constexpr int QA_PERIOD = 3;         // unroll period: a multiple of both ring sizes (3, and 3 or 1)
 
 __device__ __forceinline__ float v4u_elem(const v4u &v, int e) {
     // element e (0..7) of 8 packed bf16
@@ -50,15 +54,48 @@ __device__ __forceinline__ float v4u_elem(const v4u &v, int e) {
     return (e & 1) ? bf16_hi(w) : bf16_lo(w);
 }
 
+struct F16 { float v[16]; };
+
+// Rare paths, kept out of line so that the unrolled main loop stays small.
+// Smoothing by IEEE fp32 division, for lanes whose fast product is an fp32
+// subnormal and for channels whose 1/s leaves fp32's normal range.
+__device__ __noinline__ F16 smooth_exact(v4u x0, v4u x1, const uint16_t *__restrict__ smooth, int kbase) {
+    F16 r;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const float xv = v4u_elem(e < 8 ? x0 : x1, e & 7);
+        const int k = kbase + (e >> 3) * 32 + (e & 7);
+        const float s = smooth ? bf16_to_f32(smooth[k]) : 1.0f;
+        r.v[e] = xv / s;
+    }
+    return r;
+}
+
+// int4 codes of a group whose bf16 scale is tiny or zero: IEEE division
+// (a zero scale gives zero codes).  Returns the two packed code words.
+__device__ __noinline__ v2u int4_codes_exact(F16 xh, float sb) {
+    v2u word = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const float q = sb == 0.0f ? 0.0f : __builtin_amdgcn_fmed3f(__builtin_rintf(xh.v[e] / sb), -8.0f, 7.0f);
+        const uint32_t nib = __float_as_uint(q + 8388624.0f) & 15u;
+        word[e >> 3] |= nib << (4 * (e & 7));
+    }
+    return word;
+}
+
 template <int PREC, int RT>
-__global__ __launch_bounds__(QA_WAVES * 64)
+__global__ __launch_bounds__(qa_waves<RT>() * 64)
 void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
                          const uint16_t *__restrict__ smooth,
                          const uint16_t *__restrict__ lora_down,
                          uint8_t *__restrict__ codes, void *__restrict__ scales,
                          float *__restrict__ lora_act)
 {
-    constexpr int LSLOTS = RT <= 4 ? 3 : 1;   // low-rank slices prefetched unless the rank is large
+    constexpr int QA_WAVES = qa_waves<RT>();
+    constexpr int LSLOTS = 1;                 // low-rank slices (L2 resident): loaded per group
+    constexpr int SINV = QA_CHUNK * 64 / (QA_WAVES * 64);   // 1/s channels per thread per chunk
+    static_assert(SINV == 4 || SINV == 8, "1/s staging: 8 or 16 bytes of bf16 per thread");
     __shared__ float s_inv[QA_CHUNK * 64];
     __shared__ float s_part[RT > 0 ? QA_WAVES * QA_ROWS * RT * 16 : 1];
 
@@ -78,20 +115,15 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
     for (int c0 = 0; c0 < NG; c0 += QA_CHUNK) {
         const int cg = min(QA_CHUNK, NG - c0);
         int unsafe = 0;
-        for (int i = threadIdx.x; i < cg * 64; i += blockDim.x) {
-            float s = smooth ? bf16_to_f32(smooth[c0 * 64 + i]) : 1.0f;
-            float as = fabsf(s);
-            bool ok = (as >= 0x1p-64f) && (as <= 0x1p64f);
-            s_inv[i] = ok ? 1.0f / s : 0.0f;
-            unsafe |= ok ? 0 : 1;
-        }
-        unsafe = __syncthreads_or(unsafe);
 
         // This wave's groups in the chunk: g_i = c0 + wave + i * QA_WAVES.  x
-        // slices stream two groups ahead and the low-rank factor slices (L2
-        // resident) one group ahead, in register rings with compile-time slots.
+        // slices stream QA_XDEPTH groups ahead and the low-rank factor slices
+        // (L2 resident) one group ahead, in register rings with compile-time
+        // slots.  The loop body is one unroll period; a partial last period
+        // runs the same body with its surplus steps skipped, so that the
+        // kernel stays small enough for the instruction cache.
         const int n_w = wave < cg ? (cg - wave + QA_WAVES - 1) / QA_WAVES : 0;
-        v4u xring[3][2];
+        v4u xring[QA_XDEPTH + 1][2];
         v4u lring[LSLOTS][RT > 0 ? RT : 1][2];
         auto load_x = [&](int i, auto slot_c) __attribute__((always_inline)) {
             constexpr int S = decltype(slot_c)::value;
@@ -129,15 +161,12 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
                 xh[e] = v;
             }
             if (__builtin_expect(unsafe | __any(bad), 0)) {
-                // exact path: IEEE fp32 division
+                const F16 ex = smooth_exact(xr[0], xr[1], smooth, kbase);   // IEEE fp32 division
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    float xv = v4u_elem(xr[e >> 3], e & 7);
-                    int k = kbase + (e >> 3) * 32 + (e & 7);
-                    float s = smooth ? bf16_to_f32(smooth[k]) : 1.0f;
-                    xh[e] = xv / s;
-                }
+                for (int e = 0; e < 16; ++e) xh[e] = ex.v[e];
             }
+            // RNE to bf16 two at a time (v_cvt_pk_bf16_f32; fp32 subnormals are
+            // kept, so it equals the scalar rule for every finite value)
             v4u ah[2];
             float amax = 0.0f;
             float amax_j[2] = {0.0f, 0.0f};
@@ -145,11 +174,10 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
             for (int j = 0; j < 2; ++j) {
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
-                    uint32_t lo = f32_to_bf16_rne(xh[8 * j + 2 * p]);
-                    uint32_t hi = f32_to_bf16_rne(xh[8 * j + 2 * p + 1]);
-                    ah[j][p] = lo | (hi << 16);
-                    xh[8 * j + 2 * p] = __uint_as_float(lo << 16);
-                    xh[8 * j + 2 * p + 1] = __uint_as_float(hi << 16);
+                    const uint32_t pk = pack_bf16x2_rne(xh[8 * j + 2 * p], xh[8 * j + 2 * p + 1]);
+                    ah[j][p] = pk;
+                    xh[8 * j + 2 * p] = bf16_lo(pk);
+                    xh[8 * j + 2 * p + 1] = bf16_hi(pk);
                     amax_j[j] = fmaxf(amax_j[j], fmaxf(fabsf(xh[8 * j + 2 * p]),
                                                        fabsf(xh[8 * j + 2 * p + 1])));
                 }
@@ -176,14 +204,12 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
                 const float sb = __uint_as_float(sbits << 16);
                 uint32_t word[2] = {0u, 0u};
                 if (__builtin_expect(__any(sb < 0x1p-100f), 0)) {
-                    // tiny or zero scales: IEEE division (zero scale -> zero codes)
+                    F16 xv;
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        float q = sb == 0.0f ? 0.0f
-                                             : __builtin_amdgcn_fmed3f(__builtin_rintf(xh[e] / sb), -8.0f, 7.0f);
-                        uint32_t nib = __float_as_uint(q + 8388624.0f) & 15u;
-                        word[e >> 3] |= nib << (4 * (e & 7));
-                    }
+                    for (int e = 0; e < 16; ++e) xv.v[e] = xh[e];
+                    const v2u w = int4_codes_exact(xv, sb);
+                    word[0] = w[0];
+                    word[1] = w[1];
                 } else {
                     const float inv_s = 1.0f / sb;
 #pragma unroll
@@ -245,10 +271,11 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
         // group; surplus loads read valid memory and are never used) so that
         // the compiler can count the loads in flight exactly.
         const int i_last = n_w - 1;
-        auto step = [&](int i, auto xs_c, auto ls_c) __attribute__((always_inline)) {
-            constexpr int XS = decltype(xs_c)::value;
-            constexpr int LS = decltype(ls_c)::value;
-            load_x(min(i + 2, i_last), std::integral_constant<int, (XS + 2) % 3>{});
+        constexpr int XR = QA_XDEPTH + 1;                 // x ring slots
+        auto step = [&](int i, auto q_c) __attribute__((always_inline)) {
+            constexpr int Q = decltype(q_c)::value;       // i % QA_PERIOD
+            constexpr int XS = Q % XR, LS = Q % LSLOTS;
+            load_x(min(i + QA_XDEPTH, i_last), std::integral_constant<int, (XS + QA_XDEPTH) % XR>{});
             if constexpr (LSLOTS == 3) {
                 load_l(min(i + 1, i_last), std::integral_constant<int, (LS + 1) % 3>{});
                 process(i, xring[XS], lring[LS]);
@@ -257,21 +284,47 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
                 process(i, xring[XS], lring[0]);
             }
         };
-        using I0 = std::integral_constant<int, 0>;
-        using I1 = std::integral_constant<int, 1>;
-        using I2 = std::integral_constant<int, 2>;
         if (n_w > 0) {
-            load_x(0, I0{});
-            load_x(min(1, i_last), I1{});
-            if constexpr (LSLOTS == 3) load_l(0, I0{});
-            const int nfull = (n_w / 3) * 3;
-            for (int i = 0; i < nfull; i += 3) {
-                step(i, I0{}, I0{});
-                step(i + 1, I1{}, I1{});
-                step(i + 2, I2{}, I2{});
+            [&]<int... P>(std::integer_sequence<int, P...>) __attribute__((always_inline)) {
+                (load_x(min(P, i_last), std::integral_constant<int, P>{}), ...);
+            }(std::make_integer_sequence<int, QA_XDEPTH>{});
+            if constexpr (LSLOTS == 3) load_l(0, std::integral_constant<int, 0>{});
+        }
+        // 1/s of the chunk's channels (IEEE division), staged in LDS: thread t
+        // takes channels SINV*t .. +SINV-1 with one load, issued after the
+        // first x slices so that both latencies overlap.
+        {
+            const int i0 = threadIdx.x * SINV;
+            if (i0 < cg * 64) {
+                v4u sv = v4u{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};   // s = 1
+                if (smooth) {
+                    if constexpr (SINV == 8) {
+                        sv = *(const v4u *)(smooth + (size_t)c0 * 64 + i0);
+                    } else {
+                        const v2u s2 = *(const v2u *)(smooth + (size_t)c0 * 64 + i0);
+                        sv[0] = s2[0];
+                        sv[1] = s2[1];
+                    }
+                }
+                v4f inv[2];
+#pragma unroll
+                for (int e = 0; e < SINV; ++e) {
+                    const float sf = v4u_elem(sv, e);
+                    const float as = fabsf(sf);
+                    const bool ok = (as >= 0x1p-64f) && (as <= 0x1p64f);
+                    inv[e >> 2][e & 3] = ok ? 1.0f / sf : 0.0f;
+                    unsafe |= ok ? 0 : 1;
+                }
+                *(v4f *)(s_inv + i0) = inv[0];
+                if constexpr (SINV == 8) *(v4f *)(s_inv + i0 + 4) = inv[1];
             }
-            if (nfull < n_w) step(nfull, I0{}, I0{});
-            if (nfull + 1 < n_w) step(nfull + 1, I1{}, I1{});
+        }
+        unsafe = __syncthreads_or(unsafe);
+        if (n_w > 0) {
+            for (int i = 0; i < n_w; i += QA_PERIOD)
+                [&]<int... P>(std::integer_sequence<int, P...>) __attribute__((always_inline)) {
+                    ((i + P < n_w ? step(i + P, std::integral_constant<int, P>{}) : void()), ...);
+                }(std::make_integer_sequence<int, QA_PERIOD>{});
         }
         __syncthreads();
     }
@@ -303,14 +356,14 @@ static hipError_t launch_prec(int M, int K, int rank, const void *x, const void 
                               const void *lora_down, void *codes, void *scales, float *lora_act,
                               hipStream_t st)
 {
-    dim3 grid((M + QA_ROWS - 1) / QA_ROWS), block(QA_WAVES * 64);
+    dim3 grid((M + QA_ROWS - 1) / QA_ROWS);
     const uint16_t *xp = (const uint16_t *)x, *sp = (const uint16_t *)smooth,
                    *lp = (const uint16_t *)lora_down;
     uint8_t *cp = (uint8_t *)codes;
 #define QA_CASE(RTV)                                                                            \
     case RTV:                                                                                   \
-        hipLaunchKernelGGL((quantize_act_kernel<PREC, RTV>), grid, block, 0, st, M, K, xp, sp, lp, \
-                           cp, scales, lora_act);                                               \
+        hipLaunchKernelGGL((quantize_act_kernel<PREC, RTV>), grid, dim3(qa_waves<RTV>() * 64), 0, st, \
+                           M, K, xp, sp, lp, cp, scales, lora_act);                             \
         break;
     switch (rank / 16) {
         QA_CASE(0) QA_CASE(1) QA_CASE(2) QA_CASE(3) QA_CASE(4)
