@@ -148,7 +148,17 @@ def gemv_sweep(torch, synth, reps=50):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_int4_mlp_up_traffic.txt")
-GEMM_INT4_SOURCE = os.path.join(ROOT, "bit_w4a4_quantized_svdq_amd", "csrc", "gemm_w4a4_int4.hip")
+TRACE_FILE = os.path.join(ROOT, "profiles", "hot_path_dit_block_kernel_trace.txt")
+GEMM_INT4_SOURCES = [os.path.join(ROOT, "bit_w4a4_quantized_svdq_amd", "csrc", f)
+                     for f in ("gemm_w4a4_int4.hip", "gemm_common.h", "device_common.h")]
+STEP_KERNELS = [f"{n}.{k}" for n, *_ in LAYERS for k in ("quantize_act", "gemm_w4a4")] + ["adaln.awq_gemv"]
+
+
+def gemm_int4_source_hash():
+    h = hashlib.sha256()
+    for f in GEMM_INT4_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def recorded_traffic():
@@ -161,8 +171,7 @@ def recorded_traffic():
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 rec[k.strip()] = v.strip()
-        src = hashlib.sha256(open(GEMM_INT4_SOURCE, "rb").read()).hexdigest()
-        if rec.get("source_sha256") != src:
+        if rec.get("source_sha256") != gemm_int4_source_hash():
             return None
         return int(float(rec["hbm_bytes_per_launch"]))
     except (OSError, KeyError, ValueError):
@@ -198,6 +207,105 @@ def copy_calibration(torch, mb, reps):
         b.copy_(a)
     torch.cuda.synchronize()
     print(f"[bench] copied {mb} MiB x{reps}", file=sys.stderr, flush=True)
+
+
+def _csv_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _counter_mean_kib(run_dir, kernel_substr):
+    """Mean per-dispatch value of the one counter in a rocprofv3 --pmc csv run."""
+    import glob
+    vals = {}
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in _csv_rows(f):
+            if kernel_substr in r["Kernel_Name"]:
+                vals.setdefault(r["Dispatch_Id"], 0.0)
+                vals[r["Dispatch_Id"]] += float(r["Counter_Value"])
+    if not vals:
+        raise SystemExit(f"no {kernel_substr} dispatches in {run_dir}")
+    return sum(vals.values()) / len(vals), len(vals)
+
+
+def summarize_profiles(run_dir, warmup, steps):
+    """Write the committed profile summaries from a rocprofv3 run directory:
+    <run_dir>/trace (kernel trace of `bench.py --steps S --warmup W`, whose
+    JSON line is <run_dir>/trace_bench.json) and the FETCH_SIZE / WRITE_SIZE
+    runs <run_dir>/pmc_{gemm,copy}_{FETCH,WRITE}_SIZE."""
+    import glob
+    trace = glob.glob(os.path.join(run_dir, "trace", "**", "*kernel_trace.csv"), recursive=True)[0]
+    ours = [r for r in _csv_rows(trace)
+            if any(k in r["Kernel_Name"] for k in ("quantize_act_kernel", "gemm_w4a4", "awq_gemv_kernel"))]
+    ours.sort(key=lambda r: int(r["Start_Timestamp"]))
+    per = len(STEP_KERNELS)
+    if len(ours) != per * (warmup + steps):
+        raise SystemExit(f"expected {per * (warmup + steps)} hot-path dispatches, found {len(ours)}")
+    timed = ours[per * warmup:]
+    agg = {}
+    for i, r in enumerate(timed):
+        key = STEP_KERNELS[i % per]
+        kind = key.split(".")[1]
+        if kind.split("_")[0] not in r["Kernel_Name"]:
+            raise SystemExit(f"dispatch {i} of the timed steps is {r['Kernel_Name'][:60]}, expected {key}")
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        a = agg.setdefault(key, {"name": r["Kernel_Name"].split("(")[0].replace("void ", ""),
+                                 "grid": r["Grid_Size_X"], "vgpr": r["VGPR_Count"],
+                                 "agpr": r.get("Accum_VGPR_Count", "0"), "lds": r["LDS_Block_Size"], "us": []})
+        a["us"].append(d)
+    bench_line = None
+    for line in open(os.path.join(run_dir, "trace_bench.json")):
+        if line.startswith("{") and '"metric"' in line:
+            bench_line = json.loads(line)
+    ev = bench_line["kernels"]
+    lines = ["# Kernel durations of the hot-path step (bench.py), MI355X, rocprofv3 kernel trace",
+             "# Command (paths relative to the repository root; run with TMPDIR=/tmp):",
+             f"#   rocprofv3 --kernel-trace --stats -f csv -d {run_dir}/trace -o bench -- "
+             f"python3 bench.py --steps {steps} --warmup {warmup} --no-cpu-baseline --no-gemv-sweep",
+             f"# Trace columns: the {steps} timed steps only (dispatch order within a step gives the layer);",
+             "# event_us: the same run's bench.py HIP-event average for that kernel (launch stream).",
+             f"# Same-run bench value: {bench_line['value']} TOPS, {bench_line['ms_per_step']} ms/step.",
+             "#",
+             f"{'layer.kernel':24s} {'kernel':46s} {'grid':>7s} {'n':>3s} {'trace_avg_us':>12s} "
+             f"{'trace_min_us':>12s} {'event_us':>9s} {'VGPR':>5s} {'AGPR':>5s} {'LDS_B':>6s}"]
+    for key in STEP_KERNELS:
+        a = agg[key]
+        lines.append(f"{key:24s} {a['name'][:46]:46s} {a['grid']:>7s} {len(a['us']):3d} "
+                     f"{sum(a['us']) / len(a['us']):12.2f} {min(a['us']):12.2f} {ev[key]['us']:9.2f} "
+                     f"{a['vgpr']:>5s} {a['agpr']:>5s} {a['lds']:>6s}")
+    open(TRACE_FILE, "w").write("\n".join(lines) + "\n")
+
+    cf, _ = _counter_mean_kib(os.path.join(run_dir, "pmc_copy_FETCH_SIZE"), "copyBuffer")
+    cw, _ = _counter_mean_kib(os.path.join(run_dir, "pmc_copy_WRITE_SIZE"), "copyBuffer")
+    gf, nf = _counter_mean_kib(os.path.join(run_dir, "pmc_gemm_FETCH_SIZE"), "gemm_w4a4_int4")
+    gw, nw = _counter_mean_kib(os.path.join(run_dir, "pmc_gemm_WRITE_SIZE"), "gemm_w4a4_int4")
+    copy_kib = 256 * 1024
+    ff, fw = copy_kib / cf, copy_kib / cw
+    fetch, write = gf * 1024 * ff, gw * 1024 * fw
+    alg = algorithmic_bytes_gemm(TOKENS, 4 * HIDDEN, HIDDEN, 32, "int4")
+    out_b = TOKENS * 4 * HIDDEN * 2
+    cmd = "python3 bench.py"
+    t = ["# HBM traffic of the int4 W4A4 GEMM, DiT MLP up 4096x3072 -> 12288 (rank 32), per launch",
+         "# Commands (paths relative to the repository root; run with TMPDIR=/tmp):"]
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        t.append(f"#   rocprofv3 --pmc {c} -f csv -d {run_dir}/pmc_gemm_{c} -o run -- {cmd} "
+                 f"--profile-kernel mlp_up.gemm_w4a4 --steps 5")
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        t.append(f"#   rocprofv3 --pmc {c} -f csv -d {run_dir}/pmc_copy_{c} -o run -- {cmd} --copy-mb 256 --steps 5")
+    t += ["# Calibration: a plain device copy of 256 MiB (torch copy_, dispatched as __amd_rocclr_copyBuffer)",
+          f"#   reads FETCH_SIZE = {cf:.1f} KiB -> factor {ff:.4f};  WRITE_SIZE = {cw:.1f} KiB -> factor {fw:.4f}",
+          f"# GEMM (mean of {nf} / {nw} launches): FETCH_SIZE = {gf:.1f} KiB, WRITE_SIZE = {gw:.1f} KiB",
+          f"# Algorithmic bytes per launch: {alg} (codes + scales of both operands, lora_act, lora_up, bf16 out)",
+          f"# Reads are {fetch / (alg - out_b):.2f}x the algorithmic input bytes; "
+          f"writes are {write / out_b:.2f}x the {out_b / 1e6:.1f} MB output.",
+          "# source_sha256 covers gemm_w4a4_int4.hip, gemm_common.h and device_common.h (in that order).",
+          f"source_sha256: {gemm_int4_source_hash()}",
+          f"fetch_bytes_per_launch: {int(fetch)}",
+          f"write_bytes_per_launch: {int(write)}",
+          f"hbm_bytes_per_launch: {int(fetch + write)}"]
+    open(TRAFFIC_FILE, "w").write("\n".join(t) + "\n")
+    print(f"wrote {TRACE_FILE} and {TRAFFIC_FILE}")
 
 
 def cpu_baseline(synth, budget_rows=32):
@@ -239,7 +347,12 @@ def main():
                     help="run only this kernel --steps times (e.g. mlp_up.gemm_w4a4), for rocprofv3")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="run only a plain copy of this many MiB --steps times (counter calibration)")
+    ap.add_argument("--summarize", default=None, metavar="RUN_DIR",
+                    help="write the profiles/ summaries from a rocprofv3 run directory (no GPU needed)")
     args = ap.parse_args()
+    if args.summarize:
+        summarize_profiles(args.summarize, args.warmup, args.steps)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build measures the single-GPU hot path "
               f"(--gpus {args.gpus} was requested)", file=sys.stderr)
