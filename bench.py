@@ -113,7 +113,7 @@ def run_step(layers, xs, events=None):
     timed("adaln.awq_gemv", lambda: layers["adaln"](xs["adaln"][:1]))
 
 
-def gemv_sweep(torch, synth, reps=50):
+def gemv_sweep(torch, synth, reps=160):
     """W4A16 GEMV alone, M in {1,2,8}, rotating 16 weight copies (512 MB)."""
     from bit_w4a4_quantized_svdq_amd import capi
     name, K, N, seed = ADALN
@@ -132,16 +132,19 @@ def gemv_sweep(torch, synth, reps=50):
             c = copies[i % 16]
             capi.awq_gemv_w4a16(x[:M], c[0], c[1], c[2], None, y)
         torch.cuda.synchronize()
+        # batches of 16 back-to-back launches (one per weight copy) between two
+        # events: a single launch bracketed by events would add the launch gap
+        # (several us) to a kernel of ~10 us
         ev = []
-        for i in range(reps):
-            c = copies[i % 16]
+        for i in range(reps // 16):
             s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             s.record()
-            capi.awq_gemv_w4a16(x[:M], c[0], c[1], c[2], None, y)
+            for c in copies:
+                capi.awq_gemv_w4a16(x[:M], c[0], c[1], c[2], None, y)
             e.record()
             ev.append((s, e))
         torch.cuda.synchronize()
-        us = float(np.median([s.elapsed_time(e) for s, e in ev])) * 1e3
+        us = float(np.median([s.elapsed_time(e) for s, e in ev])) * 1e3 / 16
         gbps = algorithmic_bytes_gemv(M, N, K) / (us * 1e-6) / 1e9
         out[f"M={M}"] = {"us": round(us, 3), "GB/s": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4)}
     return out

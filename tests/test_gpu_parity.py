@@ -204,6 +204,9 @@ def test_layer_end_to_end_and_determinism():
 @pytest.mark.parametrize("M,N,K,with_bias", [
     (1, 1024, 3072, False), (2, 512, 3072, True), (8, 256, 3072, False), (17, 100, 128, True),
     (70, 96, 64, True), (3, 5, 64, False), (16, 48, 4160, True),
+    # small M with ragged N and K that is not a multiple of the 6-way K split
+    # or of 4 groups (the 2-byte scale path), and large K (several x chunks)
+    (1, 5, 64, True), (2, 33, 192, False), (1, 100, 4160, True), (2, 40, 8192, True), (1, 64, 8256, False),
 ])
 def test_awq_gemv_shapes(M, N, K, with_bias):
     rng = np.random.default_rng(4000 + M + N + K)
@@ -217,10 +220,11 @@ def test_awq_gemv_shapes(M, N, K, with_bias):
     assert_bf16_close(y, ref, f"gemv {M}x{N}x{K}")
 
 
-def test_awq_gemv_extreme_codes():
+@pytest.mark.parametrize("M", [1, 4])
+def test_awq_gemv_extreme_codes(M):
     """Codes 0 and 15 with zero points 0 and 15 (the (q - z) range ends)."""
     rng = np.random.default_rng(43)
-    M, N, K = 4, 64, 256
+    N, K = 64, 256
     x = synth.to_bf16_bits(rng.standard_normal((M, K)))
     q = np.where(rng.random((N, K)) < 0.5, 0, 15)
     codes = synth.pack_nibbles(q)
