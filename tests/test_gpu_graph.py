@@ -1,0 +1,64 @@
+"""A hot-path step captured into one HIP graph (torch.cuda.CUDAGraph on ROCm)
+gives, on every replay, exactly the outputs of the same step run eagerly --
+the form in which bench.py times the step.  Replays are interleaved with
+eager work and synchronizations, and each is compared bit for bit."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from bit_w4a4_quantized_svdq_amd import synth  # noqa: E402
+from tests.gpu_helpers import announce  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def _layers():
+    from bit_w4a4_quantized_svdq_amd.layer import AWQW4A16Linear, SVDQW4A4Linear
+    out = []
+    for i, (prec, M, K, N) in enumerate((("int4", 200, 512, 320), ("nvfp4", 130, 256, 192))):
+        w = synth.synthetic_w4a4_weights(100 + i, N, K, 32, prec)
+        L = SVDQW4A4Linear(prec, w["wgt_codes"], w["wgt_scales"], w["lora_down"], w["lora_up"], w["smooth"],
+                           synth.to_bf16_bits(np.random.default_rng(i).standard_normal(N)))
+        x, _ = synth.draw_activations(np.random.default_rng(200 + i), M, K, 4, 30.0)
+        xt = torch.from_numpy(synth.to_bf16_bits(x).view(np.int16)).view(torch.bfloat16).cuda()
+        out.append((L, xt))
+    aw = synth.synthetic_awq_weights(7, 256, 512)
+    G = AWQW4A16Linear(aw["wgt_codes"], aw["wgt_scales"], aw["wgt_zeros"], None)
+    xg = torch.from_numpy(synth.to_bf16_bits(np.random.default_rng(9).standard_normal((1, 512))).view(np.int16))
+    return out, (G, xg.view(torch.bfloat16).cuda())
+
+
+def _step(w4a4, gemv):
+    outs = [L(x) for L, x in w4a4]
+    G, xg = gemv
+    outs.append(G(xg))
+    return outs
+
+
+def test_graph_replay_matches_eager():
+    announce("graph replay", "int4 200x512->320 + nvfp4 130x256->192 + awq 1x512->256")
+    w4a4, gemv = _layers()
+    ref = [o.clone() for o in _step(w4a4, gemv)]            # eager; also allocates every buffer
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        _step(w4a4, gemv)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        outs = _step(w4a4, gemv)
+    for rep in range(3):
+        for o in outs:
+            o.zero_()                                        # stale results cannot pass
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (o, r) in enumerate(zip(outs, ref)):
+            assert torch.equal(o.view(torch.int16), r.view(torch.int16)), f"replay {rep}, output {i}"
+        eager = _step(w4a4, gemv)                            # eager work between replays
+        torch.cuda.synchronize()
+        for o, r in zip(eager, ref):
+            assert torch.equal(o.view(torch.int16), r.view(torch.int16))
