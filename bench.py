@@ -381,7 +381,7 @@ def main():
         summarize_profiles(args.summarize, args.warmup, args.steps)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build measures the single-GPU hot path "
+        print(f"bench.py runs on one GPU only: it measures the single-GPU hot path "
               f"(--gpus {args.gpus} was requested)", file=sys.stderr)
         sys.exit(2)
 
