@@ -27,9 +27,17 @@
 // core: per slice and wave 128 vector instructions against 16 MFMAs.  A
 // dot product does not depend on the order of k, so lane half h takes k =
 // 32h .. 32h+31 of the slice and MFMA step s its k = 32h + 8s .. +7, for A
-// and B alike.  When K is a multiple of 256 the scales travel 4 slices at a
-// time (16 bytes per row) and the loop runs in chunks of 4 slices with
-// compile-time wait counts; otherwise each slice's 4 scale bytes per row are
+// and B alike.
+//
+// Copies.  A copy instruction moves 64 lanes x 16 bytes; the vector memory
+// path handles it per distinct cache line, so 16 bytes from each of 64 rows
+// (one slice) costs four times the address work of 64 bytes from each of 16
+// rows.  When K is a multiple of 512 (the main path) a stage therefore holds
+// two slices, 64 bytes of every row, the scales travel 8 slices (32 bytes per
+// row) at a time, and two stages alternate with one barrier per stage.
+// Otherwise a 4-stage ring of single slices is used: when K is a multiple of
+// 256 its scales travel 4 slices at a time (16 bytes per row) with
+// compile-time wait counts, else each slice's 4 scale bytes per row are
 // copied on their own.
 #include "device_common.h"
 #include "gemm_common.h"
@@ -230,6 +238,171 @@ void gemm_w4a4_nvfp4_kernel(int M, int N, int K, int rank,
     gemm_epilogue(acc, alpha, M, N, rank, m0, n0, wm, wn, lane, lora_act, lora_up, bias, out);
 }
 
+// Main path (K a multiple of 512): a stage holds two slices, 64 bytes of
+// every row, so each copy instruction reads 16 rows x 64 B (four lanes per
+// row).  Within a row's 64 bytes the four 16-byte chunks are stored in the
+// order c ^ ((row >> 1) & 3), so that the 8 consecutive rows that a fragment
+// load serves per LDS cycle fall on distinct banks.
+constexpr int CO_ROWB = 64;                               // bytes per row and stage
+constexpr int CO_CODES = NV_BM * CO_ROWB;                 // 8 KB of A (or B) codes per stage
+constexpr int CO_STAGE = 2 * CO_CODES;                    // 16 KB
+constexpr int CO_SC_ROWB = 32;                            // scale bytes per row and chunk (8 slices)
+constexpr int CO_SC_SLOT = (NV_BM + NV_BN) * CO_SC_ROWB;  // 8 KB
+constexpr int CO_SC = 2 * CO_STAGE;
+constexpr int CO_SMEM = CO_SC + 2 * CO_SC_SLOT;           // 48 KB
+
+__device__ __forceinline__ int co_chunk_slot(int row, int c) { return c ^ ((row >> 1) & 3); }
+
+__global__ __launch_bounds__(NV_THREADS, 2)
+void gemm_w4a4_nvfp4_co_kernel(int M, int N, int K, int rank,
+                               const uint8_t *__restrict__ act_codes,
+                               const uint8_t *__restrict__ act_scales,
+                               const uint8_t *__restrict__ wgt_codes,
+                               const uint8_t *__restrict__ wgt_scales, float alpha,
+                               const float *__restrict__ lora_act,
+                               const uint16_t *__restrict__ lora_up,
+                               const uint16_t *__restrict__ bias, uint16_t *__restrict__ out)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t smem[CO_SMEM];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int l32 = lane & 31, h = lane >> 5;
+    const int nbm = (M + NV_BM - 1) / NV_BM, nbn = (N + NV_BN - 1) / NV_BN;
+    int bm, bn;
+    tile_of_block((int)blockIdx.x, nbm, nbn, NV_GROUP_M, bm, bn);
+    const int m0 = bm * NV_BM, n0 = bn * NV_BN;
+    const int NP = K >> 7;                            // stages of two slices
+    const int rowbytes = K >> 1;
+    const int NG16 = K >> 4;
+    const int rows_a = min(NV_BM, M - m0), rows_b = min(NV_BN, N - n0);
+
+    // copies of codes: wave w issues instructions w and w + 4 of A and of B
+    // (16 rows each); lane i -> row 16q + i/4, LDS slot i % 4, chunk c.
+    uint32_t ca_off[2], cb_off[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int q = wave + 4 * u, r = 16 * q + (lane >> 2), c = co_chunk_slot(r, lane & 3);
+        ca_off[u] = (uint32_t)(min(r, rows_a - 1) * rowbytes + 16 * c);
+        cb_off[u] = (uint32_t)(min(r, rows_b - 1) * rowbytes + 16 * c);
+    }
+    // copies of scales: 256 rows [A | B] x 32 B per chunk; wave w issues
+    // instructions 2w, 2w+1 (32 rows each): lane i -> row 32q + i/2, half i%2
+    const bool ps_is_a = wave < 2;
+    uint32_t s_off[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int q = 2 * wave + u, r = 32 * q + (lane >> 1) - (ps_is_a ? 0 : NV_BM);
+        s_off[u] = (uint32_t)(min(r, (ps_is_a ? rows_a : rows_b) - 1) * NG16 + 16 * (lane & 1));
+    }
+    const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(act_codes + (size_t)m0 * rowbytes), (short)0, rows_a * rowbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(wgt_codes + (size_t)n0 * rowbytes), (short)0, rows_b * rowbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rss = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(ps_is_a ? act_scales + (size_t)m0 * NG16 : wgt_scales + (size_t)n0 * NG16), (short)0,
+        (ps_is_a ? rows_a : rows_b) * NG16, 0x00020000);
+    auto issue_codes = [&](int p) {
+        uint8_t *st = smem + (p & 1) * CO_STAGE;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lptr_t)(st + (wave + 4 * u) * 1024), 16, ca_off[u], p * CO_ROWB, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lptr_t)(st + CO_CODES + (wave + 4 * u) * 1024), 16, cb_off[u], p * CO_ROWB, 0, 0);
+        }
+    };
+    auto issue_scales = [&](int ch) {
+        uint8_t *sl = smem + CO_SC + (ch & 1) * CO_SC_SLOT;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rss, (lptr_t)(sl + (2 * wave + u) * 1024), 16, s_off[u], ch * CO_SC_ROWB, 0, 0);
+    };
+
+    v16f acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+
+    // consumer offsets: for slice-in-stage s, fragment of tile t at
+    // row * 64 + 16 * slot(row, 2s + h); scale pair at row * 32 + 4 * slice + 2h
+    int a_row[2], b_row[2], a_sw[2], b_sw[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        a_row[t] = wm * 64 + t * 32 + l32;
+        b_row[t] = wn * 64 + t * 32 + l32;
+        a_sw[t] = (a_row[t] >> 1) & 3;
+        b_sw[t] = (b_row[t] >> 1) & 3;
+    }
+
+    auto deq = [](uint32_t c, v2h sc2, int s) {
+        const v2h f = (s < 2) ? v2h{sc2[0], sc2[0]} : v2h{sc2[1], sc2[1]};
+        v4u o;
+        o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 0) * f);
+        o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 1) * f);
+        o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 2) * f);
+        o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 3) * f);
+        return __builtin_bit_cast(v8h, o);
+    };
+    // slice si (0, 1) of the stage at st; its scales at slice index ss of slot sc
+    auto compute = [&](const uint8_t *st, const uint8_t *sc, int si, int ss) {
+        v4u fa[2], fb[2];
+        v2h sa[2], sb[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            fa[t] = *(const v4u *)(st + a_row[t] * CO_ROWB + 16 * ((2 * si + h) ^ a_sw[t]));
+            fb[t] = *(const v4u *)(st + CO_CODES + b_row[t] * CO_ROWB + 16 * ((2 * si + h) ^ b_sw[t]));
+            sa[t] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
+                *(const uint16_t *)(sc + a_row[t] * CO_SC_ROWB + 4 * ss + 2 * h), 1.0f, false);
+            sb[t] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
+                *(const uint16_t *)(sc + (NV_BM + b_row[t]) * CO_SC_ROWB + 4 * ss + 2 * h), 1.0f, false);
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            v8h av[2], bv[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                av[t] = deq(fa[t][s], sa[t], s);
+                bv[t] = deq(fb[t][s], sb[t], s);
+            }
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[a], bv[b], acc[a][b], 0, 0, 0);
+        }
+    };
+
+    // Stage p: wait for its copies (issued one iteration earlier), barrier
+    // (every wave is past stage p-1, whose buffer receives stage p+1), issue
+    // stage p+1 and, at the first stage of a scale chunk, the next chunk's
+    // scales into the other slot (its previous chunk is finished).  Only the
+    // copies of that chunk may still be in flight at the next wait.
+    issue_scales(0);
+    issue_codes(0);
+    for (int p = 0; p < NP; ++p) {
+        __builtin_amdgcn_sched_barrier(0);
+        if ((p & 3) == 1 && (p >> 2) + 1 < (NP >> 2)) wait_vmcnt(2);
+        else wait_vmcnt(0);
+        lds_barrier();
+        if (p + 1 < NP) issue_codes(p + 1);
+        if ((p & 3) == 0 && (p >> 2) + 1 < (NP >> 2)) issue_scales((p >> 2) + 1);
+        const uint8_t *st = smem + (p & 1) * CO_STAGE;
+        const uint8_t *sc = smem + CO_SC + ((p >> 2) & 1) * CO_SC_SLOT;
+        compute(st, sc, 0, 2 * (p & 3));
+        compute(st, sc, 1, 2 * (p & 3) + 1);
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 2; ++b) opaque(acc[a][b]);
+    }
+
+    gemm_epilogue(acc, alpha, M, N, rank, m0, n0, wm, wn, lane, lora_act, lora_up, bias, out);
+}
+
 hipError_t launch_gemm_w4a4_nvfp4(int M, int N, int K, int rank, const void *act_codes,
                                   const void *act_scales, const void *wgt_codes,
                                   const void *wgt_scales, float alpha, const float *lora_act,
@@ -237,7 +410,12 @@ hipError_t launch_gemm_w4a4_nvfp4(int M, int N, int K, int rank, const void *act
                                   hipStream_t stream)
 {
     dim3 grid(((N + NV_BN - 1) / NV_BN) * ((M + NV_BM - 1) / NV_BM)), block(NV_THREADS);
-    if (K % 256 == 0)
+    if (K % 512 == 0)
+        hipLaunchKernelGGL(gemm_w4a4_nvfp4_co_kernel, grid, block, 0, stream, M, N, K, rank,
+                           (const uint8_t *)act_codes, (const uint8_t *)act_scales,
+                           (const uint8_t *)wgt_codes, (const uint8_t *)wgt_scales, alpha, lora_act,
+                           (const uint16_t *)lora_up, (const uint16_t *)bias, (uint16_t *)out);
+    else if (K % 256 == 0)
         hipLaunchKernelGGL((gemm_w4a4_nvfp4_kernel<true>), grid, block, 0, stream, M, N, K, rank,
                            (const uint8_t *)act_codes, (const uint8_t *)act_scales,
                            (const uint8_t *)wgt_codes, (const uint8_t *)wgt_scales, alpha, lora_act,

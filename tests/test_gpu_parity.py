@@ -134,6 +134,9 @@ def _random_gemm_case(prec, M, N, K, rank, with_bias, seed):
     (0, 257, 129, 192, 128, False, 0.5), (0, 64, 1000, 640, 48, True, 1.0),
     (1, 200, 320, 512, 32, True, 1.0), (1, 1, 64, 64, 0, False, 1.0), (1, 130, 96, 4160, 16, True, 0.5),
     (1, 257, 129, 192, 128, False, 2.0),
+    # NVFP4 staging paths: K % 512 == 0 (two-slice stages, several 8-slice scale
+    # chunks, ragged M and N) and K % 512 == 256 (single-slice ring, 4-slice scales)
+    (1, 67, 200, 1024, 32, True, 1.0), (1, 130, 192, 2560, 16, False, 0.5), (1, 200, 320, 768, 32, True, 1.0),
 ])
 def test_gemm_shapes(prec, M, N, K, rank, with_bias, alpha):
     ac, asc, t, w, bias = _random_gemm_case(prec, M, N, K, rank, with_bias, 2000 + M + N + K + prec)
