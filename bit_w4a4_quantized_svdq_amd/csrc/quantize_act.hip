@@ -21,13 +21,17 @@
 //    BE a midpoint when the result is below 2^-126 (a bf16 subnormal), and
 //    such lanes (fp32-subnormal products) are recomputed with IEEE division,
 //    as are channels whose 1/s would leave fp32's normal range.
+//  * Group scales: absmax * fl32(1/7) (int4) and absmax * fl32(1/6) (NVFP4)
+//    give, after the scale's own rounding to bf16 resp. E4M3, the same
+//    result as the division for every bf16 absmax (checked exhaustively).
 //  * int4: q = RNE(x_hat / scale).  The quotient is formed as one Newton
-//    step on the reciprocal (qe = x*inv; r = fma(-qe, scale, x) is exact;
-//    q = fma(r, inv, qe)), which returns the exact value whenever the exact
-//    quotient is a half-integer, and is within 2^-20 otherwise, while a
-//    non-tie quotient of two bf16 values is at least 2^-10 from a
-//    half-integer.  Rounding is then the fp32 add of 2^23 + 16 (ties to
-//    even), whose low 4 mantissa bits are the two's-complement nibble.
+//    step on the hardware reciprocal inv (v_rcp_f32, within 1 ulp):
+//    qe = x*inv; r = fma(-qe, scale, x) is exact; q = fma(r, inv, qe) is
+//    within ~2^-45 (relative) of the exact quotient, so it IS the exact value
+//    whenever the exact quotient is a half-integer, while a non-tie quotient
+//    of two bf16 values is at least 2^-10 from a half-integer.  Rounding to
+//    the nearest integer (ties to even) then happens in an fp32 add of 2^23
+//    (or in v_rndne_f32), and byte permutes pack the nibbles.
 //  * NVFP4: the E2M1 code of v = x_hat/d is rint(min(2|v|, |v|+2, |v|/2+4))
 //    clamped to 7 -- the piecewise-linear map that sends the E2M1 grid
 //    {0,.5,1,1.5,2,3,4,6} onto 0..7, so round-to-nearest-even on it gives the
@@ -44,7 +48,8 @@ constexpr int QA_ROWS = 16;          // rows per block (one MFMA row tile)
 // waves per block: 16 (four per SIMD) for ranks up to 32, 8 above (the
 // low-rank partials of all waves are reduced in LDS)
 template <int RT> constexpr int qa_waves() { return RT <= 2 ? 16 : 8; }
-constexpr int QA_CHUNK = 64;         // K-groups whose 1/s is staged in LDS at a time
+// K-groups whose 1/s is staged in LDS at a time: 8 channels per thread
+template <int RT> constexpr int qa_chunk() { return qa_waves<RT>() * 8; }
 constexpr int QA_XDEPTH = 2;         // x slices in flight per wave (groups ahead)
 constexpr int QA_PERIOD = 3;         // unroll period: a multiple of both ring sizes (3, and 3 or 1)
 
@@ -55,6 +60,37 @@ __device__ __forceinline__ float v4u_elem(const v4u &v, int e) {
 }
 
 struct F16 { float v[16]; };
+
+// max(m, |a|, |b|) in one v_max3_f32 (the values are finite; fp32 denormals
+// are preserved by the kernel's float mode)
+__device__ __forceinline__ float max3_abs(float m, float a, float b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    float r;
+    asm("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(r) : "v"(m), "v"(a), "v"(b));
+    return r;
+#else
+    return fmaxf(m, fmaxf(fabsf(a), fabsf(b)));
+#endif
+}
+
+// Eight quotients clamped to [-8, 7], rounded to the nearest integer (ties
+// to even) and packed as two's-complement nibbles, element e in nibble e.
+// Even elements: the fp32 add of 2^23 + 8 rounds and leaves q + 8 in the low
+// byte; odd ones are rounded first, then 16 q + 2^23 + 128 leaves 16 (q + 8)
+// in the low byte.  Byte permutes gather the low bytes, and the final xor
+// turns q + 8 into q mod 16.
+__device__ __forceinline__ uint32_t pack_int4_word(const float (&q)[8]) {
+    uint32_t t[8];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+        t[e] = __float_as_uint(q[e] + 8388616.0f);                                             // 2^23 + 8
+        t[e + 1] = __float_as_uint(__builtin_fmaf(__builtin_rintf(q[e + 1]), 16.0f, 8388736.0f));   // 2^23 + 128
+    }
+    // v_perm_b32: selector bytes 0-3 pick bytes of the second operand, 4-7 of the first, 0x0C gives 0
+    const uint32_t lo = __builtin_amdgcn_perm(t[2], t[0], 0x0C0C0400u) | __builtin_amdgcn_perm(t[6], t[4], 0x04000C0Cu);
+    const uint32_t hi = __builtin_amdgcn_perm(t[3], t[1], 0x0C0C0400u) | __builtin_amdgcn_perm(t[7], t[5], 0x04000C0Cu);
+    return (lo | hi) ^ 0x88888888u;
+}
 
 // Rare paths, kept out of line so that the unrolled main loop stays small.
 // Smoothing by IEEE fp32 division, for lanes whose fast product is an fp32
@@ -94,6 +130,7 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
 {
     constexpr int QA_WAVES = qa_waves<RT>();
     constexpr int LSLOTS = 1;                 // low-rank slices (L2 resident): loaded per group
+    constexpr int QA_CHUNK = qa_chunk<RT>();
     constexpr int SINV = QA_CHUNK * 64 / (QA_WAVES * 64);   // 1/s channels per thread per chunk
     static_assert(SINV == 4 || SINV == 8, "1/s staging: 8 or 16 bytes of bf16 per thread");
     __shared__ float s_inv[QA_CHUNK * 64];
@@ -178,8 +215,7 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
                     ah[j][p] = pk;
                     xh[8 * j + 2 * p] = bf16_lo(pk);
                     xh[8 * j + 2 * p + 1] = bf16_hi(pk);
-                    amax_j[j] = fmaxf(amax_j[j], fmaxf(fabsf(xh[8 * j + 2 * p]),
-                                                       fabsf(xh[8 * j + 2 * p + 1])));
+                    amax_j[j] = max3_abs(amax_j[j], xh[8 * j + 2 * p], xh[8 * j + 2 * p + 1]);
                 }
             }
 
@@ -199,7 +235,9 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
                 amax = fmaxf(amax_j[0], amax_j[1]);
                 amax = fmaxf(amax, shfl_xor_f(amax, 16));
                 amax = fmaxf(amax, shfl_xor_f(amax, 32));
-                const float s_f = amax / 7.0f;
+                // fl32(amax / 7) and fl32(amax * fl32(1/7)) round to the same bf16
+                // for every bf16 amax (checked exhaustively)
+                const float s_f = amax * (1.0f / 7.0f);
                 const uint32_t sbits = f32_to_bf16_rne(s_f);
                 const float sb = __uint_as_float(sbits << 16);
                 uint32_t word[2] = {0u, 0u};
@@ -211,15 +249,22 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
                     word[0] = w[0];
                     word[1] = w[1];
                 } else {
-                    const float inv_s = 1.0f / sb;
+                    // a reciprocal within 1 ulp suffices: the Newton step below
+                    // leaves an error of ~2^-45 relative, so half-integer quotients
+                    // come out exact and others stay far from a tie
+                    const float inv_s = __builtin_amdgcn_rcpf(sb);
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        float qe = xh[e] * inv_s;
-                        float rr = __builtin_fmaf(-qe, sb, xh[e]);
-                        float qc = __builtin_fmaf(rr, inv_s, qe);
-                        qc = __builtin_amdgcn_fmed3f(qc, -8.0f, 7.0f);
-                        uint32_t nib = __float_as_uint(qc + 8388624.0f) & 15u;   // + 2^23 + 16
-                        word[e >> 3] |= nib << (4 * (e & 7));
+                    for (int w = 0; w < 2; ++w) {
+                        float qv[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const float xv = xh[8 * w + e];
+                            float qe = xv * inv_s;
+                            float rr = __builtin_fmaf(-qe, sb, xv);
+                            float qc = __builtin_fmaf(rr, inv_s, qe);
+                            qv[e] = __builtin_amdgcn_fmed3f(qc, -8.0f, 7.0f);
+                        }
+                        word[w] = pack_int4_word(qv);
                     }
                 }
                 if (row_ok) {
@@ -235,12 +280,12 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     float a = fmaxf(amax_j[j], shfl_xor_f(amax_j[j], 16));
-                    const float s_f = a / 6.0f;
+                    const float s_f = a * (1.0f / 6.0f);   // same E4M3 code as fl32(a / 6) for every bf16 a
                     const uint32_t se = e4m3_encode_nonneg(s_f);
                     const float d = e4m3_decode_nonneg(se);
                     sc[j] = se;
                     if (d != 0.0f) {
-                        const float inv_d = 1.0f / d;
+                        const float inv_d = __builtin_amdgcn_rcpf(d);
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
                             float xv = xh[8 * j + e];

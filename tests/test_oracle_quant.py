@@ -251,3 +251,19 @@ def test_quantize_act_composes_the_steps(oracle):
     c_none, _, _ = oracle.quantize_act(oracle.INT4, x, None, L1)
     c_one, _, _ = oracle.quantize_act(oracle.INT4, x, np.full(256, 0x3F80, np.uint16), L1)
     assert np.array_equal(c_none, c_one)
+
+
+def test_scale_rules_by_reciprocal_product_equal_division_for_every_bf16():
+    """The GPU quantizer forms the group scale as amax * fl32(1/7) (int4) and
+    amax * fl32(1/6) (NVFP4) instead of dividing.  After the scale's own
+    rounding (RNE to bf16, resp. the E4M3 encoder) both equal the oracle's
+    fl32(amax / 7) and fl32(amax / 6) rules for every finite non-negative bf16
+    amax, subnormals included (exhaustive over all 32640 values)."""
+    import oracle
+    a = (np.arange(0, 0x7F80, dtype=np.uint32) << 16).view(np.float32)
+    by_div = (a / np.float32(7)).astype(np.float32)
+    by_mul = (a * (np.float32(1) / np.float32(7))).astype(np.float32)
+    assert np.array_equal(oracle.f32_to_bf16(by_div), oracle.f32_to_bf16(by_mul))
+    by_div = (a / np.float32(6)).astype(np.float32)
+    by_mul = (a * (np.float32(1) / np.float32(6))).astype(np.float32)
+    assert np.array_equal(oracle.f32_to_e4m3(by_div), oracle.f32_to_e4m3(by_mul))
