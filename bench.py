@@ -133,7 +133,10 @@ def capture_step(torch, layers, xs):
 
 
 def gemv_sweep(torch, synth, reps=160):
-    """W4A16 GEMV alone, M in {1,2,8}, rotating 16 weight copies (512 MB)."""
+    """The W4A16 layer alone on the adaptive-norm weights (3072 -> 18432),
+    rotating 16 weight copies (512 MB): M in {1,2,8} (the GEMV, GB/s against
+    HBM) and M in {256,1024,4096} (the library's GEMM regime, TFLOP/s against
+    the bf16 matrix-core peak)."""
     from bit_w4a4_quantized_svdq_amd import capi
     name, K, N, seed = ADALN
     copies = []
@@ -143,9 +146,9 @@ def gemv_sweep(torch, synth, reps=160):
                        torch.from_numpy(aw["wgt_scales"].view(np.int16)).view(torch.bfloat16).cuda(),
                        torch.from_numpy(aw["wgt_zeros"].view(np.int16)).view(torch.bfloat16).cuda()])
     rng = np.random.default_rng(seed)
-    x = torch.from_numpy(synth.to_bf16_bits(rng.standard_normal((8, K))).view(np.int16)).view(torch.bfloat16).cuda()
+    x = torch.from_numpy(synth.to_bf16_bits(rng.standard_normal((4096, K))).view(np.int16)).view(torch.bfloat16).cuda()
     out = {}
-    for M in (1, 2, 8):
+    for M in (1, 2, 8, 256, 1024, 4096):
         y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
         for i in range(20):
             c = copies[i % 16]
@@ -155,7 +158,7 @@ def gemv_sweep(torch, synth, reps=160):
         # events: a single launch bracketed by events would add the launch gap
         # (several us) to a kernel of ~10 us
         ev = []
-        for i in range(reps // 16):
+        for i in range(reps // 16 if M <= 8 else 3):
             s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             s.record()
             for c in copies:
@@ -164,8 +167,14 @@ def gemv_sweep(torch, synth, reps=160):
             ev.append((s, e))
         torch.cuda.synchronize()
         us = float(np.median([s.elapsed_time(e) for s, e in ev])) * 1e3 / 16
-        gbps = algorithmic_bytes_gemv(M, N, K) / (us * 1e-6) / 1e9
-        out[f"M={M}"] = {"us": round(us, 3), "GB/s": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4)}
+        if M <= 8:
+            gbps = algorithmic_bytes_gemv(M, N, K) / (us * 1e-6) / 1e9
+            out[f"M={M}"] = {"us": round(us, 3), "GB/s": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4)}
+        else:
+            tf = 2.0 * M * N * K / (us * 1e-6) / 1e12
+            out[f"M={M}"] = {"us": round(us, 3), "TFLOP/s": round(tf, 1),
+                             "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        print(f"[bench] awq M={M}: {us:.1f} us", file=sys.stderr, flush=True)
     return out
 
 
@@ -202,12 +211,18 @@ def recorded_traffic():
 
 def profile_kernel(torch, synth, name, reps):
     """Run one hot-path kernel ``reps`` times on its full-size inputs (for
-    rocprofv3).  name: <layer>.quantize_act | <layer>.gemm_w4a4 | adaln.awq_gemv"""
+    rocprofv3).  name: <layer>.quantize_act | <layer>.gemm_w4a4 | adaln.awq_gemv |
+    adaln.awq_gemm (the adaptive-norm weights applied to 4096 rows of x)"""
     layers, xs = build_inputs(torch, synth)
     layer, kind = name.split(".")
     L = layers[layer]
     if kind == "awq_gemv":
         fn = lambda: L(xs[layer][:1])
+    elif kind == "awq_gemm":
+        rng = np.random.default_rng(4096)
+        xl = torch.from_numpy(synth.to_bf16_bits(rng.standard_normal((4096, ADALN[1]))).view(np.int16))
+        xl = xl.view(torch.bfloat16).cuda()
+        fn = lambda: L(xl)
     else:
         b = L.buffers(xs[layer].shape[0])
         L.quantize(xs[layer], b)

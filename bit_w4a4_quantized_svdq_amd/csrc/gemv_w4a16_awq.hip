@@ -43,12 +43,14 @@ constexpr int AW_XBYTES = 64 * 1024;     // LDS for one K-chunk of x (without ro
 constexpr int AW_MAXCG = 64;             // groups per K-chunk at most
 constexpr int AW_XPAD = 16;              // bytes of padding per staged x row (bank spread)
 
-// Groups of one K-chunk: as many as fit in AW_XBYTES for Mt rows; with
-// 8-byte scale loads (VEC) a multiple of 4 * AW_KP so every K-part starts on
-// a multiple of 4 groups.
+// Groups of one K-chunk: as many as fit in AW_XBYTES for Mt rows, a multiple
+// of 8 (a row is staged in whole 1 KB copies of 8 groups, so its LDS stride
+// must hold them all); with 8-byte scale loads (VEC) a multiple of 4 * AW_KP
+// so every K-part starts on a multiple of 4 groups.
 __host__ __device__ inline int aw_chunk_groups(int Mt, bool vec) {
     int cg = AW_XBYTES / (Mt * 128);
     if (cg > AW_MAXCG) cg = AW_MAXCG;
+    cg -= cg % 8;
     return vec ? cg - cg % (4 * AW_KP) : cg;
 }
 
@@ -182,7 +184,7 @@ void awq_gemv_kernel(int M, int N, int K, const uint16_t *__restrict__ x,
         const float rcg8 = 1.0f / (float)cg8;
         // ---- x first: the chunk is copied global -> LDS (row m: cg*128 bytes
         // in 1 KB copies; a last partial copy reads clamped, valid elements of
-        // the row into the row's padding), and waited for before any code
+        // the row into the rest of the row's stride), and waited for before any code
         // load goes out, so that no copy is pending later and every wait on
         // the codes is for exactly the group about to be used.
         const int per_row = (cg + 7) >> 3, copies = Mt * per_row;
@@ -315,13 +317,19 @@ hipError_t launch_awq_gemv(int M, int N, int K, const void *x, const void *codes
 {
     const int MR = M <= 2 ? 2 : (M <= 8 ? 8 : (M <= 16 ? 16 : 32));
     const int nmt = (M + MR - 1) / MR;
+    const int Mt = M < MR ? M : MR;   // rows of the largest M-tile
     dim3 grid(((N + AW_TILE_N - 1) / AW_TILE_N) * nmt);
     const uint16_t *xp = (const uint16_t *)x, *sp = (const uint16_t *)scales,
                    *zp = (const uint16_t *)zeros, *bp = (const uint16_t *)bias;
     const uint8_t *cp = (const uint8_t *)codes;
     uint16_t *op = (uint16_t *)out;
-    // 8-byte scale/zero loads need every K-part to start on a multiple of 4 groups
-    const bool vec = ((K >> 6) % (4 * AW_KP)) == 0;
+    // 8-byte scale/zero loads need every K-part to start on a multiple of 4
+    // groups, i.e. chunks of a multiple of 4 * AW_KP groups.  From 22 rows of x
+    // on no such chunk fits the LDS budget (the rounding leaves 0 groups per
+    // chunk, and the chunk loop would never advance): those tiles take the
+    // 2-byte loads, which take any chunk of 8k groups (16 for 32 rows).
+    // Smaller tiles of the same launch get at least as many groups.
+    const bool vec = ((K >> 6) % (4 * AW_KP)) == 0 && aw_chunk_groups(Mt, true) > 0;
     switch (MR) {
         case 2: launch_mr<2>(vec, grid, stream, M, N, K, xp, cp, sp, zp, bp, op); break;
         case 8: launch_mr<8>(vec, grid, stream, M, N, K, xp, cp, sp, zp, bp, op); break;

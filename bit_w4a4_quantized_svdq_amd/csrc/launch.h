@@ -30,4 +30,17 @@ hipError_t launch_awq_gemv(int M, int N, int K, const void *x, const void *codes
                            const void *scales, const void *zeros, const void *bias, void *out,
                            hipStream_t stream);
 
+// The AWQ layer in the GEMM regime (awq_gemm_applies): K a multiple of 512,
+// at least AWQ_GEMM_MIN_M rows of x and at least AWQ_GEMM_MIN_TILES 32 x 32
+// output tiles (the GEMV's blocks); the GEMV otherwise.  Measured at K = 3072:
+// the GEMM takes ~53 us for any grid up to about one block per CU and
+// ~0.15 us per 128 x 128 tile beyond; the GEMV ~27 us up to ~400 of its
+// tiles and ~0.072 us per tile beyond; both scale with K.
+constexpr int AWQ_GEMM_MIN_M = 32;
+constexpr long long AWQ_GEMM_MIN_TILES = 576;
+bool awq_gemm_applies(int M, int N, int K);
+hipError_t launch_awq_gemm(int M, int N, int K, const void *x, const void *codes,
+                           const void *scales, const void *zeros, const void *bias, void *out,
+                           hipStream_t stream);
+
 }  // namespace svdq

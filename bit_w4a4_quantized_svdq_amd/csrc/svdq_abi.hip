@@ -151,9 +151,12 @@ svdq_status awq_gemv_w4a16(int64_t M, int64_t N, int64_t K, int32_t group_size, 
     if (M == 0 || N == 0) return SVDQ_OK;
     SVDQ_TRY(check_grid(M, N, 64, 16));
     SVDQ_TRY(check_device());
-    return launched(svdq::launch_awq_gemv((int)M, (int)N, (int)K, x, wgt_codes, wgt_scales, wgt_zeros,
-                                          bias, out, (hipStream_t)stream),
-                    "awq_gemv_w4a16");
+    const hipError_t e = svdq::awq_gemm_applies((int)M, (int)N, (int)K)
+        ? svdq::launch_awq_gemm((int)M, (int)N, (int)K, x, wgt_codes, wgt_scales, wgt_zeros, bias, out,
+                                (hipStream_t)stream)
+        : svdq::launch_awq_gemv((int)M, (int)N, (int)K, x, wgt_codes, wgt_scales, wgt_zeros, bias, out,
+                                (hipStream_t)stream);
+    return launched(e, "awq_gemv_w4a16");
 }
 
 svdq_status svdq_debug_group_sums(int64_t M, int64_t N, int64_t K, const void *act_codes,

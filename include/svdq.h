@@ -108,8 +108,11 @@ svdq_status svdq_gemm_w4a4(int32_t precision, int64_t M, int64_t N, int64_t K, i
  * memory-bound, precision-sensitive layers (adaptive-norm modulation;
  * "Nunchaku Lite" docs, awq_w4a16 int4 group 64).
  *   y[m,n] = RNE_bf16( sum_k x[m,k] * (q[n,k] - z[n,k/64]) * s[n,k/64] + bias[n] )
- * The sum is fp32 in unspecified order.  Tuned for M <= 32 (a GEMV); any M
- * works, the weights being streamed once per 32 rows of x.
+ * The sum is fp32 in unspecified order.  Any M works.  Small M runs as a
+ * GEMV that streams the weights once per 32 rows of x; when K is a multiple
+ * of 512, M >= 32 and ceil(M/32) * ceil(N/32) >= 576 it runs as a tiled
+ * matrix-core GEMM (bf16 products over 128 x 128 output tiles, codes unpacked
+ * in registers).  Both paths give the same result up to fp32 summation order.
  *
  *   group_size must be 64
  *   x          bf16 [M, K]

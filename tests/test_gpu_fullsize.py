@@ -7,7 +7,8 @@ Workloads (seeded, synthetic; weights prepared offline by the oracle):
   QKV    M=4096 K=3072 N=9216  int4 g64 rank 32
   MLP    up 4096x3072->12288, down 4096x12288->3072 (GELU-tanh input), int4, rank 32
   NVFP4  attention out 4096x3072->3072, rank 32
-  AWQ    adaptive-norm modulation, M in {1,2,8}, K=3072, N=18432"""
+  AWQ    adaptive-norm modulation, M in {1,2,8}, K=3072, N=18432; and the same
+         weights applied to all 4096 tokens (the GEMM regime), sampled rows"""
 import numpy as np
 import pytest
 import torch
@@ -75,3 +76,20 @@ def test_fullsize_adaln_awq(M):
     y = gpu_gemv(x, codes, scales, zeros, None)
     ref = oracle.awq_gemv(x, codes, scales, zeros, None)
     assert_bf16_close(y, ref, f"{cfg.name} M={M}")
+
+
+def test_fullsize_awq_gemm_regime():
+    """The AWQ weights of the adaptive-norm shape (N=18432, K=3072) applied to
+    4096 rows of x: the GEMM path, checked on sampled rows."""
+    cfg = synth.ADALN_AWQ
+    case = synth.linear_case(cfg, M=8)
+    codes, scales, zeros = oracle.awq_quantize_weight(case["W"])
+    rng = np.random.default_rng(4711)
+    M = 4096
+    x = synth.to_bf16_bits(rng.standard_normal((M, cfg.K)))
+    announce("fullsize awq gemm regime", cfg.name, "M", M)
+    y = gpu_gemv(x, codes, scales, zeros, None)
+    rows = _rows(M, 4711)
+    ref = oracle.awq_gemv(x[rows], codes, scales, zeros, None)
+    assert_bf16_close(y[rows], ref, f"{cfg.name} M={M}")
+    assert np.isfinite(synth.bf16_bits_to_f32(y)).all()

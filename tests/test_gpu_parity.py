@@ -210,6 +210,12 @@ def test_layer_end_to_end_and_determinism():
     # small M with ragged N and K that is not a multiple of the 6-way K split
     # or of 4 groups (the 2-byte scale path), and large K (several x chunks)
     (1, 5, 64, True), (2, 33, 192, False), (1, 100, 4160, True), (2, 40, 8192, True), (1, 64, 8256, False),
+    # K a multiple of 24 groups: 21 rows still take 8-byte scale loads, from 22
+    # rows on (and every multi-tile M up to the GEMM's range) the 2-byte loads
+    (21, 64, 1536, True), (22, 96, 3072, False), (32, 70, 1536, True), (64, 100, 3072, True),
+    (255, 40, 3072, False),
+    # tiles of 17..31 rows on the 2-byte path with several x copies per row
+    (20, 64, 4096, True), (40, 50, 4160, False), (23, 33, 2240, True),
 ])
 def test_awq_gemv_shapes(M, N, K, with_bias):
     rng = np.random.default_rng(4000 + M + N + K)
@@ -221,6 +227,43 @@ def test_awq_gemv_shapes(M, N, K, with_bias):
     y = gpu_gemv(x, codes, scales, zeros, bias)
     ref = oracle.awq_gemv(x, codes, scales, zeros, bias)
     assert_bf16_close(y, ref, f"gemv {M}x{N}x{K}")
+
+
+def awq_runs_as_gemm(M, N, K):
+    """The library's choice between its AWQ GEMV and GEMM kernels (K a
+    multiple of 512, at least 32 rows, at least 576 output tiles of 32 x 32)."""
+    return K % 512 == 0 and M >= 32 and -(-M // 32) * -(-N // 32) >= 576
+
+
+def gemm_tile_rows(M):
+    """Rows of x that cover, in every 128-row GEMM tile, each position class
+    of the kernel's row handling (the 8-row LDS swizzle, the 32-row MFMA
+    blocks, the two 64-row wave halves), plus the ragged tail."""
+    inner = np.array([0, 1, 7, 8, 30, 31, 33, 62, 63, 64, 66, 95, 96, 101, 126, 127])
+    rows = np.concatenate([t + inner for t in range(0, M, 128)] + [np.arange(max(M - 3, 0), M)])
+    return np.unique(rows[rows < M])
+
+
+@pytest.mark.parametrize("M,N,K,with_bias,sampled", [
+    # shapes in the GEMM regime: the smallest (one 128-row tile with 32 real
+    # rows, 576 tiles exactly), ragged M and N, several scale chunks, the
+    # smallest K; the larger K (3 and 8 scale chunks) on sampled rows
+    (32, 18432, 512, False, False), (256, 2304, 512, True, False), (300, 2000, 1024, False, False),
+    (513, 1200, 512, True, False), (1000, 600, 3072, False, True), (257, 2300, 4096, True, True),
+])
+def test_awq_gemm_regime_shapes(M, N, K, with_bias, sampled):
+    assert awq_runs_as_gemm(M, N, K)
+    rng = np.random.default_rng(4500 + M + N + K)
+    x = synth.to_bf16_bits(rng.standard_normal((M, K)))
+    W = synth.to_bf16_bits(rng.standard_normal((N, K)) * 0.02)
+    codes, scales, zeros = oracle.awq_quantize_weight(W)
+    bias = synth.to_bf16_bits(rng.standard_normal(N)) if with_bias else None
+    announce("awq gemm regime", M, N, K, "bias", with_bias)
+    y = gpu_gemv(x, codes, scales, zeros, bias)
+    rows = gemm_tile_rows(M) if sampled else np.arange(M)
+    ref = oracle.awq_gemv(x[rows], codes, scales, zeros, bias)
+    assert_bf16_close(y[rows], ref, f"awq gemm {M}x{N}x{K}")
+    assert np.isfinite(synth.bf16_bits_to_f32(y)).all()
 
 
 @pytest.mark.parametrize("M", [1, 4])
