@@ -80,6 +80,8 @@ _SIGS = {
                               None),
     "oracle_awq_quantize_weight": ([_I64, _I64, _P, _P, _P, _P], None),
     "oracle_awq_gemv_w4a16": ([_I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P], None),
+    "oracle_gelu_tanh_bf16": ([ctypes.c_uint16], ctypes.c_uint16),
+    "oracle_gelu_tanh_bf16_array": ([_I64, _P, _P], None),
 }
 
 
@@ -238,6 +240,21 @@ def quantize_act(precision, x, smooth, lora_down):
     lib().oracle_svdq_quantize_act(precision, M, K, rank, _ptr(x), _ptr(sm), _ptr(ld),
                                    _ptr(codes), _ptr(scales), _ptr(t), _ptr(xhat), _ptr(vals))
     return codes, scales, t[:, :rank].copy()
+
+
+def gelu_tanh_bf16(x):
+    """GELU (tanh form) of bf16 values, rounded once to bf16.  x: uint16 bits."""
+    x = _c(x, np.uint16)
+    out = np.empty(x.shape, np.uint16)
+    lib().oracle_gelu_tanh_bf16_array(x.size, _ptr(x), _ptr(out))
+    return out
+
+
+def gelu_quantize_act(precision, x, smooth, lora_down):
+    """The activation step of a layer that consumes GELU(x): x is the
+    preceding layer's bf16 output; GELU is applied before the smoothing.
+    Returns what ``quantize_act`` returns for gelu_tanh_bf16(x)."""
+    return quantize_act(precision, gelu_tanh_bf16(x), smooth, lora_down)
 
 
 def group_sums_int4(act_codes, wgt_codes, K):

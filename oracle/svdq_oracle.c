@@ -579,3 +579,52 @@ EXPORT void oracle_f32_to_e2m1_array(int64_t n, const float *in, uint8_t *out)
 {
     for (int64_t i = 0; i < n; ++i) out[i] = oracle_f32_to_e2m1(in[i]);
 }
+
+/* ------------------------------------------------------------------------ */
+/* O-12  GELU (tanh form) on bf16 values                                     */
+/* ------------------------------------------------------------------------ */
+/* The original engine runs the MLP's GELU fused into its kernels ([DOC]
+ * "Fused kernels": a fused GELU kernel for the MLP).  The pages name neither
+ * the GELU variant nor its precision; readings:
+ *   - the tanh form, gelu(y) = y/2 * (1 + tanh( sqrt(2/pi) * (y + 0.044715 y^3) )),
+ *     the variant of the DiT feed-forward blocks this layer serves;
+ *   - input and output are bf16 (compute_dtype): the result is the exact
+ *     function value rounded once to bf16 (RNE);
+ *   - non-finite inputs: +inf -> +inf, -inf -> -0 (the limit), NaN -> NaN.
+ * Evaluation in fp64 as y / (1 + exp(-2u)), u = sqrt(2/pi) (y + 0.044715 y^3):
+ * the same function (1 + tanh u = 2 / (1 + e^{-2u})) without the cancellation
+ * of 1 + tanh u for large negative u.  Ties: the exact value is a bf16
+ * rounding midpoint only in the limit of tiny |y|, where
+ * gelu(y) = y/2 + (y tanh u)/2 and the second term is positive but below
+ * fp64's resolution; so when the fp64 value lands exactly on a midpoint the
+ * exact value lies above it, and the tie goes toward +infinity. */
+static double gelu_tanh_f64(double y)
+{
+    const double c = 0.79788456080286535588;   /* sqrt(2/pi) */
+    const double u = c * (y + 0.044715 * y * y * y);
+    return y / (1.0 + exp(-2.0 * u));
+}
+
+EXPORT uint16_t oracle_gelu_tanh_bf16(uint16_t h)
+{
+    const double y = (double)oracle_bf16_to_f32(h);
+    if (isnan(y)) return (uint16_t)((h & 0x8000u) | 0x7FC0u);
+    if (isinf(y)) return y > 0 ? (uint16_t)0x7F80u : (uint16_t)0x8000u;
+    if (y == 0.0) return h;                       /* gelu(+-0) = +-0 */
+    const double v = gelu_tanh_f64(y);
+    const double a = fabs(v);
+    if (a < ldexp(1.0, -126)) {
+        /* bf16 subnormal range: spacing 2^-133, scaling exact */
+        const double s = a / ldexp(1.0, -133);
+        double q = nearbyint(s);
+        if (s - floor(s) == 0.5) q = v > 0 ? ceil(s) : floor(s);   /* tie toward +infinity */
+        const uint16_t sign = signbit(v) ? 0x8000u : 0u;   /* -0 when exp(-2u) overflowed */
+        return (uint16_t)(sign | (uint16_t)q);    /* q = 128 is the least normal, encoded alike */
+    }
+    return oracle_f64_to_bf16(v);
+}
+
+EXPORT void oracle_gelu_tanh_bf16_array(int64_t n, const uint16_t *in, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_gelu_tanh_bf16(in[i]);
+}
