@@ -209,10 +209,52 @@ def recorded_traffic():
         return None
 
 
+def gelu_fusion(torch, synth, layers, batches=3, per=10):
+    """The MLP down layer's activation step (4096 x 12288, rank 32, int4) fed
+    with the up projection's pre-activation output: svdq_gelu_quantize_act
+    (GELU inside the step) beside svdq_quantize_act on the activated input
+    and the standalone bf16 GELU pass (torch) that the fused step removes.
+    HIP events around batches of ``per`` launches; median of ``batches``."""
+    name, prec, M, K, N, rank, seed = next(l for l in LAYERS if l[0] == "mlp_down")
+    L = layers[name]
+    rng = np.random.default_rng(seed + 1000)
+    u = torch.from_numpy(synth.to_bf16_bits(rng.standard_normal((M, K)) * 5.7).view(np.int16))
+    u = u.view(torch.bfloat16).cuda()
+    h = torch.empty_like(u)
+    b = L.buffers(M)
+    fns = {"gelu_quantize_act": lambda: L.quantize(u, b, gelu=True),
+           "quantize_act": lambda: L.quantize(h, b),
+           "torch_gelu_pass": lambda: torch.ops.aten.gelu.out(u, approximate="tanh", out=h)}
+    out = {}
+    for key, fn in fns.items():
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ev = []
+        for _ in range(batches):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for _ in range(per):
+                fn()
+            e.record()
+            ev.append((s, e))
+        torch.cuda.synchronize()
+        us = float(np.median([s.elapsed_time(e) for s, e in ev])) * 1e3 / per
+        nb = algorithmic_bytes_quantize(M, K, rank, prec) if key != "torch_gelu_pass" else 4 * M * K
+        gbps = nb / (us * 1e-6) / 1e9
+        out[key] = {"us": round(us, 3), "GB/s": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4)}
+    out["unfused_us"] = round(out["quantize_act"]["us"] + out["torch_gelu_pass"]["us"], 3)
+    out["saved_us"] = round(out["unfused_us"] - out["gelu_quantize_act"]["us"], 3)
+    print(f"[bench] gelu fusion: {out['gelu_quantize_act']['us']:.1f} us fused, "
+          f"{out['unfused_us']:.1f} us unfused", file=sys.stderr, flush=True)
+    return out
+
+
 def profile_kernel(torch, synth, name, reps):
     """Run one hot-path kernel ``reps`` times on its full-size inputs (for
     rocprofv3).  name: <layer>.quantize_act | <layer>.gemm_w4a4 | adaln.awq_gemv |
-    adaln.awq_gemm (the adaptive-norm weights applied to 4096 rows of x)"""
+    adaln.awq_gemm (the adaptive-norm weights applied to 4096 rows of x) |
+    mlp_down.gelu_quantize_act (the activation step fed with pre-activations)"""
     layers, xs = build_inputs(torch, synth)
     layer, kind = name.split(".")
     L = layers[layer]
@@ -223,6 +265,12 @@ def profile_kernel(torch, synth, name, reps):
         xl = torch.from_numpy(synth.to_bf16_bits(rng.standard_normal((4096, ADALN[1]))).view(np.int16))
         xl = xl.view(torch.bfloat16).cuda()
         fn = lambda: L(xl)
+    elif kind == "gelu_quantize_act":
+        rng = np.random.default_rng(4097)
+        u = torch.from_numpy(synth.to_bf16_bits(rng.standard_normal(tuple(xs[layer].shape)) * 5.7).view(np.int16))
+        u = u.view(torch.bfloat16).cuda()
+        b = L.buffers(u.shape[0])
+        fn = lambda: L.quantize(u, b, gelu=True)
     else:
         b = L.buffers(xs[layer].shape[0])
         L.quantize(xs[layer], b)
@@ -384,7 +432,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-gemv-sweep", action="store_true")
+    ap.add_argument("--no-gemv-sweep", action="store_true",
+                    help="skip the side measurements (AWQ sweep, GELU fusion)")
     ap.add_argument("--profile-kernel", default=None,
                     help="run only this kernel --steps times (e.g. mlp_up.gemm_w4a4), for rocprofv3")
     ap.add_argument("--copy-mb", type=int, default=0,
@@ -478,6 +527,7 @@ def main():
                 "avg_launch_us": dom["us"]}
 
     gemv = None if args.no_gemv_sweep else gemv_sweep(torch, synth)
+    fusion = None if args.no_gemv_sweep else gelu_fusion(torch, synth, layers)
     cpu = None if args.no_cpu_baseline else cpu_baseline(synth)
 
     rec = {"metric": "W4A4 GEMM effective TOPS + % MFMA peak; W4A16 GEMV GB/s + % HBM peak",
@@ -489,7 +539,8 @@ def main():
                       "hidden": HIDDEN,
                       "layers": {n: f"{p} {M}x{K}->{N} rank {r}" for n, p, M, K, N, r, _ in LAYERS} |
                                 {"adaln": f"awq_w4a16 1x{K}->{N} g64"}},
-           "roofline": roofline, "kernels": kernels, "gemv": gemv, "cpu_baseline": cpu}
+           "roofline": roofline, "kernels": kernels, "gemv": gemv, "gelu_fusion": fusion,
+           "cpu_baseline": cpu}
     print(json.dumps(rec))
 
 

@@ -21,8 +21,9 @@ LIB_PATH = os.path.join(PKG, "_lib", "libsvdq.so")
 SVDQ_OK, SVDQ_ERR_INVALID_ARG, SVDQ_ERR_UNSUPPORTED, SVDQ_ERR_HIP = 0, 1, 2, 3
 SVDQ_INT4, SVDQ_NVFP4 = 0, 1
 
-EXPORTED = ("svdq_quantize_act", "svdq_gemm_w4a4", "awq_gemv_w4a16", "svdq_debug_group_sums",
-            "svdq_status_string", "svdq_last_error", "svdq_abi_version")
+EXPORTED = ("svdq_quantize_act", "svdq_gelu_quantize_act", "svdq_gemm_w4a4", "awq_gemv_w4a16",
+            "svdq_debug_group_sums", "svdq_debug_gelu_bf16", "svdq_status_string", "svdq_last_error",
+            "svdq_abi_version")
 
 
 class SvdqError(RuntimeError):
@@ -44,11 +45,14 @@ def lib() -> ctypes.CDLL:
                                "`python -m bit_w4a4_quantized_svdq_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
         L.svdq_quantize_act.argtypes = [_I32, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P]
+        L.svdq_gelu_quantize_act.argtypes = [_I32, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P]
         L.svdq_gemm_w4a4.argtypes = [_I32, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _F32, _P, _P, _P,
                                      _P, _P]
         L.awq_gemv_w4a16.argtypes = [_I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P]
         L.svdq_debug_group_sums.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P]
-        for f in ("svdq_quantize_act", "svdq_gemm_w4a4", "awq_gemv_w4a16", "svdq_debug_group_sums"):
+        L.svdq_debug_gelu_bf16.argtypes = [_I64, _P, _P, _P]
+        for f in ("svdq_quantize_act", "svdq_gelu_quantize_act", "svdq_gemm_w4a4", "awq_gemv_w4a16",
+                  "svdq_debug_group_sums", "svdq_debug_gelu_bf16"):
             getattr(L, f).restype = ctypes.c_int
         L.svdq_status_string.argtypes = [ctypes.c_int]
         L.svdq_status_string.restype = ctypes.c_char_p
@@ -102,6 +106,16 @@ def svdq_quantize_act(precision, x, smooth, lora_down, act_codes, act_scales, lo
                                    _stream(stream)), "svdq_quantize_act")
 
 
+def svdq_gelu_quantize_act(precision, x, smooth, lora_down, act_codes, act_scales, lora_act,
+                           stream=None):
+    """svdq_quantize_act of GELU(x) (tanh form), x being a GELU MLP's up-projection output."""
+    M, K = x.shape
+    rank = 0 if lora_down is None else lora_down.shape[0]
+    _check(lib().svdq_gelu_quantize_act(precision, M, K, rank, _ptr(x), _ptr(smooth), _ptr(lora_down),
+                                        _ptr(act_codes), _ptr(act_scales), _ptr(lora_act),
+                                        _stream(stream)), "svdq_gelu_quantize_act")
+
+
 def svdq_gemm_w4a4(precision, act_codes, act_scales, wgt_codes, wgt_scales, alpha, lora_act,
                    lora_up, bias, out, stream=None):
     """4-bit GEMM with the low-rank up-projection and bias; out is [M,N] bf16."""
@@ -121,6 +135,12 @@ def awq_gemv_w4a16(x, wgt_codes, wgt_scales, wgt_zeros, bias, out, group_size=64
     _check(lib().awq_gemv_w4a16(M, N, K, group_size, _ptr(x), _ptr(wgt_codes), _ptr(wgt_scales),
                                 _ptr(wgt_zeros), _ptr(bias), _ptr(out), _stream(stream)),
            "awq_gemv_w4a16")
+
+
+def svdq_debug_gelu_bf16(x, out, stream=None):
+    """GELU of bf16 values on the GELU-quantize step's own device code."""
+    _check(lib().svdq_debug_gelu_bf16(x.numel(), _ptr(x), _ptr(out), _stream(stream)),
+           "svdq_debug_gelu_bf16")
 
 
 def svdq_debug_group_sums(act_codes, wgt_codes, G, stream=None):

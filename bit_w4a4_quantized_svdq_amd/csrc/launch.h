@@ -7,9 +7,10 @@
 
 namespace svdq {
 
-hipError_t launch_quantize_act(int precision, int M, int K, int rank, const void *x,
+hipError_t launch_quantize_act(int precision, bool gelu, int M, int K, int rank, const void *x,
                                const void *smooth, const void *lora_down, void *act_codes,
                                void *act_scales, float *lora_act, hipStream_t stream);
+hipError_t launch_gelu_bf16(int64_t n, const void *in, void *out, hipStream_t stream);
 
 hipError_t launch_gemm_w4a4_int4(int M, int N, int K, int rank, const void *act_codes,
                                  const void *act_scales, const void *wgt_codes,

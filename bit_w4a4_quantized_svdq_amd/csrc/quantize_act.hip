@@ -37,19 +37,27 @@
 //    {0,.5,1,1.5,2,3,4,6} onto 0..7, so round-to-nearest-even on it gives the
 //    nearest value with ties to the even code.  v comes from the same Newton
 //    step; ties are exact and non-ties stay 2^-11 (relative) away.
+//
+// GELU variant (a layer fed by a GELU MLP's up projection): x is first
+// mapped through GELU (tanh form) of bf16 to bf16, exact by construction
+// (gelu_bf16.h: a 9.5 KB LDS table each block fills in fp64, plus exact rules
+// outside the table's range); everything after it is unchanged.
 #include <type_traits>
 
 #include "device_common.h"
+#include "gelu_bf16.h"
 #include "launch.h"
 
 namespace svdq {
 
 constexpr int QA_ROWS = 16;          // rows per block (one MFMA row tile)
-// waves per block: 16 (four per SIMD) for ranks up to 32, 8 above (the
-// low-rank partials of all waves are reduced in LDS)
-template <int RT> constexpr int qa_waves() { return RT <= 2 ? 16 : 8; }
+// waves per block: 16 (four per SIMD) for ranks up to 16, else 8 (the
+// low-rank partials of all waves are reduced in LDS).  At rank 32, 8 waves
+// were measured 2-4 % faster than 16 (whose 128-register budget also
+// spilled), and the GELU variants need more than 128 registers.
+template <int RT, bool GELU> constexpr int qa_waves() { return RT <= 1 && !GELU ? 16 : 8; }
 // K-groups whose 1/s is staged in LDS at a time: 8 channels per thread
-template <int RT> constexpr int qa_chunk() { return qa_waves<RT>() * 8; }
+template <int RT, bool GELU> constexpr int qa_chunk() { return qa_waves<RT, GELU>() * 8; }
 constexpr int QA_XDEPTH = 2;         // x slices in flight per wave (groups ahead)
 constexpr int QA_PERIOD = 3;         // unroll period: a multiple of both ring sizes (3, and 3 or 1)
 
@@ -120,21 +128,22 @@ __device__ __noinline__ v2u int4_codes_exact(F16 xh, float sb) {
     return word;
 }
 
-template <int PREC, int RT>
-__global__ __launch_bounds__(qa_waves<RT>() * 64)
+template <int PREC, int RT, bool GELU>
+__global__ __launch_bounds__((qa_waves<RT, GELU>() * 64))
 void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
                          const uint16_t *__restrict__ smooth,
                          const uint16_t *__restrict__ lora_down,
                          uint8_t *__restrict__ codes, void *__restrict__ scales,
                          float *__restrict__ lora_act)
 {
-    constexpr int QA_WAVES = qa_waves<RT>();
+    constexpr int QA_WAVES = qa_waves<RT, GELU>();
     constexpr int LSLOTS = 1;                 // low-rank slices (L2 resident): loaded per group
-    constexpr int QA_CHUNK = qa_chunk<RT>();
+    constexpr int QA_CHUNK = qa_chunk<RT, GELU>();
     constexpr int SINV = QA_CHUNK * 64 / (QA_WAVES * 64);   // 1/s channels per thread per chunk
     static_assert(SINV == 4 || SINV == 8, "1/s staging: 8 or 16 bytes of bf16 per thread");
     __shared__ float s_inv[QA_CHUNK * 64];
     __shared__ float s_part[RT > 0 ? QA_WAVES * QA_ROWS * RT * 16 : 1];
+    __shared__ uint16_t s_gelu[GELU ? GELU_TAB : 2];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -148,6 +157,8 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
     v4f acc[RT > 0 ? RT : 1];
 #pragma unroll
     for (int t = 0; t < (RT > 0 ? RT : 1); ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+    // the GELU table: published by the barrier before the first group is processed
+    if constexpr (GELU) gelu_table_fill(s_gelu, threadIdx.x, QA_WAVES * 64);
 
     for (int c0 = 0; c0 < NG; c0 += QA_CHUNK) {
         const int cg = min(QA_CHUNK, NG - c0);
@@ -182,7 +193,9 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
             asm volatile("" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
         };
-        auto process = [&](int i, const v4u (&xr)[2], const v4u (&lr)[RT > 0 ? RT : 1][2]) __attribute__((always_inline)) {
+        auto process = [&](int i, const v4u (&xin)[2], const v4u (&lr)[RT > 0 ? RT : 1][2]) __attribute__((always_inline)) {
+            v4u xr[2] = {xin[0], xin[1]};
+            if constexpr (GELU) gelu_bf16x16(xr, s_gelu);
             const int g = c0 + wave + i * QA_WAVES;
             const int kbase = g * 64 + 8 * kq;
             const float *inv = s_inv + (g - c0) * 64 + 8 * kq;
@@ -396,7 +409,7 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
     }
 }
 
-template <int PREC>
+template <int PREC, bool GELU>
 static hipError_t launch_prec(int M, int K, int rank, const void *x, const void *smooth,
                               const void *lora_down, void *codes, void *scales, float *lora_act,
                               hipStream_t st)
@@ -407,7 +420,7 @@ static hipError_t launch_prec(int M, int K, int rank, const void *x, const void 
     uint8_t *cp = (uint8_t *)codes;
 #define QA_CASE(RTV)                                                                            \
     case RTV:                                                                                   \
-        hipLaunchKernelGGL((quantize_act_kernel<PREC, RTV>), grid, dim3(qa_waves<RTV>() * 64), 0, st, \
+        hipLaunchKernelGGL((quantize_act_kernel<PREC, RTV, GELU>), grid, dim3((qa_waves<RTV, GELU>() * 64)), 0, st, \
                            M, K, xp, sp, lp, cp, scales, lora_act);                             \
         break;
     switch (rank / 16) {
@@ -419,13 +432,59 @@ static hipError_t launch_prec(int M, int K, int rank, const void *x, const void 
     return hipGetLastError();
 }
 
-hipError_t launch_quantize_act(int precision, int M, int K, int rank, const void *x,
+hipError_t launch_quantize_act(int precision, bool gelu, int M, int K, int rank, const void *x,
                                const void *smooth, const void *lora_down, void *act_codes,
                                void *act_scales, float *lora_act, hipStream_t stream)
 {
     if (precision == 0)
-        return launch_prec<0>(M, K, rank, x, smooth, lora_down, act_codes, act_scales, lora_act, stream);
-    return launch_prec<1>(M, K, rank, x, smooth, lora_down, act_codes, act_scales, lora_act, stream);
+        return gelu ? launch_prec<0, true>(M, K, rank, x, smooth, lora_down, act_codes, act_scales, lora_act, stream)
+                    : launch_prec<0, false>(M, K, rank, x, smooth, lora_down, act_codes, act_scales, lora_act, stream);
+    return gelu ? launch_prec<1, true>(M, K, rank, x, smooth, lora_down, act_codes, act_scales, lora_act, stream)
+                : launch_prec<1, false>(M, K, rank, x, smooth, lora_down, act_codes, act_scales, lora_act, stream);
+}
+
+// The GELU of n bf16 values through the quantize kernel's own code
+// (gelu_bf16x16: table, sentinel check and fallback), 16 values per thread;
+// a test hook.
+__global__ __launch_bounds__(256) void gelu_bf16_kernel(int64_t n, const uint16_t *__restrict__ in,
+                                                        uint16_t *__restrict__ out)
+{
+    __shared__ uint16_t tab[GELU_TAB];
+    gelu_table_fill(tab, threadIdx.x, 256);
+    __syncthreads();
+    const int64_t base = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 16;
+    v4u x[2];
+    if (base + 16 <= n) {
+        x[0] = *(const v4u *)(in + base);
+        x[1] = *(const v4u *)(in + base + 8);
+    } else {
+        // the tail (and lanes past n): zeros beyond n, nothing stored there
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+            const uint32_t lo = base + e < n ? in[base + e] : 0u;
+            const uint32_t hi = base + e + 1 < n ? in[base + e + 1] : 0u;
+            x[e >> 3][(e >> 1) & 3] = lo | (hi << 16);
+        }
+    }
+    gelu_bf16x16(x, tab);   // every lane takes part: the fallback's branch is wave-uniform
+    if (base + 16 <= n) {
+        *(v4u *)(out + base) = x[0];
+        *(v4u *)(out + base + 8) = x[1];
+    } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const uint32_t w = x[e >> 3][(e >> 1) & 3];
+            if (base + e < n) out[base + e] = (uint16_t)((e & 1) ? (w >> 16) : (w & 0xFFFFu));
+        }
+    }
+}
+
+hipError_t launch_gelu_bf16(int64_t n, const void *in, void *out, hipStream_t stream)
+{
+    const int64_t blocks = (n + 16 * 256 - 1) / (16 * 256);
+    hipLaunchKernelGGL(gelu_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       n, (const uint16_t *)in, (uint16_t *)out);
+    return hipGetLastError();
 }
 
 }  // namespace svdq

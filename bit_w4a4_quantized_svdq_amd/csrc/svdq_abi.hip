@@ -88,9 +88,10 @@ svdq_status launched(hipError_t e, const char *what) {
 
 extern "C" {
 
-svdq_status svdq_quantize_act(int32_t precision, int64_t M, int64_t K, int32_t rank,
-                              const void *x, const void *smooth, const void *lora_down,
-                              void *act_codes, void *act_scales, float *lora_act, void *stream)
+static svdq_status quantize_act_common(bool gelu, const char *name, int32_t precision, int64_t M,
+                                       int64_t K, int32_t rank, const void *x, const void *smooth,
+                                       const void *lora_down, void *act_codes, void *act_scales,
+                                       float *lora_act, void *stream)
 {
     if (precision != SVDQ_INT4 && precision != SVDQ_NVFP4)
         return fail(SVDQ_ERR_UNSUPPORTED, "precision must be SVDQ_INT4 or SVDQ_NVFP4 (got %d)", precision);
@@ -103,9 +104,35 @@ svdq_status svdq_quantize_act(int32_t precision, int64_t M, int64_t K, int32_t r
     SVDQ_TRY(check_ptr(lora_act, "lora_act", rank == 0));
     if (M == 0) return SVDQ_OK;
     SVDQ_TRY(check_device());
-    return launched(svdq::launch_quantize_act(precision, (int)M, (int)K, rank, x, smooth, lora_down,
+    return launched(svdq::launch_quantize_act(precision, gelu, (int)M, (int)K, rank, x, smooth, lora_down,
                                               act_codes, act_scales, lora_act, (hipStream_t)stream),
-                    "svdq_quantize_act");
+                    name);
+}
+
+svdq_status svdq_quantize_act(int32_t precision, int64_t M, int64_t K, int32_t rank,
+                              const void *x, const void *smooth, const void *lora_down,
+                              void *act_codes, void *act_scales, float *lora_act, void *stream)
+{
+    return quantize_act_common(false, "svdq_quantize_act", precision, M, K, rank, x, smooth, lora_down,
+                               act_codes, act_scales, lora_act, stream);
+}
+
+svdq_status svdq_gelu_quantize_act(int32_t precision, int64_t M, int64_t K, int32_t rank,
+                                   const void *x, const void *smooth, const void *lora_down,
+                                   void *act_codes, void *act_scales, float *lora_act, void *stream)
+{
+    return quantize_act_common(true, "svdq_gelu_quantize_act", precision, M, K, rank, x, smooth,
+                               lora_down, act_codes, act_scales, lora_act, stream);
+}
+
+svdq_status svdq_debug_gelu_bf16(int64_t n, const void *x, void *out, void *stream)
+{
+    if (n < 0 || n > ((int64_t)1 << 36)) return fail(SVDQ_ERR_INVALID_ARG, "n out of range (got %lld)", (long long)n);
+    SVDQ_TRY(check_ptr(x, "x", false));
+    SVDQ_TRY(check_ptr(out, "out", false));
+    if (n == 0) return SVDQ_OK;
+    SVDQ_TRY(check_device());
+    return launched(svdq::launch_gelu_bf16(n, x, out, (hipStream_t)stream), "svdq_debug_gelu_bf16");
 }
 
 svdq_status svdq_gemm_w4a4(int32_t precision, int64_t M, int64_t N, int64_t K, int32_t rank,
@@ -187,6 +214,6 @@ const char *svdq_status_string(svdq_status s)
 
 const char *svdq_last_error(void) { return g_last_error; }
 
-int32_t svdq_abi_version(void) { return 1; }
+int32_t svdq_abi_version(void) { return 2; }
 
 }  // extern "C"

@@ -62,9 +62,12 @@ class SVDQW4A4Linear:
             self._bufs[M] = b
         return b
 
-    def quantize(self, x, b):
-        capi.svdq_quantize_act(self.prec, x, self.smooth, self.lora_down, b["codes"], b["scales"],
-                               b["lora_act"] if self.rank else None)
+    def quantize(self, x, b, gelu=False):
+        """The activation step into the buffers ``b``; with ``gelu`` x is the
+        preceding GELU MLP up projection's output and GELU runs inside the step."""
+        fn = capi.svdq_gelu_quantize_act if gelu else capi.svdq_quantize_act
+        fn(self.prec, x, self.smooth, self.lora_down, b["codes"], b["scales"],
+           b["lora_act"] if self.rank else None)
 
     def gemm(self, b):
         capi.svdq_gemm_w4a4(self.prec, b["codes"], b["scales"], self.wgt_codes, self.wgt_scales,

@@ -94,7 +94,8 @@ def gelu_tanh(u):
 
 
 def gelu_activations(cfg_up: LinearConfig, cfg_down: LinearConfig, M: int | None = None):
-    """Input of the MLP down layer: bf16(gelu_tanh(u)), u ~ N(0, sigma^2).
+    """Input of the MLP down layer: bf16(gelu_tanh(u)), u ~ N(0, sigma^2);
+    also bf16(u) itself ("u", the up layer's output before the activation).
 
     sigma is the standard deviation of the up layer's output for the up
     layer's own input distribution: sqrt(w_std^2 * (K - n + n*scale^2)).
@@ -106,7 +107,7 @@ def gelu_activations(cfg_up: LinearConfig, cfg_down: LinearConfig, M: int | None
     sigma = cfg_up.w_std * math.sqrt(cfg_up.K - n + n * s * s)
     u = rng.standard_normal((M, cfg_down.K)) * sigma
     W = rng.standard_normal((cfg_down.N, cfg_down.K)) * cfg_down.w_std
-    return {"x": to_bf16_bits(gelu_tanh(u)), "W": to_bf16_bits(W), "sigma": sigma}
+    return {"x": to_bf16_bits(gelu_tanh(u)), "u": to_bf16_bits(u), "W": to_bf16_bits(W), "sigma": sigma}
 
 
 def pack_nibbles(vals) -> np.ndarray:

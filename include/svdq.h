@@ -34,8 +34,9 @@
  *  - A launch failure returns SVDQ_ERR_HIP.  Faults inside a kernel surface
  *    at the caller's next synchronization.  Outputs must not alias inputs.
  *    Calls keep no state besides a per-device architecture check; they may
- *    be made from several threads.  Non-finite inputs give unspecified
- *    (but memory-safe) outputs.
+ *    be made from several threads.  Non-finite inputs, and finite ones whose
+ *    smoothed value x/smooth overflows, give unspecified (but memory-safe)
+ *    outputs.
  */
 #ifndef SVDQ_H
 #define SVDQ_H
@@ -80,6 +81,22 @@ svdq_status svdq_quantize_act(int32_t precision, int64_t M, int64_t K, int32_t r
                               const void *x, const void *smooth, const void *lora_down,
                               void *act_codes, void *act_scales, float *lora_act,
                               void *stream);
+
+/*
+ * svdq_gelu_quantize_act -- svdq_quantize_act of GELU(x), for the layer that
+ * consumes a GELU MLP's up projection: x is that projection's bf16 output
+ * and the GELU runs inside this step, so it makes no pass of its own over
+ * the intermediate ("Nunchaku Lite" docs, "Fused kernels": the original
+ * engine's MLP uses a fused GELU).  GELU is the tanh form,
+ *   gelu(y) = y/2 * (1 + tanh( sqrt(2/pi) * (y + 0.044715 y^3) )),
+ * rounded once to bf16 from its exact value (bit-exact for every bf16 y;
+ * +inf -> +inf, -inf -> -0, NaN -> quiet NaN).  Arguments, layouts, checks
+ * and results are those of svdq_quantize_act with x replaced by GELU(x).
+ */
+svdq_status svdq_gelu_quantize_act(int32_t precision, int64_t M, int64_t K, int32_t rank,
+                                   const void *x, const void *smooth, const void *lora_down,
+                                   void *act_codes, void *act_scales, float *lora_act,
+                                   void *stream);
 
 /*
  * svdq_gemm_w4a4 -- second step: 4-bit GEMM with the fused low-rank
@@ -136,13 +153,21 @@ svdq_status awq_gemv_w4a16(int64_t M, int64_t N, int64_t K, int32_t group_size,
 svdq_status svdq_debug_group_sums(int64_t M, int64_t N, int64_t K, const void *act_codes,
                                   const void *wgt_codes, int32_t *G, void *stream);
 
+/*
+ * svdq_debug_gelu_bf16 -- test hook on the GELU of svdq_gelu_quantize_act
+ * (the same table and rules): out[i] = GELU(x[i]) for n bf16 values.
+ *   x, out     bf16 [n], device, 16-byte aligned; 0 <= n <= 2^36
+ * Not needed to run the layer.
+ */
+svdq_status svdq_debug_gelu_bf16(int64_t n, const void *x, void *out, void *stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *svdq_status_string(svdq_status s);
 
 /* Text of the last argument-check failure on the calling thread ("" if none). */
 const char *svdq_last_error(void);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2 (1 plus svdq_gelu_quantize_act and svdq_debug_gelu_bf16). */
 int32_t svdq_abi_version(void);
 
 #ifdef __cplusplus

@@ -95,15 +95,15 @@ def svdq_case(cfg: synth.LinearConfig, with_bias=False, M=None, x=None):
     return case
 
 
-def gpu_quantize(prec, x, smooth, lora_down, K):
+def gpu_quantize(prec, x, smooth, lora_down, K, gelu=False):
     from bit_w4a4_quantized_svdq_amd import capi
     M = x.shape[0]
     rank = 0 if lora_down is None else lora_down.shape[0]
     codes = poison(empty((M, K // 2), "u8"))
     scales = poison(empty((M, K // 64), "bf16") if prec == 0 else empty((M, K // 16), "u8"))
     lact = poison(empty((M, rank), "f32")) if rank else None
-    capi.svdq_quantize_act(prec, to_dev(x, "bf16"), to_dev(smooth, "bf16"), to_dev(lora_down, "bf16"),
-                           codes, scales, lact)
+    fn = capi.svdq_gelu_quantize_act if gelu else capi.svdq_quantize_act
+    fn(prec, to_dev(x, "bf16"), to_dev(smooth, "bf16"), to_dev(lora_down, "bf16"), codes, scales, lact)
     torch.cuda.synchronize()
     return (to_host(codes, "u8"), to_host(scales, "bf16" if prec == 0 else "u8"),
             None if lact is None else to_host(lact, "f32"))
