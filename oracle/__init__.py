@@ -82,6 +82,7 @@ _SIGS = {
     "oracle_awq_gemv_w4a16": ([_I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P], None),
     "oracle_gelu_tanh_bf16": ([ctypes.c_uint16], ctypes.c_uint16),
     "oracle_gelu_tanh_bf16_array": ([_I64, _P, _P], None),
+    "oracle_qk_norm_rope": ([_I64, _I64, _P, _P, _P, ctypes.c_double, _P, _P, _P], None),
 }
 
 
@@ -255,6 +256,32 @@ def gelu_quantize_act(precision, x, smooth, lora_down):
     preceding layer's bf16 output; GELU is applied before the smoothing.
     Returns what ``quantize_act`` returns for gelu_tanh_bf16(x)."""
     return quantize_act(precision, gelu_tanh_bf16(x), smooth, lora_down)
+
+
+def qk_norm_rope(y, q_w, k_w, eps, rope_cos, rope_sin):
+    """Per-head RMSNorm + rotary embedding of the Q and K columns of a grouped
+    QKV output y (bf16 [M, 3*H*128]); V columns unchanged.  q_w, k_w: bf16
+    [128]; rope_cos, rope_sin: fp32 [M, 64].  Returns bf16 [M, N]."""
+    y = _c(y, np.uint16)
+    M, N = y.shape
+    assert N % 384 == 0
+    out = np.empty((M, N), np.uint16)
+    lib().oracle_qk_norm_rope(M, N, _ptr(y), _ptr(_c(q_w, np.uint16)), _ptr(_c(k_w, np.uint16)),
+                              float(eps), _ptr(_c(rope_cos, np.float32)), _ptr(_c(rope_sin, np.float32)),
+                              _ptr(out))
+    return out
+
+
+def gemm_w4a4_qk_norm_rope(precision, act_codes, act_scales, wgt_codes, wgt_scales, lora_act,
+                           lora_up, bias, q_w, k_w, eps, rope_cos, rope_sin, alpha=1.0, rows=None):
+    """The grouped QKV layer's GEMM step followed by per-head RMSNorm and
+    rotary embedding of Q and K (``qk_norm_rope`` of the ``gemm_w4a4`` output);
+    ``rows`` as in ``gemm_w4a4`` (the angles of those rows are used)."""
+    y = gemm_w4a4(precision, act_codes, act_scales, wgt_codes, wgt_scales, lora_act, lora_up, bias,
+                  alpha=alpha, rows=rows)
+    if rows is not None:
+        rope_cos, rope_sin = np.asarray(rope_cos)[rows], np.asarray(rope_sin)[rows]
+    return qk_norm_rope(y, q_w, k_w, eps, rope_cos, rope_sin)
 
 
 def group_sums_int4(act_codes, wgt_codes, K):

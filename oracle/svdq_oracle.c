@@ -628,3 +628,49 @@ EXPORT void oracle_gelu_tanh_bf16_array(int64_t n, const uint16_t *in, uint16_t 
 {
     for (int64_t i = 0; i < n; ++i) out[i] = oracle_gelu_tanh_bf16(in[i]);
 }
+
+/* ------------------------------------------------------------------------ */
+/* O-13  per-head RMSNorm + rotary embedding of the Q and K projections      */
+/* ------------------------------------------------------------------------ */
+/* The original engine fuses the grouped Q, K, V projection with RMSNorm and
+ * RoPE ([DOC] "Fused kernels").  The pages give neither the head size nor the
+ * rotary layout; readings:
+ *   - heads of D = 128 channels; the N = 3 H D output columns are Q | K | V,
+ *     head h of Q at columns h D .. h D + 127 (likewise K, V);
+ *   - RMSNorm of each (row, Q or K head) over its D channels with its own
+ *     bf16 weight w (one for Q, one for K, shared by the heads):
+ *       n_j = y_j * w_j / sqrt( (1/D) sum_i y_i^2 + eps );
+ *   - the rotary embedding turns each adjacent channel pair (2i, 2i+1) of n
+ *     by the row's angle for pair i, given as cos/sin (fp32 [M, D/2], the
+ *     caller's positions and frequencies):
+ *       out_2i   = n_2i cos_i - n_2i+1 sin_i
+ *       out_2i+1 = n_2i+1 cos_i + n_2i sin_i;
+ *   - y is the layer's bf16 output (the unfused path's stored value); the
+ *     result is computed in fp64 and rounded once to bf16; V is unchanged. */
+EXPORT void oracle_qk_norm_rope(int64_t M, int64_t N, const uint16_t *y, const uint16_t *q_w,
+                                const uint16_t *k_w, double eps, const float *rope_cos,
+                                const float *rope_sin, uint16_t *out)
+{
+    const int64_t D = 128, HD = N / 3;
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t *yr = y + m * N;
+        uint16_t *orow = out + m * N;
+        for (int64_t c = 2 * HD; c < N; ++c) orow[c] = yr[c];          /* V */
+        for (int64_t c0 = 0; c0 < 2 * HD; c0 += D) {                    /* Q and K heads */
+            const uint16_t *w = c0 < HD ? q_w : k_w;
+            double ss = 0.0;
+            for (int64_t j = 0; j < D; ++j) {
+                const double v = (double)oracle_bf16_to_f32(yr[c0 + j]);
+                ss += v * v;
+            }
+            const double r = 1.0 / sqrt(ss / (double)D + eps);
+            for (int64_t i = 0; i < D / 2; ++i) {
+                const double n0 = (double)oracle_bf16_to_f32(yr[c0 + 2 * i]) * r * (double)oracle_bf16_to_f32(w[2 * i]);
+                const double n1 = (double)oracle_bf16_to_f32(yr[c0 + 2 * i + 1]) * r * (double)oracle_bf16_to_f32(w[2 * i + 1]);
+                const double cs = (double)rope_cos[m * (D / 2) + i], sn = (double)rope_sin[m * (D / 2) + i];
+                orow[c0 + 2 * i] = oracle_f64_to_bf16(n0 * cs - n1 * sn);
+                orow[c0 + 2 * i + 1] = oracle_f64_to_bf16(n1 * cs + n0 * sn);
+            }
+        }
+    }
+}
