@@ -209,12 +209,33 @@ def recorded_traffic():
         return None
 
 
+def interleaved_us(torch, fns, rounds=8, per=5):
+    """Median per-launch time of each function, the functions taking turns
+    in every round (batches of ``per`` launches between two HIP events), so
+    that the GPU's clock drift under sustained load affects all alike."""
+    for fn in fns.values():
+        for _ in range(2):
+            fn()
+    torch.cuda.synchronize()
+    ev = {k: [] for k in fns}
+    for _ in range(rounds):
+        for key, fn in fns.items():
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for _ in range(per):
+                fn()
+            e.record()
+            ev[key].append((s, e))
+    torch.cuda.synchronize()
+    return {k: float(np.median([s.elapsed_time(e) for s, e in v])) * 1e3 / per for k, v in ev.items()}
+
+
 def gelu_fusion(torch, synth, layers, batches=3, per=10):
     """The MLP down layer's activation step (4096 x 12288, rank 32, int4) fed
     with the up projection's pre-activation output: svdq_gelu_quantize_act
     (GELU inside the step) beside svdq_quantize_act on the activated input
     and the standalone bf16 GELU pass (torch) that the fused step removes.
-    HIP events around batches of ``per`` launches; median of ``batches``."""
+    Timed by ``interleaved_us``."""
     name, prec, M, K, N, rank, seed = next(l for l in LAYERS if l[0] == "mlp_down")
     L = layers[name]
     rng = np.random.default_rng(seed + 1000)
@@ -226,20 +247,9 @@ def gelu_fusion(torch, synth, layers, batches=3, per=10):
            "quantize_act": lambda: L.quantize(h, b),
            "torch_gelu_pass": lambda: torch.ops.aten.gelu.out(u, approximate="tanh", out=h)}
     out = {}
-    for key, fn in fns.items():
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
-        ev = []
-        for _ in range(batches):
-            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s.record()
-            for _ in range(per):
-                fn()
-            e.record()
-            ev.append((s, e))
-        torch.cuda.synchronize()
-        us = float(np.median([s.elapsed_time(e) for s, e in ev])) * 1e3 / per
+    times = interleaved_us(torch, fns, rounds=batches * 3, per=per)
+    for key in fns:
+        us = times[key]
         nb = algorithmic_bytes_quantize(M, K, rank, prec) if key != "torch_gelu_pass" else 4 * M * K
         gbps = nb / (us * 1e-6) / 1e9
         out[key] = {"us": round(us, 3), "GB/s": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4)}
@@ -250,11 +260,57 @@ def gelu_fusion(torch, synth, layers, batches=3, per=10):
     return out
 
 
+def qk_fusion(torch, synth, layers, xs, per=5):
+    """The grouped QKV layer's GEMM (4096 x 3072 -> 9216, 24 heads of 128)
+    with per-head RMSNorm + rotary embedding of Q and K in its epilogue,
+    beside the plain GEMM and an unfused norm/rotary pass over Q and K in
+    torch (fp32 math on the bf16 output).  Timed by ``interleaved_us``."""
+    L = layers["qkv"]
+    M, N = xs["qkv"].shape[0], L.N
+    b = L.buffers(M)
+    L.quantize(xs["qkv"], b)
+    rng = np.random.default_rng(4321)
+    qw = torch.from_numpy(synth.to_bf16_bits(rng.uniform(0.5, 1.5, 128)).view(np.int16)).view(torch.bfloat16).cuda()
+    kw = torch.from_numpy(synth.to_bf16_bits(rng.uniform(0.5, 1.5, 128)).view(np.int16)).view(torch.bfloat16).cuda()
+    th = rng.uniform(-np.pi, np.pi, (M, 64))
+    cs = torch.from_numpy(np.cos(th).astype(np.float32)).cuda()
+    sn = torch.from_numpy(np.sin(th).astype(np.float32)).cuda()
+    HD = N // 3
+    y = b["out"]
+    wqk = torch.cat([qw.float().expand(HD // 128, 128), kw.float().expand(HD // 128, 128)])
+
+    def unfused():
+        h = y[:, : 2 * HD].view(M, 2 * HD // 128, 128).float()
+        h = h * torch.rsqrt(h.pow(2).mean(-1, keepdim=True) + 1e-6) * wqk
+        e, o = h[..., 0::2], h[..., 1::2]
+        c, s = cs[:, None, :], sn[:, None, :]
+        r = torch.stack([e * c - o * s, o * c + e * s], -1).flatten(-2)
+        y[:, : 2 * HD] = r.reshape(M, 2 * HD).to(torch.bfloat16)
+
+    fns = {"gemm_qk_norm_rope": lambda: L.gemm_qk_norm_rope(b, qw, kw, 1e-6, cs, sn),
+           "gemm": lambda: L.gemm(b),
+           "torch_norm_rope_pass": unfused}
+    times = interleaved_us(torch, fns, rounds=12, per=per)
+    out = {key: {"us": round(times[key], 3)} for key in fns}
+    ops = 2.0 * M * N * L.K
+    for key in ("gemm_qk_norm_rope", "gemm"):
+        out[key]["TOPS"] = round(ops / (out[key]["us"] * 1e-6) / 1e12, 1)
+    out["unfused_us"] = round(out["gemm"]["us"] + out["torch_norm_rope_pass"]["us"], 3)
+    out["saved_us"] = round(out["unfused_us"] - out["gemm_qk_norm_rope"]["us"], 3)
+    out["epilogue_us"] = round(out["gemm_qk_norm_rope"]["us"] - out["gemm"]["us"], 3)
+    # any separate pass reads and writes the Q and K columns once: its HBM floor
+    out["separate_pass_hbm_floor_us"] = round(2 * M * 2 * HD * 2 / (PEAK_HBM_GBPS * 1e3), 3)
+    print(f"[bench] qk fusion: {out['gemm_qk_norm_rope']['us']:.1f} us fused, "
+          f"{out['gemm']['us']:.1f} us plain GEMM", file=sys.stderr, flush=True)
+    return out
+
+
 def profile_kernel(torch, synth, name, reps):
     """Run one hot-path kernel ``reps`` times on its full-size inputs (for
     rocprofv3).  name: <layer>.quantize_act | <layer>.gemm_w4a4 | adaln.awq_gemv |
     adaln.awq_gemm (the adaptive-norm weights applied to 4096 rows of x) |
-    mlp_down.gelu_quantize_act (the activation step fed with pre-activations)"""
+    mlp_down.gelu_quantize_act (the activation step fed with pre-activations) |
+    qkv.gemm_qk_norm_rope (the QKV GEMM with per-head RMSNorm + rotary epilogue)"""
     layers, xs = build_inputs(torch, synth)
     layer, kind = name.split(".")
     L = layers[layer]
@@ -265,6 +321,15 @@ def profile_kernel(torch, synth, name, reps):
         xl = torch.from_numpy(synth.to_bf16_bits(rng.standard_normal((4096, ADALN[1]))).view(np.int16))
         xl = xl.view(torch.bfloat16).cuda()
         fn = lambda: L(xl)
+    elif kind == "gemm_qk_norm_rope":
+        rng = np.random.default_rng(4322)
+        b = L.buffers(xs[layer].shape[0])
+        L.quantize(xs[layer], b)
+        w = torch.from_numpy(synth.to_bf16_bits(rng.uniform(0.5, 1.5, 128)).view(np.int16)).view(torch.bfloat16).cuda()
+        th = rng.uniform(-np.pi, np.pi, (xs[layer].shape[0], 64))
+        cs = torch.from_numpy(np.cos(th).astype(np.float32)).cuda()
+        sn = torch.from_numpy(np.sin(th).astype(np.float32)).cuda()
+        fn = lambda: L.gemm_qk_norm_rope(b, w, w, 1e-6, cs, sn)
     elif kind == "gelu_quantize_act":
         rng = np.random.default_rng(4097)
         u = torch.from_numpy(synth.to_bf16_bits(rng.standard_normal(tuple(xs[layer].shape)) * 5.7).view(np.int16))
@@ -433,7 +498,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemv-sweep", action="store_true",
-                    help="skip the side measurements (AWQ sweep, GELU fusion)")
+                    help="skip the side measurements (AWQ sweep, GELU and QK fusions)")
     ap.add_argument("--profile-kernel", default=None,
                     help="run only this kernel --steps times (e.g. mlp_up.gemm_w4a4), for rocprofv3")
     ap.add_argument("--copy-mb", type=int, default=0,
@@ -528,6 +593,7 @@ def main():
 
     gemv = None if args.no_gemv_sweep else gemv_sweep(torch, synth)
     fusion = None if args.no_gemv_sweep else gelu_fusion(torch, synth, layers)
+    qk = None if args.no_gemv_sweep else qk_fusion(torch, synth, layers, xs)
     cpu = None if args.no_cpu_baseline else cpu_baseline(synth)
 
     rec = {"metric": "W4A4 GEMM effective TOPS + % MFMA peak; W4A16 GEMV GB/s + % HBM peak",
@@ -539,7 +605,7 @@ def main():
                       "hidden": HIDDEN,
                       "layers": {n: f"{p} {M}x{K}->{N} rank {r}" for n, p, M, K, N, r, _ in LAYERS} |
                                 {"adaln": f"awq_w4a16 1x{K}->{N} g64"}},
-           "roofline": roofline, "kernels": kernels, "gemv": gemv, "gelu_fusion": fusion,
+           "roofline": roofline, "kernels": kernels, "gemv": gemv, "gelu_fusion": fusion, "qk_fusion": qk,
            "cpu_baseline": cpu}
     print(json.dumps(rec))
 

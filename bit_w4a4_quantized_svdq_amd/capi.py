@@ -21,7 +21,8 @@ LIB_PATH = os.path.join(PKG, "_lib", "libsvdq.so")
 SVDQ_OK, SVDQ_ERR_INVALID_ARG, SVDQ_ERR_UNSUPPORTED, SVDQ_ERR_HIP = 0, 1, 2, 3
 SVDQ_INT4, SVDQ_NVFP4 = 0, 1
 
-EXPORTED = ("svdq_quantize_act", "svdq_gelu_quantize_act", "svdq_gemm_w4a4", "awq_gemv_w4a16",
+EXPORTED = ("svdq_quantize_act", "svdq_gelu_quantize_act", "svdq_gemm_w4a4", "svdq_gemm_w4a4_qk_norm_rope",
+            "awq_gemv_w4a16",
             "svdq_debug_group_sums", "svdq_debug_gelu_bf16", "svdq_status_string", "svdq_last_error",
             "svdq_abi_version")
 
@@ -48,10 +49,13 @@ def lib() -> ctypes.CDLL:
         L.svdq_gelu_quantize_act.argtypes = [_I32, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P]
         L.svdq_gemm_w4a4.argtypes = [_I32, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _F32, _P, _P, _P,
                                      _P, _P]
+        L.svdq_gemm_w4a4_qk_norm_rope.argtypes = [_I32, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _F32, _P, _P,
+                                                  _P, _P, _P, _F32, _P, _P, _P, _P]
         L.awq_gemv_w4a16.argtypes = [_I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P]
         L.svdq_debug_group_sums.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P]
         L.svdq_debug_gelu_bf16.argtypes = [_I64, _P, _P, _P]
-        for f in ("svdq_quantize_act", "svdq_gelu_quantize_act", "svdq_gemm_w4a4", "awq_gemv_w4a16",
+        for f in ("svdq_quantize_act", "svdq_gelu_quantize_act", "svdq_gemm_w4a4",
+                  "svdq_gemm_w4a4_qk_norm_rope", "awq_gemv_w4a16",
                   "svdq_debug_group_sums", "svdq_debug_gelu_bf16"):
             getattr(L, f).restype = ctypes.c_int
         L.svdq_status_string.argtypes = [ctypes.c_int]
@@ -126,6 +130,22 @@ def svdq_gemm_w4a4(precision, act_codes, act_scales, wgt_codes, wgt_scales, alph
                                 _ptr(wgt_codes), _ptr(wgt_scales), float(alpha), _ptr(lora_act),
                                 _ptr(lora_up), _ptr(bias), _ptr(out), _stream(stream)),
            "svdq_gemm_w4a4")
+
+
+def svdq_gemm_w4a4_qk_norm_rope(precision, act_codes, act_scales, wgt_codes, wgt_scales, alpha,
+                                lora_act, lora_up, bias, q_norm_weight, k_norm_weight, eps, rope_cos,
+                                rope_sin, out, stream=None):
+    """4-bit GEMM of a grouped QKV layer with per-head RMSNorm + rotary embedding
+    of Q and K in the epilogue; out is [M, 3*H*128] bf16."""
+    M = act_codes.shape[0]
+    N, Kh = wgt_codes.shape
+    rank = 0 if lora_up is None else lora_up.shape[1]
+    _check(lib().svdq_gemm_w4a4_qk_norm_rope(precision, M, N, 2 * Kh, rank, _ptr(act_codes),
+                                             _ptr(act_scales), _ptr(wgt_codes), _ptr(wgt_scales),
+                                             float(alpha), _ptr(lora_act), _ptr(lora_up), _ptr(bias),
+                                             _ptr(q_norm_weight), _ptr(k_norm_weight), float(eps),
+                                             _ptr(rope_cos), _ptr(rope_sin), _ptr(out), _stream(stream)),
+           "svdq_gemm_w4a4_qk_norm_rope")
 
 
 def awq_gemv_w4a16(x, wgt_codes, wgt_scales, wgt_zeros, bias, out, group_size=64, stream=None):

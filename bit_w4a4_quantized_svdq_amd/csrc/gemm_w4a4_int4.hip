@@ -85,7 +85,9 @@ __device__ __forceinline__ void unpack_i8(const v4u &c, v4i &lo, v4i &hi) {
 }
 
 // SC16: scales copied 8 groups per 16-byte copy (K/64 a multiple of 8)
-template <bool GROUP_SUMS, bool SC16>
+// QK: grouped QKV layer, per-head RMSNorm + rotary embedding of Q and K in
+// the epilogue (gemm_epilogue_qk)
+template <bool GROUP_SUMS, bool SC16, bool QK = false>
 __global__ __launch_bounds__(G4_THREADS, GROUP_SUMS ? 2 : 3)
 void gemm_w4a4_int4_kernel(int M, int N, int K, int rank,
                            const uint8_t *__restrict__ act_codes,
@@ -95,8 +97,10 @@ void gemm_w4a4_int4_kernel(int M, int N, int K, int rank,
                            const float *__restrict__ lora_act,
                            const uint16_t *__restrict__ lora_up,
                            const uint16_t *__restrict__ bias,
-                           uint16_t *__restrict__ out, int32_t *__restrict__ gsum)
+                           uint16_t *__restrict__ out, int32_t *__restrict__ gsum,
+                           QkNormRope qk)
 {
+    static_assert(G4_SMEM >= QK_SMEM, "the QK epilogue stages a 128-row tile in the operand LDS");
     __shared__ __attribute__((aligned(16))) uint8_t smem[G4_SMEM];
 
     const int tid = threadIdx.x;
@@ -312,7 +316,15 @@ void gemm_w4a4_int4_kernel(int M, int N, int K, int rank,
 
     if constexpr (!GROUP_SUMS) {
         // acc = 2^8 * sum_g G_g sx_g sw_g (the codes entered as 16*code)
-        gemm_epilogue(acc, alpha * 0.00390625f, M, N, rank, m0, n0, wm, wn, lane, lora_act, lora_up, bias, out);
+        if constexpr (QK) {
+            gemm_epilogue_sum(acc, alpha * 0.00390625f, M, N, rank, m0, n0, wm, wn, lane, lora_act, lora_up, bias);
+            if (n0 < qk.qk_cols)   // block-uniform: a Q or K head
+                gemm_epilogue_qk(acc, M, m0, n0, wm, wn, lane, qk, smem, N, out);
+            else
+                gemm_epilogue_store(acc, M, N, m0, n0, wm, wn, lane, out);
+        } else {
+            gemm_epilogue(acc, alpha * 0.00390625f, M, N, rank, m0, n0, wm, wn, lane, lora_act, lora_up, bias, out);
+        }
     }
 }
 
@@ -328,13 +340,35 @@ hipError_t launch_gemm_w4a4_int4(int M, int N, int K, int rank, const void *act_
                            (const uint8_t *)act_codes, (const uint16_t *)act_scales,
                            (const uint8_t *)wgt_codes, (const uint16_t *)wgt_scales, alpha, lora_act,
                            (const uint16_t *)lora_up, (const uint16_t *)bias, (uint16_t *)out,
-                           (int32_t *)nullptr);
+                           (int32_t *)nullptr, QkNormRope{});
     else
         hipLaunchKernelGGL((gemm_w4a4_int4_kernel<false, false>), grid, block, 0, stream, M, N, K, rank,
                            (const uint8_t *)act_codes, (const uint16_t *)act_scales,
                            (const uint8_t *)wgt_codes, (const uint16_t *)wgt_scales, alpha, lora_act,
                            (const uint16_t *)lora_up, (const uint16_t *)bias, (uint16_t *)out,
-                           (int32_t *)nullptr);
+                           (int32_t *)nullptr, QkNormRope{});
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_w4a4_int4_qk(int M, int N, int K, int rank, const void *act_codes,
+                                    const void *act_scales, const void *wgt_codes,
+                                    const void *wgt_scales, float alpha, const float *lora_act,
+                                    const void *lora_up, const void *bias, const QkNormRope &qk,
+                                    void *out, hipStream_t stream)
+{
+    dim3 grid(((N + G4_BN - 1) / G4_BN) * ((M + G4_BM - 1) / G4_BM)), block(G4_THREADS);
+    if ((K >> 6) % G4_SC_GROUPS == 0)
+        hipLaunchKernelGGL((gemm_w4a4_int4_kernel<false, true, true>), grid, block, 0, stream, M, N, K, rank,
+                           (const uint8_t *)act_codes, (const uint16_t *)act_scales,
+                           (const uint8_t *)wgt_codes, (const uint16_t *)wgt_scales, alpha, lora_act,
+                           (const uint16_t *)lora_up, (const uint16_t *)bias, (uint16_t *)out,
+                           (int32_t *)nullptr, qk);
+    else
+        hipLaunchKernelGGL((gemm_w4a4_int4_kernel<false, false, true>), grid, block, 0, stream, M, N, K, rank,
+                           (const uint8_t *)act_codes, (const uint16_t *)act_scales,
+                           (const uint8_t *)wgt_codes, (const uint16_t *)wgt_scales, alpha, lora_act,
+                           (const uint16_t *)lora_up, (const uint16_t *)bias, (uint16_t *)out,
+                           (int32_t *)nullptr, qk);
     return hipGetLastError();
 }
 
@@ -346,7 +380,7 @@ hipError_t launch_group_sums_int4(int M, int N, int K, const void *act_codes,
                        (const uint8_t *)act_codes, (const uint16_t *)nullptr,
                        (const uint8_t *)wgt_codes, (const uint16_t *)nullptr, 1.0f,
                        (const float *)nullptr, (const uint16_t *)nullptr,
-                       (const uint16_t *)nullptr, (uint16_t *)nullptr, G);
+                       (const uint16_t *)nullptr, (uint16_t *)nullptr, G, QkNormRope{});
     return hipGetLastError();
 }
 

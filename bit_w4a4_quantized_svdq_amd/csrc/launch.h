@@ -7,6 +7,17 @@
 
 namespace svdq {
 
+// Epilogue parameters of the grouped QKV layer: per-head RMSNorm and rotary
+// embedding of the Q and K heads (128 channels each; columns Q | K | V).
+struct QkNormRope {
+    const uint16_t *q_w;   // bf16 [128], norm weight of the Q heads
+    const uint16_t *k_w;   // bf16 [128], norm weight of the K heads
+    const float *cos;      // fp32 [M, 64], the rows' rotary angles
+    const float *sin;      // fp32 [M, 64]
+    float eps;
+    int qk_cols;           // 2 * heads * 128: the Q and K columns
+};
+
 hipError_t launch_quantize_act(int precision, bool gelu, int M, int K, int rank, const void *x,
                                const void *smooth, const void *lora_down, void *act_codes,
                                void *act_scales, float *lora_act, hipStream_t stream);
@@ -17,6 +28,11 @@ hipError_t launch_gemm_w4a4_int4(int M, int N, int K, int rank, const void *act_
                                  const void *wgt_scales, float alpha, const float *lora_act,
                                  const void *lora_up, const void *bias, void *out,
                                  hipStream_t stream);
+hipError_t launch_gemm_w4a4_int4_qk(int M, int N, int K, int rank, const void *act_codes,
+                                    const void *act_scales, const void *wgt_codes,
+                                    const void *wgt_scales, float alpha, const float *lora_act,
+                                    const void *lora_up, const void *bias, const QkNormRope &qk,
+                                    void *out, hipStream_t stream);
 
 hipError_t launch_gemm_w4a4_nvfp4(int M, int N, int K, int rank, const void *act_codes,
                                   const void *act_scales, const void *wgt_codes,

@@ -135,6 +135,49 @@ svdq_status svdq_debug_gelu_bf16(int64_t n, const void *x, void *out, void *stre
     return launched(svdq::launch_gelu_bf16(n, x, out, (hipStream_t)stream), "svdq_debug_gelu_bf16");
 }
 
+svdq_status svdq_gemm_w4a4_qk_norm_rope(int32_t precision, int64_t M, int64_t N, int64_t K, int32_t rank,
+                                        const void *act_codes, const void *act_scales,
+                                        const void *wgt_codes, const void *wgt_scales, float alpha,
+                                        const float *lora_act, const void *lora_up, const void *bias,
+                                        const void *q_norm_weight, const void *k_norm_weight, float eps,
+                                        const float *rope_cos, const float *rope_sin, void *out,
+                                        void *stream)
+{
+    if (precision != SVDQ_INT4)
+        return fail(SVDQ_ERR_UNSUPPORTED, "the QK norm/rotary epilogue is built for SVDQ_INT4 (got %d)", precision);
+    SVDQ_TRY(check_shape(M, N, K, rank));
+    if (N % 384 != 0)
+        return fail(SVDQ_ERR_INVALID_ARG, "N must be 3 * heads * 128 (got %lld)", (long long)N);
+    if (!(eps >= 0.0f) || eps > 3.0e38f)
+        return fail(SVDQ_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    SVDQ_TRY(check_ptr(act_codes, "act_codes", false));
+    SVDQ_TRY(check_ptr(act_scales, "act_scales", false));
+    SVDQ_TRY(check_ptr(wgt_codes, "wgt_codes", false));
+    SVDQ_TRY(check_ptr(wgt_scales, "wgt_scales", false));
+    SVDQ_TRY(check_ptr(lora_act, "lora_act", rank == 0));
+    SVDQ_TRY(check_ptr(lora_up, "lora_up", rank == 0));
+    SVDQ_TRY(check_ptr(bias, "bias", true));
+    SVDQ_TRY(check_ptr(q_norm_weight, "q_norm_weight", false));
+    SVDQ_TRY(check_ptr(k_norm_weight, "k_norm_weight", false));
+    SVDQ_TRY(check_ptr(rope_cos, "rope_cos", false));
+    SVDQ_TRY(check_ptr(rope_sin, "rope_sin", false));
+    SVDQ_TRY(check_ptr(out, "out", false));
+    if (M == 0) return SVDQ_OK;
+    SVDQ_TRY(check_grid(M, N, 128, 128));
+    SVDQ_TRY(check_device());
+    svdq::QkNormRope qk;
+    qk.q_w = (const uint16_t *)q_norm_weight;
+    qk.k_w = (const uint16_t *)k_norm_weight;
+    qk.cos = rope_cos;
+    qk.sin = rope_sin;
+    qk.eps = eps;
+    qk.qk_cols = (int)(2 * (N / 3));
+    return launched(svdq::launch_gemm_w4a4_int4_qk((int)M, (int)N, (int)K, rank, act_codes, act_scales,
+                                                   wgt_codes, wgt_scales, alpha, lora_act, lora_up, bias,
+                                                   qk, out, (hipStream_t)stream),
+                    "svdq_gemm_w4a4_qk_norm_rope");
+}
+
 svdq_status svdq_gemm_w4a4(int32_t precision, int64_t M, int64_t N, int64_t K, int32_t rank,
                            const void *act_codes, const void *act_scales, const void *wgt_codes,
                            const void *wgt_scales, float alpha, const float *lora_act,
@@ -214,6 +257,6 @@ const char *svdq_status_string(svdq_status s)
 
 const char *svdq_last_error(void) { return g_last_error; }
 
-int32_t svdq_abi_version(void) { return 2; }
+int32_t svdq_abi_version(void) { return 3; }
 
 }  // extern "C"

@@ -74,6 +74,14 @@ class SVDQW4A4Linear:
                             self.alpha, b["lora_act"] if self.rank else None, self.lora_up,
                             self.bias, b["out"])
 
+    def gemm_qk_norm_rope(self, b, q_norm_weight, k_norm_weight, eps, rope_cos, rope_sin):
+        """The GEMM step of a grouped QKV layer (N = 3 * heads * 128) with
+        per-head RMSNorm and rotary embedding of Q and K in its epilogue."""
+        capi.svdq_gemm_w4a4_qk_norm_rope(self.prec, b["codes"], b["scales"], self.wgt_codes,
+                                         self.wgt_scales, self.alpha,
+                                         b["lora_act"] if self.rank else None, self.lora_up, self.bias,
+                                         q_norm_weight, k_norm_weight, eps, rope_cos, rope_sin, b["out"])
+
     def forward(self, x):
         """x: bf16 [M,K] device tensor -> bf16 [M,N] (a reused buffer)."""
         b = self.buffers(x.shape[0])

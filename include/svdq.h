@@ -121,6 +121,32 @@ svdq_status svdq_gemm_w4a4(int32_t precision, int64_t M, int64_t N, int64_t K, i
                            void *out, void *stream);
 
 /*
+ * svdq_gemm_w4a4_qk_norm_rope -- svdq_gemm_w4a4 of a grouped QKV projection
+ * with per-head RMSNorm and rotary embedding of Q and K in the epilogue (the
+ * original engine fuses the QKV projection with RMSNorm and RoPE: "Nunchaku
+ * Lite" docs, "Fused kernels").  Heads are 128 channels; the N = 3 H 128
+ * output columns are Q | K | V, head h of Q at columns 128h .. 128h + 127.
+ * With y the bf16 output svdq_gemm_w4a4 would write, for each row and each Q
+ * or K head:
+ *   n_j = y_j * w_j / sqrt( (1/128) sum_i y_i^2 + eps )   (w = q or k weight)
+ *   out_2i   = RNE_bf16( n_2i cos[m,i] - n_2i+1 sin[m,i] )
+ *   out_2i+1 = RNE_bf16( n_2i+1 cos[m,i] + n_2i sin[m,i] ),   i < 64,
+ * computed in fp32; V columns are y.  Arguments as for svdq_gemm_w4a4, plus:
+ *   precision      SVDQ_INT4 only (SVDQ_ERR_UNSUPPORTED otherwise)
+ *   N              a multiple of 384
+ *   q_norm_weight  bf16 [128]; k_norm_weight bf16 [128]
+ *   eps            finite, >= 0
+ *   rope_cos, rope_sin  fp32 [M, 64]: each row's rotary angle per channel pair
+ */
+svdq_status svdq_gemm_w4a4_qk_norm_rope(int32_t precision, int64_t M, int64_t N, int64_t K, int32_t rank,
+                                        const void *act_codes, const void *act_scales,
+                                        const void *wgt_codes, const void *wgt_scales, float alpha,
+                                        const float *lora_act, const void *lora_up, const void *bias,
+                                        const void *q_norm_weight, const void *k_norm_weight, float eps,
+                                        const float *rope_cos, const float *rope_sin, void *out,
+                                        void *stream);
+
+/*
  * awq_gemv_w4a16 -- int4 weight-only layer with bf16 activations, for the
  * memory-bound, precision-sensitive layers (adaptive-norm modulation;
  * "Nunchaku Lite" docs, awq_w4a16 int4 group 64).
@@ -167,7 +193,8 @@ const char *svdq_status_string(svdq_status s);
 /* Text of the last argument-check failure on the calling thread ("" if none). */
 const char *svdq_last_error(void);
 
-/* ABI version of this header: 2 (1 plus svdq_gelu_quantize_act and svdq_debug_gelu_bf16). */
+/* ABI version of this header: 3 (1 plus svdq_gelu_quantize_act, svdq_debug_gelu_bf16 and
+ * svdq_gemm_w4a4_qk_norm_rope). */
 int32_t svdq_abi_version(void);
 
 #ifdef __cplusplus
