@@ -305,12 +305,68 @@ def qk_fusion(torch, synth, layers, xs, per=5):
     return out
 
 
+def prepare_inputs(torch, synth):
+    """The MLP up layer's weight (12288 x 3072, bf16) and 4096 calibration
+    tokens, synthetic, on the GPU, with the outputs and workspace of the
+    offline preparation."""
+    from bit_w4a4_quantized_svdq_amd import capi
+    name, prec, M, K, N, rank, seed = next(l for l in LAYERS if l[0] == "mlp_up")
+    rng = np.random.default_rng(seed + 2000)
+    x, _ = synth.draw_activations(rng, M, K, max(1, K // 100), 50.0)
+    bf = lambda a: torch.from_numpy(synth.to_bf16_bits(a).view(np.int16)).view(torch.bfloat16).cuda()
+    d = {"x": bf(x), "W": bf(rng.standard_normal((N, K)) * 0.02), "rank": rank,
+         "s": torch.empty(K, dtype=torch.bfloat16, device="cuda"),
+         "up": torch.empty((N, rank), dtype=torch.bfloat16, device="cuda"),
+         "down": torch.empty((rank, K), dtype=torch.bfloat16, device="cuda"),
+         "codes": torch.empty((N, K // 2), dtype=torch.uint8, device="cuda"),
+         "scales": torch.empty((N, K // 64), dtype=torch.bfloat16, device="cuda")}
+    d["ws"] = torch.empty(capi.svdq_lowrank_workspace_bytes(N, K, rank), dtype=torch.uint8, device="cuda")
+    steps = {"smooth_factors": lambda: capi.svdq_smooth_factors(d["x"], d["W"], d["s"]),
+             "lowrank_factors": lambda: capi.svdq_lowrank_factors(d["W"], d["s"], rank, 1, d["ws"], d["up"], d["down"]),
+             "quantize_weight": lambda: capi.svdq_quantize_weight(0, d["W"], d["s"], d["up"], d["down"], d["codes"],
+                                                                  d["scales"])}
+    return d, steps
+
+
+def prepare_timing(torch, synth, reps=3):
+    """The offline preparation of the MLP up layer's weight on the GPU: each
+    step's median over ``reps`` runs (HIP events), milliseconds."""
+    d, steps = prepare_inputs(torch, synth)
+    out = {}
+    for key, fn in steps.items():
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            fn()
+            e.record()
+            torch.cuda.synchronize()
+            ts.append(s.elapsed_time(e))
+        out[key] = {"ms": round(float(np.median(ts)), 3)}
+    out["total_ms"] = round(sum(v["ms"] for v in out.values()), 3)
+    N, K = d["W"].shape
+    out["layer"] = f"{N}x{K} rank {d['rank']} int4, calibration {d['x'].shape[0]} tokens"
+    print(f"[bench] preparation: {out['total_ms']:.2f} ms", file=sys.stderr, flush=True)
+    return out
+
+
 def profile_kernel(torch, synth, name, reps):
     """Run one hot-path kernel ``reps`` times on its full-size inputs (for
     rocprofv3).  name: <layer>.quantize_act | <layer>.gemm_w4a4 | adaln.awq_gemv |
     adaln.awq_gemm (the adaptive-norm weights applied to 4096 rows of x) |
     mlp_down.gelu_quantize_act (the activation step fed with pre-activations) |
-    qkv.gemm_qk_norm_rope (the QKV GEMM with per-head RMSNorm + rotary epilogue)"""
+    qkv.gemm_qk_norm_rope (the QKV GEMM with per-head RMSNorm + rotary epilogue) |
+    mlp_up.prepare (the offline preparation of the weight: its three steps)"""
+    if name == "mlp_up.prepare":
+        _, steps = prepare_inputs(torch, synth)
+        for _ in range(reps):
+            for fn in steps.values():
+                fn()
+        torch.cuda.synchronize()
+        print(f"[bench] ran {name} x{reps}", file=sys.stderr, flush=True)
+        return
     layers, xs = build_inputs(torch, synth)
     layer, kind = name.split(".")
     L = layers[layer]
@@ -498,7 +554,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemv-sweep", action="store_true",
-                    help="skip the side measurements (AWQ sweep, GELU and QK fusions)")
+                    help="skip the side measurements (AWQ sweep, GELU and QK fusions, weight preparation)")
     ap.add_argument("--profile-kernel", default=None,
                     help="run only this kernel --steps times (e.g. mlp_up.gemm_w4a4), for rocprofv3")
     ap.add_argument("--copy-mb", type=int, default=0,
@@ -594,6 +650,7 @@ def main():
     gemv = None if args.no_gemv_sweep else gemv_sweep(torch, synth)
     fusion = None if args.no_gemv_sweep else gelu_fusion(torch, synth, layers)
     qk = None if args.no_gemv_sweep else qk_fusion(torch, synth, layers, xs)
+    prep = None if args.no_gemv_sweep else prepare_timing(torch, synth)
     cpu = None if args.no_cpu_baseline else cpu_baseline(synth)
 
     rec = {"metric": "W4A4 GEMM effective TOPS + % MFMA peak; W4A16 GEMV GB/s + % HBM peak",
@@ -606,6 +663,7 @@ def main():
                       "layers": {n: f"{p} {M}x{K}->{N} rank {r}" for n, p, M, K, N, r, _ in LAYERS} |
                                 {"adaln": f"awq_w4a16 1x{K}->{N} g64"}},
            "roofline": roofline, "kernels": kernels, "gemv": gemv, "gelu_fusion": fusion, "qk_fusion": qk,
+           "weight_preparation": prep,
            "cpu_baseline": cpu}
     print(json.dumps(rec))
 

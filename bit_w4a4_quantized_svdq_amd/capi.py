@@ -23,6 +23,8 @@ SVDQ_INT4, SVDQ_NVFP4 = 0, 1
 
 EXPORTED = ("svdq_quantize_act", "svdq_gelu_quantize_act", "svdq_gemm_w4a4", "svdq_gemm_w4a4_qk_norm_rope",
             "awq_gemv_w4a16",
+            "svdq_smooth_factors", "svdq_quantize_weight", "svdq_lowrank_workspace_bytes",
+            "svdq_lowrank_factors",
             "svdq_debug_group_sums", "svdq_debug_gelu_bf16", "svdq_status_string", "svdq_last_error",
             "svdq_abi_version")
 
@@ -54,9 +56,15 @@ def lib() -> ctypes.CDLL:
         L.awq_gemv_w4a16.argtypes = [_I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P]
         L.svdq_debug_group_sums.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P]
         L.svdq_debug_gelu_bf16.argtypes = [_I64, _P, _P, _P]
+        L.svdq_smooth_factors.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P]
+        L.svdq_quantize_weight.argtypes = [_I32, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P]
+        L.svdq_lowrank_workspace_bytes.argtypes = [_I64, _I64, _I32]
+        L.svdq_lowrank_workspace_bytes.restype = _I64
+        L.svdq_lowrank_factors.argtypes = [_I64, _I64, _I32, _P, _P, ctypes.c_uint64, _P, _I64, _P, _P, _P]
         for f in ("svdq_quantize_act", "svdq_gelu_quantize_act", "svdq_gemm_w4a4",
                   "svdq_gemm_w4a4_qk_norm_rope", "awq_gemv_w4a16",
-                  "svdq_debug_group_sums", "svdq_debug_gelu_bf16"):
+                  "svdq_debug_group_sums", "svdq_debug_gelu_bf16", "svdq_smooth_factors",
+                  "svdq_quantize_weight", "svdq_lowrank_factors"):
             getattr(L, f).restype = ctypes.c_int
         L.svdq_status_string.argtypes = [ctypes.c_int]
         L.svdq_status_string.restype = ctypes.c_char_p
@@ -155,6 +163,34 @@ def awq_gemv_w4a16(x, wgt_codes, wgt_scales, wgt_zeros, bias, out, group_size=64
     _check(lib().awq_gemv_w4a16(M, N, K, group_size, _ptr(x), _ptr(wgt_codes), _ptr(wgt_scales),
                                 _ptr(wgt_zeros), _ptr(bias), _ptr(out), _stream(stream)),
            "awq_gemv_w4a16")
+
+
+def svdq_smooth_factors(x, W, smooth, stream=None):
+    """Smoothing factors [K] from calibration activations x [M,K] and the weight W [N,K]."""
+    M, K = x.shape
+    _check(lib().svdq_smooth_factors(M, W.shape[0], K, _ptr(x), _ptr(W), _ptr(smooth), _stream(stream)),
+           "svdq_smooth_factors")
+
+
+def svdq_lowrank_workspace_bytes(N, K, rank) -> int:
+    return int(lib().svdq_lowrank_workspace_bytes(N, K, rank))
+
+
+def svdq_lowrank_factors(W, smooth, rank, seed, workspace, lora_up, lora_down, stream=None):
+    """Low-rank branch (randomized SVD) of W diag(smooth); workspace: a uint8 device tensor."""
+    N, K = W.shape
+    _check(lib().svdq_lowrank_factors(N, K, rank, _ptr(W), _ptr(smooth), int(seed), _ptr(workspace),
+                                      workspace.numel(), _ptr(lora_up), _ptr(lora_down), _stream(stream)),
+           "svdq_lowrank_factors")
+
+
+def svdq_quantize_weight(precision, W, smooth, lora_up, lora_down, wgt_codes, wgt_scales, stream=None):
+    """4-bit residual of the smoothed weight after the low-rank branch, group-quantized."""
+    N, K = W.shape
+    rank = 0 if lora_up is None else lora_up.shape[1]
+    _check(lib().svdq_quantize_weight(precision, N, K, rank, _ptr(W), _ptr(smooth), _ptr(lora_up),
+                                      _ptr(lora_down), _ptr(wgt_codes), _ptr(wgt_scales), _stream(stream)),
+           "svdq_quantize_weight")
 
 
 def svdq_debug_gelu_bf16(x, out, stream=None):

@@ -49,6 +49,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{lo, hi}), v2bf));
 }
 
+// fp64 -> bf16, round to nearest even, in one step (bf16: 8-bit significand,
+// binary32's exponent range, subnormal spacing 2^-133).  NaN -> quiet NaN
+// with the sign; overflow -> infinity.
+__device__ inline uint32_t f64_to_bf16_rne(double v) {
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint32_t sign = (uint32_t)(b >> 48) & 0x8000u;
+    const uint64_t m = b & 0x7FFFFFFFFFFFFFFFull;
+    if (m > 0x7FF0000000000000ull) return sign | 0x7FC0u;
+    const double a = __longlong_as_double((long long)m);
+    if (a < 0x1p-126) return sign | (uint32_t)__builtin_rint(a * 0x1p133);   // exact scaling; 128 -> least normal
+    const uint64_t r = m + 0x00000FFFFFFFFFFFull + ((m >> 45) & 1u);       // round at bit 45
+    const int64_t e = (int64_t)(r >> 52) - 1023 + 127;
+    if (e >= 255) return sign | 0x7F80u;
+    return sign | ((uint32_t)e << 7) | (uint32_t)((r >> 45) & 0x7Fu);
+}
+
 // Largest-magnitude reduction across lanes xor-distance `mask` (wave64).
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) {
     return __shfl_xor(v, mask, kWave);

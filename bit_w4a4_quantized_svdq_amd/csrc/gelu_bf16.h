@@ -52,18 +52,7 @@ __device__ inline uint16_t gelu_table_entry(int i)
     const double y = (double)__uint_as_float((neg | mag) << 16);
     const double u = 0.79788456080286535588 * (y + 0.044715 * y * y * y);   // sqrt(2/pi)
     const double v = y / (1.0 + exp(-2.0 * u));
-    // round to bf16 (RNE); the sign is taken from the bits (v may be -0)
-    const uint64_t b = (uint64_t)__double_as_longlong(v);
-    const uint32_t sign = (uint32_t)(b >> 48) & 0x8000u;
-    const uint64_t m = b & 0x7FFFFFFFFFFFFFFFull;
-    const double a = __longlong_as_double((long long)m);
-    if (a < 0x1p-126) {
-        // bf16 subnormal range: spacing 2^-133, the scaling is exact
-        return (uint16_t)(sign | (uint32_t)__builtin_rint(a * 0x1p133));
-    }
-    const uint64_t r = m + 0x00000FFFFFFFFFFFull + ((m >> 45) & 1u);   // round at bit 45
-    const uint32_t e = (uint32_t)(r >> 52) - 1023u + 127u;              // <= 132 here
-    return (uint16_t)(sign | (e << 7) | (uint32_t)((r >> 45) & 0x7Fu));
+    return (uint16_t)f64_to_bf16_rne(v);   // the sign comes from the bits: v may be -0
 }
 
 // Fill a block's table (tid, nthreads: the block's threads); the caller's

@@ -22,6 +22,13 @@ hipError_t launch_quantize_act(int precision, bool gelu, int M, int K, int rank,
                                const void *smooth, const void *lora_down, void *act_codes,
                                void *act_scales, float *lora_act, hipStream_t stream);
 hipError_t launch_gelu_bf16(int64_t n, const void *in, void *out, hipStream_t stream);
+size_t lowrank_workspace_bytes(int N, int K, int r);
+hipError_t launch_lowrank_factors(int N, int K, int r, const void *W, const void *s, uint64_t seed,
+                                  void *workspace, void *up, void *down, hipStream_t stream);
+hipError_t launch_smooth_factors(int M, int N, int K, const void *x, const void *W, void *s, hipStream_t stream);
+hipError_t launch_quantize_weight(int precision, int N, int K, int rank, const void *W, const void *s,
+                                  const void *up, const void *down, void *codes, void *scales,
+                                  hipStream_t stream);
 
 hipError_t launch_gemm_w4a4_int4(int M, int N, int K, int rank, const void *act_codes,
                                  const void *act_scales, const void *wgt_codes,

@@ -125,6 +125,69 @@ svdq_status svdq_gelu_quantize_act(int32_t precision, int64_t M, int64_t K, int3
                                lora_down, act_codes, act_scales, lora_act, stream);
 }
 
+svdq_status svdq_smooth_factors(int64_t M, int64_t N, int64_t K, const void *x, const void *W, void *smooth,
+                                void *stream)
+{
+    SVDQ_TRY(check_shape(M, N, K, 0));
+    SVDQ_TRY(check_ptr(x, "x", false));
+    SVDQ_TRY(check_ptr(W, "W", false));
+    SVDQ_TRY(check_ptr(smooth, "smooth", false));
+    SVDQ_TRY(check_device());
+    return launched(svdq::launch_smooth_factors((int)M, (int)N, (int)K, x, W, smooth, (hipStream_t)stream),
+                    "svdq_smooth_factors");
+}
+
+int64_t svdq_lowrank_workspace_bytes(int64_t N, int64_t K, int32_t rank)
+{
+    if (check_shape(1, N, K, rank) != SVDQ_OK || rank < 16 || N < rank + 8 || K < rank + 8) return -1;
+    return (int64_t)svdq::lowrank_workspace_bytes((int)N, (int)K, rank);
+}
+
+svdq_status svdq_lowrank_factors(int64_t N, int64_t K, int32_t rank, const void *W, const void *smooth,
+                                 uint64_t seed, void *workspace, int64_t workspace_bytes, void *lora_up,
+                                 void *lora_down, void *stream)
+{
+    SVDQ_TRY(check_shape(1, N, K, rank));
+    if (rank < 16)
+        return fail(SVDQ_ERR_INVALID_ARG, "rank must be at least 16 (got %d)", rank);
+    if (N < rank + 8 || K < rank + 8)
+        return fail(SVDQ_ERR_INVALID_ARG, "N and K must be at least rank + 8 (got N=%lld, K=%lld)", (long long)N,
+                    (long long)K);
+    SVDQ_TRY(check_ptr(W, "W", false));
+    SVDQ_TRY(check_ptr(smooth, "smooth", true));
+    SVDQ_TRY(check_ptr(workspace, "workspace", false));
+    SVDQ_TRY(check_ptr(lora_up, "lora_up", false));
+    SVDQ_TRY(check_ptr(lora_down, "lora_down", false));
+    const int64_t need = (int64_t)svdq::lowrank_workspace_bytes((int)N, (int)K, rank);
+    if (workspace_bytes < need)
+        return fail(SVDQ_ERR_INVALID_ARG, "workspace too small: %lld bytes, %lld needed", (long long)workspace_bytes,
+                    (long long)need);
+    SVDQ_TRY(check_device());
+    return launched(svdq::launch_lowrank_factors((int)N, (int)K, rank, W, smooth, seed, workspace, lora_up, lora_down,
+                                                 (hipStream_t)stream),
+                    "svdq_lowrank_factors");
+}
+
+svdq_status svdq_quantize_weight(int32_t precision, int64_t N, int64_t K, int32_t rank, const void *W,
+                                 const void *smooth, const void *lora_up, const void *lora_down,
+                                 void *wgt_codes, void *wgt_scales, void *stream)
+{
+    if (precision != SVDQ_INT4 && precision != SVDQ_NVFP4)
+        return fail(SVDQ_ERR_UNSUPPORTED, "precision must be SVDQ_INT4 or SVDQ_NVFP4 (got %d)", precision);
+    SVDQ_TRY(check_shape(1, N, K, rank));
+    SVDQ_TRY(check_ptr(W, "W", false));
+    SVDQ_TRY(check_ptr(smooth, "smooth", true));
+    SVDQ_TRY(check_ptr(lora_up, "lora_up", rank == 0));
+    SVDQ_TRY(check_ptr(lora_down, "lora_down", rank == 0));
+    SVDQ_TRY(check_ptr(wgt_codes, "wgt_codes", false));
+    SVDQ_TRY(check_ptr(wgt_scales, "wgt_scales", false));
+    if (N == 0) return SVDQ_OK;
+    SVDQ_TRY(check_device());
+    return launched(svdq::launch_quantize_weight(precision, (int)N, (int)K, rank, W, smooth, lora_up, lora_down,
+                                                 wgt_codes, wgt_scales, (hipStream_t)stream),
+                    "svdq_quantize_weight");
+}
+
 svdq_status svdq_debug_gelu_bf16(int64_t n, const void *x, void *out, void *stream)
 {
     if (n < 0 || n > ((int64_t)1 << 36)) return fail(SVDQ_ERR_INVALID_ARG, "n out of range (got %lld)", (long long)n);
@@ -257,6 +320,6 @@ const char *svdq_status_string(svdq_status s)
 
 const char *svdq_last_error(void) { return g_last_error; }
 
-int32_t svdq_abi_version(void) { return 3; }
+int32_t svdq_abi_version(void) { return 5; }
 
 }  // extern "C"

@@ -170,6 +170,57 @@ svdq_status awq_gemv_w4a16(int64_t M, int64_t N, int64_t K, int32_t group_size,
                            const void *wgt_zeros, const void *bias, void *out, void *stream);
 
 /*
+ * Offline weight preparation ("SVDQuant and the Nunchaku engine": activation
+ * outliers migrate into the weights, the hardest part of each weight stays
+ * in a 16-bit low-rank branch, the residual is quantized to 4 bits).
+ *
+ * svdq_smooth_factors -- smoothing factors from calibration activations:
+ *   smooth[k] = RNE_bf16( sqrt( max_m |x[m,k]| / max_n |W[n,k]| ) )
+ * (fp64 quotient and square root), 1 when either maximum is 0.
+ *   x       bf16 [M, K] calibration activations (M >= 0)
+ *   W       bf16 [N, K] the layer's weight
+ *   smooth  out: bf16 [K]
+ */
+svdq_status svdq_smooth_factors(int64_t M, int64_t N, int64_t K, const void *x, const void *W, void *smooth,
+                                void *stream);
+
+/*
+ * svdq_lowrank_factors -- the 16-bit low-rank branch of the smoothed weight
+ * W_hat = W diag(smooth): approximately its top-rank singular triplets, as
+ *   lora_up[n,j] = RNE_bf16(U[n,j]),  lora_down[j,k] = RNE_bf16(sigma_j V[k,j]),
+ * each left vector's largest-magnitude entry positive.  Randomized subspace
+ * iteration (a Gaussian sketch of rank + 8 columns drawn from `seed`, two
+ * power iterations, CholeskyQR2 bases, a small Jacobi eigendecomposition):
+ * the residual norm is close to, not equal to, the optimal one; results
+ * depend on `seed` and are repeatable for a given seed and device.
+ *   W          bf16 [N, K]; smooth bf16 [K] or NULL (= 1)
+ *   rank       multiple of 16 in [16, 128]; N, K >= rank + 8
+ *   workspace  device scratch of at least svdq_lowrank_workspace_bytes(N, K,
+ *              rank) bytes, owned by the caller; contents on return unspecified
+ *   lora_up    out: bf16 [N, rank]; lora_down out: bf16 [rank, K]
+ */
+int64_t svdq_lowrank_workspace_bytes(int64_t N, int64_t K, int32_t rank);   /* -1 if invalid */
+svdq_status svdq_lowrank_factors(int64_t N, int64_t K, int32_t rank, const void *W, const void *smooth,
+                                 uint64_t seed, void *workspace, int64_t workspace_bytes, void *lora_up,
+                                 void *lora_down, void *stream);
+
+/*
+ * svdq_quantize_weight -- the 4-bit residual of the smoothed weight after the
+ * low-rank branch, and its group quantization:
+ *   R[n,k] = fl32( W[n,k] smooth[k] - sum_{j=0..rank-1} up[n,j] down[j,k] )
+ * (fp64 sum in ascending j, one rounding), then per row and group, from the
+ * fp32 values: int4 g64 -- scale RNE_bf16(absmax/7), code RNE(R/scale)
+ * clamped to [-8,7]; NVFP4 g16 -- scale E4M3_RNE_sat(absmax/6), code
+ * E2M1_RNE_sat(R/scale); fp32 IEEE division, zero scale -> zero codes.
+ *   W          bf16 [N, K]; smooth bf16 [K] or NULL (= 1)
+ *   lora_up    bf16 [N, rank]; lora_down bf16 [rank, K]; ignored when rank == 0
+ *   wgt_codes  out: u8 [N, K/2]; wgt_scales out: int4 bf16 [N, K/64], nvfp4 u8 [N, K/16]
+ */
+svdq_status svdq_quantize_weight(int32_t precision, int64_t N, int64_t K, int32_t rank, const void *W,
+                                 const void *smooth, const void *lora_up, const void *lora_down,
+                                 void *wgt_codes, void *wgt_scales, void *stream);
+
+/*
  * svdq_debug_group_sums -- test hook on the int4 GEMM's own device code
  * path (operand unpacking and integer matrix-core products): writes the
  * exact integer group sums
@@ -193,8 +244,9 @@ const char *svdq_status_string(svdq_status s);
 /* Text of the last argument-check failure on the calling thread ("" if none). */
 const char *svdq_last_error(void);
 
-/* ABI version of this header: 3 (1 plus svdq_gelu_quantize_act, svdq_debug_gelu_bf16 and
- * svdq_gemm_w4a4_qk_norm_rope). */
+/* ABI version of this header: 5 (1 plus svdq_gelu_quantize_act, svdq_debug_gelu_bf16,
+ * svdq_gemm_w4a4_qk_norm_rope, svdq_smooth_factors, svdq_quantize_weight,
+ * svdq_lowrank_workspace_bytes and svdq_lowrank_factors). */
 int32_t svdq_abi_version(void);
 
 #ifdef __cplusplus

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(capi.LIB_PATH)
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert capi.svdq_abi_version() == 3
+    assert capi.svdq_abi_version() == 5
     for s in range(4):
         assert capi.svdq_status_string(s).startswith(("SVDQ_OK", "SVDQ_ERR"))
     assert "unknown" in capi.svdq_status_string(99)
@@ -125,3 +125,43 @@ def test_python_binding_raises_on_bad_status():
         capi.svdq_quantize_act(0, x, None, None, codes, scales, None, stream=0)
     assert ei.value.status == INV
     assert "K must" in str(ei.value)
+
+
+def test_newer_entry_points_reject_bad_arguments_on_the_host():
+    L = capi.lib()
+    # GELU-fed activation step: same checks as svdq_quantize_act
+    assert L.svdq_gelu_quantize_act(7, 4, 64, 16, A, A, A, A, A, A, None) == UNS
+    assert L.svdq_gelu_quantize_act(0, 4, 65, 16, A, A, A, A, A, A, None) == INV
+    assert L.svdq_gelu_quantize_act(0, 4, 64, 16, MIS, A, A, A, A, A, None) == INV
+    assert L.svdq_gelu_quantize_act(0, 0, 64, 16, A, A, A, A, A, A, None) == capi.SVDQ_OK
+    assert L.svdq_debug_gelu_bf16(-1, A, A, None) == INV
+    assert L.svdq_debug_gelu_bf16(0, A, A, None) == capi.SVDQ_OK
+    # QKV epilogue: int4 only, N = 3 * heads * 128, finite eps >= 0
+    qk = lambda prec=0, N=384, eps=1e-6, cos=A: L.svdq_gemm_w4a4_qk_norm_rope(
+        prec, 4, N, 64, 16, A, A, A, A, 1.0, A, A, A, A, A, eps, cos, A, A, None)
+    assert qk(prec=1) == UNS
+    assert qk(N=256) == INV
+    assert qk(eps=-1.0) == INV
+    assert qk(eps=float("inf")) == INV
+    assert qk(cos=0) == INV
+    # offline preparation
+    assert L.svdq_smooth_factors(4, 8, 100, A, A, A, None) == INV
+    assert L.svdq_quantize_weight(5, 8, 64, 16, A, A, A, A, A, A, None) == UNS
+    assert L.svdq_quantize_weight(0, 8, 64, 16, A, A, 0, A, A, A, None) == INV
+    assert L.svdq_quantize_weight(0, 0, 64, 0, A, 0, 0, 0, A, A, None) == capi.SVDQ_OK
+
+
+def test_lowrank_workspace_query_and_checks():
+    ws = capi.svdq_lowrank_workspace_bytes
+    assert ws(256, 512, 32) > 0
+    assert ws(512, 512, 32) >= ws(256, 512, 32)
+    assert ws(256, 512, 8) == -1          # rank below 16
+    assert ws(30, 512, 32) == -1          # N < rank + 8
+    assert ws(256, 100, 32) == -1         # K not a multiple of 64
+    L = capi.lib()
+    need = ws(256, 512, 32)
+    f = lambda rank=32, N=256, K=512, wb=need, work=A: L.svdq_lowrank_factors(N, K, rank, A, A, 1, work, wb, A, A, None)
+    assert f(wb=need - 1) == INV
+    assert f(rank=8) == INV
+    assert f(N=39) == INV
+    assert f(work=0) == INV
