@@ -248,4 +248,21 @@ __device__ __forceinline__ void gemm_epilogue_qk(v16f (&acc)[2][2], int M, int m
     }
 }
 
+// The epilogue with or without the grouped QKV layer's per-head norm/rotary
+// step (QK: Q and K head tiles take gemm_epilogue_qk, the others the plain store).
+template <bool QK>
+__device__ __forceinline__ void gemm_epilogue_any(v16f (&acc)[2][2], float post, int M, int N, int rank, int m0,
+                                                  int n0, int wm, int wn, int lane,
+                                                  const float *__restrict__ lora_act,
+                                                  const uint16_t *__restrict__ lora_up,
+                                                  const uint16_t *__restrict__ bias, uint16_t *__restrict__ out,
+                                                  const QkNormRope &qk, uint8_t *smem)
+{
+    gemm_epilogue_sum(acc, post, M, N, rank, m0, n0, wm, wn, lane, lora_act, lora_up, bias);
+    if (QK && n0 < qk.qk_cols)   // block-uniform
+        gemm_epilogue_qk(acc, M, m0, n0, wm, wn, lane, qk, smem, N, out);
+    else
+        gemm_epilogue_store(acc, M, N, m0, n0, wm, wn, lane, out);
+}
+
 }  // namespace svdq

@@ -58,7 +58,9 @@ typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 // SC4: scales copied 4 slices (16 bytes per row) at a time (K a multiple of 256)
-template <bool SC4>
+// QK: grouped QKV layer, per-head RMSNorm + rotary embedding of Q and K in
+// the epilogue (gemm_epilogue_qk)
+template <bool SC4, bool QK = false>
 __global__ __launch_bounds__(NV_THREADS, 2)
 void gemm_w4a4_nvfp4_kernel(int M, int N, int K, int rank,
                             const uint8_t *__restrict__ act_codes,
@@ -67,8 +69,10 @@ void gemm_w4a4_nvfp4_kernel(int M, int N, int K, int rank,
                             const uint8_t *__restrict__ wgt_scales, float alpha,
                             const float *__restrict__ lora_act,
                             const uint16_t *__restrict__ lora_up,
-                            const uint16_t *__restrict__ bias, uint16_t *__restrict__ out)
+                            const uint16_t *__restrict__ bias, uint16_t *__restrict__ out,
+                            QkNormRope qk)
 {
+    static_assert(NV_SMEM >= QK_SMEM, "the QK epilogue stages a 128-row tile in the operand LDS");
     __shared__ __attribute__((aligned(16))) uint8_t smem[NV_SMEM];
 
     const int tid = threadIdx.x;
@@ -235,7 +239,7 @@ void gemm_w4a4_nvfp4_kernel(int M, int N, int K, int rank,
         }
     }
 
-    gemm_epilogue(acc, alpha, M, N, rank, m0, n0, wm, wn, lane, lora_act, lora_up, bias, out);
+    gemm_epilogue_any<QK>(acc, alpha, M, N, rank, m0, n0, wm, wn, lane, lora_act, lora_up, bias, out, qk, smem);
 }
 
 // Main path (K a multiple of 512): a stage holds two slices, 64 bytes of
@@ -253,6 +257,7 @@ constexpr int CO_SMEM = CO_SC + 2 * CO_SC_SLOT;           // 48 KB
 
 __device__ __forceinline__ int co_chunk_slot(int row, int c) { return c ^ ((row >> 1) & 3); }
 
+template <bool QK = false>
 __global__ __launch_bounds__(NV_THREADS, 2)
 void gemm_w4a4_nvfp4_co_kernel(int M, int N, int K, int rank,
                                const uint8_t *__restrict__ act_codes,
@@ -261,8 +266,10 @@ void gemm_w4a4_nvfp4_co_kernel(int M, int N, int K, int rank,
                                const uint8_t *__restrict__ wgt_scales, float alpha,
                                const float *__restrict__ lora_act,
                                const uint16_t *__restrict__ lora_up,
-                               const uint16_t *__restrict__ bias, uint16_t *__restrict__ out)
+                               const uint16_t *__restrict__ bias, uint16_t *__restrict__ out,
+                               QkNormRope qk)
 {
+    static_assert(CO_SMEM >= QK_SMEM, "the QK epilogue stages a 128-row tile in the operand LDS");
     __shared__ __attribute__((aligned(16))) uint8_t smem[CO_SMEM];
 
     const int tid = threadIdx.x;
@@ -400,7 +407,32 @@ void gemm_w4a4_nvfp4_co_kernel(int M, int N, int K, int rank,
             for (int b = 0; b < 2; ++b) opaque(acc[a][b]);
     }
 
-    gemm_epilogue(acc, alpha, M, N, rank, m0, n0, wm, wn, lane, lora_act, lora_up, bias, out);
+    gemm_epilogue_any<QK>(acc, alpha, M, N, rank, m0, n0, wm, wn, lane, lora_act, lora_up, bias, out, qk, smem);
+}
+
+template <bool QK>
+static hipError_t launch_nvfp4(int M, int N, int K, int rank, const void *act_codes, const void *act_scales,
+                               const void *wgt_codes, const void *wgt_scales, float alpha, const float *lora_act,
+                               const void *lora_up, const void *bias, const QkNormRope &qk, void *out,
+                               hipStream_t stream)
+{
+    dim3 grid(((N + NV_BN - 1) / NV_BN) * ((M + NV_BM - 1) / NV_BM)), block(NV_THREADS);
+    if (K % 512 == 0)
+        hipLaunchKernelGGL((gemm_w4a4_nvfp4_co_kernel<QK>), grid, block, 0, stream, M, N, K, rank,
+                           (const uint8_t *)act_codes, (const uint8_t *)act_scales,
+                           (const uint8_t *)wgt_codes, (const uint8_t *)wgt_scales, alpha, lora_act,
+                           (const uint16_t *)lora_up, (const uint16_t *)bias, (uint16_t *)out, qk);
+    else if (K % 256 == 0)
+        hipLaunchKernelGGL((gemm_w4a4_nvfp4_kernel<true, QK>), grid, block, 0, stream, M, N, K, rank,
+                           (const uint8_t *)act_codes, (const uint8_t *)act_scales,
+                           (const uint8_t *)wgt_codes, (const uint8_t *)wgt_scales, alpha, lora_act,
+                           (const uint16_t *)lora_up, (const uint16_t *)bias, (uint16_t *)out, qk);
+    else
+        hipLaunchKernelGGL((gemm_w4a4_nvfp4_kernel<false, QK>), grid, block, 0, stream, M, N, K, rank,
+                           (const uint8_t *)act_codes, (const uint8_t *)act_scales,
+                           (const uint8_t *)wgt_codes, (const uint8_t *)wgt_scales, alpha, lora_act,
+                           (const uint16_t *)lora_up, (const uint16_t *)bias, (uint16_t *)out, qk);
+    return hipGetLastError();
 }
 
 hipError_t launch_gemm_w4a4_nvfp4(int M, int N, int K, int rank, const void *act_codes,
@@ -409,23 +441,18 @@ hipError_t launch_gemm_w4a4_nvfp4(int M, int N, int K, int rank, const void *act
                                   const void *lora_up, const void *bias, void *out,
                                   hipStream_t stream)
 {
-    dim3 grid(((N + NV_BN - 1) / NV_BN) * ((M + NV_BM - 1) / NV_BM)), block(NV_THREADS);
-    if (K % 512 == 0)
-        hipLaunchKernelGGL(gemm_w4a4_nvfp4_co_kernel, grid, block, 0, stream, M, N, K, rank,
-                           (const uint8_t *)act_codes, (const uint8_t *)act_scales,
-                           (const uint8_t *)wgt_codes, (const uint8_t *)wgt_scales, alpha, lora_act,
-                           (const uint16_t *)lora_up, (const uint16_t *)bias, (uint16_t *)out);
-    else if (K % 256 == 0)
-        hipLaunchKernelGGL((gemm_w4a4_nvfp4_kernel<true>), grid, block, 0, stream, M, N, K, rank,
-                           (const uint8_t *)act_codes, (const uint8_t *)act_scales,
-                           (const uint8_t *)wgt_codes, (const uint8_t *)wgt_scales, alpha, lora_act,
-                           (const uint16_t *)lora_up, (const uint16_t *)bias, (uint16_t *)out);
-    else
-        hipLaunchKernelGGL((gemm_w4a4_nvfp4_kernel<false>), grid, block, 0, stream, M, N, K, rank,
-                           (const uint8_t *)act_codes, (const uint8_t *)act_scales,
-                           (const uint8_t *)wgt_codes, (const uint8_t *)wgt_scales, alpha, lora_act,
-                           (const uint16_t *)lora_up, (const uint16_t *)bias, (uint16_t *)out);
-    return hipGetLastError();
+    return launch_nvfp4<false>(M, N, K, rank, act_codes, act_scales, wgt_codes, wgt_scales, alpha, lora_act,
+                               lora_up, bias, QkNormRope{}, out, stream);
+}
+
+hipError_t launch_gemm_w4a4_nvfp4_qk(int M, int N, int K, int rank, const void *act_codes,
+                                     const void *act_scales, const void *wgt_codes,
+                                     const void *wgt_scales, float alpha, const float *lora_act,
+                                     const void *lora_up, const void *bias, const QkNormRope &qk,
+                                     void *out, hipStream_t stream)
+{
+    return launch_nvfp4<true>(M, N, K, rank, act_codes, act_scales, wgt_codes, wgt_scales, alpha, lora_act,
+                              lora_up, bias, qk, out, stream);
 }
 
 }  // namespace svdq

@@ -35,6 +35,11 @@ hipError_t launch_gemm_w4a4_int4(int M, int N, int K, int rank, const void *act_
                                  const void *wgt_scales, float alpha, const float *lora_act,
                                  const void *lora_up, const void *bias, void *out,
                                  hipStream_t stream);
+hipError_t launch_gemm_w4a4_nvfp4_qk(int M, int N, int K, int rank, const void *act_codes,
+                                     const void *act_scales, const void *wgt_codes,
+                                     const void *wgt_scales, float alpha, const float *lora_act,
+                                     const void *lora_up, const void *bias, const QkNormRope &qk,
+                                     void *out, hipStream_t stream);
 hipError_t launch_gemm_w4a4_int4_qk(int M, int N, int K, int rank, const void *act_codes,
                                     const void *act_scales, const void *wgt_codes,
                                     const void *wgt_scales, float alpha, const float *lora_act,

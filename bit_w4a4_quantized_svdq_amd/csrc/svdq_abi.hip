@@ -206,8 +206,8 @@ svdq_status svdq_gemm_w4a4_qk_norm_rope(int32_t precision, int64_t M, int64_t N,
                                         const float *rope_cos, const float *rope_sin, void *out,
                                         void *stream)
 {
-    if (precision != SVDQ_INT4)
-        return fail(SVDQ_ERR_UNSUPPORTED, "the QK norm/rotary epilogue is built for SVDQ_INT4 (got %d)", precision);
+    if (precision != SVDQ_INT4 && precision != SVDQ_NVFP4)
+        return fail(SVDQ_ERR_UNSUPPORTED, "precision must be SVDQ_INT4 or SVDQ_NVFP4 (got %d)", precision);
     SVDQ_TRY(check_shape(M, N, K, rank));
     if (N % 384 != 0)
         return fail(SVDQ_ERR_INVALID_ARG, "N must be 3 * heads * 128 (got %lld)", (long long)N);
@@ -235,10 +235,12 @@ svdq_status svdq_gemm_w4a4_qk_norm_rope(int32_t precision, int64_t M, int64_t N,
     qk.sin = rope_sin;
     qk.eps = eps;
     qk.qk_cols = (int)(2 * (N / 3));
-    return launched(svdq::launch_gemm_w4a4_int4_qk((int)M, (int)N, (int)K, rank, act_codes, act_scales,
-                                                   wgt_codes, wgt_scales, alpha, lora_act, lora_up, bias,
-                                                   qk, out, (hipStream_t)stream),
-                    "svdq_gemm_w4a4_qk_norm_rope");
+    const hipError_t e = precision == SVDQ_INT4
+        ? svdq::launch_gemm_w4a4_int4_qk((int)M, (int)N, (int)K, rank, act_codes, act_scales, wgt_codes,
+                                         wgt_scales, alpha, lora_act, lora_up, bias, qk, out, (hipStream_t)stream)
+        : svdq::launch_gemm_w4a4_nvfp4_qk((int)M, (int)N, (int)K, rank, act_codes, act_scales, wgt_codes,
+                                          wgt_scales, alpha, lora_act, lora_up, bias, qk, out, (hipStream_t)stream);
+    return launched(e, "svdq_gemm_w4a4_qk_norm_rope");
 }
 
 svdq_status svdq_gemm_w4a4(int32_t precision, int64_t M, int64_t N, int64_t K, int32_t rank,

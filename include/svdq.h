@@ -132,7 +132,7 @@ svdq_status svdq_gemm_w4a4(int32_t precision, int64_t M, int64_t N, int64_t K, i
  *   out_2i   = RNE_bf16( n_2i cos[m,i] - n_2i+1 sin[m,i] )
  *   out_2i+1 = RNE_bf16( n_2i+1 cos[m,i] + n_2i sin[m,i] ),   i < 64,
  * computed in fp32; V columns are y.  Arguments as for svdq_gemm_w4a4, plus:
- *   precision      SVDQ_INT4 only (SVDQ_ERR_UNSUPPORTED otherwise)
+ *   precision      SVDQ_INT4 or SVDQ_NVFP4
  *   N              a multiple of 384
  *   q_norm_weight  bf16 [128]; k_norm_weight bf16 [128]
  *   eps            finite, >= 0

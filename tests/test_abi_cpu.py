@@ -139,7 +139,7 @@ def test_newer_entry_points_reject_bad_arguments_on_the_host():
     # QKV epilogue: int4 only, N = 3 * heads * 128, finite eps >= 0
     qk = lambda prec=0, N=384, eps=1e-6, cos=A: L.svdq_gemm_w4a4_qk_norm_rope(
         prec, 4, N, 64, 16, A, A, A, A, 1.0, A, A, A, A, A, eps, cos, A, A, None)
-    assert qk(prec=1) == UNS
+    assert qk(prec=2) == UNS
     assert qk(N=256) == INV
     assert qk(eps=-1.0) == INV
     assert qk(eps=float("inf")) == INV

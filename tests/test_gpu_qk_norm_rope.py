@@ -24,39 +24,42 @@ def _norm_rope_inputs(rng, M):
     return qw, kw, np.cos(th).astype(np.float32), np.sin(th).astype(np.float32)
 
 
-def _gpu_qk(ac, asc, w, t, bias, qw, kw, eps, cs, sn, alpha=1.0):
+def _gpu_qk(ac, asc, w, t, bias, qw, kw, eps, cs, sn, alpha=1.0, prec=0):
     M, N = ac.shape[0], w["wgt_codes"].shape[0]
     out = poison(empty((M, N), "bf16"))
-    capi.svdq_gemm_w4a4_qk_norm_rope(0, to_dev(ac, "u8"), to_dev(asc, "bf16"), to_dev(w["wgt_codes"], "u8"),
-                                     to_dev(w["wgt_scales"], "bf16"), alpha, to_dev(t, "f32"),
+    sk = "bf16" if prec == 0 else "u8"
+    capi.svdq_gemm_w4a4_qk_norm_rope(prec, to_dev(ac, "u8"), to_dev(asc, sk), to_dev(w["wgt_codes"], "u8"),
+                                     to_dev(w["wgt_scales"], sk), alpha, to_dev(t, "f32"),
                                      to_dev(w["lora_up"], "bf16"), to_dev(bias, "bf16"), to_dev(qw, "bf16"),
                                      to_dev(kw, "bf16"), eps, to_dev(cs, "f32"), to_dev(sn, "f32"), out)
     torch.cuda.synchronize()
     return to_host(out, "bf16")
 
 
-def _case(M, H, K, rank, with_bias, seed):
+def _case(M, H, K, rank, with_bias, seed, prec=0):
     rng = np.random.default_rng(seed)
     N = 3 * H * 128
     x = synth.to_bf16_bits(rng.standard_normal((M, K)))
     smooth = synth.to_bf16_bits(np.exp(rng.standard_normal(K) * 0.5))
-    w = synth.synthetic_w4a4_weights(seed + 1, N, K, rank, "int4")
-    ac, asc, t = oracle.quantize_act(0, x, smooth, w["lora_down"])
+    w = synth.synthetic_w4a4_weights(seed + 1, N, K, rank, "int4" if prec == 0 else "nvfp4")
+    ac, asc, t = oracle.quantize_act(prec, x, smooth, w["lora_down"])
     bias = synth.to_bf16_bits(rng.standard_normal(N)) if with_bias else None
     return ac, asc, t, w, bias, rng
 
 
-@pytest.mark.parametrize("M,H,K,rank,with_bias,alpha", [
-    (64, 1, 256, 16, True, 1.0), (200, 2, 512, 32, False, 1.0), (33, 3, 4160, 0, True, 1.0),
-    (130, 1, 192, 48, False, 0.5), (1, 2, 128, 16, True, 1.0), (257, 2, 640, 32, True, 1.0),
+@pytest.mark.parametrize("prec,M,H,K,rank,with_bias,alpha", [
+    (0, 64, 1, 256, 16, True, 1.0), (0, 200, 2, 512, 32, False, 1.0), (0, 33, 3, 4160, 0, True, 1.0),
+    (0, 130, 1, 192, 48, False, 0.5), (0, 1, 2, 128, 16, True, 1.0), (0, 257, 2, 640, 32, True, 1.0),
+    # NVFP4: the three staging paths (K % 512 == 0, K % 256 == 0, neither)
+    (1, 200, 2, 1024, 32, True, 1.0), (1, 33, 1, 768, 16, False, 0.5), (1, 130, 2, 4160, 0, True, 1.0),
 ])
-def test_qk_norm_rope_shapes(M, H, K, rank, with_bias, alpha):
-    ac, asc, t, w, bias, rng = _case(M, H, K, rank, with_bias, 3000 + M + H + K)
+def test_qk_norm_rope_shapes(prec, M, H, K, rank, with_bias, alpha):
+    ac, asc, t, w, bias, rng = _case(M, H, K, rank, with_bias, 3000 + M + H + K, prec)
     qw, kw, cs, sn = _norm_rope_inputs(rng, M)
     eps = 1e-6
-    announce("gemm qk_norm_rope", "M,H,K,r", M, H, K, rank, "bias", with_bias)
-    y = _gpu_qk(ac, asc, w, t, bias, qw, kw, eps, cs, sn, alpha)
-    plain = gpu_gemm(0, ac, asc, w["wgt_codes"], w["wgt_scales"], t, w["lora_up"], bias, alpha)
+    announce("gemm qk_norm_rope", "prec", prec, "M,H,K,r", M, H, K, rank, "bias", with_bias)
+    y = _gpu_qk(ac, asc, w, t, bias, qw, kw, eps, cs, sn, alpha, prec)
+    plain = gpu_gemm(prec, ac, asc, w["wgt_codes"], w["wgt_scales"], t, w["lora_up"], bias, alpha)
     HD = H * 128
     assert np.array_equal(y[:, 2 * HD:], plain[:, 2 * HD:]), "V columns differ from the plain GEMM"
     # the epilogue alone: the oracle's norm/rotary on the GPU's own bf16 y
@@ -64,9 +67,9 @@ def test_qk_norm_rope_shapes(M, H, K, rank, with_bias, alpha):
     assert_bf16_close(y, ep, f"epilogue {M}x{H}x{K}")
     ulp = np.abs(y.view(np.int16).astype(np.int32) - ep.view(np.int16).astype(np.int32))
     assert np.mean(ulp <= 1) >= 0.999, f"epilogue: {np.mean(ulp <= 1):.5f} within 1 ulp"
-    ref = oracle.gemm_w4a4_qk_norm_rope(0, ac, asc, w["wgt_codes"], w["wgt_scales"], t, w["lora_up"], bias,
+    ref = oracle.gemm_w4a4_qk_norm_rope(prec, ac, asc, w["wgt_codes"], w["wgt_scales"], t, w["lora_up"], bias,
                                         qw, kw, eps, cs, sn, alpha=alpha)
-    assert_bf16_close(y, ref, f"qkv {M}x{H}x{K} r{rank}")
+    assert_bf16_close(y, ref, f"qkv p{prec} {M}x{H}x{K} r{rank}")
 
 
 def test_qk_norm_rope_zero_and_tiny_heads():
