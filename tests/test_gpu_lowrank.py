@@ -33,13 +33,20 @@ def _what(W, s):
 
 
 def _low_rank_plus_noise(rng, N, K, r0, noise):
+    """A spectrum decaying geometrically from 0.5 to 5e-4 over r0 values, so
+    that even its tail stays well above the bf16 rounding noise of W
+    (~1e-4 in singular value at these sizes), plus Gaussian noise."""
     U, _ = np.linalg.qr(rng.standard_normal((N, r0)))
     V, _ = np.linalg.qr(rng.standard_normal((K, r0)))
-    sig = 0.5 * 0.85 ** np.arange(r0)
+    sig = 0.5 * (1e-3 ** (1.0 / r0)) ** np.arange(r0)
     return synth.to_bf16_bits(U @ np.diag(sig) @ V.T + noise * rng.standard_normal((N, K)))
 
 
-@pytest.mark.parametrize("N,K,rank", [(256, 512, 32), (200, 640, 16), (448, 192, 48)])
+@pytest.mark.parametrize("N,K,rank", [
+    # l = rank + 8: Cholesky and Jacobi in LDS (24, 40), Cholesky in global
+    # memory (56), both in global memory (72), and the largest l (136)
+    (256, 512, 32), (200, 640, 16), (448, 192, 48), (320, 576, 64), (384, 640, 128),
+])
 def test_lowrank_decaying_spectrum(N, K, rank):
     rng = np.random.default_rng(7000 + N + K + rank)
     # noise far below the rank-th singular value (bf16 rounding of W dominates it)
