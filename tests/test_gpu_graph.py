@@ -62,3 +62,58 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         for o, r in zip(eager, ref):
             assert torch.equal(o.view(torch.int16), r.view(torch.int16))
+
+
+def test_graph_replay_matches_eager_fused_paths():
+    """The next-row paths in one graph: a grouped QKV layer with the per-head
+    norm/rotary epilogue, a down layer whose activation step applies GELU,
+    and the AWQ layer in its GEMM regime."""
+    from bit_w4a4_quantized_svdq_amd.layer import AWQW4A16Linear, SVDQW4A4Linear
+    announce("graph replay", "qkv norm/rotary 130x256->384, gelu-fed 96x512->192, awq gemm 256x512->2304")
+    rng = np.random.default_rng(31)
+    bf = lambda a: torch.from_numpy(synth.to_bf16_bits(a).view(np.int16)).view(torch.bfloat16).cuda()
+    wq = synth.synthetic_w4a4_weights(40, 384, 256, 32, "int4")
+    Q = SVDQW4A4Linear("int4", wq["wgt_codes"], wq["wgt_scales"], wq["lora_down"], wq["lora_up"], wq["smooth"], None)
+    xq = bf(rng.standard_normal((130, 256)))
+    qw, kw = bf(rng.uniform(0.5, 1.5, 128)), bf(rng.uniform(0.5, 1.5, 128))
+    th = rng.uniform(-np.pi, np.pi, (130, 64))
+    cs = torch.from_numpy(np.cos(th).astype(np.float32)).cuda()
+    sn = torch.from_numpy(np.sin(th).astype(np.float32)).cuda()
+    wd = synth.synthetic_w4a4_weights(41, 192, 512, 32, "int4")
+    D = SVDQW4A4Linear("int4", wd["wgt_codes"], wd["wgt_scales"], wd["lora_down"], wd["lora_up"], wd["smooth"], None)
+    ud = bf(rng.standard_normal((96, 512)) * 3.0)
+    aw = synth.synthetic_awq_weights(42, 2304, 512)
+    A = AWQW4A16Linear(aw["wgt_codes"], aw["wgt_scales"], aw["wgt_zeros"], None)
+    xa = bf(rng.standard_normal((256, 512)))
+    bq, bd = Q.buffers(130), D.buffers(96)
+
+    def step():
+        Q.quantize(xq, bq)
+        Q.gemm_qk_norm_rope(bq, qw, kw, 1e-6, cs, sn)
+        D.quantize(ud, bd, gelu=True)
+        D.gemm(bd)
+        return [bq["out"], bd["out"], A(xa)]
+
+    ref = [o.clone() for o in step()]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        outs = step()
+    for rep in range(3):
+        for o in outs:
+            o.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (o, r) in enumerate(zip(outs, ref)):
+            assert torch.equal(o.view(torch.int16), r.view(torch.int16)), f"replay {rep}, output {i}"
+        eager = step()
+        torch.cuda.synchronize()
+        for o, r in zip(eager, ref):
+            assert torch.equal(o.view(torch.int16), r.view(torch.int16))
