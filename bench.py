@@ -180,6 +180,8 @@ def gemv_sweep(torch, synth, reps=160):
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_int4_mlp_up_traffic.txt")
 TRACE_FILE = os.path.join(ROOT, "profiles", "hot_path_dit_block_kernel_trace.txt")
+UTIL_FILE = os.path.join(ROOT, "profiles", "gemm_int4_mlp_up_utilisation.txt")
+GEMV_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "awq_gemv_m1_traffic.txt")
 GEMM_INT4_SOURCES = [os.path.join(ROOT, "bit_w4a4_quantized_svdq_amd", "csrc", f)
                      for f in ("gemm_w4a4_int4.hip", "gemm_common.h", "device_common.h")]
 STEP_KERNELS = [f"{n}.{k}" for n, *_ in LAYERS for k in ("quantize_act", "gemm_w4a4")] + ["adaln.awq_gemv"]
@@ -435,6 +437,83 @@ def _counter_mean_kib(run_dir, kernel_substr):
     return sum(vals.values()) / len(vals), len(vals)
 
 
+def _counter_means(run_dir, kernel_substr):
+    """Per-counter mean per-dispatch values (summed over a counter's
+    dimensions) of a rocprofv3 --pmc csv run."""
+    import glob
+    vals = {}
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in _csv_rows(f):
+            if kernel_substr in r["Kernel_Name"]:
+                d = vals.setdefault(r["Counter_Name"], {})
+                d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not vals:
+        raise SystemExit(f"no {kernel_substr} dispatches in {run_dir}")
+    return {c: (sum(d.values()) / len(d), len(d)) for c, d in vals.items()}
+
+
+def summarize_utilisation(run_dir, trace_us):
+    """Matrix-core and vector-ALU use of the int4 MLP-up GEMM (runs
+    <run_dir>/pmc_gemm_util and pmc_gemm_insts) and the HBM traffic of the
+    M = 1 AWQ GEMV (pmc_gemv_{FETCH,WRITE}_SIZE, scaled like the GEMM's).
+    trace_us: the hot-path trace's average durations per step kernel."""
+    cmd = "python3 bench.py"
+    util = _counter_means(os.path.join(run_dir, "pmc_gemm_util"), "gemm_w4a4_int4")
+    ins = _counter_means(os.path.join(run_dir, "pmc_gemm_insts"), "gemm_w4a4_int4")
+    M, N, K = TOKENS, 4 * HIDDEN, HIDDEN
+    wave_groups = (M // 64) * (N // 64) * (K // 64)     # one wave: 64x64 outputs, one K-group of 64
+    t = ["# Matrix-core and vector-ALU use of the int4 W4A4 GEMM, DiT MLP up 4096x3072 -> 12288 (rank 32)",
+         "# Commands (paths relative to the repository root; run with TMPDIR=/tmp):",
+         f"#   rocprofv3 --pmc MfmaUtil VALUBusy -f csv -d {run_dir}/pmc_gemm_util -o run -- {cmd} "
+         "--profile-kernel mlp_up.gemm_w4a4 --steps 5",
+         f"#   rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU SQ_WAVES -f csv "
+         f"-d {run_dir}/pmc_gemm_insts -o run -- {cmd} --profile-kernel mlp_up.gemm_w4a4 --steps 5",
+         "# MfmaUtil = matrix-core busy cycles / (GPU active cycles x SIMDs); VALUBusy = vector-ALU",
+         "# issue cycles / (GPU active cycles x CUs) (rocprofv3's derived metrics, in percent).",
+         f"# Instruction counts are per launch, all waves; one wave-group = one wave's 64x64 outputs over",
+         f"# one K-group of 64 ({wave_groups} per launch).  Per wave-group the main loop issues 8",
+         "# v_mfma_i32_32x32x32_i8 (32 cycles each) and 1 v_mfma_f32_32x32x4_2b_bf16 (64 cycles) per",
+         "# pair of 32x32 tiles, i.e. 10 MFMAs = 384 matrix-core cycles, and the vector ALU 4 cycles per",
+         "# instruction.",
+         "# source_sha256 covers gemm_w4a4_int4.hip, gemm_common.h and device_common.h (in that order).",
+         f"source_sha256: {gemm_int4_source_hash()}"]
+    for c in ("MfmaUtil", "VALUBusy"):
+        t.append(f"{c}_percent: {util[c][0]:.1f}  (mean of {util[c][1]} launches)")
+    for c in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_WAVES"):
+        t.append(f"{c}_per_launch: {int(ins[c][0])}")
+    v, m = ins["SQ_INSTS_VALU"][0] / wave_groups, ins["SQ_INSTS_MFMA"][0] / wave_groups
+    t.append(f"valu_insts_per_wave_group: {v:.1f}  ({4 * v:.0f} vector-ALU cycles)")
+    t.append(f"mfma_insts_per_wave_group: {m:.2f}")
+    open(UTIL_FILE, "w").write("\n".join(t) + "\n")
+
+    cf, _ = _counter_mean_kib(os.path.join(run_dir, "pmc_copy_FETCH_SIZE"), "copyBuffer")
+    cw, _ = _counter_mean_kib(os.path.join(run_dir, "pmc_copy_WRITE_SIZE"), "copyBuffer")
+    gf, nf = _counter_mean_kib(os.path.join(run_dir, "pmc_gemv_FETCH_SIZE"), "awq_gemv")
+    gw, nw = _counter_mean_kib(os.path.join(run_dir, "pmc_gemv_WRITE_SIZE"), "awq_gemv")
+    copy_kib = 256 * 1024
+    fetch, write = gf * 1024 * copy_kib / cf, gw * 1024 * copy_kib / cw
+    _, K, N, _ = ADALN
+    alg = algorithmic_bytes_gemv(1, N, K)
+    us = trace_us["adaln.awq_gemv"]
+    g = ["# HBM traffic of the AWQ W4A16 GEMV, adaLN modulation 1x3072 -> 18432 (int4 g64), per launch",
+         "# Commands (paths relative to the repository root; run with TMPDIR=/tmp):"]
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        g.append(f"#   rocprofv3 --pmc {c} -f csv -d {run_dir}/pmc_gemv_{c} -o run -- {cmd} "
+                 "--profile-kernel adaln.awq_gemv --steps 5")
+    g += ["# Counter scaling: the plain-copy factors recorded with the GEMM's traffic "
+          f"(FETCH_SIZE x{copy_kib / cf:.4f}, WRITE_SIZE x{copy_kib / cw:.4f}).",
+          f"# GEMV (mean of {nf} / {nw} launches): FETCH_SIZE = {gf:.1f} KiB, WRITE_SIZE = {gw:.1f} KiB",
+          f"# Algorithmic bytes per launch: {alg} (codes, scales, zero points, x, bias, bf16 out)",
+          f"# Duration: the hot-path kernel trace's average for the in-step GEMV, {us:.2f} us.",
+          f"fetch_bytes_per_launch: {int(fetch)}",
+          f"write_bytes_per_launch: {int(write)}",
+          f"hbm_bytes_per_launch: {int(fetch + write)}",
+          f"measured_hbm_GBps: {(fetch + write) / us / 1e3:.0f}  ({(fetch + write) / us / 1e3 / 8000 * 100:.1f} % of 8 TB/s)",
+          f"algorithmic_GBps: {alg / us / 1e3:.0f}  ({alg / us / 1e3 / 8000 * 100:.1f} % of 8 TB/s)"]
+    open(GEMV_TRAFFIC_FILE, "w").write("\n".join(g) + "\n")
+    print(f"wrote {UTIL_FILE} and {GEMV_TRAFFIC_FILE}")
+
+
 def summarize_profiles(run_dir, warmup, steps):
     """Write the committed profile summaries from a rocprofv3 run directory:
     <run_dir>/trace (kernel trace of `bench.py --steps S --warmup W`, whose
@@ -517,6 +596,8 @@ def summarize_profiles(run_dir, warmup, steps):
           f"hbm_bytes_per_launch: {int(fetch + write)}"]
     open(TRAFFIC_FILE, "w").write("\n".join(t) + "\n")
     print(f"wrote {TRACE_FILE} and {TRAFFIC_FILE}")
+    if os.path.isdir(os.path.join(run_dir, "pmc_gemm_util")):
+        summarize_utilisation(run_dir, {k: sum(a["us"]) / len(a["us"]) for k, a in agg.items()})
 
 
 def cpu_baseline(synth, budget_rows=32):

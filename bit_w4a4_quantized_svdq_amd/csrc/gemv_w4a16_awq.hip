@@ -65,6 +65,19 @@ __device__ __forceinline__ void aw_divmod(int idx, int d, float rd, int &m, int 
 
 __host__ __device__ constexpr int aw_xs_bytes(int MR) { return (AW_MAXCG * MR + 8) * 4; }
 
+// Memory instructions one load_quad issues: four 16-byte code loads, plus
+// one 8-byte scale and one 8-byte zero-point load (VEC) or four 2-byte loads
+// of each.
+__host__ __device__ constexpr int aw_quad_loads(bool vec) { return vec ? 6 : 12; }
+
+// s_waitcnt vmcnt(N) (N < 64: low 4 bits in [3:0], high 2 bits in [15:14]);
+// expcnt and lgkmcnt unconstrained
+template <int N>
+__device__ __forceinline__ void aw_wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit count");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
 __device__ __forceinline__ void aw_lds_barrier() {
     // LDS traffic done, then the workgroup barrier; outstanding global loads
     // (the weight stream) stay in flight.
@@ -184,9 +197,12 @@ void awq_gemv_kernel(int M, int N, int K, const uint16_t *__restrict__ x,
         const float rcg8 = 1.0f / (float)cg8;
         // ---- x first: the chunk is copied global -> LDS (row m: cg*128 bytes
         // in 1 KB copies; a last partial copy reads clamped, valid elements of
-        // the row into the rest of the row's stride), and waited for before any code
-        // load goes out, so that no copy is pending later and every wait on
-        // the codes is for exactly the group about to be used.
+        // the row into the rest of the row's stride), then the first two quads
+        // of codes go out behind it.  Memory operations complete in order, so
+        // waiting until at most those quads' loads are outstanding means this
+        // wave's copies have landed, while the codes stay in flight; no copy
+        // is pending after the barrier, so every later wait on the codes is
+        // for exactly the group about to be used.
         const int per_row = (cg + 7) >> 3, copies = Mt * per_row;
         for (int j = wave; j < copies; j += AW_KP) {
             const int m = j / per_row, pc = j - m * per_row;
@@ -194,10 +210,14 @@ void awq_gemv_kernel(int M, int N, int K, const uint16_t *__restrict__ x,
             __builtin_amdgcn_global_load_lds((gptr_t)(xt + (size_t)m * K + e),
                                              (lptr_t)(s_x + m * xstride + pc * 1024), 16, 0, 0);
         }
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
         if (nw > 0) {
             load_quad(0, I0{});
             load_quad(1, I1{});
+            aw_wait_vmcnt<2 * aw_quad_loads(VEC)>();
+        } else {
+            aw_wait_vmcnt<0>();
         }
         aw_lds_barrier();
         for (int i0 = 0; i0 < P; i0 += AW_THREADS) {
