@@ -600,7 +600,7 @@ def summarize_profiles(run_dir, warmup, steps):
         summarize_utilisation(run_dir, {k: sum(a["us"]) / len(a["us"]) for k, a in agg.items()})
 
 
-def cpu_baseline(synth, budget_rows=32):
+def cpu_baseline(synth, budget_rows=48):
     """The CPU oracle (single-threaded C, as it stands) on a bounded sample of
     the same step: the first ``budget_rows`` rows of each W4A4 layer
     (quantize + GEMM) and the M=1 GEMV."""
