@@ -216,6 +216,10 @@ def test_layer_end_to_end_and_determinism():
     (255, 40, 3072, False),
     # tiles of 17..31 rows on the 2-byte path with several x copies per row
     (20, 64, 4096, True), (40, 50, 4160, False), (23, 33, 2240, True),
+    # 8-byte scale loads with several x chunks (the first code loads go out
+    # behind each chunk's x copy): 16-row tiles take 24 groups per chunk,
+    # 2-row tiles 48
+    (12, 96, 3072, True), (2, 64, 4608, False), (1, 32, 4608, True),
 ])
 def test_awq_gemv_shapes(M, N, K, with_bias):
     rng = np.random.default_rng(4000 + M + N + K)
