@@ -152,14 +152,20 @@ __global__ __launch_bounds__(256) void sv_gram_partial_kernel(int R, int L, cons
     }
 }
 
-// G = sum of the partials, as a full symmetric L x L matrix
+// G = sum of the partials, as a full symmetric L x L matrix.  32 lanes per
+// entry: lane l adds partials l, l+32, ... in order, then a fixed butterfly
+// over the 32 lanes (the same order on every run).
+constexpr int SV_RED_PAIRS = 8;   // entries per 256-thread block
 __global__ __launch_bounds__(256) void sv_gram_reduce_kernel(int nb, int L, const double *__restrict__ part,
                                                              double *__restrict__ G)
 {
     const int npair = L * (L + 1) / 2;
-    for (int p = threadIdx.x; p < npair; p += 256) {
-        double s = 0.0;
-        for (int b = 0; b < nb; ++b) s += part[(size_t)b * npair + p];
+    const int p = blockIdx.x * SV_RED_PAIRS + (threadIdx.x >> 5), l = threadIdx.x & 31;
+    double s = 0.0;
+    if (p < npair)
+        for (int b = l; b < nb; b += 32) s += part[(size_t)b * npair + p];
+    for (int o = 16; o > 0; o >>= 1) s += __shfl_xor(s, o, 32);
+    if (p < npair && l == 0) {
         int i = 0, rem = p;
         while (rem >= L - i) { rem -= L - i; ++i; }
         const int j = i + rem;
@@ -171,55 +177,69 @@ __global__ __launch_bounds__(256) void sv_gram_reduce_kernel(int nb, int L, cons
 // ---------------------------------------------------------------- CholeskyQR step
 // G (L x L, fp64) -> T = L^{-T} (upper triangular, fp32) for X <- X T, where
 // G + delta I = L L^T; delta = 1e-13 trace / L (1e-300 for a zero matrix)
-// keeps a rank-deficient basis from breaking down.  IN_LDS: G, L and L^{-1}
-// in LDS (3 L^2 doubles); else in global memory (Lg, Xg).
+// keeps a rank-deficient basis from breaking down.  Both steps are written
+// so that every thread of the block has work at every column: the factor by
+// right-looking elimination (scale column j, then a rank-1 update of the
+// trailing lower triangle), the inverse by column-oriented forward
+// substitution (row j of L^{-1} is final once divided by L[j][j], and is
+// then eliminated from the rows below).  IN_LDS: the factor and the inverse
+// in LDS (2 L^2 doubles); else in global memory (Lg, Xg).
 template <bool IN_LDS>
 __global__ __launch_bounds__(256) void sv_chol_inv_kernel(int L, const double *__restrict__ Gg, double *__restrict__ Lg,
                                                           double *__restrict__ Xg, float *__restrict__ Tout)
 {
     extern __shared__ double sv_dyn[];
     __shared__ double shift;
-    const double *G = Gg;
-    double *Lw = Lg, *Xi = Xg;
+    __shared__ double diag[SV_MAXL];
+    double *A = Lg, *Xi = Xg;   // A: G + delta I, factored in place (strict lower triangle; diagonal in diag[])
     if constexpr (IN_LDS) {
-        double *g = sv_dyn;
-        for (int e = threadIdx.x; e < L * L; e += 256) g[e] = Gg[e];
-        G = g;
-        Lw = sv_dyn + L * L;
-        Xi = sv_dyn + 2 * L * L;
-        __syncthreads();
+        A = sv_dyn;
+        Xi = sv_dyn + L * L;
     }
-    if (threadIdx.x == 0) {
+    const int tid = threadIdx.x;
+    for (int e = tid; e < L * L; e += 256) {
+        A[e] = Gg[e];
+        Xi[e] = (e / L == e % L) ? 1.0 : 0.0;
+    }
+    __syncthreads();
+    if (tid == 0) {
         double tr = 0.0;
-        for (int i = 0; i < L; ++i) tr += G[i * L + i];
+        for (int i = 0; i < L; ++i) tr += A[i * L + i];
         shift = tr > 0.0 ? 1e-13 * tr / L : 1e-300;
     }
-    for (int e = threadIdx.x; e < L * L; e += 256) Lw[e] = 0.0;
     __syncthreads();
+    for (int i = tid; i < L; i += 256) A[i * L + i] += shift;
+    __syncthreads();
+    // The diagonal of the factor goes to diag[] (every thread computes it from
+    // the untouched A[j][j]), so a column needs two barriers, not three.
     for (int j = 0; j < L; ++j) {
-        if (threadIdx.x == 0) {
-            double d = G[j * L + j] + shift;
-            for (int k = 0; k < j; ++k) d -= Lw[j * L + k] * Lw[j * L + k];
-            Lw[j * L + j] = __builtin_sqrt(d > 0.0 ? d : shift);
-        }
+        const double d = A[j * L + j];
+        const double djj = __builtin_sqrt(d > 0.0 ? d : shift);
+        if (tid == 0) diag[j] = djj;
+        for (int i = j + 1 + tid; i < L; i += 256) A[i * L + j] /= djj;
         __syncthreads();
-        const double djj = Lw[j * L + j];
-        for (int i = j + 1 + threadIdx.x; i < L; i += 256) {
-            double v = G[i * L + j];
-            for (int k = 0; k < j; ++k) v -= Lw[i * L + k] * Lw[j * L + k];
-            Lw[i * L + j] = v / djj;
+        const int m = L - 1 - j;   // trailing block: rows and columns j+1 .. L-1
+        for (int e = tid; e < m * m; e += 256) {
+            const int i = j + 1 + e / m, k = j + 1 + e % m;
+            if (k <= i) A[i * L + k] -= A[i * L + j] * A[k * L + j];
         }
         __syncthreads();
     }
-    // column c of L^{-1} by forward substitution (thread c); T[c][i] = (L^{-1})[i][c]
-    for (int c = threadIdx.x; c < L; c += 256) {
-        for (int i = 0; i < L; ++i) {
-            double v = i == c ? 1.0 : 0.0;
-            for (int k = c; k < i; ++k) v -= Lw[i * L + k] * Xi[k * L + c];
-            const double x = i < c ? 0.0 : v / Lw[i * L + i];
-            Xi[i * L + c] = x;
-            Tout[c * L + i] = (float)x;
+    // Rows of L^{-1} are kept undivided: row j's final value is Xi[j][:] /
+    // diag[j], formed by every thread that eliminates it (one barrier per row).
+    for (int j = 0; j < L; ++j) {
+        const double ljj = diag[j];
+        const int m = L - 1 - j, w = j + 1;   // rows j+1 .. L-1, columns 0 .. j
+        for (int e = tid; e < m * w; e += 256) {
+            const int i = j + 1 + e / w, c = e % w;
+            Xi[i * L + c] -= A[i * L + j] * (Xi[j * L + c] / ljj);
         }
+        __syncthreads();
+    }
+    // T[c][i] = (L^{-1})[i][c]
+    for (int e = tid; e < L * L; e += 256) {
+        const int i = e / L, c = e - i * L;
+        Tout[c * L + i] = (float)(Xi[i * L + c] / diag[i]);
     }
 }
 
@@ -227,41 +247,54 @@ __global__ __launch_bounds__(256) void sv_chol_inv_kernel(int L, const double *_
 // Symmetric C (L x L, fp64, even L) -> eigenvalues on its diagonal and
 // eigenvectors in the columns of E, by cyclic parallel Jacobi: each step
 // rotates L/2 disjoint pairs (round-robin pairing), at most 40 sweeps.
+// Round robin: index 0 stays in place and the other L-1 rotate by one place
+// per step, so after s steps place i >= 1 holds 1 + ((i - 1 - s) mod (L-1));
+// step s pairs the indices at places k and L-1-k.
 // C and E live in (dynamic) LDS when IN_LDS (2 L^2 doubles), else in global memory.
 template <bool IN_LDS>
 __global__ __launch_bounds__(256) void sv_jacobi_kernel(int L, double *__restrict__ Cg, double *__restrict__ Eg)
 {
     constexpr bool in_lds = IN_LDS;
     extern __shared__ double sv_dyn[];
-    __shared__ int pos[SV_MAXL];
     __shared__ double cs[SV_MAXL / 2], sn[SV_MAXL / 2];
     __shared__ int pp[SV_MAXL / 2], qq[SV_MAXL / 2];
+    __shared__ double roff[SV_MAXL], rtot[SV_MAXL];
     __shared__ double off, tot;
     double *C = in_lds ? sv_dyn : Cg;
     double *E = in_lds ? sv_dyn + L * L : Eg;
     if (in_lds)
         for (int e = threadIdx.x; e < L * L; e += 256) C[e] = Cg[e];
     for (int e = threadIdx.x; e < L * L; e += 256) E[e] = (e / L == e % L) ? 1.0 : 0.0;
-    for (int i = threadIdx.x; i < L; i += 256) pos[i] = i;
     const int H = L / 2;
+    auto place = [L](int i, int step) { return i == 0 ? 0 : 1 + (i - 1 - step % (L - 1) + (L - 1)) % (L - 1); };
     __syncthreads();
     for (int sweep = 0; sweep < 40; ++sweep) {
+        // squared off-diagonal and diagonal mass: one row per thread, rows added in order
+        for (int i = threadIdx.x; i < L; i += 256) {
+            double o = 0.0, t = 0.0;
+            for (int j = 0; j < L; ++j) {
+                const double v = C[i * L + j] * C[i * L + j];
+                if (i == j) t += v; else o += v;
+            }
+            roff[i] = o;
+            rtot[i] = t;
+        }
+        __syncthreads();
         if (threadIdx.x == 0) {
             double o = 0.0, t = 0.0;
-            for (int i = 0; i < L; ++i)
-                for (int j = 0; j < L; ++j) {
-                    const double v = C[i * L + j] * C[i * L + j];
-                    if (i == j) t += v; else o += v;
-                }
+            for (int i = 0; i < L; ++i) {
+                o += roff[i];
+                t += rtot[i];
+            }
             off = o;
             tot = t;
         }
         __syncthreads();
         if (!(off > 1e-30 * tot)) break;   // block-uniform
         for (int step = 0; step < L - 1; ++step) {
-            // pairs (pos[k], pos[L-1-k])
+            // pairs (place k, place L-1-k)
             for (int k = threadIdx.x; k < H; k += 256) {
-                int p = pos[k], q = pos[L - 1 - k];
+                int p = place(k, step), q = place(L - 1 - k, step);
                 if (p > q) { const int t = p; p = q; q = t; }
                 const double apq = C[p * L + q], app = C[p * L + p], aqq = C[q * L + q];
                 double c = 1.0, s = 0.0;
@@ -297,13 +330,6 @@ __global__ __launch_bounds__(256) void sv_jacobi_kernel(int L, double *__restric
                 E[row * L + q] = s * ep + c * eq;
             }
             __syncthreads();
-            // round-robin: position 0 fixed, the others rotate by one
-            if (threadIdx.x == 0) {
-                const int last = pos[L - 1];
-                for (int i = L - 1; i > 1; --i) pos[i] = pos[i - 1];
-                pos[1] = last;
-            }
-            __syncthreads();
         }
     }
     if (in_lds) {
@@ -320,14 +346,15 @@ __global__ __launch_bounds__(256) void sv_select_kernel(int L, int r, const doub
                                                         const double *__restrict__ E, float *__restrict__ Er)
 {
     __shared__ int order[SV_MAXL];
-    if (threadIdx.x == 0) {
-        for (int i = 0; i < L; ++i) order[i] = i;
-        for (int i = 0; i < r; ++i) {            // partial selection sort, ties to the lower index
-            int best = i;
-            for (int j = i + 1; j < L; ++j)
-                if (C[order[j] * L + order[j]] > C[order[best] * L + order[best]]) best = j;
-            const int t = order[i]; order[i] = order[best]; order[best] = t;
-        }
+    __shared__ double dg[SV_MAXL];
+    for (int i = threadIdx.x; i < L; i += 256) dg[i] = C[i * L + i];
+    __syncthreads();
+    // rank of eigenvalue i in descending order, ties to the lower index
+    for (int i = threadIdx.x; i < L; i += 256) {
+        const double v = dg[i];
+        int rank = 0;
+        for (int j = 0; j < L; ++j) rank += (dg[j] > v || (dg[j] == v && j < i)) ? 1 : 0;
+        order[rank] = i;
     }
     __syncthreads();
     for (int e = threadIdx.x; e < L * r; e += 256) {
@@ -453,9 +480,9 @@ static hipError_t sv_orth(int R, int L, float *&X, float *&Xtmp, const SvWork &w
     const int nb = (R + SV_GROWS - 1) / SV_GROWS;
     for (int pass = 0; pass < 2; ++pass) {
         hipLaunchKernelGGL(sv_gram_partial_kernel, dim3(nb), dim3(256), 0, st, R, L, X, w.part);
-        hipLaunchKernelGGL(sv_gram_reduce_kernel, dim3(1), dim3(256), 0, st, nb, L, w.part, w.G);
-        if (3 * L * L * 8 <= 62 * 1024)
-            hipLaunchKernelGGL(sv_chol_inv_kernel<true>, dim3(1), dim3(256), 3 * L * L * 8, st, L, w.G, w.Lw, w.E, w.T);
+        hipLaunchKernelGGL(sv_gram_reduce_kernel, dim3((L * (L + 1) / 2 + SV_RED_PAIRS - 1) / SV_RED_PAIRS), dim3(256), 0, st, nb, L, w.part, w.G);
+        if (2 * L * L * 8 <= 62 * 1024)
+            hipLaunchKernelGGL(sv_chol_inv_kernel<true>, dim3(1), dim3(256), 2 * L * L * 8, st, L, w.G, w.Lw, w.E, w.T);
         else
             hipLaunchKernelGGL(sv_chol_inv_kernel<false>, dim3(1), dim3(256), 0, st, L, w.G, w.Lw, w.E, w.T);
         hipLaunchKernelGGL((sv_product_kernel<float, false>), dim3((R + 63) / 64), dim3(256), 0, st, R, L, L, X,
@@ -492,7 +519,7 @@ hipError_t launch_lowrank_factors(int N, int K, int r, const void *W, const void
     SV_TRY(sv_wprod(true, K, N, L, Wb, sb, Y, Z, w.ppart, st));
     const int nbk = (K + SV_GROWS - 1) / SV_GROWS;
     hipLaunchKernelGGL(sv_gram_partial_kernel, dim3(nbk), dim3(256), 0, st, K, L, Z, w.part);
-    hipLaunchKernelGGL(sv_gram_reduce_kernel, dim3(1), dim3(256), 0, st, nbk, L, w.part, w.G);
+    hipLaunchKernelGGL(sv_gram_reduce_kernel, dim3((L * (L + 1) / 2 + SV_RED_PAIRS - 1) / SV_RED_PAIRS), dim3(256), 0, st, nbk, L, w.part, w.G);
     if (2 * L * L * 8 <= 62 * 1024)
         hipLaunchKernelGGL(sv_jacobi_kernel<true>, dim3(1), dim3(256), 2 * L * L * 8, st, L, w.G, w.E);
     else
