@@ -66,9 +66,36 @@ __global__ __launch_bounds__(256) void sv_product_kernel(int I, int T, int L, co
     };
     for (int t0 = tb; t0 < te; t0 += 32) {
         __syncthreads();
-        for (int e = tid; e < 32 * 64; e += 256) {
-            const int tt = TRANS ? e >> 6 : e & 31, ii = TRANS ? e & 63 : e >> 5;   // contiguous along a's rows
-            As[tt][ii] = aval(i0 + ii, t0 + tt);
+        if constexpr (sizeof(TA) == 2) {
+            // bf16 W: 8 consecutive elements of a row of `a` per thread, one
+            // 16-byte load (and one of s).  The chunk is wholly inside or
+            // outside: I (TRANS) resp. T and the slice bounds (!TRANS) are
+            // multiples of 8, and a and s are 16-byte aligned.
+            const int tt = TRANS ? tid >> 3 : (tid & 3) * 8, ii = TRANS ? (tid & 7) * 8 : tid >> 2;
+            const int i = i0 + ii, t = t0 + tt;
+            float v[8];
+            if (i < I && t < te) {
+                const v4u w = *(const v4u *)(TRANS ? a + (size_t)t * I + i : a + (size_t)i * T + t);
+                const v4u sc = s ? *(const v4u *)(s + (TRANS ? i : t)) : v4u{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    v[2 * q] = bf16_lo(w[q]) * bf16_lo(sc[q]);
+                    v[2 * q + 1] = bf16_hi(w[q]) * bf16_hi(sc[q]);
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) v[q] = 0.0f;
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                if constexpr (TRANS) As[tt][ii + q] = v[q];
+                else As[tt + q][ii] = v[q];
+            }
+        } else {
+            for (int e = tid; e < 32 * 64; e += 256) {
+                const int tt = TRANS ? e >> 6 : e & 31, ii = TRANS ? e & 63 : e >> 5;   // contiguous along a's rows
+                As[tt][ii] = aval(i0 + ii, t0 + tt);
+            }
         }
         for (int e = tid; e < 32 * L; e += 256) {
             const int tt = e / L, c = e - tt * L;
