@@ -258,15 +258,18 @@ void gemm_w4a4_int4_kernel(int M, int N, int K, int rank,
         }
     };
 
-    if constexpr (SC16 && !GROUP_SUMS) {
+    if constexpr (SC16) {
         // K/64 is a multiple of 8: the loop runs over chunks of 8 groups, the
         // period of the scale copies, so that every wait count and every LDS
         // offset below is a compile-time constant.  Per wave, group g costs
         // two copies (codes), plus one (scales) when g % 8 == 0; waiting until
         // at most the copies of the two groups issued after g are in flight
-        // means that g has landed.
+        // means that g has landed.  The group-sum mode runs this same loop
+        // with the scale copies left out (its wait counts drop by the one
+        // scale copy that would be in flight).
+        constexpr int SCW = GROUP_SUMS ? 0 : 1;
         issue_codes(0, 0);
-        issue_scales8(0, 0);
+        if constexpr (!GROUP_SUMS) issue_scales8(0, 0);
         issue_codes(1, 1);
         issue_codes(2, 2);
         for (int c = 0; c < NG; c += G4_SC_GROUPS) {
@@ -277,14 +280,15 @@ void gemm_w4a4_int4_kernel(int M, int N, int K, int rank,
             for (int j = 0; j < G4_SC_GROUPS; ++j) {
                 __builtin_amdgcn_sched_barrier(0);            // groups stay in program order
                 if (j < 6) wait_vmcnt(4);                   // groups c+j+1, c+j+2: codes only
-                else if (j == 6) { if (last) wait_vmcnt(2); else wait_vmcnt(5); }
-                else { if (last) wait_vmcnt(0); else wait_vmcnt(5); }
+                else if (j == 6) { if (last) wait_vmcnt(2); else wait_vmcnt(4 + SCW); }
+                else { if (last) wait_vmcnt(0); else wait_vmcnt(4 + SCW); }
                 lds_barrier();
                 if (j < 5) {
                     issue_codes(c + j + 3, (j + 3) & 3);
                 } else if (!last) {
                     issue_codes(c + j + 3, (j + 3) & 3);
-                    if (j == 5) issue_scales8(c + G4_SC_GROUPS, par ^ 1);
+                    if constexpr (!GROUP_SUMS)
+                        if (j == 5) issue_scales8(c + G4_SC_GROUPS, par ^ 1);
                 }
                 compute(smem + (j & 3) * G4_STAGE, slot + 2 * j, c + j);
                 // the group's accumulation completes here, before the next
@@ -297,7 +301,7 @@ void gemm_w4a4_int4_kernel(int M, int N, int K, int rank,
             }
         }
     } else {
-        // general loop: any K/64, and the group-sum mode (no scales)
+        // general loop: any K/64 (the group-sum mode copies no scales)
         auto loads_of = [](int g) { return GROUP_SUMS ? 2 : 3; };
         auto issue = [&](int g) {
             issue_codes(g, g % G4_STAGES);
@@ -375,12 +379,21 @@ hipError_t launch_gemm_w4a4_int4_qk(int M, int N, int K, int rank, const void *a
 hipError_t launch_group_sums_int4(int M, int N, int K, const void *act_codes,
                                   const void *wgt_codes, int32_t *G, hipStream_t stream)
 {
+    // the same main loop as the GEMM launch of this K (the chunked loop when
+    // K/64 is a multiple of 8), writing G instead of accumulating
     dim3 grid(((N + G4_BN - 1) / G4_BN) * ((M + G4_BM - 1) / G4_BM)), block(G4_THREADS);
-    hipLaunchKernelGGL((gemm_w4a4_int4_kernel<true, false>), grid, block, 0, stream, M, N, K, 0,
-                       (const uint8_t *)act_codes, (const uint16_t *)nullptr,
-                       (const uint8_t *)wgt_codes, (const uint16_t *)nullptr, 1.0f,
-                       (const float *)nullptr, (const uint16_t *)nullptr,
-                       (const uint16_t *)nullptr, (uint16_t *)nullptr, G, QkNormRope{});
+    if ((K >> 6) % G4_SC_GROUPS == 0)
+        hipLaunchKernelGGL((gemm_w4a4_int4_kernel<true, true>), grid, block, 0, stream, M, N, K, 0,
+                           (const uint8_t *)act_codes, (const uint16_t *)nullptr,
+                           (const uint8_t *)wgt_codes, (const uint16_t *)nullptr, 1.0f,
+                           (const float *)nullptr, (const uint16_t *)nullptr,
+                           (const uint16_t *)nullptr, (uint16_t *)nullptr, G, QkNormRope{});
+    else
+        hipLaunchKernelGGL((gemm_w4a4_int4_kernel<true, false>), grid, block, 0, stream, M, N, K, 0,
+                           (const uint8_t *)act_codes, (const uint16_t *)nullptr,
+                           (const uint8_t *)wgt_codes, (const uint16_t *)nullptr, 1.0f,
+                           (const float *)nullptr, (const uint16_t *)nullptr,
+                           (const uint16_t *)nullptr, (uint16_t *)nullptr, G, QkNormRope{});
     return hipGetLastError();
 }
 

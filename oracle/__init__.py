@@ -106,7 +106,15 @@ def _ptr(a):
 
 
 def _c(a, dtype):
-    return np.ascontiguousarray(a, dtype=dtype)
+    """Contiguous array of ``dtype``.  Integer storage (bf16 / E4M3 bit
+    patterns, packed nibbles) is never produced by casting floating-point
+    values: that would silently turn, e.g., weights of magnitude 0.02 into
+    the bf16 pattern 0x0000."""
+    src = np.asarray(a)
+    if np.issubdtype(np.dtype(dtype), np.integer) and np.issubdtype(src.dtype, np.floating):
+        raise TypeError(f"oracle: float array ({src.dtype}) where {np.dtype(dtype)} bit patterns "
+                        "are expected; convert the values first (e.g. to bf16 bits)")
+    return np.ascontiguousarray(src, dtype=dtype)
 
 
 # --------------------------------------------------------------------------

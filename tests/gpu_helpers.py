@@ -36,7 +36,26 @@ def to_dev(a, kind):
     return torch.from_numpy(a).to(DEV)
 
 
+GUARD_BYTES = 256     # poisoned canary bytes on each side of every output buffer
+
+
+def check_guards(t):
+    """The canaries around a buffer from empty() are intact: no kernel wrote
+    before its start or past its end."""
+    guard = getattr(t, "_svdq_guard", None)
+    if guard is None:
+        return
+    flat, g, n = guard
+    head = flat[:g].view(torch.uint8)
+    tail = flat[g + n:].view(torch.uint8)
+    bad_head = int((head != 0xFF).sum())
+    bad_tail = int((tail != 0xFF).sum())
+    assert bad_head == 0 and bad_tail == 0, \
+        f"out-of-bounds write: {bad_head} canary bytes before and {bad_tail} after a {tuple(t.shape)} buffer"
+
+
 def to_host(t, kind):
+    check_guards(t)
     t = t.detach().cpu().contiguous()
     if kind == "bf16":
         return t.view(torch.int16).numpy().view(np.uint16).copy()
@@ -44,8 +63,17 @@ def to_host(t, kind):
 
 
 def empty(shape, kind):
+    """A device buffer with GUARD_BYTES of 0xFF canaries before and after it
+    (the buffer itself keeps 256-byte alignment); to_host() checks them."""
     dt = {"bf16": torch.bfloat16, "u8": torch.uint8, "f32": torch.float32, "i32": torch.int32}[kind]
-    return torch.empty(shape, dtype=dt, device=DEV)
+    item = torch.empty((), dtype=dt).element_size()
+    g = GUARD_BYTES // item
+    n = int(np.prod(shape))
+    flat = torch.empty(n + 2 * g, dtype=dt, device=DEV)
+    flat.view(torch.uint8).fill_(0xFF)
+    t = flat[g:g + n].view(shape)
+    t._svdq_guard = (flat, g, n)
+    return t
 
 
 def poison(t):
@@ -109,9 +137,13 @@ def gpu_quantize(prec, x, smooth, lora_down, K, gelu=False):
             None if lact is None else to_host(lact, "f32"))
 
 
-def gpu_gemm(prec, act_codes, act_scales, wgt_codes, wgt_scales, lora_act, lora_up, bias, alpha=1.0):
+def gpu_gemm(prec, act_codes, act_scales, wgt_codes, wgt_scales, lora_act, lora_up, bias, alpha=1.0,
+             zero_weight_ok=False):
     from bit_w4a4_quantized_svdq_amd import capi
     M, N = act_codes.shape[0], wgt_codes.shape[0]
+    # a layer whose weight scales are all zero tests only the bias and low-rank
+    # terms; only a test that means to (the zero-residual invariant) may pass one
+    assert zero_weight_ok or N == 0 or np.any(wgt_scales != 0), "degenerate layer: all weight scales zero"
     out = poison(empty((M, N), "bf16"))
     skind = "bf16" if prec == 0 else "u8"
     capi.svdq_gemm_w4a4(prec, to_dev(act_codes, "u8"), to_dev(act_scales, skind), to_dev(wgt_codes, "u8"),
@@ -125,6 +157,7 @@ def gpu_gemv(x, codes, scales, zeros, bias):
     """scales, zeros [N, K/64], the oracle's and the library's layout."""
     from bit_w4a4_quantized_svdq_amd import capi
     M, N = x.shape[0], codes.shape[0]
+    assert N == 0 or np.any(scales != 0), "degenerate AWQ layer: all scales zero"
     out = poison(empty((M, N), "bf16"))
     capi.awq_gemv_w4a16(to_dev(x, "bf16"), to_dev(codes, "u8"), to_dev(scales, "bf16"),
                         to_dev(zeros, "bf16"), to_dev(bias, "bf16"), out)

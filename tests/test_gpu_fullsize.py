@@ -22,11 +22,29 @@ pytestmark = [pytest.mark.gpu,
 
 SAMPLE_ROWS = 24
 
+# Row positions inside a 128-row GEMM tile that fall in different classes of
+# the kernels' row handling (the 8-row LDS swizzle, the 32-row MFMA blocks,
+# the two 64-row wave halves, first/last rows of each).
+TILE_POSITIONS = np.array([0, 1, 7, 8, 30, 31, 33, 62, 63, 64, 66, 95, 96, 101, 126, 127])
+
 
 def _rows(M, seed):
     rng = np.random.default_rng(seed)
     extra = rng.choice(np.arange(2, M - 1), SAMPLE_ROWS - 3, replace=False)
     return np.concatenate([[0, 1, M - 1], np.sort(extra)])
+
+
+def _tile_rows(M, per_tile=4):
+    """per_tile rows in every 128-row tile, the position classes taken in
+    turn so that every class is checked every 16/per_tile tiles, plus the
+    first and last rows."""
+    rows = [0, 1, M - 1]
+    for t, base in enumerate(range(0, M, 128)):
+        for j in range(per_tile):
+            r = base + TILE_POSITIONS[(per_tile * t + j) % len(TILE_POSITIONS)]
+            if r < M:
+                rows.append(r)
+    return np.unique(np.array(rows))
 
 
 def _layer_parity(cfg, case, prec):
@@ -39,7 +57,7 @@ def _layer_parity(cfg, case, prec):
     assert_f32_close(gt, ot, 1e-5, cfg.name + " lora_act")
     announce("fullsize gemm_w4a4", cfg.name)
     y = gpu_gemm(prec, oc, os_, case["wgt_codes"], case["wgt_scales"], ot, case["lora_up"], case["bias"])
-    rows = _rows(cfg.M, cfg.seed)
+    rows = _tile_rows(cfg.M)
     ref = oracle.gemm_w4a4(prec, oc, os_, case["wgt_codes"], case["wgt_scales"], ot, case["lora_up"],
                            case["bias"], rows=rows)
     stats = assert_bf16_close(y[rows], ref, cfg.name)

@@ -146,7 +146,12 @@ def test_gemm_shapes(prec, M, N, K, rank, with_bias, alpha):
     assert_bf16_close(y, ref, f"gemm p{prec} {M}x{N}x{K} r{rank}")
 
 
-@pytest.mark.parametrize("M,N,K", [(64, 64, 64), (200, 320, 512), (33, 130, 4160), (1, 1, 128)])
+@pytest.mark.parametrize("M,N,K", [
+    (64, 64, 64), (33, 130, 4160), (1, 1, 128), (65, 200, 4160),
+    # K/64 a multiple of 8: the chunked main loop that every DiT-shaped GEMM
+    # launch runs (QKV / MLP-up K = 3072, MLP-down K = 12288), ragged M and N
+    (200, 320, 512), (130, 384, 3072), (130, 384, 12288), (257, 129, 1024),
+])
 def test_debug_group_sums_exact(M, N, K):
     rng = np.random.default_rng(3000 + M + N + K)
     qa = rng.integers(-8, 8, (M, K))                        # includes foreign -8 codes
@@ -176,7 +181,7 @@ def test_zero_residual_layer_on_gpu():
     zs = np.zeros((N, K // 64), np.uint16)
     announce("zero residual layer")
     gc, gs, gt = gpu_quantize(0, x, None, down, K)
-    y = gpu_gemm(0, gc, gs, zc, zs, gt, up, bias)
+    y = gpu_gemm(0, gc, gs, zc, zs, gt, up, bias, zero_weight_ok=True)
     ref_t = (synth.bf16_bits_to_f32(x).astype(np.float64) @ synth.bf16_bits_to_f32(down).astype(np.float64).T)
     ref = oracle.f64_to_bf16(ref_t @ synth.bf16_bits_to_f32(up).astype(np.float64).T +
                              synth.bf16_bits_to_f32(bias).astype(np.float64)[None, :])

@@ -75,8 +75,9 @@ def test_random_layer_shapes(i, prec, M, N, K, rank, with_bias, gelu):
 def test_random_awq_shapes(i, M, N, K, with_bias):
     rng = np.random.default_rng(7000 + i)
     x = synth.to_bf16_bits(rng.standard_normal((M, K)))
-    W = rng.standard_normal((N, K)) * 0.02
+    W = synth.to_bf16_bits(rng.standard_normal((N, K)) * 0.02)
     codes, scales, zeros = oracle.awq_quantize_weight(W)
+    assert np.count_nonzero(scales) == scales.size, "degenerate AWQ layer (zero scales)"
     bias = synth.to_bf16_bits(rng.standard_normal(N)) if with_bias else None
     announce("random awq", i, "M,N,K", M, N, K, "bias", with_bias)
     y = gpu_gemv(x, codes, scales, zeros, bias)
