@@ -24,7 +24,7 @@ SVDQ_INT4, SVDQ_NVFP4 = 0, 1
 EXPORTED = ("svdq_quantize_act", "svdq_gelu_quantize_act", "svdq_gemm_w4a4", "svdq_gemm_w4a4_qk_norm_rope",
             "awq_gemv_w4a16",
             "svdq_smooth_factors", "svdq_quantize_weight", "svdq_lowrank_workspace_bytes",
-            "svdq_lowrank_factors",
+            "svdq_lowrank_factors", "svdq_lowrank_factors_noalloc",
             "svdq_debug_group_sums", "svdq_debug_gelu_bf16", "svdq_status_string", "svdq_last_error",
             "svdq_abi_version")
 
@@ -61,10 +61,11 @@ def lib() -> ctypes.CDLL:
         L.svdq_lowrank_workspace_bytes.argtypes = [_I64, _I64, _I32]
         L.svdq_lowrank_workspace_bytes.restype = _I64
         L.svdq_lowrank_factors.argtypes = [_I64, _I64, _I32, _P, _P, ctypes.c_uint64, _P, _I64, _P, _P, _P]
+        L.svdq_lowrank_factors_noalloc.argtypes = [_I64, _I64, _I32, _P, _P, ctypes.c_uint64, _P, _P, _P]
         for f in ("svdq_quantize_act", "svdq_gelu_quantize_act", "svdq_gemm_w4a4",
                   "svdq_gemm_w4a4_qk_norm_rope", "awq_gemv_w4a16",
                   "svdq_debug_group_sums", "svdq_debug_gelu_bf16", "svdq_smooth_factors",
-                  "svdq_quantize_weight", "svdq_lowrank_factors"):
+                  "svdq_quantize_weight", "svdq_lowrank_factors", "svdq_lowrank_factors_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         L.svdq_status_string.argtypes = [ctypes.c_int]
         L.svdq_status_string.restype = ctypes.c_char_p
@@ -182,6 +183,14 @@ def svdq_lowrank_factors(W, smooth, rank, seed, workspace, lora_up, lora_down, s
     _check(lib().svdq_lowrank_factors(N, K, rank, _ptr(W), _ptr(smooth), int(seed), _ptr(workspace),
                                       workspace.numel(), _ptr(lora_up), _ptr(lora_down), _stream(stream)),
            "svdq_lowrank_factors")
+
+
+def svdq_lowrank_factors_noalloc(W, smooth, rank, seed, lora_up, lora_down, stream=None):
+    """svdq_lowrank_factors on the library's fixed per-device scratch (no workspace, no allocation)."""
+    N, K = W.shape
+    _check(lib().svdq_lowrank_factors_noalloc(N, K, rank, _ptr(W), _ptr(smooth), int(seed), _ptr(lora_up),
+                                              _ptr(lora_down), _stream(stream)),
+           "svdq_lowrank_factors_noalloc")
 
 
 def svdq_quantize_weight(precision, W, smooth, lora_up, lora_down, wgt_codes, wgt_scales, stream=None):

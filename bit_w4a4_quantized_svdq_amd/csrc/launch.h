@@ -23,6 +23,10 @@ hipError_t launch_quantize_act(int precision, bool gelu, int M, int K, int rank,
                                void *act_scales, float *lora_act, hipStream_t stream);
 hipError_t launch_gelu_bf16(int64_t n, const void *in, void *out, hipStream_t stream);
 size_t lowrank_workspace_bytes(int N, int K, int r);
+// Fixed per-device scratch of the allocation-free low-rank entry point: its
+// size, and its device address on the current device.
+constexpr size_t LOWRANK_SCRATCH_BYTES = size_t(32) << 20;
+hipError_t lowrank_scratch(void **ptr);
 hipError_t launch_lowrank_factors(int N, int K, int r, const void *W, const void *s, uint64_t seed,
                                   void *workspace, void *up, void *down, hipStream_t stream);
 hipError_t launch_smooth_factors(int M, int N, int K, const void *x, const void *W, void *s, hipStream_t stream);

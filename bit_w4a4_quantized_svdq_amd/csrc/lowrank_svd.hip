@@ -18,8 +18,10 @@
 // Kernels: a tiled fp32 product (W_hat or an fp32 basis against an l-column
 // block, plain or transposed), fp64 Gram partials + reduction, and three
 // single-workgroup steps (Cholesky with triangular inverse, Jacobi, final sort
-// and signs).  All scratch lives in a caller-provided workspace.
+// and signs).  All scratch lives in a caller-provided workspace, or, for
+// callers that cannot allocate, in this file's fixed device array `scratch`.
 #include <algorithm>
+#include <mutex>
 
 #include "device_common.h"
 #include "launch.h"
@@ -477,6 +479,36 @@ static size_t sv_layout(int N, int K, int r, char *base, SvWork *w)
 }
 
 size_t lowrank_workspace_bytes(int N, int K, int r) { return sv_layout(N, K, r, nullptr, nullptr); }
+
+// ------------------------------------------------ fixed scratch (no allocation)
+// The workspace of the allocation-free entry point: one array per device,
+// resident from the library's load until the process ends.  In host code the
+// name `scratch` is a host-side handle, not a device address; kernels get the
+// address that hipGetSymbolAddress returns for the current device.  Every
+// call shares its device's array: calls that overlap on one device race.
+// Nothing in it needs to start at zero (every kernel of the branch writes
+// each scratch element before reading it), so it is never cleared.
+static __device__ __align__(256) char scratch[LOWRANK_SCRATCH_BYTES];
+
+hipError_t lowrank_scratch(void **ptr)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {   // once per device, with that device current
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 #define SV_TRY(x) do { hipError_t e_ = (x); if (e_ != hipSuccess) return e_; } while (0)
 

@@ -168,6 +168,36 @@ svdq_status svdq_lowrank_factors(int64_t N, int64_t K, int32_t rank, const void 
                     "svdq_lowrank_factors");
 }
 
+svdq_status svdq_lowrank_factors_noalloc(int64_t N, int64_t K, int32_t rank, const void *W, const void *smooth,
+                                         uint64_t seed, void *lora_up, void *lora_down, void *stream)
+{
+    SVDQ_TRY(check_shape(1, N, K, rank));
+    if (rank < 16)
+        return fail(SVDQ_ERR_INVALID_ARG, "rank must be at least 16 (got %d)", rank);
+    if (N < rank + 8 || K < rank + 8)
+        return fail(SVDQ_ERR_INVALID_ARG, "N and K must be at least rank + 8 (got N=%lld, K=%lld)", (long long)N,
+                    (long long)K);
+    SVDQ_TRY(check_ptr(W, "W", false));
+    SVDQ_TRY(check_ptr(smooth, "smooth", true));
+    SVDQ_TRY(check_ptr(lora_up, "lora_up", false));
+    SVDQ_TRY(check_ptr(lora_down, "lora_down", false));
+    const size_t need = svdq::lowrank_workspace_bytes((int)N, (int)K, rank);
+    if (need > svdq::LOWRANK_SCRATCH_BYTES)
+        return fail(SVDQ_ERR_INVALID_ARG,
+                    "N=%lld K=%lld rank=%d needs %zu bytes of scratch, more than the fixed %zu; "
+                    "use svdq_lowrank_factors with a workspace", (long long)N, (long long)K, rank, need,
+                    svdq::LOWRANK_SCRATCH_BYTES);
+    SVDQ_TRY(check_device());
+    void *ws = nullptr;
+    const hipError_t e = svdq::lowrank_scratch(&ws);
+    if (e != hipSuccess)
+        return fail(SVDQ_ERR_HIP, "svdq_lowrank_factors_noalloc: scratch address lookup failed: %s",
+                    hipGetErrorString(e));
+    return launched(svdq::launch_lowrank_factors((int)N, (int)K, rank, W, smooth, seed, ws, lora_up, lora_down,
+                                                 (hipStream_t)stream),
+                    "svdq_lowrank_factors_noalloc");
+}
+
 svdq_status svdq_quantize_weight(int32_t precision, int64_t N, int64_t K, int32_t rank, const void *W,
                                  const void *smooth, const void *lora_up, const void *lora_down,
                                  void *wgt_codes, void *wgt_scales, void *stream)
@@ -322,6 +352,6 @@ const char *svdq_status_string(svdq_status s)
 
 const char *svdq_last_error(void) { return g_last_error; }
 
-int32_t svdq_abi_version(void) { return 5; }
+int32_t svdq_abi_version(void) { return 6; }
 
 }  // extern "C"

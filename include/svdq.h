@@ -205,6 +205,26 @@ svdq_status svdq_lowrank_factors(int64_t N, int64_t K, int32_t rank, const void 
                                  void *lora_down, void *stream);
 
 /*
+ * svdq_lowrank_factors_noalloc -- svdq_lowrank_factors for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same kernels and results (bit
+ * for bit, for the same arguments and seed), with the workspace taken from a
+ * fixed scratch array that the library holds on each device from its load
+ * until the process ends.  The call allocates and frees nothing.
+ *   arguments  as svdq_lowrank_factors, without workspace / workspace_bytes
+ *   limit      svdq_lowrank_workspace_bytes(N, K, rank) <= 32 MiB, e.g. every
+ *              layer of a 3072-wide DiT block at rank 32 (about 14 MB), or
+ *              N, K <= 16384 at rank 32; larger shapes return
+ *              SVDQ_ERR_INVALID_ARG (use svdq_lowrank_factors)
+ *   sharing    all calls on one device use that device's one array, which
+ *              keeps the last call's contents: calls that overlap on a device
+ *              (several streams or threads) race and must be serialized by
+ *              the caller; nothing in it needs clearing between calls
+ */
+svdq_status svdq_lowrank_factors_noalloc(int64_t N, int64_t K, int32_t rank, const void *W, const void *smooth,
+                                         uint64_t seed, void *lora_up, void *lora_down, void *stream);
+
+/*
  * svdq_quantize_weight -- the 4-bit residual of the smoothed weight after the
  * low-rank branch, and its group quantization:
  *   R[n,k] = fl32( W[n,k] smooth[k] - sum_{j=0..rank-1} up[n,j] down[j,k] )
@@ -244,9 +264,10 @@ const char *svdq_status_string(svdq_status s);
 /* Text of the last argument-check failure on the calling thread ("" if none). */
 const char *svdq_last_error(void);
 
-/* ABI version of this header: 5 (1 plus svdq_gelu_quantize_act, svdq_debug_gelu_bf16,
+/* ABI version of this header: 6 (1 plus svdq_gelu_quantize_act, svdq_debug_gelu_bf16,
  * svdq_gemm_w4a4_qk_norm_rope, svdq_smooth_factors, svdq_quantize_weight,
- * svdq_lowrank_workspace_bytes and svdq_lowrank_factors). */
+ * svdq_lowrank_workspace_bytes, svdq_lowrank_factors and
+ * svdq_lowrank_factors_noalloc). */
 int32_t svdq_abi_version(void);
 
 #ifdef __cplusplus

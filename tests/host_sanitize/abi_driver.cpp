@@ -157,6 +157,14 @@ int main() {
                   "lowrank workspace too small");
     expect_reject(svdq_lowrank_factors(12288, 3072, 0, P, P, 7, P, ws, P, P, nullptr), INV, "lowrank rank 0");
     expect_reject(svdq_lowrank_factors(36, 3072, 32, P, P, 7, P, ws, P, P, nullptr), INV, "lowrank N < rank + 8");
+    expect_launch(svdq_lowrank_factors_noalloc(12288, 3072, 32, P, P, 7, P, P, nullptr), "lowrank_factors", 12288,
+                  3072, 32);
+    expect_launch(svdq_lowrank_factors_noalloc(3072, 12288, 32, P, nullptr, 7, P, P, nullptr), "lowrank_factors",
+                  3072, 12288, 32);
+    expect_reject(svdq_lowrank_factors_noalloc(65536, 65536, 128, P, P, 7, P, P, nullptr), INV,
+                  "lowrank noalloc beyond the fixed scratch");
+    expect_reject(svdq_lowrank_factors_noalloc(12288, 3072, 32, P, P, 7, nullptr, P, nullptr), INV,
+                  "lowrank noalloc lora_up NULL");
     expect_launch(svdq_quantize_weight(SVDQ_NVFP4, 3072, 3072, 32, P, P, P, P, P, P, nullptr), "quantize_weight",
                   3072, 3072, 1032);
     expect_reject(svdq_quantize_weight(SVDQ_INT4, 64, 64, 16, P, P, nullptr, P, P, P, nullptr), INV,

@@ -40,6 +40,10 @@ hipError_t launch_lowrank_factors(int N, int K, int r, const void *, const void 
                                   void *, hipStream_t) {
     return rec("lowrank_factors", N, K, r);
 }
+hipError_t lowrank_scratch(void **ptr) {
+    *ptr = (void *)(uintptr_t)0x200000;   // a fake, aligned device address
+    return g_stub.result;
+}
 hipError_t launch_smooth_factors(int M, int N, int K, const void *, const void *, void *, hipStream_t) {
     return rec("smooth_factors", M, N, K);
 }

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(capi.LIB_PATH)
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert capi.svdq_abi_version() == 5
+    assert capi.svdq_abi_version() == 6
     for s in range(4):
         assert capi.svdq_status_string(s).startswith(("SVDQ_OK", "SVDQ_ERR"))
     assert "unknown" in capi.svdq_status_string(99)
@@ -165,3 +165,22 @@ def test_lowrank_workspace_query_and_checks():
     assert f(rank=8) == INV
     assert f(N=39) == INV
     assert f(work=0) == INV
+
+
+def test_lowrank_noalloc_host_checks():
+    """The allocation-free low-rank entry point rejects, on the host, shapes
+    whose workspace exceeds its fixed 32 MiB scratch, and the other bad
+    arguments of svdq_lowrank_factors."""
+    L = capi.lib()
+    f = lambda rank=32, N=256, K=512, up=A, down=A: L.svdq_lowrank_factors_noalloc(N, K, rank, A, A, 1, up, down,
+                                                                                    None)
+    assert capi.svdq_lowrank_workspace_bytes(65536, 65536, 128) > 32 << 20
+    assert f(rank=128, N=65536, K=65536) == INV
+    assert "32" in capi.lib().svdq_last_error().decode() or "scratch" in capi.lib().svdq_last_error().decode()
+    assert f(rank=8) == INV
+    assert f(N=39) == INV
+    assert f(up=0) == INV
+    assert f(down=MIS) == INV
+    # every layer of a 3072-wide DiT block at rank 32 fits
+    for N, K in ((9216, 3072), (12288, 3072), (3072, 12288), (3072, 3072)):
+        assert 0 < capi.svdq_lowrank_workspace_bytes(N, K, 32) <= 32 << 20
