@@ -19,12 +19,13 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "_lib", "libsvdq.so")
 
 SVDQ_OK, SVDQ_ERR_INVALID_ARG, SVDQ_ERR_UNSUPPORTED, SVDQ_ERR_HIP = 0, 1, 2, 3
-SVDQ_INT4, SVDQ_NVFP4 = 0, 1
+SVDQ_INT4, SVDQ_NVFP4, SVDQ_INT4_PACKED = 0, 1, 2
 
 EXPORTED = ("svdq_quantize_act", "svdq_gelu_quantize_act", "svdq_gemm_w4a4", "svdq_gemm_w4a4_qk_norm_rope",
             "awq_gemv_w4a16",
             "svdq_smooth_factors", "svdq_quantize_weight", "svdq_lowrank_workspace_bytes",
             "svdq_lowrank_factors", "svdq_lowrank_factors_noalloc",
+            "svdq_packed_weight_bytes", "svdq_pack_weight_int4", "svdq_debug_group_sums_packed",
             "svdq_debug_group_sums", "svdq_debug_gelu_bf16", "svdq_status_string", "svdq_last_error",
             "svdq_abi_version")
 
@@ -55,6 +56,10 @@ def lib() -> ctypes.CDLL:
                                                   _P, _P, _P, _F32, _P, _P, _P, _P]
         L.awq_gemv_w4a16.argtypes = [_I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P]
         L.svdq_debug_group_sums.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P]
+        L.svdq_debug_group_sums_packed.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P]
+        L.svdq_packed_weight_bytes.argtypes = [_I64, _I64]
+        L.svdq_packed_weight_bytes.restype = _I64
+        L.svdq_pack_weight_int4.argtypes = [_I64, _I64, _P, _P, _P, _P, _P]
         L.svdq_debug_gelu_bf16.argtypes = [_I64, _P, _P, _P]
         L.svdq_smooth_factors.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P]
         L.svdq_quantize_weight.argtypes = [_I32, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P]
@@ -64,7 +69,8 @@ def lib() -> ctypes.CDLL:
         L.svdq_lowrank_factors_noalloc.argtypes = [_I64, _I64, _I32, _P, _P, ctypes.c_uint64, _P, _P, _P]
         for f in ("svdq_quantize_act", "svdq_gelu_quantize_act", "svdq_gemm_w4a4",
                   "svdq_gemm_w4a4_qk_norm_rope", "awq_gemv_w4a16",
-                  "svdq_debug_group_sums", "svdq_debug_gelu_bf16", "svdq_smooth_factors",
+                  "svdq_debug_group_sums", "svdq_debug_group_sums_packed", "svdq_pack_weight_int4",
+                  "svdq_debug_gelu_bf16", "svdq_smooth_factors",
                   "svdq_quantize_weight", "svdq_lowrank_factors", "svdq_lowrank_factors_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         L.svdq_status_string.argtypes = [ctypes.c_int]
@@ -129,13 +135,42 @@ def svdq_gelu_quantize_act(precision, x, smooth, lora_down, act_codes, act_scale
                                         _stream(stream)), "svdq_gelu_quantize_act")
 
 
+def _weight_shape(precision, wgt_codes, wgt_scales):
+    """(N, K) of a layer's weight: from the codes [N, K/2], or for a packed
+    blob (one-dimensional) from the int4 scales [N, K/64]."""
+    if precision == SVDQ_INT4_PACKED:
+        N, G = wgt_scales.shape
+        return N, 64 * G
+    N, Kh = wgt_codes.shape
+    return N, 2 * Kh
+
+
+def svdq_packed_weight_bytes(N, K) -> int:
+    return int(lib().svdq_packed_weight_bytes(N, K))
+
+
+def svdq_pack_weight_int4(wgt_codes, wgt_scales, packed_weight, invalid_codes=None, stream=None):
+    """Offline re-encoding of int4 weight codes [N, K/2] (+ bf16 scales) into the
+    packed blob of the SVDQ_INT4_PACKED GEMM; invalid_codes: optional int32 [1]."""
+    N, Kh = wgt_codes.shape
+    _check(lib().svdq_pack_weight_int4(N, 2 * Kh, _ptr(wgt_codes), _ptr(wgt_scales), _ptr(packed_weight),
+                                       _ptr(invalid_codes), _stream(stream)), "svdq_pack_weight_int4")
+
+
+def svdq_debug_group_sums_packed(act_codes, packed_weight, N, G, stream=None):
+    """Exact int32 group sums [M,N,K/64] on the packed int4 GEMM's device path."""
+    M, Kh = act_codes.shape
+    _check(lib().svdq_debug_group_sums_packed(M, N, 2 * Kh, _ptr(act_codes), _ptr(packed_weight), _ptr(G),
+                                              _stream(stream)), "svdq_debug_group_sums_packed")
+
+
 def svdq_gemm_w4a4(precision, act_codes, act_scales, wgt_codes, wgt_scales, alpha, lora_act,
                    lora_up, bias, out, stream=None):
     """4-bit GEMM with the low-rank up-projection and bias; out is [M,N] bf16."""
     M = act_codes.shape[0]
-    N, Kh = wgt_codes.shape
+    N, K = _weight_shape(precision, wgt_codes, wgt_scales)
     rank = 0 if lora_up is None else lora_up.shape[1]
-    _check(lib().svdq_gemm_w4a4(precision, M, N, 2 * Kh, rank, _ptr(act_codes), _ptr(act_scales),
+    _check(lib().svdq_gemm_w4a4(precision, M, N, K, rank, _ptr(act_codes), _ptr(act_scales),
                                 _ptr(wgt_codes), _ptr(wgt_scales), float(alpha), _ptr(lora_act),
                                 _ptr(lora_up), _ptr(bias), _ptr(out), _stream(stream)),
            "svdq_gemm_w4a4")
@@ -147,9 +182,9 @@ def svdq_gemm_w4a4_qk_norm_rope(precision, act_codes, act_scales, wgt_codes, wgt
     """4-bit GEMM of a grouped QKV layer with per-head RMSNorm + rotary embedding
     of Q and K in the epilogue; out is [M, 3*H*128] bf16."""
     M = act_codes.shape[0]
-    N, Kh = wgt_codes.shape
+    N, K = _weight_shape(precision, wgt_codes, wgt_scales)
     rank = 0 if lora_up is None else lora_up.shape[1]
-    _check(lib().svdq_gemm_w4a4_qk_norm_rope(precision, M, N, 2 * Kh, rank, _ptr(act_codes),
+    _check(lib().svdq_gemm_w4a4_qk_norm_rope(precision, M, N, K, rank, _ptr(act_codes),
                                              _ptr(act_scales), _ptr(wgt_codes), _ptr(wgt_scales),
                                              float(alpha), _ptr(lora_act), _ptr(lora_up), _ptr(bias),
                                              _ptr(q_norm_weight), _ptr(k_norm_weight), float(eps),

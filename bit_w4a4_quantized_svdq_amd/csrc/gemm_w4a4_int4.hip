@@ -46,6 +46,32 @@
 // on the matrix core (t split into bf16 hi + lo), packed hardware bf16
 // conversion, and for a tile fully inside the output, 2-byte buffer stores
 // whose row offsets are scalar.
+//
+// Packed weights (PACKED): the fp8 formulation.  The int8 products above
+// leave one int->float conversion per output and group on the vector ALU,
+// which is the unit this loop runs out of.  gfx950's
+// v_mfma_scale_f32_32x32x64_f8f6f4 takes E4M3 bytes and returns fp32, and
+// small integers are exact E4M3 values: the byte u (u = 0..15, exponent field
+// 0 or 1) is u * 2^-9, and sign | m (m = 0..7) is +-m * 2^-9.  So
+//   * an activation nibble n (two's complement q) becomes the byte n ^ 8,
+//     i.e. the offset code u = q + 8 in [0, 15]: one and/xor (v_bitop3) per
+//     dword for the even nibbles, one shift more for the odd ones;
+//   * a weight code is stored, once, in sign-magnitude form in a bit layout
+//     made for this step (svdq_pack_weight_int4, see pack_int4_kernel): a
+//     dword d gives four E4M3 bytes as d & 0x87878787 and four more as
+//     rotr(d, 4) & 0x87878787;
+//   * with E8M0 block scales 2^9 on both operands the instruction returns
+//     X_g = sum_k u_k qw_k = G_g + 8 Sw_g exactly (Sw_g = sum_k qw_k of the
+//     weight row's group), in fp32, with no conversion;
+//   * acc += X_g * P_g (one fma per output and group, P_g as above), and the
+//     offset's share sum_g P_g 8 Sw_g = sum_g sx_g (8 sw_g Sw_g) is a product
+//     over groups with a per-(column, group) factor that depends on the weight
+//     only: the packer stores -8 sw_g Sw_g as two bf16 planes (hi + lo) and
+//     the epilogue adds act_scales . corr^T on bf16 MFMAs (gemm_corr_int4).
+// Codes -8 cannot be written in sign-magnitude form: the packer reports them
+// (the group quantizer never produces them: its codes lie in [-7, 7]).
+#include <utility>
+
 #include "device_common.h"
 #include "gemm_common.h"
 #include "launch.h"
@@ -54,7 +80,8 @@ namespace svdq {
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef float v32f __attribute__((ext_vector_type(32)));
 
-constexpr int G4_BM = 128, G4_BN = 128, G4_THREADS = 256, G4_STAGES = 4;
+constexpr int G4_BM = 128, G4_BN = 128, G4_THREADS = 256;
+constexpr int G4_STAGES = 4;                           // stages of the general loop (and the least ring)
 constexpr int G4_CODES = G4_BM * 32;                   // bytes of A (or B) codes per group
 constexpr int G4_STAGE = 2 * G4_CODES;                 // one group of A and B codes: 8 KB
 // Scales travel 8 groups at a time: each row's 8 consecutive bf16 scales are
@@ -69,7 +96,15 @@ constexpr int G4_SC_GROUPS = 8;
 constexpr int G4_SC_SLOT = G4_SC_GROUPS * (G4_BM + G4_BN) * 4;   // 8 KB (the larger layout)
 constexpr int G4_SC = G4_STAGES * G4_STAGE;            // offset of the two scale slots
 constexpr int G4_SMEM = G4_SC + 2 * G4_SC_SLOT;        // 48 KB
+// The chunked loop (K/64 a multiple of 8) stages two groups at a time: 64
+// bytes of each row, written by copy instructions of 16 rows x 64 B (four
+// lanes per row), two such stages alternating in the first 32 KB.
+constexpr int G4_CO_ROWB = 64;                         // bytes per row and stage
+constexpr int G4_CO_CODES = G4_BM * G4_CO_ROWB;        // 8 KB of A (or B) codes per stage
+constexpr int G4_CO_STAGE = 2 * G4_CO_CODES;           // 16 KB
+static_assert(2 * G4_CO_STAGE <= G4_SC, "the two-group stages fit below the scale slots");
 constexpr int G4_GROUP_M = 8;                          // M-tiles per raster group
+
 
 // 32x32 MFMA accumulator layout: lane l, register i -> row 8*(i/4) + 4*(l/32) + i%4, col l%32.
 
@@ -84,10 +119,108 @@ __device__ __forceinline__ void unpack_i8(const v4u &c, v4i &lo, v4i &hi) {
     for (int i = 0; i < 4; ++i) hi[i] = (int)(c[i] & 0xF0F0F0F0u);
 }
 
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+// 32 activation codes (16 bytes of two's complement nibbles of one row and
+// K-half) -> 32 E4M3 bytes of the offset codes q + 8, in the k order
+// [even nibbles of dword 0 | odd nibbles of dword 0 | even of dword 1 | ...].
+__device__ __forceinline__ v8i act_fp8_offset(const v4u &d) {
+    v8i r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r[2 * i] = (int)((d[i] ^ 0x88888888u) & 0x0F0F0F0Fu);
+        r[2 * i + 1] = (int)(((d[i] >> 4) ^ 0x08080808u) & 0x0F0F0F0Fu);
+    }
+    return r;
+}
+
+// 32 packed weight codes -> 32 E4M3 sign-magnitude bytes in the same k order
+// as act_fp8_offset (the packer's layout makes this two masks and a rotate).
+__device__ __forceinline__ v8i wgt_fp8_signmag(const v4u &p) {
+    v8i r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r[2 * i] = (int)(p[i] & 0x87878787u);
+        r[2 * i + 1] = (int)(__builtin_amdgcn_alignbit(p[i], p[i], 4) & 0x87878787u);
+    }
+    return r;
+}
+
+// X = sum_k u_k * qw_k over one group (both operands E4M3 at 2^-9, block
+// scales 2^9 * 2^9 in E8M0: exact integers in fp32)
+__device__ __forceinline__ v16f mfma_group_fp8(const v8i &a, const v8i &b) {
+    constexpr int kScale2p9 = 127 + 9;
+    const v16f z = {};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, z, 0, 0, 0, kScale2p9, 0, kScale2p9);
+}
+
+// acc += act_scales . corr^T over the groups: the offset correction of the
+// packed formulation (corr = -8 sw Sw per weight row and group, bf16 hi and
+// lo planes of [N][2][NG]).  VEC: NG a multiple of 8 (16-byte loads).
+template <bool VEC>
+__device__ __forceinline__ void gemm_corr_int4(v16f (&acc)[2][2], int M, int N, int NG, int m0, int n0, int wm,
+                                               int wn, int lane, const uint16_t *__restrict__ act_scales,
+                                               const uint16_t *__restrict__ corr)
+{
+    const int l32 = lane & 31, h = lane >> 5;
+    int arow[2], bcol[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        arow[t] = min(m0 + wm * 64 + t * 32 + l32, M - 1);   // rows past M feed no stored output
+        bcol[t] = min(n0 + wn * 64 + t * 32 + l32, N - 1);
+    }
+    for (int c = 0; c < NG; c += 16) {
+        const int g = c + 8 * h;
+        v8bf sa[2], chi[2], clo[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const uint16_t *ap = act_scales + (size_t)arow[t] * NG + g;
+            const uint16_t *bp = corr + (size_t)bcol[t] * 2 * NG + g;
+            v4u va = {0u, 0u, 0u, 0u}, vh = va, vl = va;
+            if constexpr (VEC) {
+                if (g < NG) {                     // all 8 groups valid or none
+                    va = *(const v4u *)ap;
+                    vh = *(const v4u *)bp;
+                    vl = *(const v4u *)(bp + NG);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; j += 2) {
+                    const uint32_t a0 = g + j < NG ? ap[j] : 0u, a1 = g + j + 1 < NG ? ap[j + 1] : 0u;
+                    const uint32_t h0 = g + j < NG ? bp[j] : 0u, h1 = g + j + 1 < NG ? bp[j + 1] : 0u;
+                    const uint32_t l0 = g + j < NG ? bp[NG + j] : 0u, l1 = g + j + 1 < NG ? bp[NG + j + 1] : 0u;
+                    va[j >> 1] = a0 | a1 << 16;
+                    vh[j >> 1] = h0 | h1 << 16;
+                    vl[j >> 1] = l0 | l1 << 16;
+                }
+            }
+            sa[t] = __builtin_bit_cast(v8bf, va);
+            chi[t] = __builtin_bit_cast(v8bf, vh);
+            clo[t] = __builtin_bit_cast(v8bf, vl);
+        }
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa[a], chi[b], acc[a][b], 0, 0, 0);
+                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa[a], clo[b], acc[a][b], 0, 0, 0);
+            }
+    }
+}
+
 // SC16: scales copied 8 groups per 16-byte copy (K/64 a multiple of 8)
 // QK: grouped QKV layer, per-head RMSNorm + rotary embedding of Q and K in
 // the epilogue (gemm_epilogue_qk)
-template <bool GROUP_SUMS, bool SC16, bool QK = false>
+// s_waitcnt vmcnt(N) for a compile-time N < 64 (expcnt, lgkmcnt unconstrained)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_c() {
+    static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// PACKED: weights in the packed layout (the fp8 formulation; wgt_codes is
+// the packer's blob, its correction planes follow the codes)
+template <bool GROUP_SUMS, bool SC16, bool QK = false, bool PACKED = false>
 __global__ __launch_bounds__(G4_THREADS, GROUP_SUMS ? 2 : 3)
 void gemm_w4a4_int4_kernel(int M, int N, int K, int rank,
                            const uint8_t *__restrict__ act_codes,
@@ -147,6 +280,36 @@ void gemm_w4a4_int4_kernel(int M, int N, int K, int rank,
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lptr_t)st, 16, pa_off, g * 32, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lptr_t)(st + G4_CODES), 16, pb_off, g * 32, 0, 0);
     };
+    // Two-group stages (chunked loop).  A copy instruction moves 64 lanes x
+    // 16 bytes and the vector memory path handles it per distinct cache line:
+    // 16 bytes from each of 64 rows (one group) touches 64 lines, 64 bytes
+    // from each of 16 rows (two groups) 16.  Copy instruction q (0..7) of an
+    // operand covers rows 16q .. 16q+15: lane i -> row 16q + i/4 and LDS
+    // slot i % 4 of that row's 64 bytes, which receives the row's 16-byte
+    // chunk c = slot ^ ((row >> 1) & 3) (chunk c = 2 * group-of-the-stage +
+    // K-half).  The swizzle spreads the 8 rows that one LDS cycle of a
+    // fragment read serves over distinct banks.  Wave w issues instructions w
+    // and w + 4 of A and of B.
+    // The swizzle (row >> 1) & 3 = (lane >> 3) & 3 is the same for both
+    // instructions of a wave, which differ by 64 rows.  Rows past M (columns
+    // past N) lie beyond the buffer descriptor's range (their per-lane offset
+    // alone exceeds it) and read as zeros: they only feed outputs that are
+    // never stored.
+    uint32_t c_off = 0u;
+    if constexpr (SC16)
+        c_off = (uint32_t)((16 * wave + (lane >> 2)) * rowbytes + 16 * ((lane & 3) ^ ((lane >> 3) & 3)));
+    // groups 2s, 2s+1 into two-group stage `buf`
+    auto issue_pair = [&](int s, int buf) {
+        uint8_t *st = smem + buf * G4_CO_STAGE;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const uint32_t voff = c_off + (uint32_t)(u * 64 * rowbytes);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lptr_t)(st + (wave + 4 * u) * 1024), 16, voff,
+                                                     s * G4_CO_ROWB, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lptr_t)(st + G4_CO_CODES + (wave + 4 * u) * 1024), 16,
+                                                     voff, s * G4_CO_ROWB, 0, 0);
+        }
+    };
     // The byte offset of this lane's scale row is that of the same clamped
     // row's codes divided by 16: pa_off / 16 (waves 0,1: row * K/2) or
     // (pb_off - 16) / 16 (waves 2,3: row * K/2 + 16).  It is derived where it
@@ -179,10 +342,20 @@ void gemm_w4a4_int4_kernel(int M, int N, int K, int rank,
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
 
-    // consumer offsets inside a stage and inside a scale slot
+    // consumer offsets inside a single-group stage and inside a scale slot
     int a_off[2], b_off[2], sa_off[2], sb_off[2];
     // 2-block P operand B: lane l carries column wn*64 + l (block l/32)
     const int sb2_off = SC16 ? G4_BM * 16 + (wn * 64 + lane) * 16 : 4 * G4_BM + (wn * 64 + lane) * 4;
+    // Fragment offsets in a two-group stage: row r's chunk c sits at r * 64 +
+    // 16 * (c ^ ((r >> 1) & 3)), and (r >> 1) & 3 = (l32 >> 1) & 3 for every
+    // row this lane reads; tile t adds 32 rows (2 KB).  [group of the stage]
+    int a_co[2], b_co[2];
+#pragma unroll
+    for (int gg = 0; gg < 2; ++gg) {
+        const int sw = ((2 * gg + h) ^ ((l32 >> 1) & 3)) << 4;
+        a_co[gg] = (wm * 64 + l32) * G4_CO_ROWB + sw;
+        b_co[gg] = G4_CO_CODES + (wn * 64 + l32) * G4_CO_ROWB + sw;
+    }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         a_off[t] = h * (G4_CODES / 2) + (wm * 64 + t * 32 + l32) * 16;
@@ -197,12 +370,76 @@ void gemm_w4a4_int4_kernel(int M, int N, int K, int rank,
 
     // One group: fragments from the stage at `st`, scales from `sc` (this
     // group's column of a scale slot), G_g on the integer matrix core.
-    auto compute = [&](const uint8_t *st, const uint8_t *sc, int g) {
+    // tstride: bytes between the 32-row tiles of a fragment in the stage layout
+    auto compute = [&](const uint8_t *st, int ao, int bo, auto tstride, const uint8_t *sc, int g) {
         v4u fa[2], fb[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            fa[t] = *(const v4u *)(st + a_off[t]);
-            fb[t] = *(const v4u *)(st + b_off[t]);
+            fa[t] = *(const v4u *)(st + ao + t * decltype(tstride)::value);
+            fb[t] = *(const v4u *)(st + bo + t * decltype(tstride)::value);
+        }
+        if constexpr (PACKED) {
+            v8i A[2], B[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                A[t] = act_fp8_offset(fa[t]);
+                B[t] = wgt_fp8_signmag(fb[t]);
+            }
+            if constexpr (GROUP_SUMS) {
+                // G = X - 8 Sw: the weight column's code sum of the group from
+                // its E4M3 bytes (this lane's 32 plus the other K-half's)
+                int sw[2];
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    int s = 0;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int byte = (B[b][i] >> (8 * e)) & 0xFF;
+                            s += (byte & 0x80) ? -(byte & 7) : (byte & 7);
+                        }
+                    sw[b] = s + __shfl_xor(s, 32, 64);
+                }
+#pragma unroll
+                for (int a = 0; a < 2; ++a)
+#pragma unroll
+                    for (int b = 0; b < 2; ++b) {
+                        const v16f X = mfma_group_fp8(A[a], B[b]);
+                        const int col = n0 + wn * 64 + b * 32 + l32;
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            const int rowi = m0 + wm * 64 + a * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+                            if (rowi < M && col < N) gsum[((size_t)rowi * N + col) * NG + g] = (int)X[i] - 8 * sw[b];
+                        }
+                    }
+            } else {
+                v4s pa_op[2], pb_op;
+                {
+                    uint32_t sa[2], sb;
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+                        sa[t] = SC16 ? *(const uint16_t *)(sc + sa_off[t]) : *(const uint32_t *)(sc + sa_off[t]) & 0xFFFFu;
+                    sb = SC16 ? *(const uint16_t *)(sc + sb2_off) : *(const uint32_t *)(sc + sb2_off) & 0xFFFFu;
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) pa_op[t] = __builtin_bit_cast(v4s, v2u{sa[t], 0u});
+                    pb_op = __builtin_bit_cast(v4s, v2u{sb, 0u});
+                }
+#pragma unroll
+                for (int a = 0; a < 2; ++a) {
+                    v32f P = {};
+                    P = __builtin_amdgcn_mfma_f32_32x32x4bf16_1k(pa_op[a], pb_op, P, 0, 0, 0);
+#pragma unroll
+                    for (int b = 0; b < 2; ++b) {
+                        const v16f X = mfma_group_fp8(A[a], B[b]);
+#pragma unroll
+                        for (int i = 0; i < 16; ++i)
+                            acc[a][b][i] = __builtin_fmaf(X[i], P[16 * b + i], acc[a][b][i]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            return;
         }
         v4i alo[2], ahi[2], blo[2], bhi[2];
 #pragma unroll
@@ -259,49 +496,50 @@ void gemm_w4a4_int4_kernel(int M, int N, int K, int rank,
     };
 
     if constexpr (SC16) {
-        // K/64 is a multiple of 8: the loop runs over chunks of 8 groups, the
-        // period of the scale copies, so that every wait count and every LDS
-        // offset below is a compile-time constant.  Per wave, group g costs
-        // two copies (codes), plus one (scales) when g % 8 == 0; waiting until
-        // at most the copies of the two groups issued after g are in flight
-        // means that g has landed.  The group-sum mode runs this same loop
-        // with the scale copies left out (its wait counts drop by the one
-        // scale copy that would be in flight).
-        constexpr int SCW = GROUP_SUMS ? 0 : 1;
-        issue_codes(0, 0);
+        // K/64 is a multiple of 8: the loop runs over chunks of 8 groups (the
+        // period of the scale copies) in four two-group stages, so every LDS
+        // offset below is a compile-time constant.  Two stage buffers
+        // alternate: after the barrier of stage s every wave is done with
+        // stage s-1, whose buffer then receives stage s+1 while stage s is
+        // computed.  A chunk's scales (one copy per wave) follow the codes of
+        // its first stage.  Waiting for all of this wave's copies before the
+        // barrier means stage s (and its chunk's scales) has landed.
+        issue_pair(0, 0);
         if constexpr (!GROUP_SUMS) issue_scales8(0, 0);
-        issue_codes(1, 1);
-        issue_codes(2, 2);
         for (int c = 0; c < NG; c += G4_SC_GROUPS) {
             const bool last = c + G4_SC_GROUPS == NG;
             const int par = (c >> 3) & 1;
             const uint8_t *slot = smem + G4_SC + par * G4_SC_SLOT;
-#pragma unroll
-            for (int j = 0; j < G4_SC_GROUPS; ++j) {
-                __builtin_amdgcn_sched_barrier(0);            // groups stay in program order
-                if (j < 6) wait_vmcnt(4);                   // groups c+j+1, c+j+2: codes only
-                else if (j == 6) { if (last) wait_vmcnt(2); else wait_vmcnt(4 + SCW); }
-                else { if (last) wait_vmcnt(0); else wait_vmcnt(4 + SCW); }
+            // stage p of the chunk (groups c + 2p, c + 2p + 1), p a compile-time constant
+            auto step = [&](auto pc) {
+                constexpr int p = decltype(pc)::value;
+                __builtin_amdgcn_sched_barrier(0);            // stages stay in program order
+                wait_vmcnt_c<0>();
                 lds_barrier();
-                if (j < 5) {
-                    issue_codes(c + j + 3, (j + 3) & 3);
-                } else if (!last) {
-                    issue_codes(c + j + 3, (j + 3) & 3);
+                if (!last || p < 3) {
+                    issue_pair((c >> 1) + p + 1, (p + 1) & 1);
                     if constexpr (!GROUP_SUMS)
-                        if (j == 5) issue_scales8(c + G4_SC_GROUPS, par ^ 1);
+                        if (p == 3) issue_scales8(c + G4_SC_GROUPS, par ^ 1);
                 }
-                compute(smem + (j & 3) * G4_STAGE, slot + 2 * j, c + j);
-                // the group's accumulation completes here, before the next
-                // barrier (otherwise the unrolled groups' products would be
-                // kept live and summed later)
+                const uint8_t *st = smem + (p & 1) * G4_CO_STAGE;
 #pragma unroll
-                for (int a = 0; a < 2; ++a)
+                for (int gg = 0; gg < 2; ++gg) {
+                    compute(st, a_co[gg], b_co[gg], std::integral_constant<int, 32 * G4_CO_ROWB>{},
+                            slot + 2 * (2 * p + gg), c + 2 * p + gg);
+                    // the group's accumulation completes here (otherwise the
+                    // unrolled groups' products would be kept live and summed later)
 #pragma unroll
-                    for (int b = 0; b < 2; ++b) opaque(acc[a][b]);
-            }
+                    for (int a = 0; a < 2; ++a)
+#pragma unroll
+                        for (int b = 0; b < 2; ++b) opaque(acc[a][b]);
+                }
+            };
+            [&]<int... P>(std::integer_sequence<int, P...>) {
+                (step(std::integral_constant<int, P>{}), ...);
+            }(std::make_integer_sequence<int, G4_SC_GROUPS / 2>{});
         }
     } else {
-        // general loop: any K/64 (the group-sum mode copies no scales)
+        // general loop: any K/64, 4 stages (the group-sum mode copies no scales)
         auto loads_of = [](int g) { return GROUP_SUMS ? 2 : 3; };
         auto issue = [&](int g) {
             issue_codes(g, g % G4_STAGES);
@@ -313,88 +551,87 @@ void gemm_w4a4_int4_kernel(int M, int N, int K, int rank,
             wait_vmcnt(newer * loads_of(g));
             lds_barrier();
             if (g + G4_STAGES - 1 < NG) issue(g + G4_STAGES - 1);
-            compute(smem + (g % G4_STAGES) * G4_STAGE,
+            compute(smem + (g % G4_STAGES) * G4_STAGE, a_off[0], b_off[0], std::integral_constant<int, 32 * 16>{},
                     smem + G4_SC + ((g >> 3) & 1) * G4_SC_SLOT + (g & 7) * (4 * (G4_BM + G4_BN)), g);
         }
     }
 
     if constexpr (!GROUP_SUMS) {
-        // acc = 2^8 * sum_g G_g sx_g sw_g (the codes entered as 16*code)
+        // plain: acc = 2^8 * sum_g G_g sx_g sw_g (the codes entered as 16*code);
+        // packed: acc = sum_g (G_g + 8 Sw_g) sx_g sw_g, and the correction
+        // brings it to sum_g G_g sx_g sw_g
+        float post = alpha * 0.00390625f;
+        if constexpr (PACKED) {
+            const uint16_t *corr = (const uint16_t *)(wgt_codes + (size_t)N * rowbytes);
+            gemm_corr_int4<SC16>(acc, M, N, NG, m0, n0, wm, wn, lane, act_scales, corr);
+            post = alpha;
+        }
         if constexpr (QK) {
-            gemm_epilogue_sum(acc, alpha * 0.00390625f, M, N, rank, m0, n0, wm, wn, lane, lora_act, lora_up, bias);
+            gemm_epilogue_sum(acc, post, M, N, rank, m0, n0, wm, wn, lane, lora_act, lora_up, bias);
             if (n0 < qk.qk_cols)   // block-uniform: a Q or K head
                 gemm_epilogue_qk(acc, M, m0, n0, wm, wn, lane, qk, smem, N, out);
             else
                 gemm_epilogue_store(acc, M, N, m0, n0, wm, wn, lane, out);
         } else {
-            gemm_epilogue(acc, alpha * 0.00390625f, M, N, rank, m0, n0, wm, wn, lane, lora_act, lora_up, bias, out);
+            gemm_epilogue(acc, post, M, N, rank, m0, n0, wm, wn, lane, lora_act, lora_up, bias, out);
         }
     }
 }
 
-hipError_t launch_gemm_w4a4_int4(int M, int N, int K, int rank, const void *act_codes,
-                                 const void *act_scales, const void *wgt_codes,
-                                 const void *wgt_scales, float alpha, const float *lora_act,
-                                 const void *lora_up, const void *bias, void *out,
+template <bool GROUP_SUMS, bool QK, bool PACKED>
+static hipError_t launch_int4(int M, int N, int K, int rank, const void *act_codes, const void *act_scales,
+                              const void *wgt_codes, const void *wgt_scales, float alpha, const float *lora_act,
+                              const void *lora_up, const void *bias, void *out, int32_t *G, const QkNormRope &qk,
+                              hipStream_t stream)
+{
+    dim3 grid(((N + G4_BN - 1) / G4_BN) * ((M + G4_BM - 1) / G4_BM)), block(G4_THREADS);
+    // K/64 a multiple of 8: the chunked main loop with 16-byte scale copies
+    if ((K >> 6) % G4_SC_GROUPS == 0)
+        hipLaunchKernelGGL((gemm_w4a4_int4_kernel<GROUP_SUMS, true, QK, PACKED>), grid, block, 0, stream, M, N, K,
+                           rank, (const uint8_t *)act_codes, (const uint16_t *)act_scales,
+                           (const uint8_t *)wgt_codes, (const uint16_t *)wgt_scales, alpha, lora_act,
+                           (const uint16_t *)lora_up, (const uint16_t *)bias, (uint16_t *)out, G, qk);
+    else
+        hipLaunchKernelGGL((gemm_w4a4_int4_kernel<GROUP_SUMS, false, QK, PACKED>), grid, block, 0, stream, M, N, K,
+                           rank, (const uint8_t *)act_codes, (const uint16_t *)act_scales,
+                           (const uint8_t *)wgt_codes, (const uint16_t *)wgt_scales, alpha, lora_act,
+                           (const uint16_t *)lora_up, (const uint16_t *)bias, (uint16_t *)out, G, qk);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_w4a4_int4(bool packed, int M, int N, int K, int rank, const void *act_codes,
+                                 const void *act_scales, const void *wgt_codes, const void *wgt_scales, float alpha,
+                                 const float *lora_act, const void *lora_up, const void *bias, void *out,
                                  hipStream_t stream)
 {
-    dim3 grid(((N + G4_BN - 1) / G4_BN) * ((M + G4_BM - 1) / G4_BM)), block(G4_THREADS);
-    if ((K >> 6) % G4_SC_GROUPS == 0)
-        hipLaunchKernelGGL((gemm_w4a4_int4_kernel<false, true>), grid, block, 0, stream, M, N, K, rank,
-                           (const uint8_t *)act_codes, (const uint16_t *)act_scales,
-                           (const uint8_t *)wgt_codes, (const uint16_t *)wgt_scales, alpha, lora_act,
-                           (const uint16_t *)lora_up, (const uint16_t *)bias, (uint16_t *)out,
-                           (int32_t *)nullptr, QkNormRope{});
-    else
-        hipLaunchKernelGGL((gemm_w4a4_int4_kernel<false, false>), grid, block, 0, stream, M, N, K, rank,
-                           (const uint8_t *)act_codes, (const uint16_t *)act_scales,
-                           (const uint8_t *)wgt_codes, (const uint16_t *)wgt_scales, alpha, lora_act,
-                           (const uint16_t *)lora_up, (const uint16_t *)bias, (uint16_t *)out,
-                           (int32_t *)nullptr, QkNormRope{});
-    return hipGetLastError();
+    const QkNormRope none{};
+    return packed ? launch_int4<false, false, true>(M, N, K, rank, act_codes, act_scales, wgt_codes, wgt_scales,
+                                                    alpha, lora_act, lora_up, bias, out, nullptr, none, stream)
+                  : launch_int4<false, false, false>(M, N, K, rank, act_codes, act_scales, wgt_codes, wgt_scales,
+                                                     alpha, lora_act, lora_up, bias, out, nullptr, none, stream);
 }
 
-hipError_t launch_gemm_w4a4_int4_qk(int M, int N, int K, int rank, const void *act_codes,
-                                    const void *act_scales, const void *wgt_codes,
-                                    const void *wgt_scales, float alpha, const float *lora_act,
-                                    const void *lora_up, const void *bias, const QkNormRope &qk,
-                                    void *out, hipStream_t stream)
+hipError_t launch_gemm_w4a4_int4_qk(bool packed, int M, int N, int K, int rank, const void *act_codes,
+                                    const void *act_scales, const void *wgt_codes, const void *wgt_scales,
+                                    float alpha, const float *lora_act, const void *lora_up, const void *bias,
+                                    const QkNormRope &qk, void *out, hipStream_t stream)
 {
-    dim3 grid(((N + G4_BN - 1) / G4_BN) * ((M + G4_BM - 1) / G4_BM)), block(G4_THREADS);
-    if ((K >> 6) % G4_SC_GROUPS == 0)
-        hipLaunchKernelGGL((gemm_w4a4_int4_kernel<false, true, true>), grid, block, 0, stream, M, N, K, rank,
-                           (const uint8_t *)act_codes, (const uint16_t *)act_scales,
-                           (const uint8_t *)wgt_codes, (const uint16_t *)wgt_scales, alpha, lora_act,
-                           (const uint16_t *)lora_up, (const uint16_t *)bias, (uint16_t *)out,
-                           (int32_t *)nullptr, qk);
-    else
-        hipLaunchKernelGGL((gemm_w4a4_int4_kernel<false, false, true>), grid, block, 0, stream, M, N, K, rank,
-                           (const uint8_t *)act_codes, (const uint16_t *)act_scales,
-                           (const uint8_t *)wgt_codes, (const uint16_t *)wgt_scales, alpha, lora_act,
-                           (const uint16_t *)lora_up, (const uint16_t *)bias, (uint16_t *)out,
-                           (int32_t *)nullptr, qk);
-    return hipGetLastError();
+    return packed ? launch_int4<false, true, true>(M, N, K, rank, act_codes, act_scales, wgt_codes, wgt_scales,
+                                                   alpha, lora_act, lora_up, bias, out, nullptr, qk, stream)
+                  : launch_int4<false, true, false>(M, N, K, rank, act_codes, act_scales, wgt_codes, wgt_scales,
+                                                    alpha, lora_act, lora_up, bias, out, nullptr, qk, stream);
 }
 
-hipError_t launch_group_sums_int4(int M, int N, int K, const void *act_codes,
-                                  const void *wgt_codes, int32_t *G, hipStream_t stream)
+// the same main loop as the GEMM launch of this K and weight layout (the
+// chunked loop when K/64 is a multiple of 8), writing G instead of accumulating
+hipError_t launch_group_sums_int4(bool packed, int M, int N, int K, const void *act_codes, const void *wgt_codes,
+                                  int32_t *G, hipStream_t stream)
 {
-    // the same main loop as the GEMM launch of this K (the chunked loop when
-    // K/64 is a multiple of 8), writing G instead of accumulating
-    dim3 grid(((N + G4_BN - 1) / G4_BN) * ((M + G4_BM - 1) / G4_BM)), block(G4_THREADS);
-    if ((K >> 6) % G4_SC_GROUPS == 0)
-        hipLaunchKernelGGL((gemm_w4a4_int4_kernel<true, true>), grid, block, 0, stream, M, N, K, 0,
-                           (const uint8_t *)act_codes, (const uint16_t *)nullptr,
-                           (const uint8_t *)wgt_codes, (const uint16_t *)nullptr, 1.0f,
-                           (const float *)nullptr, (const uint16_t *)nullptr,
-                           (const uint16_t *)nullptr, (uint16_t *)nullptr, G, QkNormRope{});
-    else
-        hipLaunchKernelGGL((gemm_w4a4_int4_kernel<true, false>), grid, block, 0, stream, M, N, K, 0,
-                           (const uint8_t *)act_codes, (const uint16_t *)nullptr,
-                           (const uint8_t *)wgt_codes, (const uint16_t *)nullptr, 1.0f,
-                           (const float *)nullptr, (const uint16_t *)nullptr,
-                           (const uint16_t *)nullptr, (uint16_t *)nullptr, G, QkNormRope{});
-    return hipGetLastError();
+    const QkNormRope none{};
+    return packed ? launch_int4<true, false, true>(M, N, K, 0, act_codes, nullptr, wgt_codes, nullptr, 1.0f,
+                                                   nullptr, nullptr, nullptr, nullptr, G, none, stream)
+                  : launch_int4<true, false, false>(M, N, K, 0, act_codes, nullptr, wgt_codes, nullptr, 1.0f,
+                                                    nullptr, nullptr, nullptr, nullptr, G, none, stream);
 }
 
 }  // namespace svdq

@@ -34,17 +34,24 @@ hipError_t launch_quantize_weight(int precision, int N, int K, int rank, const v
                                   const void *up, const void *down, void *codes, void *scales,
                                   hipStream_t stream);
 
-hipError_t launch_gemm_w4a4_int4(int M, int N, int K, int rank, const void *act_codes,
+// int4 GEMM; packed: wgt_codes is the blob of launch_pack_weight_int4
+hipError_t launch_gemm_w4a4_int4(bool packed, int M, int N, int K, int rank, const void *act_codes,
                                  const void *act_scales, const void *wgt_codes,
                                  const void *wgt_scales, float alpha, const float *lora_act,
                                  const void *lora_up, const void *bias, void *out,
                                  hipStream_t stream);
+// offline re-encoding of int4 weights for the packed GEMM: blob = codes
+// [N, K/2] in the packed layout, then bf16 [N][2][K/64] correction planes;
+// invalid (optional) counts the -8 codes, which the layout cannot hold
+size_t packed_weight_bytes(int N, int K);
+hipError_t launch_pack_weight_int4(int N, int K, const void *wgt_codes, const void *wgt_scales, void *blob,
+                                   int32_t *invalid, hipStream_t stream);
 hipError_t launch_gemm_w4a4_nvfp4_qk(int M, int N, int K, int rank, const void *act_codes,
                                      const void *act_scales, const void *wgt_codes,
                                      const void *wgt_scales, float alpha, const float *lora_act,
                                      const void *lora_up, const void *bias, const QkNormRope &qk,
                                      void *out, hipStream_t stream);
-hipError_t launch_gemm_w4a4_int4_qk(int M, int N, int K, int rank, const void *act_codes,
+hipError_t launch_gemm_w4a4_int4_qk(bool packed, int M, int N, int K, int rank, const void *act_codes,
                                     const void *act_scales, const void *wgt_codes,
                                     const void *wgt_scales, float alpha, const float *lora_act,
                                     const void *lora_up, const void *bias, const QkNormRope &qk,
@@ -56,7 +63,7 @@ hipError_t launch_gemm_w4a4_nvfp4(int M, int N, int K, int rank, const void *act
                                   const void *lora_up, const void *bias, void *out,
                                   hipStream_t stream);
 
-hipError_t launch_group_sums_int4(int M, int N, int K, const void *act_codes,
+hipError_t launch_group_sums_int4(bool packed, int M, int N, int K, const void *act_codes,
                                   const void *wgt_codes, int32_t *G, hipStream_t stream);
 
 hipError_t launch_awq_gemv(int M, int N, int K, const void *x, const void *codes,

@@ -236,8 +236,9 @@ svdq_status svdq_gemm_w4a4_qk_norm_rope(int32_t precision, int64_t M, int64_t N,
                                         const float *rope_cos, const float *rope_sin, void *out,
                                         void *stream)
 {
-    if (precision != SVDQ_INT4 && precision != SVDQ_NVFP4)
-        return fail(SVDQ_ERR_UNSUPPORTED, "precision must be SVDQ_INT4 or SVDQ_NVFP4 (got %d)", precision);
+    if (precision != SVDQ_INT4 && precision != SVDQ_NVFP4 && precision != SVDQ_INT4_PACKED)
+        return fail(SVDQ_ERR_UNSUPPORTED,
+                    "precision must be SVDQ_INT4, SVDQ_NVFP4 or SVDQ_INT4_PACKED (got %d)", precision);
     SVDQ_TRY(check_shape(M, N, K, rank));
     if (N % 384 != 0)
         return fail(SVDQ_ERR_INVALID_ARG, "N must be 3 * heads * 128 (got %lld)", (long long)N);
@@ -265,9 +266,10 @@ svdq_status svdq_gemm_w4a4_qk_norm_rope(int32_t precision, int64_t M, int64_t N,
     qk.sin = rope_sin;
     qk.eps = eps;
     qk.qk_cols = (int)(2 * (N / 3));
-    const hipError_t e = precision == SVDQ_INT4
-        ? svdq::launch_gemm_w4a4_int4_qk((int)M, (int)N, (int)K, rank, act_codes, act_scales, wgt_codes,
-                                         wgt_scales, alpha, lora_act, lora_up, bias, qk, out, (hipStream_t)stream)
+    const hipError_t e = precision != SVDQ_NVFP4
+        ? svdq::launch_gemm_w4a4_int4_qk(precision == SVDQ_INT4_PACKED, (int)M, (int)N, (int)K, rank, act_codes,
+                                         act_scales, wgt_codes, wgt_scales, alpha, lora_act, lora_up, bias, qk, out,
+                                         (hipStream_t)stream)
         : svdq::launch_gemm_w4a4_nvfp4_qk((int)M, (int)N, (int)K, rank, act_codes, act_scales, wgt_codes,
                                           wgt_scales, alpha, lora_act, lora_up, bias, qk, out, (hipStream_t)stream);
     return launched(e, "svdq_gemm_w4a4_qk_norm_rope");
@@ -278,8 +280,9 @@ svdq_status svdq_gemm_w4a4(int32_t precision, int64_t M, int64_t N, int64_t K, i
                            const void *wgt_scales, float alpha, const float *lora_act,
                            const void *lora_up, const void *bias, void *out, void *stream)
 {
-    if (precision != SVDQ_INT4 && precision != SVDQ_NVFP4)
-        return fail(SVDQ_ERR_UNSUPPORTED, "precision must be SVDQ_INT4 or SVDQ_NVFP4 (got %d)", precision);
+    if (precision != SVDQ_INT4 && precision != SVDQ_NVFP4 && precision != SVDQ_INT4_PACKED)
+        return fail(SVDQ_ERR_UNSUPPORTED,
+                    "precision must be SVDQ_INT4, SVDQ_NVFP4 or SVDQ_INT4_PACKED (got %d)", precision);
     SVDQ_TRY(check_shape(M, N, K, rank));
     SVDQ_TRY(check_ptr(act_codes, "act_codes", false));
     SVDQ_TRY(check_ptr(act_scales, "act_scales", false));
@@ -292,9 +295,10 @@ svdq_status svdq_gemm_w4a4(int32_t precision, int64_t M, int64_t N, int64_t K, i
     if (M == 0 || N == 0) return SVDQ_OK;
     SVDQ_TRY(check_grid(M, N, 128, 128));
     SVDQ_TRY(check_device());
-    hipError_t e = precision == SVDQ_INT4
-        ? svdq::launch_gemm_w4a4_int4((int)M, (int)N, (int)K, rank, act_codes, act_scales, wgt_codes,
-                                      wgt_scales, alpha, lora_act, lora_up, bias, out, (hipStream_t)stream)
+    hipError_t e = precision != SVDQ_NVFP4
+        ? svdq::launch_gemm_w4a4_int4(precision == SVDQ_INT4_PACKED, (int)M, (int)N, (int)K, rank, act_codes,
+                                      act_scales, wgt_codes, wgt_scales, alpha, lora_act, lora_up, bias, out,
+                                      (hipStream_t)stream)
         : svdq::launch_gemm_w4a4_nvfp4((int)M, (int)N, (int)K, rank, act_codes, act_scales, wgt_codes,
                                        wgt_scales, alpha, lora_act, lora_up, bias, out, (hipStream_t)stream);
     return launched(e, "svdq_gemm_w4a4");
@@ -324,19 +328,53 @@ svdq_status awq_gemv_w4a16(int64_t M, int64_t N, int64_t K, int32_t group_size, 
     return launched(e, "awq_gemv_w4a16");
 }
 
-svdq_status svdq_debug_group_sums(int64_t M, int64_t N, int64_t K, const void *act_codes,
-                                  const void *wgt_codes, int32_t *G, void *stream)
+static svdq_status group_sums_common(bool packed, const char *name, int64_t M, int64_t N, int64_t K,
+                                     const void *act_codes, const void *wgt_codes, int32_t *G, void *stream)
 {
     SVDQ_TRY(check_shape(M, N, K, 0));
     SVDQ_TRY(check_ptr(act_codes, "act_codes", false));
-    SVDQ_TRY(check_ptr(wgt_codes, "wgt_codes", false));
+    SVDQ_TRY(check_ptr(wgt_codes, packed ? "packed_weight" : "wgt_codes", false));
     SVDQ_TRY(check_ptr(G, "G", false));
     if (M == 0 || N == 0) return SVDQ_OK;
     SVDQ_TRY(check_grid(M, N, 128, 128));
     SVDQ_TRY(check_device());
-    return launched(svdq::launch_group_sums_int4((int)M, (int)N, (int)K, act_codes, wgt_codes, G,
+    return launched(svdq::launch_group_sums_int4(packed, (int)M, (int)N, (int)K, act_codes, wgt_codes, G,
                                                  (hipStream_t)stream),
-                    "svdq_debug_group_sums");
+                    name);
+}
+
+svdq_status svdq_debug_group_sums(int64_t M, int64_t N, int64_t K, const void *act_codes,
+                                  const void *wgt_codes, int32_t *G, void *stream)
+{
+    return group_sums_common(false, "svdq_debug_group_sums", M, N, K, act_codes, wgt_codes, G, stream);
+}
+
+svdq_status svdq_debug_group_sums_packed(int64_t M, int64_t N, int64_t K, const void *act_codes,
+                                         const void *packed_weight, int32_t *G, void *stream)
+{
+    return group_sums_common(true, "svdq_debug_group_sums_packed", M, N, K, act_codes, packed_weight, G, stream);
+}
+
+int64_t svdq_packed_weight_bytes(int64_t N, int64_t K)
+{
+    if (check_shape(1, N, K, 0) != SVDQ_OK) return -1;
+    return (int64_t)svdq::packed_weight_bytes((int)N, (int)K);
+}
+
+svdq_status svdq_pack_weight_int4(int64_t N, int64_t K, const void *wgt_codes, const void *wgt_scales,
+                                  void *packed_weight, int32_t *invalid_codes, void *stream)
+{
+    SVDQ_TRY(check_shape(1, N, K, 0));
+    SVDQ_TRY(check_ptr(wgt_codes, "wgt_codes", false));
+    SVDQ_TRY(check_ptr(wgt_scales, "wgt_scales", false));
+    SVDQ_TRY(check_ptr(packed_weight, "packed_weight", false));
+    if (invalid_codes && ((uintptr_t)invalid_codes & 3u))
+        return fail(SVDQ_ERR_INVALID_ARG, "invalid_codes must be 4-byte aligned");
+    if (N == 0) return SVDQ_OK;
+    SVDQ_TRY(check_device());
+    return launched(svdq::launch_pack_weight_int4((int)N, (int)K, wgt_codes, wgt_scales, packed_weight, invalid_codes,
+                                                  (hipStream_t)stream),
+                    "svdq_pack_weight_int4");
 }
 
 const char *svdq_status_string(svdq_status s)
@@ -352,6 +390,6 @@ const char *svdq_status_string(svdq_status s)
 
 const char *svdq_last_error(void) { return g_last_error; }
 
-int32_t svdq_abi_version(void) { return 6; }
+int32_t svdq_abi_version(void) { return 7; }
 
 }  // extern "C"

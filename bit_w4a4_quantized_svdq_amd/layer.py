@@ -27,25 +27,45 @@ def _dev(a, dtype, device):
     return t.to(device)
 
 
+def pack_weight_int4(wgt_codes, wgt_scales):
+    """Device int4 codes [N, K/2] + bf16 scales -> the packed weight blob of the
+    SVDQ_INT4_PACKED GEMM (raises if a code is -8)."""
+    N, Kh = wgt_codes.shape
+    blob = torch.empty((capi.svdq_packed_weight_bytes(N, 2 * Kh),), dtype=torch.uint8, device=wgt_codes.device)
+    bad = torch.empty((1,), dtype=torch.int32, device=wgt_codes.device)
+    capi.svdq_pack_weight_int4(wgt_codes, wgt_scales, blob, bad)
+    if int(bad.item()) != 0:
+        raise ValueError(f"{int(bad.item())} weight codes of -8 cannot be packed")
+    return blob
+
+
 class SVDQW4A4Linear:
     """y = alpha * Q(x/s) . Q(R)^T + (x/s . L1^T) . L2^T + bias  (bf16 out).
 
-    precision: "int4" (group 64, bf16 scales) or "nvfp4" (group 16, E4M3)."""
+    precision: "int4" (group 64, bf16 scales) or "nvfp4" (group 16, E4M3).
+    packed (int4): the weight is re-encoded once, at construction, into the
+    packed form of svdq_pack_weight_int4, and the GEMM takes the
+    SVDQ_INT4_PACKED path (same results within the output tolerance; codes of
+    -8, which the group quantizer never produces, are refused)."""
 
     def __init__(self, precision, wgt_codes, wgt_scales, lora_down, lora_up, smooth=None,
-                 bias=None, alpha=1.0, device="cuda"):
+                 bias=None, alpha=1.0, device="cuda", packed=True):
         self.prec = capi.SVDQ_INT4 if precision == "int4" else capi.SVDQ_NVFP4
         self.group = 64 if self.prec == capi.SVDQ_INT4 else 16
         self.wgt_codes = _dev(wgt_codes, torch.uint8, device)
         sdt = torch.bfloat16 if self.prec == capi.SVDQ_INT4 else torch.uint8
         self.wgt_scales = _dev(wgt_scales, sdt, device)
+        self.gemm_prec = self.prec
+        if packed and self.prec == capi.SVDQ_INT4:
+            self.wgt_codes = pack_weight_int4(self.wgt_codes, self.wgt_scales)
+            self.gemm_prec = capi.SVDQ_INT4_PACKED
         self.lora_down = _dev(lora_down, torch.bfloat16, device)
         self.lora_up = _dev(lora_up, torch.bfloat16, device)
         self.smooth = _dev(smooth, torch.bfloat16, device)
         self.bias = _dev(bias, torch.bfloat16, device)
         self.alpha = float(alpha)
-        self.N, Kh = self.wgt_codes.shape
-        self.K = 2 * Kh
+        self.N, G = self.wgt_scales.shape
+        self.K = G * self.group
         self.rank = 0 if self.lora_up is None else self.lora_up.shape[1]
         self.device = device
         self._bufs = {}
@@ -70,14 +90,14 @@ class SVDQW4A4Linear:
            b["lora_act"] if self.rank else None)
 
     def gemm(self, b):
-        capi.svdq_gemm_w4a4(self.prec, b["codes"], b["scales"], self.wgt_codes, self.wgt_scales,
+        capi.svdq_gemm_w4a4(self.gemm_prec, b["codes"], b["scales"], self.wgt_codes, self.wgt_scales,
                             self.alpha, b["lora_act"] if self.rank else None, self.lora_up,
                             self.bias, b["out"])
 
     def gemm_qk_norm_rope(self, b, q_norm_weight, k_norm_weight, eps, rope_cos, rope_sin):
         """The GEMM step of a grouped QKV layer (N = 3 * heads * 128) with
         per-head RMSNorm and rotary embedding of Q and K in its epilogue."""
-        capi.svdq_gemm_w4a4_qk_norm_rope(self.prec, b["codes"], b["scales"], self.wgt_codes,
+        capi.svdq_gemm_w4a4_qk_norm_rope(self.gemm_prec, b["codes"], b["scales"], self.wgt_codes,
                                          self.wgt_scales, self.alpha,
                                          b["lora_act"] if self.rank else None, self.lora_up, self.bias,
                                          q_norm_weight, k_norm_weight, eps, rope_cos, rope_sin, b["out"])

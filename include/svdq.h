@@ -54,8 +54,14 @@ typedef enum svdq_status {
     SVDQ_ERR_HIP = 3
 } svdq_status;
 
-/* precision of the W4A4 layer ("Supported quantization types" table) */
-enum { SVDQ_INT4 = 0 /* group 64, bf16 scales */, SVDQ_NVFP4 = 1 /* group 16, E4M3 scales */ };
+/* precision of the W4A4 layer ("Supported quantization types" table).
+ * SVDQ_INT4_PACKED is int4 with the weight in the packed form written by
+ * svdq_pack_weight_int4 (the GEMM's fast path); its activations are int4's. */
+enum {
+    SVDQ_INT4 = 0 /* group 64, bf16 scales */,
+    SVDQ_NVFP4 = 1 /* group 16, E4M3 scales */,
+    SVDQ_INT4_PACKED = 2 /* int4, weight from svdq_pack_weight_int4 (GEMM calls only) */
+};
 
 /*
  * svdq_quantize_act -- first step of the W4A4 layer: one pass over x.
@@ -106,8 +112,12 @@ svdq_status svdq_gelu_quantize_act(int32_t precision, int64_t M, int64_t K, int3
  *                      + sum_j lora_act[m,j] * lora_up[n,j] + bias[n] )
  * deq is code * group scale.  The sum is fp32 in unspecified order.
  *
+ *   precision  SVDQ_INT4, SVDQ_NVFP4 or SVDQ_INT4_PACKED (the activations
+ *              then come from svdq_quantize_act with SVDQ_INT4)
  *   act_codes, act_scales  as written by svdq_quantize_act ([M, ...])
- *   wgt_codes  u8 [N, K/2] (int4 or E2M1 codes of the 4-bit residual)
+ *   wgt_codes  u8 [N, K/2] (int4 or E2M1 codes of the 4-bit residual);
+ *              SVDQ_INT4_PACKED: the svdq_pack_weight_int4 blob of them
+ *              (svdq_packed_weight_bytes(N, K) bytes)
  *   wgt_scales int4 bf16 [N, K/64]; nvfp4 u8 (E4M3) [N, K/16]
  *   alpha      scale of the 4-bit term (per-tensor; 1.0f for int4)
  *   lora_act   fp32 [M, rank]; lora_up bf16 [N, rank]; ignored when rank == 0
@@ -241,6 +251,31 @@ svdq_status svdq_quantize_weight(int32_t precision, int64_t N, int64_t K, int32_
                                  void *wgt_codes, void *wgt_scales, void *stream);
 
 /*
+ * svdq_pack_weight_int4 -- offline re-encoding of an int4 weight for the
+ * int4 GEMM's fast path (precision SVDQ_INT4_PACKED).  The matrix cores of
+ * gfx950 take E4M3 bytes and return fp32; the packed codes turn into exact
+ * E4M3 values with two masks and a rotate per 8 codes, so the GEMM spends no
+ * integer-to-float conversion per output and group.  The blob holds
+ *   - the codes, still 4 bits each ([N, K/2] bytes), in sign-magnitude form
+ *     and a fixed bit permutation within each dword (documented in the
+ *     source, pack_weight.hip);
+ *   - bf16 [N][2][K/64]: per row and group, hi + lo = -8 * scale * (sum of
+ *     the group's codes), the weight-only factor of the correction for the
+ *     activations' +8 offset in that GEMM.
+ *   wgt_codes     u8 [N, K/2] two's complement int4 codes (svdq_gemm_w4a4's)
+ *   wgt_scales    bf16 [N, K/64]
+ *   packed_weight out: u8 [svdq_packed_weight_bytes(N, K)], device
+ *   invalid_codes out (device int32, may be NULL): the number of codes equal
+ *                 to -8, which the packed form cannot hold (written as 0);
+ *                 the int4 group quantizer never produces them.  Set by
+ *                 the call's own kernels (no clearing needed).
+ * The weight's scales stay a separate argument of the GEMM.
+ */
+int64_t svdq_packed_weight_bytes(int64_t N, int64_t K);   /* N*K/2 + 4*N*(K/64); -1 if invalid */
+svdq_status svdq_pack_weight_int4(int64_t N, int64_t K, const void *wgt_codes, const void *wgt_scales,
+                                  void *packed_weight, int32_t *invalid_codes, void *stream);
+
+/*
  * svdq_debug_group_sums -- test hook on the int4 GEMM's own device code
  * path (operand unpacking and integer matrix-core products): writes the
  * exact integer group sums
@@ -249,6 +284,15 @@ svdq_status svdq_quantize_weight(int32_t precision, int64_t N, int64_t K, int32_
  */
 svdq_status svdq_debug_group_sums(int64_t M, int64_t N, int64_t K, const void *act_codes,
                                   const void *wgt_codes, int32_t *G, void *stream);
+
+/*
+ * svdq_debug_group_sums_packed -- the same integer group sums G [M, N, K/64]
+ * from the main loop of the SVDQ_INT4_PACKED GEMM (fp8 matrix-core products
+ * of the offset activation codes and the packed weight, minus the offset's
+ * share): packed_weight is the blob of svdq_pack_weight_int4.
+ */
+svdq_status svdq_debug_group_sums_packed(int64_t M, int64_t N, int64_t K, const void *act_codes,
+                                         const void *packed_weight, int32_t *G, void *stream);
 
 /*
  * svdq_debug_gelu_bf16 -- test hook on the GELU of svdq_gelu_quantize_act
@@ -264,10 +308,12 @@ const char *svdq_status_string(svdq_status s);
 /* Text of the last argument-check failure on the calling thread ("" if none). */
 const char *svdq_last_error(void);
 
-/* ABI version of this header: 6 (1 plus svdq_gelu_quantize_act, svdq_debug_gelu_bf16,
+/* ABI version of this header: 7 (1 plus svdq_gelu_quantize_act, svdq_debug_gelu_bf16,
  * svdq_gemm_w4a4_qk_norm_rope, svdq_smooth_factors, svdq_quantize_weight,
- * svdq_lowrank_workspace_bytes, svdq_lowrank_factors and
- * svdq_lowrank_factors_noalloc). */
+ * svdq_lowrank_workspace_bytes, svdq_lowrank_factors,
+ * svdq_lowrank_factors_noalloc, then SVDQ_INT4_PACKED with
+ * svdq_packed_weight_bytes, svdq_pack_weight_int4 and
+ * svdq_debug_group_sums_packed). */
 int32_t svdq_abi_version(void);
 
 #ifdef __cplusplus

@@ -137,8 +137,23 @@ def gpu_quantize(prec, x, smooth, lora_down, K, gelu=False):
             None if lact is None else to_host(lact, "f32"))
 
 
+def gpu_pack_weight(wgt_codes_dev, wgt_scales_dev):
+    """The packed int4 weight blob (svdq_pack_weight_int4) of device codes and
+    scales; asserts that no -8 code was met."""
+    from bit_w4a4_quantized_svdq_amd import capi
+    N, Kh = wgt_codes_dev.shape
+    blob = poison(empty((capi.svdq_packed_weight_bytes(N, 2 * Kh),), "u8"))
+    bad = poison(empty((1,), "i32"))
+    capi.svdq_pack_weight_int4(wgt_codes_dev, wgt_scales_dev, blob, bad)
+    torch.cuda.synchronize()
+    assert int(to_host(bad, "i32")[0]) == 0, "weight codes of -8 cannot be packed"
+    return blob
+
+
 def gpu_gemm(prec, act_codes, act_scales, wgt_codes, wgt_scales, lora_act, lora_up, bias, alpha=1.0,
-             zero_weight_ok=False):
+             zero_weight_ok=False, packed=False):
+    """The W4A4 GEMM on the GPU; packed (int4 only): through the packed weight
+    blob and the SVDQ_INT4_PACKED path."""
     from bit_w4a4_quantized_svdq_amd import capi
     M, N = act_codes.shape[0], wgt_codes.shape[0]
     # a layer whose weight scales are all zero tests only the bias and low-rank
@@ -146,9 +161,12 @@ def gpu_gemm(prec, act_codes, act_scales, wgt_codes, wgt_scales, lora_act, lora_
     assert zero_weight_ok or N == 0 or np.any(wgt_scales != 0), "degenerate layer: all weight scales zero"
     out = poison(empty((M, N), "bf16"))
     skind = "bf16" if prec == 0 else "u8"
-    capi.svdq_gemm_w4a4(prec, to_dev(act_codes, "u8"), to_dev(act_scales, skind), to_dev(wgt_codes, "u8"),
-                        to_dev(wgt_scales, skind), alpha, to_dev(lora_act, "f32"), to_dev(lora_up, "bf16"),
-                        to_dev(bias, "bf16"), out)
+    wc, ws = to_dev(wgt_codes, "u8"), to_dev(wgt_scales, skind)
+    if packed:
+        assert prec == 0
+        wc, prec = gpu_pack_weight(wc, ws), capi.SVDQ_INT4_PACKED
+    capi.svdq_gemm_w4a4(prec, to_dev(act_codes, "u8"), to_dev(act_scales, skind), wc, ws, alpha,
+                        to_dev(lora_act, "f32"), to_dev(lora_up, "bf16"), to_dev(bias, "bf16"), out)
     torch.cuda.synchronize()
     return to_host(out, "bf16")
 

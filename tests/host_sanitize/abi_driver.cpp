@@ -103,11 +103,34 @@ int main() {
                                  nullptr),
                   INV, "gemm out misaligned");
 
+    expect_launch(svdq_gemm_w4a4(SVDQ_INT4_PACKED, 4096, 12288, 3072, 32, P, P, P, P, 1.0f, F, P, P, P, nullptr),
+                  "gemm_int4_packed", 4096, 12288, 3072);
+    expect_reject(svdq_gemm_w4a4(3, 4, 64, 64, 0, P, P, P, P, 1.0f, nullptr, nullptr, nullptr, P, nullptr), UNS,
+                  "gemm precision 3");
+
+    // ---- packed int4 weights
+    EXPECT(svdq_packed_weight_bytes(12288, 3072) == 12288ll * 1536 + 12288ll * 4 * 48, "packed bytes");
+    EXPECT(svdq_packed_weight_bytes(8, 100) == -1, "packed bytes, K % 64");
+    expect_launch(svdq_pack_weight_int4(12288, 3072, P, P, P, I, nullptr), "pack_weight_int4", 12288, 3072, 1);
+    expect_launch(svdq_pack_weight_int4(5, 64, P, P, P, nullptr, nullptr), "pack_weight_int4", 5, 64, 0);
+    expect_noop(svdq_pack_weight_int4(0, 64, P, P, P, nullptr, nullptr), "pack N=0");
+    expect_reject(svdq_pack_weight_int4(5, 64, nullptr, P, P, nullptr, nullptr), INV, "pack codes NULL");
+    expect_reject(svdq_pack_weight_int4(5, 64, P, P, MIS, nullptr, nullptr), INV, "pack blob misaligned");
+    expect_reject(svdq_pack_weight_int4(5, 64, P, P, P, (int32_t *)((char *)P + 2), nullptr), INV,
+                  "pack counter misaligned");
+    expect_launch(svdq_debug_group_sums_packed(130, 384, 3072, P, P, I, nullptr), "group_sums_packed", 130, 384,
+                  3072);
+    expect_reject(svdq_debug_group_sums_packed(130, 384, 3072, P, nullptr, I, nullptr), INV,
+                  "group sums packed weight NULL");
+
     // ---- grouped QKV GEMM with QK norm + rotary embedding
     const float *Fc = F;
     expect_launch(svdq_gemm_w4a4_qk_norm_rope(SVDQ_INT4, 4096, 9216, 3072, 32, P, P, P, P, 1.0f, Fc, P, P, P, P,
                                               1e-6f, Fc, Fc, P, nullptr),
                   "gemm_int4_qk", 4096, 9216, 6144);
+    expect_launch(svdq_gemm_w4a4_qk_norm_rope(SVDQ_INT4_PACKED, 4096, 9216, 3072, 32, P, P, P, P, 1.0f, Fc, P, P, P,
+                                              P, 1e-6f, Fc, Fc, P, nullptr),
+                  "gemm_int4_packed_qk", 4096, 9216, 6144);
     expect_launch(svdq_gemm_w4a4_qk_norm_rope(SVDQ_NVFP4, 3, 384, 256, 0, P, P, P, P, 1.0f, nullptr, nullptr,
                                               nullptr, P, P, 0.0f, Fc, Fc, P, nullptr),
                   "gemm_nvfp4_qk", 3, 384, 256);

@@ -51,28 +51,34 @@ hipError_t launch_quantize_weight(int precision, int N, int K, int rank, const v
                                   const void *, const void *, void *, void *, hipStream_t) {
     return rec("quantize_weight", N, K, rank + 1000 * precision);
 }
-hipError_t launch_gemm_w4a4_int4(int M, int N, int K, int, const void *, const void *, const void *,
+hipError_t launch_gemm_w4a4_int4(bool packed, int M, int N, int K, int, const void *, const void *, const void *,
                                  const void *, float, const float *, const void *, const void *, void *,
                                  hipStream_t) {
-    return rec("gemm_int4", M, N, K);
+    return rec(packed ? "gemm_int4_packed" : "gemm_int4", M, N, K);
+}
+size_t packed_weight_bytes(int N, int K) { return (size_t)N * (K / 2) + (size_t)N * 4 * (K / 64); }
+hipError_t launch_pack_weight_int4(int N, int K, const void *, const void *, void *, int32_t *invalid,
+                                   hipStream_t) {
+    return rec("pack_weight_int4", N, K, invalid != nullptr);
 }
 hipError_t launch_gemm_w4a4_nvfp4(int M, int N, int K, int, const void *, const void *, const void *,
                                   const void *, float, const float *, const void *, const void *, void *,
                                   hipStream_t) {
     return rec("gemm_nvfp4", M, N, K);
 }
-hipError_t launch_gemm_w4a4_int4_qk(int M, int N, int K, int, const void *, const void *, const void *,
-                                    const void *, float, const float *, const void *, const void *,
+hipError_t launch_gemm_w4a4_int4_qk(bool packed, int M, int N, int K, int, const void *, const void *,
+                                    const void *, const void *, float, const float *, const void *, const void *,
                                     const QkNormRope &qk, void *, hipStream_t) {
-    return rec("gemm_int4_qk", M, N, qk.qk_cols);
+    return rec(packed ? "gemm_int4_packed_qk" : "gemm_int4_qk", M, N, qk.qk_cols);
 }
 hipError_t launch_gemm_w4a4_nvfp4_qk(int M, int N, int K, int, const void *, const void *, const void *,
                                      const void *, float, const float *, const void *, const void *,
                                      const QkNormRope &qk, void *, hipStream_t) {
     return rec("gemm_nvfp4_qk", M, N, qk.qk_cols);
 }
-hipError_t launch_group_sums_int4(int M, int N, int K, const void *, const void *, int32_t *, hipStream_t) {
-    return rec("group_sums", M, N, K);
+hipError_t launch_group_sums_int4(bool packed, int M, int N, int K, const void *, const void *, int32_t *,
+                                  hipStream_t) {
+    return rec(packed ? "group_sums_packed" : "group_sums", M, N, K);
 }
 hipError_t launch_awq_gemv(int M, int N, int K, const void *, const void *, const void *, const void *,
                            const void *, void *, hipStream_t) {

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(capi.LIB_PATH)
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert capi.svdq_abi_version() == 6
+    assert capi.svdq_abi_version() == 7
     for s in range(4):
         assert capi.svdq_status_string(s).startswith(("SVDQ_OK", "SVDQ_ERR"))
     assert "unknown" in capi.svdq_status_string(99)
@@ -139,7 +139,7 @@ def test_newer_entry_points_reject_bad_arguments_on_the_host():
     # QKV epilogue: int4 only, N = 3 * heads * 128, finite eps >= 0
     qk = lambda prec=0, N=384, eps=1e-6, cos=A: L.svdq_gemm_w4a4_qk_norm_rope(
         prec, 4, N, 64, 16, A, A, A, A, 1.0, A, A, A, A, A, eps, cos, A, A, None)
-    assert qk(prec=2) == UNS
+    assert qk(prec=3) == UNS
     assert qk(N=256) == INV
     assert qk(eps=-1.0) == INV
     assert qk(eps=float("inf")) == INV
@@ -184,3 +184,29 @@ def test_lowrank_noalloc_host_checks():
     # every layer of a 3072-wide DiT block at rank 32 fits
     for N, K in ((9216, 3072), (12288, 3072), (3072, 12288), (3072, 3072)):
         assert 0 < capi.svdq_lowrank_workspace_bytes(N, K, 32) <= 32 << 20
+
+
+def test_packed_weight_entry_points_host_checks():
+    """svdq_packed_weight_bytes and the host-side checks of the packed-weight
+    entry points (no GPU needed: every rejection happens before a launch)."""
+    L = capi.lib()
+    # blob = codes [N, K/2] + bf16 [N][2][K/64]
+    assert capi.svdq_packed_weight_bytes(12288, 3072) == 12288 * 1536 + 12288 * 2 * 48 * 2
+    assert capi.svdq_packed_weight_bytes(1, 64) == 32 + 4
+    assert capi.svdq_packed_weight_bytes(8, 100) == -1
+    assert capi.svdq_packed_weight_bytes(-1, 64) == -1
+    pk = lambda N=64, K=128, c=A, s=A, out=A, bad=A: L.svdq_pack_weight_int4(N, K, c, s, out, bad, None)
+    assert pk(K=96) == INV
+    assert pk(c=0) == INV
+    assert pk(s=MIS) == INV
+    assert pk(out=0) == INV
+    assert pk(bad=A + 2) == INV                      # the counter must be 4-byte aligned
+    assert pk(N=0) == capi.SVDQ_OK
+    gs = lambda M=4, N=64, K=128, ac=A, w=A, G=A: L.svdq_debug_group_sums_packed(M, N, K, ac, w, G, None)
+    assert gs(w=0) == INV
+    assert gs(K=100) == INV
+    assert gs(M=0) == capi.SVDQ_OK
+    # the GEMM accepts precision 2 (checks as for int4) and rejects 3
+    assert gm(prec=3) == UNS
+    assert gm(prec=capi.SVDQ_INT4_PACKED, wc=0) == INV
+    assert gm(prec=capi.SVDQ_INT4_PACKED, M=0) == capi.SVDQ_OK

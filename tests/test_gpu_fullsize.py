@@ -62,6 +62,13 @@ def _layer_parity(cfg, case, prec):
                            case["bias"], rows=rows)
     stats = assert_bf16_close(y[rows], ref, cfg.name)
     assert np.isfinite(synth.bf16_bits_to_f32(y)).all()
+    if prec == oracle.INT4:
+        # the production path: the packed weight (fp8 matrix-core formulation)
+        announce("fullsize gemm_w4a4 packed", cfg.name)
+        yp = gpu_gemm(prec, oc, os_, case["wgt_codes"], case["wgt_scales"], ot, case["lora_up"], case["bias"],
+                      packed=True)
+        stats = assert_bf16_close(yp[rows], ref, cfg.name + " packed")
+        assert np.isfinite(synth.bf16_bits_to_f32(yp)).all()
     return stats
 
 

@@ -144,6 +144,83 @@ def test_gemm_shapes(prec, M, N, K, rank, with_bias, alpha):
     y = gpu_gemm(prec, ac, asc, w["wgt_codes"], w["wgt_scales"], t, w["lora_up"], bias, alpha)
     ref = oracle.gemm_w4a4(prec, ac, asc, w["wgt_codes"], w["wgt_scales"], t, w["lora_up"], bias, alpha=alpha)
     assert_bf16_close(y, ref, f"gemm p{prec} {M}x{N}x{K} r{rank}")
+    if prec == 0:
+        announce("gemm_w4a4 packed", "M,N,K,r", M, N, K, rank, "alpha", alpha)
+        yp = gpu_gemm(prec, ac, asc, w["wgt_codes"], w["wgt_scales"], t, w["lora_up"], bias, alpha, packed=True)
+        assert_bf16_close(yp, ref, f"gemm packed {M}x{N}x{K} r{rank}")
+
+
+# ------------------------------------------------------- packed int4 weights
+
+def expected_packed_blob(codes, scales, N, K):
+    """The blob of svdq_pack_weight_int4 computed on the host from the plain
+    codes by the documented layout (codes in sign-magnitude form: per dword
+    (h, i) of a group and byte e, k = 64g + 32h + 8i + 2e, bits 0-2 |q[k]|,
+    bit 7 its sign, bits 4-6 |q[k+1]|, its sign in bit 3 of byte (e+1) mod 4;
+    then bf16 [N][2][K/64] with hi + lo = -8 * scale * group code sum).
+    Returns (packed code bytes [N, K/2], corr hi [N, K/64], corr lo, -8 count)."""
+    NG = K // 64
+    q = oracle.unpack_int4(codes, N, K).astype(np.int64).reshape(N, NG, 2, 4, 4, 2)
+    qe, qo = q[..., 0], q[..., 1]
+    mag_e, mag_o = np.abs(qe) & 7, np.abs(qo) & 7
+    sgn_e, sgn_o = (qe < 0).astype(np.int64), (qo < 0).astype(np.int64)
+    byte = mag_e | sgn_e << 7 | mag_o << 4 | np.roll(sgn_o, 1, axis=-1) << 3
+    packed = byte.reshape(N, K // 2).astype(np.uint8)
+    sums = q.reshape(N, NG, 64).sum(axis=2)
+    c = -8.0 * sums * synth.bf16_bits_to_f32(scales).astype(np.float64)
+    hi = oracle.f64_to_bf16(c)
+    lo = oracle.f64_to_bf16(c - synth.bf16_bits_to_f32(hi).astype(np.float64))
+    return packed, hi, lo, int((q == -8).sum())
+
+
+@pytest.mark.parametrize("N,K,with_minus8", [(64, 64, False), (130, 192, False), (257, 4160, False),
+                                             (1000, 3072, False), (40, 512, True)])
+def test_pack_weight_layout_exact(N, K, with_minus8):
+    from tests.gpu_helpers import gpu_pack_weight
+    rng = np.random.default_rng(6100 + N + K)
+    q = rng.integers(-7, 8, (N, K))
+    if with_minus8:
+        q[3, 5] = q[7, 64] = q[39, K - 1] = -8
+    codes = synth.pack_nibbles(q)
+    scales = synth.to_bf16_bits(rng.uniform(0.001, 0.02, (N, K // 64)))
+    announce("pack_weight_int4", N, K, "minus8", with_minus8)
+    wc, ws = to_dev(codes, "u8"), to_dev(scales, "bf16")
+    blob = poison(empty((capi.svdq_packed_weight_bytes(N, K),), "u8"))
+    bad = poison(empty((1,), "i32"))
+    capi.svdq_pack_weight_int4(wc, ws, blob, bad)
+    torch.cuda.synchronize()
+    got = to_host(blob, "u8")
+    packed, hi, lo, n8 = expected_packed_blob(codes, scales, N, K)
+    assert int(to_host(bad, "i32")[0]) == n8
+    nb = N * K // 2
+    assert np.array_equal(got[:nb].reshape(N, K // 2), packed), "packed codes differ"
+    corr = got[nb:].view(np.uint16).reshape(N, 2, K // 64)
+    assert np.array_equal(corr[:, 0], hi) and np.array_equal(corr[:, 1], lo), "correction planes differ"
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (64, 64, 64), (33, 130, 4160), (1, 1, 128),
+    (200, 320, 512), (130, 384, 3072), (130, 384, 12288), (257, 129, 1024),
+])
+def test_debug_group_sums_packed_exact(M, N, K):
+    """Exact int32 group sums from the main loop of the packed (fp8) GEMM:
+    activation codes anywhere in [-8, 7], weight codes in [-7, 7]."""
+    from tests.gpu_helpers import gpu_pack_weight
+    rng = np.random.default_rng(3500 + M + N + K)
+    qa = rng.integers(-8, 8, (M, K))
+    qw = rng.integers(-7, 8, (N, K))
+    qa[0, :64] = -8
+    qw[0, :64] = -7                                           # extreme group: 64 * 56
+    ac, wc = synth.pack_nibbles(qa), synth.pack_nibbles(qw)
+    ws = synth.to_bf16_bits(np.full((N, K // 64), 0.01))
+    announce("debug_group_sums_packed", M, N, K)
+    blob = gpu_pack_weight(to_dev(wc, "u8"), to_dev(ws, "bf16"))
+    G = poison(empty((M, N, K // 64), "i32"))
+    capi.svdq_debug_group_sums_packed(to_dev(ac, "u8"), blob, N, G)
+    torch.cuda.synchronize()
+    got = to_host(G, "i32")
+    ref = oracle.group_sums_int4(ac, wc, K)
+    assert np.array_equal(got, ref), f"group sums differ at {np.argwhere(got != ref)[:5].tolist()}"
 
 
 @pytest.mark.parametrize("M,N,K", [
@@ -182,6 +259,8 @@ def test_zero_residual_layer_on_gpu():
     announce("zero residual layer")
     gc, gs, gt = gpu_quantize(0, x, None, down, K)
     y = gpu_gemm(0, gc, gs, zc, zs, gt, up, bias, zero_weight_ok=True)
+    yp = gpu_gemm(0, gc, gs, zc, zs, gt, up, bias, zero_weight_ok=True, packed=True)
+    assert np.array_equal(y, yp)
     ref_t = (synth.bf16_bits_to_f32(x).astype(np.float64) @ synth.bf16_bits_to_f32(down).astype(np.float64).T)
     ref = oracle.f64_to_bf16(ref_t @ synth.bf16_bits_to_f32(up).astype(np.float64).T +
                              synth.bf16_bits_to_f32(bias).astype(np.float64)[None, :])

@@ -12,7 +12,8 @@ import torch
 
 import oracle
 from bit_w4a4_quantized_svdq_amd import capi, synth
-from tests.gpu_helpers import (announce, assert_bf16_close, empty, gpu_gemm, poison, to_dev, to_host)
+from tests.gpu_helpers import (announce, assert_bf16_close, empty, gpu_gemm, gpu_pack_weight, poison, to_dev,
+                               to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -24,12 +25,14 @@ def _norm_rope_inputs(rng, M):
     return qw, kw, np.cos(th).astype(np.float32), np.sin(th).astype(np.float32)
 
 
-def _gpu_qk(ac, asc, w, t, bias, qw, kw, eps, cs, sn, alpha=1.0, prec=0):
+def _gpu_qk(ac, asc, w, t, bias, qw, kw, eps, cs, sn, alpha=1.0, prec=0, packed=False):
     M, N = ac.shape[0], w["wgt_codes"].shape[0]
     out = poison(empty((M, N), "bf16"))
     sk = "bf16" if prec == 0 else "u8"
-    capi.svdq_gemm_w4a4_qk_norm_rope(prec, to_dev(ac, "u8"), to_dev(asc, sk), to_dev(w["wgt_codes"], "u8"),
-                                     to_dev(w["wgt_scales"], sk), alpha, to_dev(t, "f32"),
+    wc, ws = to_dev(w["wgt_codes"], "u8"), to_dev(w["wgt_scales"], sk)
+    if packed:
+        wc, prec = gpu_pack_weight(wc, ws), capi.SVDQ_INT4_PACKED
+    capi.svdq_gemm_w4a4_qk_norm_rope(prec, to_dev(ac, "u8"), to_dev(asc, sk), wc, ws, alpha, to_dev(t, "f32"),
                                      to_dev(w["lora_up"], "bf16"), to_dev(bias, "bf16"), to_dev(qw, "bf16"),
                                      to_dev(kw, "bf16"), eps, to_dev(cs, "f32"), to_dev(sn, "f32"), out)
     torch.cuda.synchronize()
@@ -70,6 +73,16 @@ def test_qk_norm_rope_shapes(prec, M, H, K, rank, with_bias, alpha):
     ref = oracle.gemm_w4a4_qk_norm_rope(prec, ac, asc, w["wgt_codes"], w["wgt_scales"], t, w["lora_up"], bias,
                                         qw, kw, eps, cs, sn, alpha=alpha)
     assert_bf16_close(y, ref, f"qkv p{prec} {M}x{H}x{K} r{rank}")
+    if prec == 0:
+        announce("gemm qk_norm_rope packed", "M,H,K,r", M, H, K, rank)
+        yp = _gpu_qk(ac, asc, w, t, bias, qw, kw, eps, cs, sn, alpha, prec, packed=True)
+        plain_p = gpu_gemm(prec, ac, asc, w["wgt_codes"], w["wgt_scales"], t, w["lora_up"], bias, alpha,
+                           packed=True)
+        assert np.array_equal(yp[:, 2 * HD:], plain_p[:, 2 * HD:]), "packed: V columns differ from its plain GEMM"
+        ep_p = oracle.qk_norm_rope(plain_p, qw, kw, eps, cs, sn)
+        ulp = np.abs(yp.view(np.int16).astype(np.int32) - ep_p.view(np.int16).astype(np.int32))
+        assert np.mean(ulp <= 1) >= 0.999, f"packed epilogue: {np.mean(ulp <= 1):.5f} within 1 ulp"
+        assert_bf16_close(yp, ref, f"qkv packed {M}x{H}x{K} r{rank}")
 
 
 def test_qk_norm_rope_zero_and_tiny_heads():
@@ -100,3 +113,7 @@ def test_qk_norm_rope_fullsize_qkv():
                                         qw, kw, 1e-6, cs, sn, rows=rows)
     assert_bf16_close(y[rows], ref, "fullsize qkv")
     assert np.isfinite(synth.bf16_bits_to_f32(y)).all()
+    announce("fullsize qkv qk_norm_rope packed")
+    yp = _gpu_qk(ac, asc, w, t, None, qw, kw, 1e-6, cs, sn, packed=True)
+    assert_bf16_close(yp[rows], ref, "fullsize qkv packed")
+    assert np.isfinite(synth.bf16_bits_to_f32(yp)).all()

@@ -69,6 +69,10 @@ def test_random_layer_shapes(i, prec, M, N, K, rank, with_bias, gelu):
     ref = oracle.gemm_w4a4(prec, oc, os_, w["wgt_codes"], w["wgt_scales"], ot if rank else None,
                            w["lora_up"], bias)
     assert_bf16_close(y, ref, f"case {i} out")
+    if prec == 0:
+        yp = gpu_gemm(prec, gc, gs, w["wgt_codes"], w["wgt_scales"], gt if rank else None, w["lora_up"], bias,
+                      packed=True)
+        assert_bf16_close(yp, ref, f"case {i} packed out")
 
 
 @pytest.mark.parametrize("i,M,N,K,with_bias", _awq_cases())
