@@ -1,0 +1,220 @@
+// gemv_w4a16_lines.hip -- the AWQ-style int4 weight-only layer ("Nunchaku
+// Lite" docs, "Supported quantization types": awq_w4a16 int4 group 64, the
+// memory-bound modulation projections) for one or two rows of x:
+//   y[m,n] = sum_k x[m,k] * (q[n,k] - z[n,g]) * s[n,g] + bias[n].
+//
+// At one or two rows the layer is a pure HBM stream of the packed weights,
+// and the matrix-core GEMV (gemv_w4a16_awq.hip) spends most of its time on
+// the shape of its loads: a lane there owns one weight row, so each load
+// instruction touches 32 rows x 32 bytes.  Here a wave owns 8 weight rows
+// and lane l reads 16-byte chunk l%8 + 8j of row l/8: every load instruction
+// covers 8 whole 128-byte lines, and all of a lane's chunks (K/256 loads)
+// are issued before anything waits, so the whole weight matrix is requested
+// at once.  The dot products run on the vector ALU (v_dot2_f32_bf16, two
+// products per instruction), which at one or two rows of x costs less than
+// the stream.
+//
+// Order of work in a block (3 waves, 24 weight rows):
+//   1. each thread issues its loads of x and of the block's scales and zero
+//      points, then all of its weight chunks;
+//   2. it waits for the first two only (loads complete in order), stores x
+//      into LDS in the pair order of the unpacked codes together with the
+//      sums of x over every 32-code chunk, and the scales and zero points;
+//   3. after one barrier, each weight chunk is used as soon as it lands.
+// Arithmetic (as in the matrix-core GEMV): a code q in 0..15 becomes the bf16
+// value 128 + q by placing it under the byte 0x43 (v_perm_b32), so
+// sum (q - z) x = sum (128 + q) x - (128 + z) sum x per chunk, and the group
+// scale multiplies the chunk's sum in fp32.  Each lane adds its chunks in
+// order; the 8 lanes of a row are summed at the end (xor shuffles 1, 2, 4).
+#include "device_common.h"
+#include "launch.h"
+
+namespace svdq {
+
+constexpr int AL_WAVES = 3, AL_THREADS = AL_WAVES * 64;
+constexpr int AL_ROWS = AL_WAVES * 8;               // weight rows per block
+constexpr int AL_MAX_K = 4096;                      // K / 256 <= 16 chunk loads per lane
+
+bool awq_gemv_lines_applies(int M, int N, int K) {
+    return M >= 1 && M <= 2 && N >= 1 && K % 512 == 0 && K <= AL_MAX_K;
+}
+
+// LDS: x [MR][K/8][16 B] (pair order), sum of x per chunk [MR][K/32] fp32,
+// scales and zero points [AL_ROWS][K/64] as (s | z << 16)
+__host__ __device__ constexpr size_t al_lds_bytes(int MR, int K) {
+    return (size_t)MR * K * 2 + (size_t)MR * (K / 32) * 4 + (size_t)AL_ROWS * (K / 64) * 4;
+}
+
+template <int MR, int NL>
+__global__ __launch_bounds__(AL_THREADS)
+void awq_gemv_lines_kernel(int N, int K, const uint16_t *__restrict__ x, const uint8_t *__restrict__ codes,
+                           const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
+                           const uint16_t *__restrict__ bias, uint16_t *__restrict__ out)
+{
+    extern __shared__ __align__(16) uint8_t al_smem[];
+    const int NG = K >> 6, NC = K >> 5;              // groups, 32-code chunks per row
+    uint8_t *s_x = al_smem;                          // [MR][K/8] x 16 B
+    float *s_sum = (float *)(al_smem + (size_t)MR * K * 2);   // [MR][NC]
+    uint32_t *s_sz = (uint32_t *)(s_sum + MR * NC);           // [AL_ROWS][NG]
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n0 = blockIdx.x * AL_ROWS;
+
+    // ---- 1. loads: x pieces (8 bf16 each), scale / zero pieces, weight chunks
+    const int xpieces = MR * (K >> 3);               // 16-byte pieces of x
+    constexpr int XP = (MR * AL_MAX_K / 8 + AL_THREADS - 1) / AL_THREADS;   // pieces per thread, at most
+    v4u xr[XP];
+#pragma unroll
+    for (int i = 0; i < XP; ++i) {
+        const int p = tid + i * AL_THREADS;
+        if (p < xpieces) xr[i] = *(const v4u *)(x + (size_t)p * 8);
+    }
+    const int spr = NG >> 3;                          // 16-byte pieces per row of scales (NG % 8 == 0)
+    const int spieces = AL_ROWS * spr;
+    constexpr int SP = (AL_ROWS * (AL_MAX_K / 512) + AL_THREADS - 1) / AL_THREADS;
+    v4u sr[SP], zr[SP];
+#pragma unroll
+    for (int i = 0; i < SP; ++i) {
+        const int p = tid + i * AL_THREADS;
+        if (p < spieces) {
+            const int row = min(n0 + p / spr, N - 1);   // rows past N: a valid row, never stored
+            const size_t off = (size_t)row * NG + (size_t)(p % spr) * 8;
+            sr[i] = *(const v4u *)(scales + off);
+            zr[i] = *(const v4u *)(zeros + off);
+        }
+    }
+    const int row = min(n0 + wave * 8 + (lane >> 3), N - 1);
+    const int c0 = lane & 7;
+    const uint8_t *wrow = codes + (size_t)row * (size_t)(K >> 1) + 16 * c0;
+    v4u wr[NL];
+#pragma unroll
+    for (int j = 0; j < NL; ++j) wr[j] = *(const v4u *)(wrow + 128 * j);
+
+    // ---- 2. wait for x and the scales (issued first), stage them in LDS
+    __builtin_amdgcn_s_waitcnt((NL & 15) | ((NL >> 4) << 14) | 0x0F70);   // vmcnt(NL)
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < XP; ++i) {
+        const int p = tid + i * AL_THREADS;
+        const bool ok = p < xpieces;
+        const v4u w = ok ? xr[i] : v4u{0u, 0u, 0u, 0u};
+        // (x0,x2) (x4,x6) (x1,x3) (x5,x7): the order the codes unpack in
+        const v4u o = {__builtin_amdgcn_perm(w[1], w[0], 0x05040100u), __builtin_amdgcn_perm(w[3], w[2], 0x05040100u),
+                       __builtin_amdgcn_perm(w[1], w[0], 0x07060302u), __builtin_amdgcn_perm(w[3], w[2], 0x07060302u)};
+        if (ok) *(v4u *)(s_x + (size_t)p * 16) = o;
+        // sum over the piece, then over the 4 pieces of a chunk (lanes 4q .. 4q+3)
+        float s = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s += bf16_lo(w[e]) + bf16_hi(w[e]);
+        s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0xB1, 0xF, 0xF, true));
+        s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0x4E, 0xF, 0xF, true));
+        if (ok && (p & 3) == 0) s_sum[p >> 2] = s;   // chunk p/4 of the flattened [MR][NC]
+    }
+#pragma unroll
+    for (int i = 0; i < SP; ++i) {
+        const int p = tid + i * AL_THREADS;
+        if (p < spieces) {
+            const int r = p / spr, g8 = (p % spr) * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t sv = (e & 1) ? sr[i][e >> 1] >> 16 : sr[i][e >> 1] & 0xFFFFu;
+                const uint32_t zv = (e & 1) ? zr[i][e >> 1] >> 16 : zr[i][e >> 1] & 0xFFFFu;
+                s_sz[r * NG + g8 + e] = sv | zv << 16;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- 3. the weight chunks, each as soon as it has landed
+    const uint32_t k43 = 0x43434343u;
+    const uint32_t *szrow = s_sz + (wave * 8 + (lane >> 3)) * NG;
+    float y[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) y[m] = 0.0f;
+    auto chunk = [&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        __builtin_amdgcn_sched_barrier(0);           // chunks stay in order (registers: one chunk's x at a time)
+        __builtin_amdgcn_s_waitcnt(((NL - 1 - j) & 15) | (((NL - 1 - j) >> 4) << 14) | 0x0F70);   // vmcnt
+        asm volatile("" ::: "memory");
+        const int c = c0 + 8 * j;                    // chunk of the row: codes 32c .. 32c+31
+        v2bf pq[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t lo = wr[j][i] & 0x0F0F0F0Fu, hi = (wr[j][i] >> 4) & 0x0F0F0F0Fu;
+            pq[4 * i + 0] = __builtin_bit_cast(v2bf, __builtin_amdgcn_perm(k43, lo, 0x04010400u));
+            pq[4 * i + 1] = __builtin_bit_cast(v2bf, __builtin_amdgcn_perm(k43, lo, 0x04030402u));
+            pq[4 * i + 2] = __builtin_bit_cast(v2bf, __builtin_amdgcn_perm(k43, hi, 0x04010400u));
+            pq[4 * i + 3] = __builtin_bit_cast(v2bf, __builtin_amdgcn_perm(k43, hi, 0x04030402u));
+        }
+        const uint32_t sz = szrow[c >> 1];
+        const float sc = __uint_as_float(sz << 16), zp = 128.0f + __uint_as_float(sz & 0xFFFF0000u);
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            const v4u *xp = (const v4u *)(s_x + ((size_t)m * (K >> 3) + 4 * c) * 16);
+            float t0 = 0.0f, t1 = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                // elements copied to scalars before the bit casts: this clang
+                // miscompiles a bit cast of an element of a vector value
+                const v4u xv = xp[i];
+                const uint32_t x0 = xv[0], x1 = xv[1], x2 = xv[2], x3 = xv[3];
+                t0 = __builtin_amdgcn_fdot2_f32_bf16(pq[4 * i + 0], __builtin_bit_cast(v2bf, x0), t0, false);
+                t1 = __builtin_amdgcn_fdot2_f32_bf16(pq[4 * i + 1], __builtin_bit_cast(v2bf, x1), t1, false);
+                t0 = __builtin_amdgcn_fdot2_f32_bf16(pq[4 * i + 2], __builtin_bit_cast(v2bf, x2), t0, false);
+                t1 = __builtin_amdgcn_fdot2_f32_bf16(pq[4 * i + 3], __builtin_bit_cast(v2bf, x3), t1, false);
+            }
+            // sum_chunk (q - z) x = sum (128 + q) x - (128 + z) sum x
+            const float part = __builtin_fmaf(-zp, s_sum[m * NC + c], t0 + t1);
+            y[m] = __builtin_fmaf(sc, part, y[m]);
+            asm volatile("" : "+v"(y[m]));           // the chunk's sum is complete here
+        }
+    };
+    [&]<int... J>(std::integer_sequence<int, J...>) { (chunk(std::integral_constant<int, J>{}), ...); }(
+        std::make_integer_sequence<int, NL>{});
+
+    // ---- 4. the 8 lanes of a row, then bias and the bf16 store
+    const int orow = n0 + wave * 8 + (lane >> 3);
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        float v = y[m];
+        v += __shfl_xor(v, 1, 64);
+        v += __shfl_xor(v, 2, 64);
+        v += __shfl_xor(v, 4, 64);
+        if (c0 == 0 && orow < N) {
+            if (bias) v += bf16_to_f32(bias[orow]);
+            out[(size_t)m * N + orow] = (uint16_t)f32_to_bf16_rne(v);
+        }
+    }
+}
+
+template <int MR>
+static hipError_t launch_lines_mr(int N, int K, const uint16_t *xp, const uint8_t *cp, const uint16_t *sp,
+                                  const uint16_t *zp, const uint16_t *bp, uint16_t *op, hipStream_t stream)
+{
+    const dim3 grid((N + AL_ROWS - 1) / AL_ROWS), block(AL_THREADS);
+    const size_t lds = al_lds_bytes(MR, K);
+#define AL_CASE(NLV)                                                                                        \
+    case NLV:                                                                                               \
+        hipLaunchKernelGGL((awq_gemv_lines_kernel<MR, NLV>), grid, block, lds, stream, N, K, xp, cp, sp, zp, bp, op); \
+        break;
+    switch (K / 256) {
+        AL_CASE(2) AL_CASE(4) AL_CASE(6) AL_CASE(8) AL_CASE(10) AL_CASE(12) AL_CASE(14) AL_CASE(16)
+        default: return hipErrorInvalidValue;
+    }
+#undef AL_CASE
+    return hipGetLastError();
+}
+
+hipError_t launch_awq_gemv_lines(int M, int N, int K, const void *x, const void *codes, const void *scales,
+                                 const void *zeros, const void *bias, void *out, hipStream_t stream)
+{
+    const uint16_t *xp = (const uint16_t *)x, *sp = (const uint16_t *)scales, *zp = (const uint16_t *)zeros,
+                   *bp = (const uint16_t *)bias;
+    const uint8_t *cp = (const uint8_t *)codes;
+    uint16_t *op = (uint16_t *)out;
+    return M == 1 ? launch_lines_mr<1>(N, K, xp, cp, sp, zp, bp, op, stream)
+                  : launch_lines_mr<2>(N, K, xp, cp, sp, zp, bp, op, stream);
+}
+
+}  // namespace svdq

@@ -66,6 +66,11 @@ hipError_t launch_gemm_w4a4_nvfp4(int M, int N, int K, int rank, const void *act
 hipError_t launch_group_sums_int4(bool packed, int M, int N, int K, const void *act_codes,
                                   const void *wgt_codes, int32_t *G, hipStream_t stream);
 
+// The AWQ layer for one or two rows of x (K a multiple of 512, at most 4096):
+// whole-line weight loads, dot products on the vector ALU.
+bool awq_gemv_lines_applies(int M, int N, int K);
+hipError_t launch_awq_gemv_lines(int M, int N, int K, const void *x, const void *codes, const void *scales,
+                                 const void *zeros, const void *bias, void *out, hipStream_t stream);
 hipError_t launch_awq_gemv(int M, int N, int K, const void *x, const void *codes,
                            const void *scales, const void *zeros, const void *bias, void *out,
                            hipStream_t stream);

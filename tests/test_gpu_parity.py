@@ -304,6 +304,10 @@ def test_layer_end_to_end_and_determinism():
     # behind each chunk's x copy): 16-row tiles take 24 groups per chunk,
     # 2-row tiles 48
     (12, 96, 3072, True), (2, 64, 4608, False), (1, 32, 4608, True),
+    # one or two rows with K a multiple of 512 up to 4096: the whole-line
+    # stream (8 rows per wave, 24 per block), ragged N, every chunk count
+    (1, 5, 512, True), (2, 33, 1024, False), (1, 25, 1536, False), (2, 48, 2048, True),
+    (1, 71, 2560, True), (2, 24, 3584, False), (1, 49, 4096, True), (2, 100, 4096, True),
 ])
 def test_awq_gemv_shapes(M, N, K, with_bias):
     rng = np.random.default_rng(4000 + M + N + K)
