@@ -17,10 +17,14 @@ kernels and the GEMV included in the time), the nine kernels launched back to
 back on one stream (the same step replayed as one HIP graph is reported in
 ``launch``).  ``kernels`` gives per-kernel average durations measured with
 HIP events on the launch stream in a separate pass;
-``roofline`` is for the dominant kernel (the int4 GEMM of mlp_up, int8
-matrix-core peak); ``gemv`` reports the W4A16 GEMV alone for
+``roofline`` is for the dominant kernel (the int4 GEMM of mlp_up on packed
+weights, fp8/int8 matrix-core peak 5000 TOPS), from those HIP events, with
+the committed rocprofv3 trace's average beside it when that trace matches
+the kernel's source; ``gemv`` reports the W4A16 GEMV alone for
 M in {1, 2, 8} streaming 16 rotating weight copies (more than the 256 MB
-Infinity Cache); ``cpu_baseline`` times the CPU oracle on a bounded sample.
+Infinity Cache), next to a plain read of the same bytes (contiguous and in
+the GEMV's row pattern); ``cpu_baseline`` times the CPU oracle on a bounded
+sample, on every host core of one GPU's share.
 """
 from __future__ import annotations
 
@@ -36,9 +40,11 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_INT8_TOPS = 5000.0        # MI355X dense int8 matrix peak, TOPS
-PEAK_BF16_TFLOPS = 2500.0      # dense bf16
+PEAK_INT8_TOPS = 5000.0        # MI355X dense int8 (and fp8) matrix peak, TOPS
+PEAK_BF16_TFLOPS = 2500.0      # dense bf16 / fp16
+PEAK_FP4_TFLOPS = 10100.0      # dense fp4 / fp6
 PEAK_HBM_GBPS = 8000.0         # HBM3E
+CPU_THREADS_MAX = 16           # host cores one GPU's share of the machine holds
 
 TOKENS, HIDDEN = 4096, 3072
 LAYERS = [  # name, precision, M, K, N, rank, seed
@@ -175,7 +181,44 @@ def gemv_sweep(torch, synth, reps=160):
             out[f"M={M}"] = {"us": round(us, 3), "TFLOP/s": round(tf, 1),
                              "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
         print(f"[bench] awq M={M}: {us:.1f} us", file=sys.stderr, flush=True)
+    out["read_ceiling"] = read_ceiling(torch, algorithmic_bytes_gemv(1, N, K), reps)
+    m1 = out["M=1"]
+    for pat in ("contiguous", "gemv_rows"):
+        m1[f"frac_of_{pat}_read"] = round(out["read_ceiling"][pat]["us"] / m1["us"], 4)
     return out
+
+
+def read_ceiling(torch, nbytes, reps=160):
+    """A plain read of ``nbytes`` (the M = 1 GEMV's algorithmic bytes) from 16
+    rotating 16-byte-aligned slices of one buffer (more than the Infinity
+    Cache), in batches of 16 launches between HIP events: contiguous, and in
+    the GEMV's row pattern (svdq_debug_stream_read)."""
+    from bit_w4a4_quantized_svdq_amd import capi
+    span = (nbytes + 4095) // 4096 * 4096
+    buf = torch.randint(0, 255, (16 * span,), dtype=torch.uint8, device="cuda")
+    acc = torch.zeros((nbytes + capi.STREAM_READ_SPAN - 1) // capi.STREAM_READ_SPAN, dtype=torch.int32,
+                      device="cuda")
+    res = {}
+    for pat, key in ((0, "contiguous"), (1, "gemv_rows")):
+        fn = lambda i: capi.svdq_debug_stream_read(buf[i * span:], acc, pat, nbytes)
+        for i in range(32):
+            fn(i % 16)
+        torch.cuda.synchronize()
+        ev = []
+        for _ in range(reps // 16):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for i in range(16):
+                fn(i)
+            e.record()
+            ev.append((s, e))
+        torch.cuda.synchronize()
+        us = float(np.median([s.elapsed_time(e) for s, e in ev])) * 1e3 / 16
+        gbps = nbytes / (us * 1e-6) / 1e9
+        res[key] = {"us": round(us, 3), "GB/s": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4)}
+        print(f"[bench] read ceiling {key}: {us:.2f} us", file=sys.stderr, flush=True)
+    res["bytes"] = int(nbytes)
+    return res
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_int4_mlp_up_traffic.txt")
@@ -208,6 +251,22 @@ def recorded_traffic():
             return None
         return int(float(rec["hbm_bytes_per_launch"]))
     except (OSError, KeyError, ValueError):
+        return None
+
+
+def recorded_trace_us(key="mlp_up.gemm_w4a4"):
+    """The committed hot-path kernel trace's average duration of one step
+    kernel, or None when the int4 GEMM's source has changed since it was
+    taken."""
+    try:
+        us, sha = None, None
+        for line in open(TRACE_FILE):
+            if line.startswith("# gemm_int4 source_sha256:"):
+                sha = line.split(":", 1)[1].strip()
+            elif line.startswith(key + " "):
+                us = float(line.split()[-6])
+        return us if sha == gemm_int4_source_hash() else None
+    except (OSError, ValueError, IndexError):
         return None
 
 
@@ -514,6 +573,50 @@ def summarize_utilisation(run_dir, trace_us):
     print(f"wrote {UTIL_FILE} and {GEMV_TRAFFIC_FILE}")
 
 
+GEMV_TRACE_FILE = os.path.join(ROOT, "profiles", "awq_gemv_read_ceiling_kernel_trace.txt")
+
+
+def summarize_gemv_trace(run_dir):
+    """Per-kernel durations of `bench.py --gemv-only` from a rocprofv3 kernel
+    trace in <run_dir>/gemv_trace: the AWQ GEMV at M = 1, 2, 8 over 16
+    rotating weight copies and the plain reads of the same bytes."""
+    import glob
+    trace = glob.glob(os.path.join(run_dir, "gemv_trace", "**", "*kernel_trace.csv"), recursive=True)[0]
+    _, K, N, _ = ADALN
+    kinds = [("awq_gemv_lines_kernel<1,", "AWQ GEMV M=1", algorithmic_bytes_gemv(1, N, K)),
+             ("awq_gemv_lines_kernel<2,", "AWQ GEMV M=2", algorithmic_bytes_gemv(2, N, K)),
+             ("awq_gemv_kernel", "AWQ GEMV M=8", algorithmic_bytes_gemv(8, N, K)),
+             ("stream_read_kernel<false>", "plain read, contiguous", algorithmic_bytes_gemv(1, N, K)),
+             ("stream_read_kernel<true>", "plain read, GEMV row pattern", algorithmic_bytes_gemv(1, N, K))]
+    durs = {k: [] for k, _, _ in kinds}
+    for r in _csv_rows(trace):
+        name = r["Kernel_Name"].replace(" ", "")
+        for k, _, _ in kinds:
+            if k.replace(" ", "") in name:
+                durs[k].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = ["# AWQ W4A16 GEMV (adaLN modulation, 3072 -> 18432, int4 g64) against a plain read of the same bytes",
+             "# Command (paths relative to the repository root; run with TMPDIR=/tmp):",
+             f"#   rocprofv3 --kernel-trace --stats -f csv -d {run_dir}/gemv_trace -o gemv -- "
+             "python3 bench.py --gemv-only",
+             "# Every kernel streams 16 rotating copies (512 MB, more than the 256 MB Infinity Cache).",
+             "# bytes: the M = 1 GEMV's algorithmic bytes (codes, scales, zero points, x, out) for the plain",
+             "# reads and M = 1; M = 2 and 8 add their x and out rows.  The plain reads are",
+             "# svdq_debug_stream_read: 12 loads of 16 B per lane in flight per wave, 12 KB per wave.",
+             "# GB/s and % of 8 TB/s from the median duration (all dispatches, warm-up launches included).",
+             "#",
+             f"{'kernel':32s} {'n':>4s} {'median_us':>10s} {'mean_us':>9s} {'min_us':>8s} {'bytes':>10s} "
+             f"{'GB/s':>7s} {'%hbm':>6s}"]
+    for k, label, nbytes in kinds:
+        d = durs[k]
+        if not d:
+            raise SystemExit(f"no {k} dispatches in {trace}")
+        med = float(np.median(d))
+        lines.append(f"{label:32s} {len(d):4d} {med:10.2f} {sum(d) / len(d):9.2f} {min(d):8.2f} {nbytes:10d} "
+                     f"{nbytes / med / 1e3:7.0f} {nbytes / med / 1e3 / PEAK_HBM_GBPS * 100:6.1f}")
+    open(GEMV_TRACE_FILE, "w").write("\n".join(lines) + "\n")
+    print(f"wrote {GEMV_TRACE_FILE}")
+
+
 def summarize_profiles(run_dir, warmup, steps):
     """Write the committed profile summaries from a rocprofv3 run directory:
     <run_dir>/trace (kernel trace of `bench.py --steps S --warmup W`, whose
@@ -522,7 +625,7 @@ def summarize_profiles(run_dir, warmup, steps):
     import glob
     trace = glob.glob(os.path.join(run_dir, "trace", "**", "*kernel_trace.csv"), recursive=True)[0]
     ours = [r for r in _csv_rows(trace)
-            if any(k in r["Kernel_Name"] for k in ("quantize_act_kernel", "gemm_w4a4", "awq_gemv_kernel"))]
+            if any(k in r["Kernel_Name"] for k in ("quantize_act_kernel", "gemm_w4a4", "awq_gemv"))]
     ours.sort(key=lambda r: int(r["Start_Timestamp"]))
     per = len(STEP_KERNELS)
     # warm-up steps, `steps` timed steps, one side-stream step before the
@@ -556,6 +659,7 @@ def summarize_profiles(run_dir, warmup, steps):
              "# within a step gives the layer).",
              "# event_us: the same run's bench.py HIP-event average for that kernel (launch stream).",
              f"# Same-run bench value: {bench_line['value']} TOPS, {bench_line['ms_per_step']} ms/step.",
+             f"# gemm_int4 source_sha256: {gemm_int4_source_hash()}",
              "#",
              f"{'layer.kernel':24s} {'kernel':46s} {'grid':>7s} {'n':>3s} {'trace_avg_us':>12s} "
              f"{'trace_min_us':>12s} {'event_us':>9s} {'VGPR':>5s} {'AGPR':>5s} {'LDS_B':>6s}"]
@@ -596,36 +700,69 @@ def summarize_profiles(run_dir, warmup, steps):
           f"hbm_bytes_per_launch: {int(fetch + write)}"]
     open(TRAFFIC_FILE, "w").write("\n".join(t) + "\n")
     print(f"wrote {TRACE_FILE} and {TRAFFIC_FILE}")
+    if os.path.isdir(os.path.join(run_dir, "gemv_trace")):
+        summarize_gemv_trace(run_dir)
     if os.path.isdir(os.path.join(run_dir, "pmc_gemm_util")):
         summarize_utilisation(run_dir, {k: sum(a["us"]) / len(a["us"]) for k, a in agg.items()})
 
 
-def cpu_baseline(synth, budget_rows=48):
-    """The CPU oracle (single-threaded C, as it stands) on a bounded sample of
-    the same step: the first ``budget_rows`` rows of each W4A4 layer
-    (quantize + GEMM) and the M=1 GEMV."""
+def cpu_threads():
+    """Host threads for the CPU baseline: the cores this process may run on,
+    at most one GPU's share of the machine."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, CPU_THREADS_MAX))
+
+
+def cpu_baseline(synth, rows_per_thread=32):
+    """The CPU oracle (plain C, as it stands) on a bounded sample of the same
+    step, on every host core this process may use: each W4A4 layer's first
+    ``rows_per_thread`` x threads rows (quantize + GEMM; rows are independent,
+    so each thread takes its own slice of rows) and the M = 1 GEMV (each
+    thread its own slice of output columns).  The oracle's C entry points are
+    called through ctypes, which releases the interpreter lock, so the
+    threads run in parallel."""
+    from concurrent.futures import ThreadPoolExecutor
     import oracle
+    oracle.lib()
+    T = cpu_threads()
+    rows = rows_per_thread * T
     ops, t_total = 0.0, 0.0
-    for name, prec, M, K, N, rank, seed in LAYERS:
-        w = synth.synthetic_w4a4_weights(seed, N, K, rank, prec)
-        rng = np.random.default_rng(seed + 1000)
-        x, _ = synth.draw_activations(rng, budget_rows, K, max(1, K // 100), 50.0)
-        xb = synth.to_bf16_bits(x)
-        p = oracle.INT4 if prec == "int4" else oracle.NVFP4
+    with ThreadPoolExecutor(max_workers=T) as pool:
+        for name, prec, M, K, N, rank, seed in LAYERS:
+            w = synth.synthetic_w4a4_weights(seed, N, K, rank, prec)
+            rng = np.random.default_rng(seed + 1000)
+            x, _ = synth.draw_activations(rng, rows, K, max(1, K // 100), 50.0)
+            xb = synth.to_bf16_bits(x)
+            p = oracle.INT4 if prec == "int4" else oracle.NVFP4
+
+            def part(i):
+                ac, asc, t = oracle.quantize_act(p, xb[i * rows_per_thread:(i + 1) * rows_per_thread],
+                                                 w["smooth"], w["lora_down"])
+                return oracle.gemm_w4a4(p, ac, asc, w["wgt_codes"], w["wgt_scales"], t, w["lora_up"], None)
+
+            t0 = time.perf_counter()
+            list(pool.map(part, range(T)))
+            t_total += time.perf_counter() - t0
+            ops += 2.0 * rows * N * K
+        name, K, N, seed = ADALN
+        aw = synth.synthetic_awq_weights(seed, N, K)
+        xg = synth.to_bf16_bits(np.random.default_rng(seed).standard_normal((1, K)))
+        cut = np.linspace(0, N, T + 1).astype(int)
+
+        def gemv_part(i):
+            a, b = cut[i], cut[i + 1]
+            return oracle.awq_gemv(xg, aw["wgt_codes"][a:b], aw["wgt_scales"][a:b], aw["wgt_zeros"][a:b], None)
+
         t0 = time.perf_counter()
-        ac, asc, t = oracle.quantize_act(p, xb, w["smooth"], w["lora_down"])
-        oracle.gemm_w4a4(p, ac, asc, w["wgt_codes"], w["wgt_scales"], t, w["lora_up"], None)
+        list(pool.map(gemv_part, range(T)))
         t_total += time.perf_counter() - t0
-        ops += 2.0 * budget_rows * N * K
-    name, K, N, seed = ADALN
-    aw = synth.synthetic_awq_weights(seed, N, K)
-    xg = synth.to_bf16_bits(np.random.default_rng(seed).standard_normal((1, K)))
-    t0 = time.perf_counter()
-    oracle.awq_gemv(xg, aw["wgt_codes"], aw["wgt_scales"], aw["wgt_zeros"], None)
-    t_total += time.perf_counter() - t0
-    return {"value": round(ops / t_total / 1e12, 6), "unit": "TOPS", "cores": 1, "kind": "oracle",
-            "sample": f"first {budget_rows} rows of each W4A4 layer (quantize + GEMM) and the M=1 GEMV; "
-                      f"{t_total:.1f} s on one host thread"}
+    return {"value": round(ops / t_total / 1e12, 6), "unit": "TOPS", "cores": T, "kind": "oracle",
+            "sample": f"first {rows} rows of each W4A4 layer (quantize + GEMM; {rows_per_thread} rows per "
+                      f"thread) and the M=1 GEMV (columns split over the threads); {t_total:.1f} s wall on "
+                      f"{T} host threads"}
 
 
 def main():
@@ -640,6 +777,8 @@ def main():
                     help="run only this kernel --steps times (e.g. mlp_up.gemm_w4a4), for rocprofv3")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="run only a plain copy of this many MiB --steps times (counter calibration)")
+    ap.add_argument("--gemv-only", action="store_true",
+                    help="run only the AWQ sweep and the plain-read ceiling, print them as JSON (for rocprofv3)")
     ap.add_argument("--summarize", default=None, metavar="RUN_DIR",
                     help="write the profiles/ summaries from a rocprofv3 run directory (no GPU needed)")
     args = ap.parse_args()
@@ -660,6 +799,9 @@ def main():
         return
     if args.profile_kernel:
         profile_kernel(torch, synth, args.profile_kernel, args.steps)
+        return
+    if args.gemv_only:
+        print(json.dumps({"gemv": gemv_sweep(torch, synth)}))
         return
     print(f"[bench] building inputs", file=sys.stderr, flush=True)
     layers, xs = build_inputs(torch, synth)
@@ -710,7 +852,10 @@ def main():
         g["TOPS"] = round(ops / (g["us"] * 1e-6) / 1e12, 2)
         peak = PEAK_INT8_TOPS if prec == "int4" else PEAK_BF16_TFLOPS
         g["frac_peak"] = round(g["TOPS"] / peak, 4)
-        g["peak"] = "int8 5000 TOPS" if prec == "int4" else "bf16 2500 TFLOP/s (exact NVFP4 path)"
+        g["peak"] = ("fp8/int8 5000 TOPS (int4 codes as exact E4M3 values)" if prec == "int4"
+                     else "fp16 2500 TFLOP/s (exact NVFP4 path)")
+        if prec == "nvfp4":
+            g["frac_fp4_peak"] = round(g["TOPS"] / PEAK_FP4_TFLOPS, 4)
         q = kernels[f"{name}.quantize_act"]
         qb = algorithmic_bytes_quantize(M, K, rank, prec)
         q["GB/s"] = round(qb / (q["us"] * 1e-6) / 1e9, 1)
@@ -722,11 +867,20 @@ def main():
 
     value = w4a4_ops / (ms_per_step * 1e-3) / 1e12
     dom = kernels["mlp_up.gemm_w4a4"]
-    roofline = {"bound": "mfma", "kernel": "svdq_gemm_w4a4 int4 (mlp_up 4096x3072->12288)",
-                "achieved": dom["TOPS"], "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
+    ops_up = 2.0 * TOKENS * 4 * HIDDEN * HIDDEN
+    trace_us = recorded_trace_us()
+    roofline = {"bound": "mfma",
+                "kernel": "svdq_gemm_w4a4 int4, packed weights on fp8 matrix cores (mlp_up 4096x3072->12288)",
+                "achieved": dom["TOPS"], "peak": PEAK_INT8_TOPS, "unit": "TOPS",
                 "frac": round(dom["TOPS"] / PEAK_INT8_TOPS, 4), "traffic": recorded_traffic(),
+                "algorithmic_ops": ops_up,
                 "algorithmic_bytes": algorithmic_bytes_gemm(TOKENS, 4 * HIDDEN, HIDDEN, 32, "int4"),
-                "avg_launch_us": dom["us"]}
+                "avg_launch_us": dom["us"],
+                "basis": "achieved = algorithmic_ops / avg_launch_us, the mean of --steps launches each "
+                         "between two HIP events on the launch stream",
+                "trace_avg_us": trace_us,
+                "frac_trace": None if trace_us is None else round(ops_up / (trace_us * 1e-6) / 1e12 /
+                                                                  PEAK_INT8_TOPS, 4)}
 
     gemv = None if args.no_gemv_sweep else gemv_sweep(torch, synth)
     fusion = None if args.no_gemv_sweep else gelu_fusion(torch, synth, layers)
@@ -737,7 +891,7 @@ def main():
     rec = {"metric": "W4A4 GEMM effective TOPS + % MFMA peak; W4A16 GEMV GB/s + % HBM peak",
            "value": round(value, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
-           "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+           "scaling": "weak", "vs_baseline": None, "dtype": "fp8", "data": "synthetic",
            "launch": "stream launches; the same step as one HIP graph replay: %.4f ms/step" % graph_ms,
            "config": {"workload": "dit_block_1024px_quantized_linears", "tokens": TOKENS,
                       "hidden": HIDDEN,

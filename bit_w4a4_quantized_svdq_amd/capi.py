@@ -26,7 +26,8 @@ EXPORTED = ("svdq_quantize_act", "svdq_gelu_quantize_act", "svdq_gemm_w4a4", "sv
             "svdq_smooth_factors", "svdq_quantize_weight", "svdq_lowrank_workspace_bytes",
             "svdq_lowrank_factors", "svdq_lowrank_factors_noalloc",
             "svdq_packed_weight_bytes", "svdq_pack_weight_int4", "svdq_debug_group_sums_packed",
-            "svdq_debug_group_sums", "svdq_debug_gelu_bf16", "svdq_status_string", "svdq_last_error",
+            "svdq_debug_group_sums", "svdq_debug_gelu_bf16", "svdq_debug_stream_read",
+            "svdq_status_string", "svdq_last_error",
             "svdq_abi_version")
 
 
@@ -61,6 +62,7 @@ def lib() -> ctypes.CDLL:
         L.svdq_packed_weight_bytes.restype = _I64
         L.svdq_pack_weight_int4.argtypes = [_I64, _I64, _P, _P, _P, _P, _P]
         L.svdq_debug_gelu_bf16.argtypes = [_I64, _P, _P, _P]
+        L.svdq_debug_stream_read.argtypes = [_P, _I64, _I32, _P, _P]
         L.svdq_smooth_factors.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P]
         L.svdq_quantize_weight.argtypes = [_I32, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P]
         L.svdq_lowrank_workspace_bytes.argtypes = [_I64, _I64, _I32]
@@ -70,7 +72,7 @@ def lib() -> ctypes.CDLL:
         for f in ("svdq_quantize_act", "svdq_gelu_quantize_act", "svdq_gemm_w4a4",
                   "svdq_gemm_w4a4_qk_norm_rope", "awq_gemv_w4a16",
                   "svdq_debug_group_sums", "svdq_debug_group_sums_packed", "svdq_pack_weight_int4",
-                  "svdq_debug_gelu_bf16", "svdq_smooth_factors",
+                  "svdq_debug_gelu_bf16", "svdq_debug_stream_read", "svdq_smooth_factors",
                   "svdq_quantize_weight", "svdq_lowrank_factors", "svdq_lowrank_factors_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         L.svdq_status_string.argtypes = [ctypes.c_int]
@@ -249,3 +251,17 @@ def svdq_debug_group_sums(act_codes, wgt_codes, G, stream=None):
     N = wgt_codes.shape[0]
     _check(lib().svdq_debug_group_sums(M, N, 2 * Kh, _ptr(act_codes), _ptr(wgt_codes), _ptr(G),
                                        _stream(stream)), "svdq_debug_group_sums")
+
+
+STREAM_READ_SPAN = 12288
+
+
+def svdq_debug_stream_read(src, out, pattern=0, nbytes=None, stream=None):
+    """Plain read of a device tensor (pattern 0 contiguous, 1 the AWQ GEMV's
+    row pattern); out (int32, at least ceil(nbytes / 12288) entries) receives
+    the xor of each 12288-byte span's 16-byte chunks."""
+    n = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    if out.numel() * out.element_size() < 4 * ((n + STREAM_READ_SPAN - 1) // STREAM_READ_SPAN):
+        raise ValueError("svdq_debug_stream_read: out holds fewer than ceil(nbytes / 12288) words")
+    _check(lib().svdq_debug_stream_read(_ptr(src), n, int(pattern), _ptr(out), _stream(stream)),
+           "svdq_debug_stream_read")

@@ -188,6 +188,56 @@ void awq_gemv_lines_kernel(int N, int K, const uint16_t *__restrict__ x, const u
     }
 }
 
+// A plain read of `bytes` of device memory, the ceiling the weight stream is
+// measured against.  Each wave reads a 12 KB span with 12 loads of 16 bytes
+// per lane, all issued before any use, either in the GEMV's pattern (rows
+// of 1536 bytes, 8 lanes per 128-byte line: lane l takes row l/8, chunk
+// l%8 + 8j; LINES) or contiguously (lane l takes 16 l + 1024 j).  The xor
+// of the span's words goes to out[span] (a plain store per wave: one shared
+// atomic would serialize thousands of waves), so that no load is dropped.
+constexpr int SR_LOADS = 12;
+constexpr int SR_SPAN = 64 * SR_LOADS * 16;   // bytes per wave
+template <bool LINES>
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint8_t *__restrict__ src, int64_t bytes,
+                                                          uint32_t *__restrict__ out)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t base = wave * SR_SPAN +
+                         (LINES ? (int64_t)(lane >> 3) * (SR_LOADS * 128) + 16 * (lane & 7) : 16 * lane);
+    constexpr int step = LINES ? 128 : 1024;
+    v4u r[SR_LOADS];
+#pragma unroll
+    for (int j = 0; j < SR_LOADS; ++j) {
+        const int64_t off = base + (int64_t)step * j;
+        r[j] = off + 16 <= bytes ? *(const v4u *)(src + off) : v4u{0u, 0u, 0u, 0u};
+    }
+    uint32_t acc = 0u;
+#pragma unroll
+    for (int j = 0; j < SR_LOADS; ++j) acc ^= r[j][0] ^ r[j][1] ^ r[j][2] ^ r[j][3];
+    acc ^= __shfl_xor(acc, 32, 64);
+    acc ^= __shfl_xor(acc, 16, 64);
+    acc ^= __shfl_xor(acc, 8, 64);
+    acc ^= __shfl_xor(acc, 4, 64);
+    acc ^= __shfl_xor(acc, 2, 64);
+    acc ^= __shfl_xor(acc, 1, 64);
+    if (lane == 0 && wave * SR_SPAN < bytes) out[wave] = acc;
+}
+
+int64_t stream_read_spans(int64_t bytes) { return (bytes + SR_SPAN - 1) / SR_SPAN; }
+
+hipError_t launch_stream_read(const void *src, int64_t bytes, bool lines, uint32_t *out, hipStream_t stream)
+{
+    const int64_t blocks = (stream_read_spans(bytes) + 3) / 4;
+    if (lines)
+        hipLaunchKernelGGL(stream_read_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           (const uint8_t *)src, bytes, out);
+    else
+        hipLaunchKernelGGL(stream_read_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           (const uint8_t *)src, bytes, out);
+    return hipGetLastError();
+}
+
 template <int MR>
 static hipError_t launch_lines_mr(int N, int K, const uint16_t *xp, const uint8_t *cp, const uint16_t *sp,
                                   const uint16_t *zp, const uint16_t *bp, uint16_t *op, hipStream_t stream)

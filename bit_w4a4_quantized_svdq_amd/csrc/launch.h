@@ -71,6 +71,9 @@ hipError_t launch_group_sums_int4(bool packed, int M, int N, int K, const void *
 bool awq_gemv_lines_applies(int M, int N, int K);
 hipError_t launch_awq_gemv_lines(int M, int N, int K, const void *x, const void *codes, const void *scales,
                                  const void *zeros, const void *bias, void *out, hipStream_t stream);
+// plain read, contiguous or in the GEMV's access pattern (a measurement hook)
+int64_t stream_read_spans(int64_t bytes);
+hipError_t launch_stream_read(const void *src, int64_t bytes, bool lines, uint32_t *out, hipStream_t stream);
 hipError_t launch_awq_gemv(int M, int N, int K, const void *x, const void *codes,
                            const void *scales, const void *zeros, const void *bias, void *out,
                            hipStream_t stream);

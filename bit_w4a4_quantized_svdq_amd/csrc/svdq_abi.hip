@@ -377,6 +377,17 @@ svdq_status svdq_pack_weight_int4(int64_t N, int64_t K, const void *wgt_codes, c
                     "svdq_pack_weight_int4");
 }
 
+svdq_status svdq_debug_stream_read(const void *src, int64_t bytes, int32_t pattern, uint32_t *out, void *stream)
+{
+    if (bytes < 0 || bytes > ((int64_t)1 << 40)) return fail(SVDQ_ERR_INVALID_ARG, "bytes out of range");
+    if (pattern != 0 && pattern != 1) return fail(SVDQ_ERR_INVALID_ARG, "pattern must be 0 or 1");
+    SVDQ_TRY(check_ptr(src, "src", false));
+    if (!out || ((uintptr_t)out & 3u)) return fail(SVDQ_ERR_INVALID_ARG, "out must be a 4-byte aligned pointer");
+    if (bytes == 0) return SVDQ_OK;
+    SVDQ_TRY(check_device());
+    return launched(svdq::launch_stream_read(src, bytes, pattern == 1, out, (hipStream_t)stream), "svdq_debug_stream_read");
+}
+
 const char *svdq_status_string(svdq_status s)
 {
     switch (s) {
@@ -390,6 +401,6 @@ const char *svdq_status_string(svdq_status s)
 
 const char *svdq_last_error(void) { return g_last_error; }
 
-int32_t svdq_abi_version(void) { return 7; }
+int32_t svdq_abi_version(void) { return 8; }
 
 }  // extern "C"

@@ -302,18 +302,33 @@ svdq_status svdq_debug_group_sums_packed(int64_t M, int64_t N, int64_t K, const 
  */
 svdq_status svdq_debug_gelu_bf16(int64_t n, const void *x, void *out, void *stream);
 
+/*
+ * svdq_debug_stream_read -- a measurement hook, not needed to run a layer:
+ * reads `bytes` of device memory at `src` in spans of 12288 bytes, one span
+ * per wave, with 12 loads of 16 bytes per lane all in flight before any use.
+ * pattern 0 reads a span contiguously (1 KB per load instruction), pattern 1
+ * in the AWQ GEMV's weight pattern (rows of 1536 bytes, 8 lanes per 128-byte
+ * line, 8 rows per load instruction).  out (device, uint32, ceil(bytes /
+ * 12288) entries, caller-owned) receives the xor of each span's whole
+ * 16-byte chunks (a tail shorter than 16 bytes is not read).  Its time is
+ * the ceiling the GEMV's HBM rate is compared with.
+ * Errors: SVDQ_ERR_INVALID_ARG for bytes < 0, a pattern other than 0 or 1,
+ * a NULL or misaligned src (16 bytes) or out (4 bytes); bytes == 0 is a no-op.
+ */
+svdq_status svdq_debug_stream_read(const void *src, int64_t bytes, int32_t pattern, uint32_t *out, void *stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *svdq_status_string(svdq_status s);
 
 /* Text of the last argument-check failure on the calling thread ("" if none). */
 const char *svdq_last_error(void);
 
-/* ABI version of this header: 7 (1 plus svdq_gelu_quantize_act, svdq_debug_gelu_bf16,
+/* ABI version of this header: 8 (1 plus svdq_gelu_quantize_act, svdq_debug_gelu_bf16,
  * svdq_gemm_w4a4_qk_norm_rope, svdq_smooth_factors, svdq_quantize_weight,
  * svdq_lowrank_workspace_bytes, svdq_lowrank_factors,
  * svdq_lowrank_factors_noalloc, then SVDQ_INT4_PACKED with
  * svdq_packed_weight_bytes, svdq_pack_weight_int4 and
- * svdq_debug_group_sums_packed). */
+ * svdq_debug_group_sums_packed, then svdq_debug_stream_read). */
 int32_t svdq_abi_version(void);
 
 #ifdef __cplusplus

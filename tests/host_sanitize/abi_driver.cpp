@@ -166,6 +166,12 @@ int main() {
     expect_launch(svdq_debug_gelu_bf16(65536, P, P, nullptr), "gelu_bf16", 65536, 0, 0);
     expect_noop(svdq_debug_gelu_bf16(0, P, P, nullptr), "gelu n=0");
     expect_reject(svdq_debug_gelu_bf16(-1, P, P, nullptr), INV, "gelu n < 0");
+    expect_launch(svdq_debug_stream_read(P, 64 << 20, 1, (uint32_t *)I, nullptr), "stream_read", 64, 1, 0);
+    expect_launch(svdq_debug_stream_read(P, 64 << 20, 0, (uint32_t *)I, nullptr), "stream_read", 64, 0, 0);
+    expect_noop(svdq_debug_stream_read(P, 0, 0, (uint32_t *)I, nullptr), "stream read 0 bytes");
+    expect_reject(svdq_debug_stream_read(P, -1, 0, (uint32_t *)I, nullptr), INV, "stream read bytes < 0");
+    expect_reject(svdq_debug_stream_read(P, 4096, 2, (uint32_t *)I, nullptr), INV, "stream read pattern 2");
+    expect_reject(svdq_debug_stream_read(P, 4096, 0, nullptr, nullptr), INV, "stream read out NULL");
 
     // ---- offline preparation
     expect_launch(svdq_smooth_factors(4096, 12288, 3072, P, P, P, nullptr), "smooth_factors", 4096, 12288, 3072);

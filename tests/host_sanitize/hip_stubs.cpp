@@ -84,6 +84,9 @@ hipError_t launch_awq_gemv(int M, int N, int K, const void *, const void *, cons
                            const void *, void *, hipStream_t) {
     return rec("awq_gemv", M, N, K);
 }
+hipError_t launch_stream_read(const void *, int64_t bytes, bool lines, uint32_t *, hipStream_t) {
+    return rec("stream_read", (int)(bytes >> 20), lines, 0);
+}
 bool awq_gemm_applies(int M, int N, int K) {
     return K % 512 == 0 && M >= AWQ_GEMM_MIN_M &&
            (long long)((M + 31) / 32) * ((N + 31) / 32) >= AWQ_GEMM_MIN_TILES;

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(capi.LIB_PATH)
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert capi.svdq_abi_version() == 7
+    assert capi.svdq_abi_version() == 8
     for s in range(4):
         assert capi.svdq_status_string(s).startswith(("SVDQ_OK", "SVDQ_ERR"))
     assert "unknown" in capi.svdq_status_string(99)

@@ -372,3 +372,25 @@ def test_awq_gemv_extreme_codes(M):
     y = gpu_gemv(x, codes, scales, zeros, None)
     ref = oracle.awq_gemv(x, codes, scales, zeros, None)
     assert_bf16_close(y, ref, "gemv extremes")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("nbytes", [16, 12288, 49152 * 3 + 4096 + 16, 1 << 22])
+@pytest.mark.parametrize("pattern", [0, 1])
+def test_stream_read_covers_every_chunk(nbytes, pattern):
+    """The plain-read measurement kernel reads each whole 16-byte chunk of the
+    range exactly once: the xor of every 12288-byte span's 32-bit words, in
+    both access patterns, and nothing is written past the last span."""
+    rng = np.random.default_rng(nbytes + pattern)
+    host = rng.integers(0, 2 ** 32, nbytes // 4 + 16, dtype=np.uint32)
+    dev = torch.from_numpy(host.view(np.int32)).cuda()
+    spans = (nbytes + 12287) // 12288
+    acc = torch.full((spans + 64,), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
+    announce("stream_read", nbytes, pattern)
+    capi.svdq_debug_stream_read(dev, acc, pattern, nbytes)
+    torch.cuda.synchronize()
+    words = host[: (nbytes // 16) * 4]
+    want = [np.bitwise_xor.reduce(words[i * 3072:(i + 1) * 3072]) for i in range(spans)]
+    got = acc.cpu().numpy().view(np.uint32)
+    assert [int(v) for v in got[:spans]] == [int(v) for v in want]
+    assert (got[spans:] == 0x5A5A5A5A).all()
