@@ -56,10 +56,16 @@ LAYERS = [  # name, precision, M, K, N, rank, seed
 ADALN = ("adaln", HIDDEN, 6 * HIDDEN, 15)   # name, K, N, seed
 
 
+def code_bytes(n, prec):
+    """Bytes of n codes: int4 layers run on the FP6 layout (48 bytes per 64
+    codes), NVFP4 on packed nibbles."""
+    return 3 * n // 4 if prec == "int4" else n // 2
+
+
 def algorithmic_bytes_quantize(M, K, rank, prec):
     """x read + smooth + lora_down read + codes/scales/lora_act written."""
     sc = M * (K // 64) * 2 if prec == "int4" else M * (K // 16)
-    return M * K * 2 + K * 2 + rank * K * 2 + M * K // 2 + sc + M * rank * 4
+    return M * K * 2 + K * 2 + rank * K * 2 + code_bytes(M * K, prec) + sc + M * rank * 4
 
 
 def algorithmic_bytes_gemm(M, N, K, rank, prec):
@@ -68,7 +74,7 @@ def algorithmic_bytes_gemm(M, N, K, rank, prec):
         sc = (M + N) * (K // 64) * 2
     else:
         sc = (M + N) * (K // 16)
-    return (M + N) * K // 2 + sc + M * rank * 4 + N * rank * 2 + M * N * 2
+    return code_bytes((M + N) * K, prec) + sc + M * rank * 4 + N * rank * 2 + M * N * 2
 
 
 def algorithmic_bytes_gemv(M, N, K):
@@ -225,8 +231,10 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_int4_mlp_up_traffic.txt")
 TRACE_FILE = os.path.join(ROOT, "profiles", "hot_path_dit_block_kernel_trace.txt")
 UTIL_FILE = os.path.join(ROOT, "profiles", "gemm_int4_mlp_up_utilisation.txt")
 GEMV_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "awq_gemv_m1_traffic.txt")
+# the dominant kernel: the int4 GEMM on the FP6 layout (layer default)
+DOM_KERNEL = "gemm_w4a4_fp6"
 GEMM_INT4_SOURCES = [os.path.join(ROOT, "bit_w4a4_quantized_svdq_amd", "csrc", f)
-                     for f in ("gemm_w4a4_int4.hip", "gemm_common.h", "device_common.h")]
+                     for f in ("gemm_w4a4_fp6.hip", "gemm_common.h", "device_common.h")]
 STEP_KERNELS = [f"{n}.{k}" for n, *_ in LAYERS for k in ("quantize_act", "gemm_w4a4")] + ["adaln.awq_gemv"]
 
 
@@ -517,24 +525,28 @@ def summarize_utilisation(run_dir, trace_us):
     M = 1 AWQ GEMV (pmc_gemv_{FETCH,WRITE}_SIZE, scaled like the GEMM's).
     trace_us: the hot-path trace's average durations per step kernel."""
     cmd = "python3 bench.py"
-    util = _counter_means(os.path.join(run_dir, "pmc_gemm_util"), "gemm_w4a4_int4")
-    ins = _counter_means(os.path.join(run_dir, "pmc_gemm_insts"), "gemm_w4a4_int4")
+    util = _counter_means(os.path.join(run_dir, "pmc_gemm_util"), DOM_KERNEL)
+    ins = _counter_means(os.path.join(run_dir, "pmc_gemm_insts"), DOM_KERNEL)
     M, N, K = TOKENS, 4 * HIDDEN, HIDDEN
     wave_groups = (M // 64) * (N // 64) * (K // 64)     # one wave: 64x64 outputs, one K-group of 64
-    t = ["# Matrix-core and vector-ALU use of the int4 W4A4 GEMM, DiT MLP up 4096x3072 -> 12288 (rank 32)",
+    t = ["# Matrix-core and vector-ALU use of the int4 W4A4 GEMM (FP6 layout), DiT MLP up 4096x3072 -> 12288 "
+         "(rank 32)",
          "# Commands (paths relative to the repository root; run with TMPDIR=/tmp):",
          f"#   rocprofv3 --pmc MfmaUtil VALUBusy -f csv -d {run_dir}/pmc_gemm_util -o run -- {cmd} "
          "--profile-kernel mlp_up.gemm_w4a4 --steps 5",
          f"#   rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU SQ_WAVES -f csv "
          f"-d {run_dir}/pmc_gemm_insts -o run -- {cmd} --profile-kernel mlp_up.gemm_w4a4 --steps 5",
+         f"#   rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_BUSY_CYCLES -f csv -d {run_dir}/pmc_gemm_clock -o run -- {cmd} "
+         "--profile-kernel mlp_up.gemm_w4a4 --steps 5",
          "# MfmaUtil = matrix-core busy cycles / (GPU active cycles x SIMDs); VALUBusy = vector-ALU",
          "# issue cycles / (GPU active cycles x CUs) (rocprofv3's derived metrics, in percent).",
          f"# Instruction counts are per launch, all waves; one wave-group = one wave's 64x64 outputs over",
-         f"# one K-group of 64 ({wave_groups} per launch).  Per wave-group the main loop issues 8",
-         "# v_mfma_i32_32x32x32_i8 (32 cycles each) and 1 v_mfma_f32_32x32x4_2b_bf16 (64 cycles) per",
-         "# pair of 32x32 tiles, i.e. 10 MFMAs = 384 matrix-core cycles, and the vector ALU 4 cycles per",
-         "# instruction.",
-         "# source_sha256 covers gemm_w4a4_int4.hip, gemm_common.h and device_common.h (in that order).",
+         f"# one K-group of 64 ({wave_groups} per launch).  Per wave-group the main loop issues 4",
+         "# v_mfma_scale_f32_32x32x64_f8f6f4 in FP6 form (32 cycles each, the integer products) and 4",
+         "# v_mfma_f32_32x32x16_bf16 (32 cycles each, the scale outer products), i.e. 8 MFMAs = 256",
+         "# matrix-core cycles, and 64 fma (acc += X * P) plus operand masks on the vector ALU, 4 cycles",
+         "# per instruction.  The clock: GRBM_GUI_ACTIVE cycles over the kernel's trace duration.",
+         "# source_sha256 covers gemm_w4a4_fp6.hip, gemm_common.h and device_common.h (in that order).",
          f"source_sha256: {gemm_int4_source_hash()}"]
     for c in ("MfmaUtil", "VALUBusy"):
         t.append(f"{c}_percent: {util[c][0]:.1f}  (mean of {util[c][1]} launches)")
@@ -543,6 +555,22 @@ def summarize_utilisation(run_dir, trace_us):
     v, m = ins["SQ_INSTS_VALU"][0] / wave_groups, ins["SQ_INSTS_MFMA"][0] / wave_groups
     t.append(f"valu_insts_per_wave_group: {v:.1f}  ({4 * v:.0f} vector-ALU cycles)")
     t.append(f"mfma_insts_per_wave_group: {m:.2f}")
+    clk_dir = os.path.join(run_dir, "pmc_gemm_clock")
+    if os.path.isdir(clk_dir):
+        import glob
+        per = {}
+        for f in glob.glob(os.path.join(clk_dir, "**", "*counter_collection.csv"), recursive=True):
+            for r in _csv_rows(f):
+                if DOM_KERNEL in r["Kernel_Name"] and r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                    per.setdefault(r["Dispatch_Id"], []).append(float(r["Counter_Value"]))
+        # one value per XCD (each counts the same GPU-active cycles): their mean
+        ga = float(np.mean([np.mean(v) for v in per.values()]))
+        inst = int(np.mean([len(v) for v in per.values()]))
+        us = trace_us["mlp_up.gemm_w4a4"]
+        t.append(f"GRBM_GUI_ACTIVE_per_launch: {int(ga)}  (mean of {inst} per-XCD values, {len(per)} launches)")
+        t.append(f"effective_clock_MHz: {ga / us:.0f}  (GRBM_GUI_ACTIVE / the trace's {us:.2f} us)")
+        t.append(f"cycles_per_wave_group_per_SIMD: {ga / (wave_groups / 1024):.0f}  "
+                 "(active cycles x 1024 SIMDs / wave-groups)")
     open(UTIL_FILE, "w").write("\n".join(t) + "\n")
 
     cf, _ = _counter_mean_kib(os.path.join(run_dir, "pmc_copy_FETCH_SIZE"), "copyBuffer")
@@ -672,15 +700,15 @@ def summarize_profiles(run_dir, warmup, steps):
 
     cf, _ = _counter_mean_kib(os.path.join(run_dir, "pmc_copy_FETCH_SIZE"), "copyBuffer")
     cw, _ = _counter_mean_kib(os.path.join(run_dir, "pmc_copy_WRITE_SIZE"), "copyBuffer")
-    gf, nf = _counter_mean_kib(os.path.join(run_dir, "pmc_gemm_FETCH_SIZE"), "gemm_w4a4_int4")
-    gw, nw = _counter_mean_kib(os.path.join(run_dir, "pmc_gemm_WRITE_SIZE"), "gemm_w4a4_int4")
+    gf, nf = _counter_mean_kib(os.path.join(run_dir, "pmc_gemm_FETCH_SIZE"), DOM_KERNEL)
+    gw, nw = _counter_mean_kib(os.path.join(run_dir, "pmc_gemm_WRITE_SIZE"), DOM_KERNEL)
     copy_kib = 256 * 1024
     ff, fw = copy_kib / cf, copy_kib / cw
     fetch, write = gf * 1024 * ff, gw * 1024 * fw
     alg = algorithmic_bytes_gemm(TOKENS, 4 * HIDDEN, HIDDEN, 32, "int4")
     out_b = TOKENS * 4 * HIDDEN * 2
     cmd = "python3 bench.py"
-    t = ["# HBM traffic of the int4 W4A4 GEMM, DiT MLP up 4096x3072 -> 12288 (rank 32), per launch",
+    t = ["# HBM traffic of the int4 W4A4 GEMM (FP6 layout), DiT MLP up 4096x3072 -> 12288 (rank 32), per launch",
          "# Commands (paths relative to the repository root; run with TMPDIR=/tmp):"]
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
         t.append(f"#   rocprofv3 --pmc {c} -f csv -d {run_dir}/pmc_gemm_{c} -o run -- {cmd} "
@@ -690,10 +718,11 @@ def summarize_profiles(run_dir, warmup, steps):
     t += ["# Calibration: a plain device copy of 256 MiB (torch copy_, dispatched as __amd_rocclr_copyBuffer)",
           f"#   reads FETCH_SIZE = {cf:.1f} KiB -> factor {ff:.4f};  WRITE_SIZE = {cw:.1f} KiB -> factor {fw:.4f}",
           f"# GEMM (mean of {nf} / {nw} launches): FETCH_SIZE = {gf:.1f} KiB, WRITE_SIZE = {gw:.1f} KiB",
-          f"# Algorithmic bytes per launch: {alg} (codes + scales of both operands, lora_act, lora_up, bf16 out)",
+          f"# Algorithmic bytes per launch: {alg} (FP6-layout codes (3/4 byte per code) + scales of both operands,",
+          "# lora_act, lora_up, bf16 out)",
           f"# Reads are {fetch / (alg - out_b):.2f}x the algorithmic input bytes; "
           f"writes are {write / out_b:.2f}x the {out_b / 1e6:.1f} MB output.",
-          "# source_sha256 covers gemm_w4a4_int4.hip, gemm_common.h and device_common.h (in that order).",
+          "# source_sha256 covers gemm_w4a4_fp6.hip, gemm_common.h and device_common.h (in that order).",
           f"source_sha256: {gemm_int4_source_hash()}",
           f"fetch_bytes_per_launch: {int(fetch)}",
           f"write_bytes_per_launch: {int(write)}",
@@ -852,8 +881,10 @@ def main():
         g["TOPS"] = round(ops / (g["us"] * 1e-6) / 1e12, 2)
         peak = PEAK_INT8_TOPS if prec == "int4" else PEAK_BF16_TFLOPS
         g["frac_peak"] = round(g["TOPS"] / peak, 4)
-        g["peak"] = ("fp8/int8 5000 TOPS (int4 codes as exact E4M3 values)" if prec == "int4"
+        g["peak"] = ("int8/fp8 5000 TOPS (int4 codes as exact E2M3 values on the FP6 MFMA)" if prec == "int4"
                      else "fp16 2500 TFLOP/s (exact NVFP4 path)")
+        if prec == "int4":
+            g["frac_fp6_rate"] = round(g["TOPS"] / PEAK_FP4_TFLOPS, 4)
         if prec == "nvfp4":
             g["frac_fp4_peak"] = round(g["TOPS"] / PEAK_FP4_TFLOPS, 4)
         q = kernels[f"{name}.quantize_act"]
@@ -870,7 +901,8 @@ def main():
     ops_up = 2.0 * TOKENS * 4 * HIDDEN * HIDDEN
     trace_us = recorded_trace_us()
     roofline = {"bound": "mfma",
-                "kernel": "svdq_gemm_w4a4 int4, packed weights on fp8 matrix cores (mlp_up 4096x3072->12288)",
+                "kernel": "svdq_gemm_w4a4 int4, both operands in the FP6 layout on the FP6 matrix-core rate "
+                          "(mlp_up 4096x3072->12288)",
                 "achieved": dom["TOPS"], "peak": PEAK_INT8_TOPS, "unit": "TOPS",
                 "frac": round(dom["TOPS"] / PEAK_INT8_TOPS, 4), "traffic": recorded_traffic(),
                 "algorithmic_ops": ops_up,
@@ -880,7 +912,10 @@ def main():
                          "between two HIP events on the launch stream",
                 "trace_avg_us": trace_us,
                 "frac_trace": None if trace_us is None else round(ops_up / (trace_us * 1e-6) / 1e12 /
-                                                                  PEAK_INT8_TOPS, 4)}
+                                                                  PEAK_INT8_TOPS, 4),
+                "peak_basis": "int8 dense 5000 TOPS, the peak the target is stated against; the products "
+                              "run as FP6 MFMAs, whose rate is 10100: frac_fp6_rate",
+                "frac_fp6_rate": round(dom["TOPS"] / PEAK_FP4_TFLOPS, 4)}
 
     gemv = None if args.no_gemv_sweep else gemv_sweep(torch, synth)
     fusion = None if args.no_gemv_sweep else gelu_fusion(torch, synth, layers)
@@ -891,7 +926,7 @@ def main():
     rec = {"metric": "W4A4 GEMM effective TOPS + % MFMA peak; W4A16 GEMV GB/s + % HBM peak",
            "value": round(value, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
-           "scaling": "weak", "vs_baseline": None, "dtype": "fp8", "data": "synthetic",
+           "scaling": "weak", "vs_baseline": None, "dtype": "fp6", "data": "synthetic",
            "launch": "stream launches; the same step as one HIP graph replay: %.4f ms/step" % graph_ms,
            "config": {"workload": "dit_block_1024px_quantized_linears", "tokens": TOKENS,
                       "hidden": HIDDEN,

@@ -19,13 +19,14 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "_lib", "libsvdq.so")
 
 SVDQ_OK, SVDQ_ERR_INVALID_ARG, SVDQ_ERR_UNSUPPORTED, SVDQ_ERR_HIP = 0, 1, 2, 3
-SVDQ_INT4, SVDQ_NVFP4, SVDQ_INT4_PACKED = 0, 1, 2
+SVDQ_INT4, SVDQ_NVFP4, SVDQ_INT4_PACKED, SVDQ_INT4_FP6 = 0, 1, 2, 3
 
 EXPORTED = ("svdq_quantize_act", "svdq_gelu_quantize_act", "svdq_gemm_w4a4", "svdq_gemm_w4a4_qk_norm_rope",
             "awq_gemv_w4a16",
             "svdq_smooth_factors", "svdq_quantize_weight", "svdq_lowrank_workspace_bytes",
             "svdq_lowrank_factors", "svdq_lowrank_factors_noalloc",
             "svdq_packed_weight_bytes", "svdq_pack_weight_int4", "svdq_debug_group_sums_packed",
+            "svdq_fp6_weight_bytes", "svdq_pack_weight_fp6", "svdq_debug_group_sums_fp6",
             "svdq_debug_group_sums", "svdq_debug_gelu_bf16", "svdq_debug_stream_read",
             "svdq_status_string", "svdq_last_error",
             "svdq_abi_version")
@@ -61,6 +62,10 @@ def lib() -> ctypes.CDLL:
         L.svdq_packed_weight_bytes.argtypes = [_I64, _I64]
         L.svdq_packed_weight_bytes.restype = _I64
         L.svdq_pack_weight_int4.argtypes = [_I64, _I64, _P, _P, _P, _P, _P]
+        L.svdq_debug_group_sums_fp6.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P]
+        L.svdq_fp6_weight_bytes.argtypes = [_I64, _I64]
+        L.svdq_fp6_weight_bytes.restype = _I64
+        L.svdq_pack_weight_fp6.argtypes = [_I64, _I64, _P, _P, _P]
         L.svdq_debug_gelu_bf16.argtypes = [_I64, _P, _P, _P]
         L.svdq_debug_stream_read.argtypes = [_P, _I64, _I32, _P, _P]
         L.svdq_smooth_factors.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P]
@@ -72,6 +77,7 @@ def lib() -> ctypes.CDLL:
         for f in ("svdq_quantize_act", "svdq_gelu_quantize_act", "svdq_gemm_w4a4",
                   "svdq_gemm_w4a4_qk_norm_rope", "awq_gemv_w4a16",
                   "svdq_debug_group_sums", "svdq_debug_group_sums_packed", "svdq_pack_weight_int4",
+                  "svdq_debug_group_sums_fp6", "svdq_pack_weight_fp6",
                   "svdq_debug_gelu_bf16", "svdq_debug_stream_read", "svdq_smooth_factors",
                   "svdq_quantize_weight", "svdq_lowrank_factors", "svdq_lowrank_factors_noalloc"):
             getattr(L, f).restype = ctypes.c_int
@@ -139,8 +145,8 @@ def svdq_gelu_quantize_act(precision, x, smooth, lora_down, act_codes, act_scale
 
 def _weight_shape(precision, wgt_codes, wgt_scales):
     """(N, K) of a layer's weight: from the codes [N, K/2], or for a packed
-    blob (one-dimensional) from the int4 scales [N, K/64]."""
-    if precision == SVDQ_INT4_PACKED:
+    blob or an FP6-layout weight from the int4 scales [N, K/64]."""
+    if precision in (SVDQ_INT4_PACKED, SVDQ_INT4_FP6):
         N, G = wgt_scales.shape
         return N, 64 * G
     N, Kh = wgt_codes.shape
@@ -164,6 +170,26 @@ def svdq_debug_group_sums_packed(act_codes, packed_weight, N, G, stream=None):
     M, Kh = act_codes.shape
     _check(lib().svdq_debug_group_sums_packed(M, N, 2 * Kh, _ptr(act_codes), _ptr(packed_weight), _ptr(G),
                                               _stream(stream)), "svdq_debug_group_sums_packed")
+
+
+def svdq_fp6_weight_bytes(N, K) -> int:
+    return int(lib().svdq_fp6_weight_bytes(N, K))
+
+
+def svdq_pack_weight_fp6(wgt_codes, fp6_weight, stream=None):
+    """Offline re-encoding of int4 weight codes [N, K/2] into the FP6 layout
+    [N, 3K/4] of the SVDQ_INT4_FP6 GEMM."""
+    N, Kh = wgt_codes.shape
+    _check(lib().svdq_pack_weight_fp6(N, 2 * Kh, _ptr(wgt_codes), _ptr(fp6_weight), _stream(stream)),
+           "svdq_pack_weight_fp6")
+
+
+def svdq_debug_group_sums_fp6(act_codes, fp6_weight, N, G, stream=None):
+    """Exact int32 group sums [M,N,K/64] on the FP6 GEMM's device path
+    (act_codes in the FP6 layout [M, 3K/4])."""
+    M, Kf = act_codes.shape
+    _check(lib().svdq_debug_group_sums_fp6(M, N, Kf * 4 // 3, _ptr(act_codes), _ptr(fp6_weight), _ptr(G),
+                                           _stream(stream)), "svdq_debug_group_sums_fp6")
 
 
 def svdq_gemm_w4a4(precision, act_codes, act_scales, wgt_codes, wgt_scales, alpha, lora_act,

@@ -18,6 +18,7 @@ struct QkNormRope {
     int qk_cols;           // 2 * heads * 128: the Q and K columns
 };
 
+// precision: 0 int4 (nibbles), 1 NVFP4, 2 int4 codes in the FP6 layout
 hipError_t launch_quantize_act(int precision, bool gelu, int M, int K, int rank, const void *x,
                                const void *smooth, const void *lora_down, void *act_codes,
                                void *act_scales, float *lora_act, hipStream_t stream);
@@ -46,6 +47,19 @@ hipError_t launch_gemm_w4a4_int4(bool packed, int M, int N, int K, int rank, con
 size_t packed_weight_bytes(int N, int K);
 hipError_t launch_pack_weight_int4(int N, int K, const void *wgt_codes, const void *wgt_scales, void *blob,
                                    int32_t *invalid, hipStream_t stream);
+// int4 GEMM on the FP6 layout of both operands (launch_pack_weight_fp6 for
+// the weight, the activation step's precision 2 for the activations)
+size_t fp6_weight_bytes(int N, int K);
+hipError_t launch_pack_weight_fp6(int N, int K, const void *wgt_codes, void *blob, hipStream_t stream);
+hipError_t launch_gemm_w4a4_fp6(int M, int N, int K, int rank, const void *act_codes, const void *act_scales,
+                                const void *wgt_codes, const void *wgt_scales, float alpha, const float *lora_act,
+                                const void *lora_up, const void *bias, void *out, hipStream_t stream);
+hipError_t launch_gemm_w4a4_fp6_qk(int M, int N, int K, int rank, const void *act_codes, const void *act_scales,
+                                   const void *wgt_codes, const void *wgt_scales, float alpha,
+                                   const float *lora_act, const void *lora_up, const void *bias,
+                                   const QkNormRope &qk, void *out, hipStream_t stream);
+hipError_t launch_group_sums_fp6(int M, int N, int K, const void *act_codes, const void *wgt_codes, int32_t *G,
+                                 hipStream_t stream);
 hipError_t launch_gemm_w4a4_nvfp4_qk(int M, int N, int K, int rank, const void *act_codes,
                                      const void *act_scales, const void *wgt_codes,
                                      const void *wgt_scales, float alpha, const float *lora_act,

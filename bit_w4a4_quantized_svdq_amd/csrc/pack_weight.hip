@@ -18,6 +18,7 @@
 //       product is exact in fp32; hi = RNE_bf16 of it, lo = RNE_bf16 of the
 //       remainder).
 // A code -8 has no sign-magnitude 4-bit form; it is written as -0 and counted.
+// The FP6 layout at the end of the file holds every code, -8 included.
 #include "device_common.h"
 #include "launch.h"
 
@@ -64,6 +65,63 @@ __global__ __launch_bounds__(256) void pack_int4_kernel(int N, int NG, const uin
     corr[g] = (uint16_t)hi;
     corr[NG + g] = (uint16_t)lo;
     if (bad && invalid) atomicAdd(invalid, bad);
+}
+
+// ---------------------------------------------------------------------------
+// FP6 layout of int4 codes (the FP6 GEMM's weight operand, the same layout as
+// the FP6 output of the activation step): per row n and group g a 48-byte
+// block at n * 48 * K/64 + 48 g holding two 192-bit strings, one per K-half
+// h, field j (bits 6j .. 6j+5) = E2M3 code of q[n, 64g + 32h + j] / 2; the
+// block's bytes are [h0 dwords 0-3 | h1 dwords 0-3 | h0 dwords 4-5 | h1
+// dwords 4-5].  Every code in [-8, 7] has an exact form: |q|/2 = 0, 0.5 (E2M3
+// subnormal 4/8), then 1 .. 4 in steps of 0.5 (normal, three mantissa bits).
+size_t fp6_weight_bytes(int N, int K) { return (size_t)N * (K / 64) * 48; }
+
+// E2M3 bits of |q| / 2 for |q| = 0 .. 8 (sign: bit 5)
+__constant__ uint8_t kE2M3Half[9] = {0, 4, 8, 12, 16, 18, 20, 22, 24};
+
+// one thread per (weight row, group of 64 codes)
+__global__ __launch_bounds__(256) void pack_fp6_kernel(int N, int NG, const uint8_t *__restrict__ codes,
+                                                       uint8_t *__restrict__ blob)
+{
+    const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (t >= (long long)N * NG) return;
+    const int n = (int)(t / NG), g = (int)(t % NG);
+    const size_t off = (size_t)n * NG * 32 + (size_t)g * 32;
+    const v4u d0 = *(const v4u *)(codes + off), d1 = *(const v4u *)(codes + off + 16);
+    const uint32_t in[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+    uint32_t dw[2][6];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        uint64_t bits[3] = {0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+            const int k = 32 * h + j;                                  // channel within the group
+            const int q = sext4(in[k >> 3] >> (4 * (k & 7)));
+            const uint64_t f = (uint64_t)(kE2M3Half[q < 0 ? -q : q] | (q < 0 ? 32u : 0u));
+            const int b = 6 * j;
+            bits[b >> 6] |= f << (b & 63);
+            if ((b & 63) > 58) bits[(b >> 6) + 1] |= f >> (64 - (b & 63));
+        }
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            dw[h][2 * i] = (uint32_t)bits[i];
+            dw[h][2 * i + 1] = (uint32_t)(bits[i] >> 32);
+        }
+    }
+    uint8_t *o = blob + ((size_t)n * NG + g) * 48;
+    *(v4u *)o = v4u{dw[0][0], dw[0][1], dw[0][2], dw[0][3]};
+    *(v4u *)(o + 16) = v4u{dw[1][0], dw[1][1], dw[1][2], dw[1][3]};
+    *(v4u *)(o + 32) = v4u{dw[0][4], dw[0][5], dw[1][4], dw[1][5]};
+}
+
+hipError_t launch_pack_weight_fp6(int N, int K, const void *wgt_codes, void *blob, hipStream_t stream)
+{
+    const int NG = K / 64;
+    const long long n = (long long)N * NG;
+    hipLaunchKernelGGL(pack_fp6_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, N, NG,
+                       (const uint8_t *)wgt_codes, (uint8_t *)blob);
+    return hipGetLastError();
 }
 
 hipError_t launch_pack_weight_int4(int N, int K, const void *wgt_codes, const void *wgt_scales, void *blob,

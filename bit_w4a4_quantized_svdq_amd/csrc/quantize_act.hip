@@ -38,6 +38,20 @@
 //    nearest value with ties to the even code.  v comes from the same Newton
 //    step; ties are exact and non-ties stay 2^-11 (relative) away.
 //
+// FP6 layout (PREC 2, int4 codes for the FP6 GEMM): the same codes q in
+// [-8, 7], written as E2M3 values q/2 (exact: every integer up to 8 has at
+// most three significant bits) in the operand layout of the gfx950 block-
+// scaled matrix instruction.  Per row and group of 64 a 48-byte block holds
+// two 192-bit strings, one per K-half h: field j (bits 6j .. 6j+5) is the
+// code of channel 32h + j.  Byte layout of the block: [h0 dwords 0-3 |
+// h1 dwords 0-3 | h0 dwords 4-5 | h1 dwords 4-5], so a GEMM lane reads its
+// 24 bytes as one 16-byte and one 8-byte piece.  A lane converts its 16
+// codes with one v_cvt_scalef32_2xpk16_fp6_f32 (two 16-value sources whose
+// fields interleave: field 2i from the first, 2i+1 from the second; the
+// scale divides, so 2.0 turns q into q/2), giving its 48 bits of each half;
+// two lane swaps (v_permlane16_swap, v_permlane32_swap) gather a whole half
+// string in each lane, and one store per lane writes a 16- or 8-byte piece.
+//
 // GELU variant (a layer fed by a GELU MLP's up projection): x is first
 // mapped through GELU (tanh form) of bf16 to bf16, exact by construction
 // (gelu_bf16.h: a 9.5 KB LDS table each block fills in fp64, plus exact rules
@@ -126,6 +140,65 @@ __device__ __noinline__ v2u int4_codes_exact(F16 xh, float sb) {
         word[e >> 3] |= nib << (4 * (e & 7));
     }
     return word;
+}
+
+// The int4 codes of a group whose bf16 scale is tiny or zero, as floats:
+// IEEE division, rounded to the nearest integer (ties to even), clamped.
+__device__ __noinline__ F16 int4_q_exact(F16 xh, float sb) {
+    F16 q;
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+        q.v[e] = sb == 0.0f ? 0.0f : __builtin_amdgcn_fmed3f(__builtin_rintf(xh.v[e] / sb), -8.0f, 7.0f);
+    return q;
+}
+
+typedef float v16f_q __attribute__((ext_vector_type(16)));
+
+// The 16 codes of one lane (q[0..7]: channels 8kq..8kq+7 of the group's
+// first K-half, q[8..15]: the same of the second), integers in [-8, 7] held
+// as floats, into the group's 48-byte FP6 block.  Lanes kq = 0..3 of a row
+// are lanes r + 16 kq; every lane of the wave takes part (the swaps are
+// wave-wide), only lanes with store set write.
+__device__ __forceinline__ void store_fp6_group(const float (&q)[16], uint8_t *blk, bool store, int kq) {
+    v16f_q a, b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        a[i] = q[2 * i];
+        b[i] = q[2 * i + 1];
+        a[8 + i] = 0.0f;
+        b[8 + i] = 0.0f;
+    }
+    // fields 2i = a[i], 2i+1 = b[i]: fields 0..7 = q[0..7], 8..15 = q[8..15], values q/2
+    const auto f = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(a, b, 2.0f);
+    const uint32_t f0 = f[0], f1 = f[1], f2 = f[2];
+    // this lane's 48 bits of each half: X (first half), Y (second half)
+    uint32_t x0 = f0, x1 = f1 & 0xFFFFu;
+    uint32_t y0 = (f1 >> 16) | (f2 << 16), y1 = f2 >> 16;
+    // rows 1, 3 of 16 lanes (kq odd) swap X with rows 0, 2 (kq even) swapping
+    // Y: kq even then holds (own X, partner's X) = 96 bits of the first half,
+    // kq odd (partner's Y, own Y) = 96 bits of the second
+    {
+        const auto s0 = __builtin_amdgcn_permlane16_swap(x0, y0, false, false);
+        const auto s1 = __builtin_amdgcn_permlane16_swap(x1, y1, false, false);
+        x0 = s0[0]; y0 = s0[1];
+        x1 = s1[0]; y1 = s1[1];
+    }
+    uint32_t v[3] = {x0, (x1 & 0xFFFFu) | (y0 << 16), (y0 >> 16) | (y1 << 16)};
+    // kq 0, 1 hold bits 0..95 of their half, kq 2, 3 bits 96..191: the upper
+    // 32 lanes swap with the lower 32, after which every lane has the whole
+    // 192-bit string of its half as (first, second) = (d, s)
+    uint32_t d[3], sr[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        const auto w = __builtin_amdgcn_permlane32_swap(v[i], v[i], false, false);
+        d[i] = w[0];
+        sr[i] = w[1];
+    }
+    if (store) {
+        const int half = kq & 1;
+        if (kq < 2) *(v4u *)(blk + 16 * half) = v4u{d[0], d[1], d[2], sr[0]};
+        else *(v2u *)(blk + 32 + 8 * half) = v2u{sr[1], sr[2]};
+    }
 }
 
 template <int PREC, int RT, bool GELU>
@@ -243,7 +316,39 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
                 }
             }
 
-            if constexpr (PREC == 0) {
+            if constexpr (PREC == 2) {
+                // ---- int4 codes in the FP6 layout: the same scale and codes
+                amax = fmaxf(amax_j[0], amax_j[1]);
+                amax = fmaxf(amax, shfl_xor_f(amax, 16));
+                amax = fmaxf(amax, shfl_xor_f(amax, 32));
+                const float s_f = amax * (1.0f / 7.0f);
+                const uint32_t sbits = f32_to_bf16_rne(s_f);
+                const float sb = __uint_as_float(sbits << 16);
+                float q[16];
+                if (__builtin_expect(__any(sb < 0x1p-100f), 0)) {
+                    F16 xv;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) xv.v[e] = xh[e];
+                    const F16 qe = int4_q_exact(xv, sb);
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) q[e] = qe.v[e];
+                } else {
+                    const float inv_s = __builtin_amdgcn_rcpf(sb);
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const float xv = xh[e];
+                        const float qe = xv * inv_s;
+                        const float rr = __builtin_fmaf(-qe, sb, xv);
+                        const float qc = __builtin_fmaf(rr, inv_s, qe);
+                        q[e] = __builtin_rintf(__builtin_amdgcn_fmed3f(qc, -8.0f, 7.0f));
+                    }
+                }
+                // a zero code is +0 in the layout (rint keeps the sign of -0.4)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) q[e] += 0.0f;
+                store_fp6_group(q, codes + (size_t)min(row, M - 1) * (size_t)(48 * NG) + g * 48, row_ok, kq);
+                if (row_ok && kq == 0) ((uint16_t *)scales)[(size_t)row * NG + g] = (uint16_t)sbits;
+            } else if constexpr (PREC == 0) {
                 // ---- int4, group 64: absmax over the row's 4 lanes
                 amax = fmaxf(amax_j[0], amax_j[1]);
                 amax = fmaxf(amax, shfl_xor_f(amax, 16));
@@ -439,6 +544,9 @@ hipError_t launch_quantize_act(int precision, bool gelu, int M, int K, int rank,
     if (precision == 0)
         return gelu ? launch_prec<0, true>(M, K, rank, x, smooth, lora_down, act_codes, act_scales, lora_act, stream)
                     : launch_prec<0, false>(M, K, rank, x, smooth, lora_down, act_codes, act_scales, lora_act, stream);
+    if (precision == 2)
+        return gelu ? launch_prec<2, true>(M, K, rank, x, smooth, lora_down, act_codes, act_scales, lora_act, stream)
+                    : launch_prec<2, false>(M, K, rank, x, smooth, lora_down, act_codes, act_scales, lora_act, stream);
     return gelu ? launch_prec<1, true>(M, K, rank, x, smooth, lora_down, act_codes, act_scales, lora_act, stream)
                 : launch_prec<1, false>(M, K, rank, x, smooth, lora_down, act_codes, act_scales, lora_act, stream);
 }

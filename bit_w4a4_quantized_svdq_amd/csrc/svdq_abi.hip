@@ -93,8 +93,9 @@ static svdq_status quantize_act_common(bool gelu, const char *name, int32_t prec
                                        const void *lora_down, void *act_codes, void *act_scales,
                                        float *lora_act, void *stream)
 {
-    if (precision != SVDQ_INT4 && precision != SVDQ_NVFP4)
-        return fail(SVDQ_ERR_UNSUPPORTED, "precision must be SVDQ_INT4 or SVDQ_NVFP4 (got %d)", precision);
+    if (precision != SVDQ_INT4 && precision != SVDQ_NVFP4 && precision != SVDQ_INT4_FP6)
+        return fail(SVDQ_ERR_UNSUPPORTED, "precision must be SVDQ_INT4, SVDQ_NVFP4 or SVDQ_INT4_FP6 (got %d)",
+                    precision);
     SVDQ_TRY(check_shape(M, 1, K, rank));
     SVDQ_TRY(check_ptr(x, "x", false));
     SVDQ_TRY(check_ptr(smooth, "smooth", true));
@@ -104,7 +105,8 @@ static svdq_status quantize_act_common(bool gelu, const char *name, int32_t prec
     SVDQ_TRY(check_ptr(lora_act, "lora_act", rank == 0));
     if (M == 0) return SVDQ_OK;
     SVDQ_TRY(check_device());
-    return launched(svdq::launch_quantize_act(precision, gelu, (int)M, (int)K, rank, x, smooth, lora_down,
+    const int kernel_prec = precision == SVDQ_INT4_FP6 ? 2 : precision;
+    return launched(svdq::launch_quantize_act(kernel_prec, gelu, (int)M, (int)K, rank, x, smooth, lora_down,
                                               act_codes, act_scales, lora_act, (hipStream_t)stream),
                     name);
 }
@@ -236,9 +238,10 @@ svdq_status svdq_gemm_w4a4_qk_norm_rope(int32_t precision, int64_t M, int64_t N,
                                         const float *rope_cos, const float *rope_sin, void *out,
                                         void *stream)
 {
-    if (precision != SVDQ_INT4 && precision != SVDQ_NVFP4 && precision != SVDQ_INT4_PACKED)
+    if (precision != SVDQ_INT4 && precision != SVDQ_NVFP4 && precision != SVDQ_INT4_PACKED &&
+        precision != SVDQ_INT4_FP6)
         return fail(SVDQ_ERR_UNSUPPORTED,
-                    "precision must be SVDQ_INT4, SVDQ_NVFP4 or SVDQ_INT4_PACKED (got %d)", precision);
+                    "precision must be SVDQ_INT4, SVDQ_NVFP4, SVDQ_INT4_PACKED or SVDQ_INT4_FP6 (got %d)", precision);
     SVDQ_TRY(check_shape(M, N, K, rank));
     if (N % 384 != 0)
         return fail(SVDQ_ERR_INVALID_ARG, "N must be 3 * heads * 128 (got %lld)", (long long)N);
@@ -266,7 +269,10 @@ svdq_status svdq_gemm_w4a4_qk_norm_rope(int32_t precision, int64_t M, int64_t N,
     qk.sin = rope_sin;
     qk.eps = eps;
     qk.qk_cols = (int)(2 * (N / 3));
-    const hipError_t e = precision != SVDQ_NVFP4
+    const hipError_t e = precision == SVDQ_INT4_FP6
+        ? svdq::launch_gemm_w4a4_fp6_qk((int)M, (int)N, (int)K, rank, act_codes, act_scales, wgt_codes, wgt_scales,
+                                        alpha, lora_act, lora_up, bias, qk, out, (hipStream_t)stream)
+        : precision != SVDQ_NVFP4
         ? svdq::launch_gemm_w4a4_int4_qk(precision == SVDQ_INT4_PACKED, (int)M, (int)N, (int)K, rank, act_codes,
                                          act_scales, wgt_codes, wgt_scales, alpha, lora_act, lora_up, bias, qk, out,
                                          (hipStream_t)stream)
@@ -280,9 +286,10 @@ svdq_status svdq_gemm_w4a4(int32_t precision, int64_t M, int64_t N, int64_t K, i
                            const void *wgt_scales, float alpha, const float *lora_act,
                            const void *lora_up, const void *bias, void *out, void *stream)
 {
-    if (precision != SVDQ_INT4 && precision != SVDQ_NVFP4 && precision != SVDQ_INT4_PACKED)
+    if (precision != SVDQ_INT4 && precision != SVDQ_NVFP4 && precision != SVDQ_INT4_PACKED &&
+        precision != SVDQ_INT4_FP6)
         return fail(SVDQ_ERR_UNSUPPORTED,
-                    "precision must be SVDQ_INT4, SVDQ_NVFP4 or SVDQ_INT4_PACKED (got %d)", precision);
+                    "precision must be SVDQ_INT4, SVDQ_NVFP4, SVDQ_INT4_PACKED or SVDQ_INT4_FP6 (got %d)", precision);
     SVDQ_TRY(check_shape(M, N, K, rank));
     SVDQ_TRY(check_ptr(act_codes, "act_codes", false));
     SVDQ_TRY(check_ptr(act_scales, "act_scales", false));
@@ -295,7 +302,10 @@ svdq_status svdq_gemm_w4a4(int32_t precision, int64_t M, int64_t N, int64_t K, i
     if (M == 0 || N == 0) return SVDQ_OK;
     SVDQ_TRY(check_grid(M, N, 128, 128));
     SVDQ_TRY(check_device());
-    hipError_t e = precision != SVDQ_NVFP4
+    hipError_t e = precision == SVDQ_INT4_FP6
+        ? svdq::launch_gemm_w4a4_fp6((int)M, (int)N, (int)K, rank, act_codes, act_scales, wgt_codes, wgt_scales,
+                                     alpha, lora_act, lora_up, bias, out, (hipStream_t)stream)
+        : precision != SVDQ_NVFP4
         ? svdq::launch_gemm_w4a4_int4(precision == SVDQ_INT4_PACKED, (int)M, (int)N, (int)K, rank, act_codes,
                                       act_scales, wgt_codes, wgt_scales, alpha, lora_act, lora_up, bias, out,
                                       (hipStream_t)stream)
@@ -328,31 +338,57 @@ svdq_status awq_gemv_w4a16(int64_t M, int64_t N, int64_t K, int32_t group_size, 
     return launched(e, "awq_gemv_w4a16");
 }
 
-static svdq_status group_sums_common(bool packed, const char *name, int64_t M, int64_t N, int64_t K,
+// layout: 0 nibbles, 1 packed weight (fp8 formulation), 2 FP6 layout of both operands
+static svdq_status group_sums_common(int layout, const char *name, int64_t M, int64_t N, int64_t K,
                                      const void *act_codes, const void *wgt_codes, int32_t *G, void *stream)
 {
     SVDQ_TRY(check_shape(M, N, K, 0));
     SVDQ_TRY(check_ptr(act_codes, "act_codes", false));
-    SVDQ_TRY(check_ptr(wgt_codes, packed ? "packed_weight" : "wgt_codes", false));
+    SVDQ_TRY(check_ptr(wgt_codes, layout == 1 ? "packed_weight" : layout == 2 ? "fp6_weight" : "wgt_codes", false));
     SVDQ_TRY(check_ptr(G, "G", false));
     if (M == 0 || N == 0) return SVDQ_OK;
     SVDQ_TRY(check_grid(M, N, 128, 128));
     SVDQ_TRY(check_device());
-    return launched(svdq::launch_group_sums_int4(packed, (int)M, (int)N, (int)K, act_codes, wgt_codes, G,
-                                                 (hipStream_t)stream),
-                    name);
+    const hipError_t e = layout == 2
+        ? svdq::launch_group_sums_fp6((int)M, (int)N, (int)K, act_codes, wgt_codes, G, (hipStream_t)stream)
+        : svdq::launch_group_sums_int4(layout == 1, (int)M, (int)N, (int)K, act_codes, wgt_codes, G,
+                                       (hipStream_t)stream);
+    return launched(e, name);
 }
 
 svdq_status svdq_debug_group_sums(int64_t M, int64_t N, int64_t K, const void *act_codes,
                                   const void *wgt_codes, int32_t *G, void *stream)
 {
-    return group_sums_common(false, "svdq_debug_group_sums", M, N, K, act_codes, wgt_codes, G, stream);
+    return group_sums_common(0, "svdq_debug_group_sums", M, N, K, act_codes, wgt_codes, G, stream);
 }
 
 svdq_status svdq_debug_group_sums_packed(int64_t M, int64_t N, int64_t K, const void *act_codes,
                                          const void *packed_weight, int32_t *G, void *stream)
 {
-    return group_sums_common(true, "svdq_debug_group_sums_packed", M, N, K, act_codes, packed_weight, G, stream);
+    return group_sums_common(1, "svdq_debug_group_sums_packed", M, N, K, act_codes, packed_weight, G, stream);
+}
+
+svdq_status svdq_debug_group_sums_fp6(int64_t M, int64_t N, int64_t K, const void *act_codes,
+                                      const void *fp6_weight, int32_t *G, void *stream)
+{
+    return group_sums_common(2, "svdq_debug_group_sums_fp6", M, N, K, act_codes, fp6_weight, G, stream);
+}
+
+int64_t svdq_fp6_weight_bytes(int64_t N, int64_t K)
+{
+    if (check_shape(1, N, K, 0) != SVDQ_OK) return -1;
+    return (int64_t)svdq::fp6_weight_bytes((int)N, (int)K);
+}
+
+svdq_status svdq_pack_weight_fp6(int64_t N, int64_t K, const void *wgt_codes, void *fp6_weight, void *stream)
+{
+    SVDQ_TRY(check_shape(1, N, K, 0));
+    SVDQ_TRY(check_ptr(wgt_codes, "wgt_codes", false));
+    SVDQ_TRY(check_ptr(fp6_weight, "fp6_weight", false));
+    if (N == 0) return SVDQ_OK;
+    SVDQ_TRY(check_device());
+    return launched(svdq::launch_pack_weight_fp6((int)N, (int)K, wgt_codes, fp6_weight, (hipStream_t)stream),
+                    "svdq_pack_weight_fp6");
 }
 
 int64_t svdq_packed_weight_bytes(int64_t N, int64_t K)
@@ -401,6 +437,6 @@ const char *svdq_status_string(svdq_status s)
 
 const char *svdq_last_error(void) { return g_last_error; }
 
-int32_t svdq_abi_version(void) { return 8; }
+int32_t svdq_abi_version(void) { return 9; }
 
 }  // extern "C"

@@ -39,26 +39,45 @@ def pack_weight_int4(wgt_codes, wgt_scales):
     return blob
 
 
+def pack_weight_fp6(wgt_codes):
+    """Device int4 codes [N, K/2] -> their FP6 layout [N, 3K/4] (the weight
+    operand of the SVDQ_INT4_FP6 GEMM)."""
+    N, Kh = wgt_codes.shape
+    out = torch.empty((N, 3 * Kh // 2), dtype=torch.uint8, device=wgt_codes.device)
+    capi.svdq_pack_weight_fp6(wgt_codes, out)
+    return out
+
+
 class SVDQW4A4Linear:
     """y = alpha * Q(x/s) . Q(R)^T + (x/s . L1^T) . L2^T + bias  (bf16 out).
 
     precision: "int4" (group 64, bf16 scales) or "nvfp4" (group 16, E4M3).
-    packed (int4): the weight is re-encoded once, at construction, into the
-    packed form of svdq_pack_weight_int4, and the GEMM takes the
-    SVDQ_INT4_PACKED path (same results within the output tolerance; codes of
-    -8, which the group quantizer never produces, are refused)."""
+    int4_layout (int4 only), how the codes reach the GEMM (same codes, scales
+    and results within the output tolerance):
+      "fp6"    both operands in the FP6 layout (SVDQ_INT4_FP6; the weight is
+               re-encoded once, at construction) -- the fastest path;
+      "packed" the weight re-encoded by svdq_pack_weight_int4
+               (SVDQ_INT4_PACKED; codes of -8, which the group quantizer
+               never produces, are refused);
+      "plain"  packed nibbles on both sides (SVDQ_INT4)."""
 
     def __init__(self, precision, wgt_codes, wgt_scales, lora_down, lora_up, smooth=None,
-                 bias=None, alpha=1.0, device="cuda", packed=True):
+                 bias=None, alpha=1.0, device="cuda", int4_layout="fp6"):
         self.prec = capi.SVDQ_INT4 if precision == "int4" else capi.SVDQ_NVFP4
         self.group = 64 if self.prec == capi.SVDQ_INT4 else 16
         self.wgt_codes = _dev(wgt_codes, torch.uint8, device)
         sdt = torch.bfloat16 if self.prec == capi.SVDQ_INT4 else torch.uint8
         self.wgt_scales = _dev(wgt_scales, sdt, device)
-        self.gemm_prec = self.prec
-        if packed and self.prec == capi.SVDQ_INT4:
-            self.wgt_codes = pack_weight_int4(self.wgt_codes, self.wgt_scales)
-            self.gemm_prec = capi.SVDQ_INT4_PACKED
+        self.gemm_prec = self.act_prec = self.prec
+        if self.prec == capi.SVDQ_INT4:
+            if int4_layout == "fp6":
+                self.wgt_codes = pack_weight_fp6(self.wgt_codes)
+                self.gemm_prec = self.act_prec = capi.SVDQ_INT4_FP6
+            elif int4_layout == "packed":
+                self.wgt_codes = pack_weight_int4(self.wgt_codes, self.wgt_scales)
+                self.gemm_prec = capi.SVDQ_INT4_PACKED
+            elif int4_layout != "plain":
+                raise ValueError(f"int4_layout must be 'fp6', 'packed' or 'plain' (got {int4_layout!r})")
         self.lora_down = _dev(lora_down, torch.bfloat16, device)
         self.lora_up = _dev(lora_up, torch.bfloat16, device)
         self.smooth = _dev(smooth, torch.bfloat16, device)
@@ -75,7 +94,8 @@ class SVDQW4A4Linear:
         if b is None:
             d = self.device
             sdt = torch.bfloat16 if self.prec == capi.SVDQ_INT4 else torch.uint8
-            b = {"codes": torch.empty((M, self.K // 2), dtype=torch.uint8, device=d),
+            cb = 3 * self.K // 4 if self.act_prec == capi.SVDQ_INT4_FP6 else self.K // 2
+            b = {"codes": torch.empty((M, cb), dtype=torch.uint8, device=d),
                  "scales": torch.empty((M, self.K // self.group), dtype=sdt, device=d),
                  "lora_act": torch.empty((M, max(self.rank, 1)), dtype=torch.float32, device=d),
                  "out": torch.empty((M, self.N), dtype=torch.bfloat16, device=d)}
@@ -86,7 +106,7 @@ class SVDQW4A4Linear:
         """The activation step into the buffers ``b``; with ``gelu`` x is the
         preceding GELU MLP up projection's output and GELU runs inside the step."""
         fn = capi.svdq_gelu_quantize_act if gelu else capi.svdq_quantize_act
-        fn(self.prec, x, self.smooth, self.lora_down, b["codes"], b["scales"],
+        fn(self.act_prec, x, self.smooth, self.lora_down, b["codes"], b["scales"],
            b["lora_act"] if self.rank else None)
 
     def gemm(self, b):

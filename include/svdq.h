@@ -56,11 +56,24 @@ typedef enum svdq_status {
 
 /* precision of the W4A4 layer ("Supported quantization types" table).
  * SVDQ_INT4_PACKED is int4 with the weight in the packed form written by
- * svdq_pack_weight_int4 (the GEMM's fast path); its activations are int4's. */
+ * svdq_pack_weight_int4; its activations are int4's.  SVDQ_INT4_FP6 is int4
+ * (the same codes and scales) with both operands' codes in the FP6 layout:
+ * the activations from svdq_quantize_act / svdq_gelu_quantize_act called
+ * with SVDQ_INT4_FP6, the weight from svdq_pack_weight_fp6 (the GEMM's
+ * fastest path).
+ *
+ * FP6 layout of int4 codes ([rows, 3K/4] bytes): per row and group of 64 a
+ * 48-byte block (group g at byte 48g of the row) holding two 192-bit strings,
+ * one per half h of the group; field j of a string (bits 6j .. 6j+5) is the
+ * E2M3 encoding (sign bit 5, two exponent bits with bias 1, three mantissa
+ * bits) of q/2 for channel 64g + 32h + j, exact for every q in [-8, 7].  The
+ * block's 32-bit words are [h0 words 0-3 | h1 words 0-3 | h0 words 4-5 |
+ * h1 words 4-5], bits numbered from the least significant bit of word 0. */
 enum {
     SVDQ_INT4 = 0 /* group 64, bf16 scales */,
     SVDQ_NVFP4 = 1 /* group 16, E4M3 scales */,
-    SVDQ_INT4_PACKED = 2 /* int4, weight from svdq_pack_weight_int4 (GEMM calls only) */
+    SVDQ_INT4_PACKED = 2 /* int4, weight from svdq_pack_weight_int4 (GEMM calls only) */,
+    SVDQ_INT4_FP6 = 3 /* int4, codes of both operands in the FP6 layout */
 };
 
 /*
@@ -75,11 +88,12 @@ enum {
  * ("SVDQuant and the Nunchaku engine").  Codes and scales are bit-exact
  * against the rule above; lora_act is an fp32 sum in unspecified order.
  *
- *   precision  SVDQ_INT4 or SVDQ_NVFP4
+ *   precision  SVDQ_INT4, SVDQ_NVFP4 or SVDQ_INT4_FP6 (int4's codes and
+ *              scales, the codes written in the FP6 layout)
  *   x          bf16 [M, K]
  *   smooth     bf16 [K] smoothing factors; NULL means 1
  *   lora_down  bf16 [rank, K]; ignored (may be NULL) when rank == 0
- *   act_codes  out: u8 [M, K/2]
+ *   act_codes  out: u8 [M, K/2]; SVDQ_INT4_FP6: u8 [M, 3K/4] (FP6 layout)
  *   act_scales out: int4 bf16 [M, K/64]; nvfp4 u8 (E4M3) [M, K/16]
  *   lora_act   out: fp32 [M, rank]; ignored (may be NULL) when rank == 0
  */
@@ -112,12 +126,15 @@ svdq_status svdq_gelu_quantize_act(int32_t precision, int64_t M, int64_t K, int3
  *                      + sum_j lora_act[m,j] * lora_up[n,j] + bias[n] )
  * deq is code * group scale.  The sum is fp32 in unspecified order.
  *
- *   precision  SVDQ_INT4, SVDQ_NVFP4 or SVDQ_INT4_PACKED (the activations
- *              then come from svdq_quantize_act with SVDQ_INT4)
+ *   precision  SVDQ_INT4, SVDQ_NVFP4, SVDQ_INT4_PACKED (the activations
+ *              then come from svdq_quantize_act with SVDQ_INT4) or
+ *              SVDQ_INT4_FP6 (activations from svdq_quantize_act with
+ *              SVDQ_INT4_FP6)
  *   act_codes, act_scales  as written by svdq_quantize_act ([M, ...])
  *   wgt_codes  u8 [N, K/2] (int4 or E2M1 codes of the 4-bit residual);
  *              SVDQ_INT4_PACKED: the svdq_pack_weight_int4 blob of them
- *              (svdq_packed_weight_bytes(N, K) bytes)
+ *              (svdq_packed_weight_bytes(N, K) bytes); SVDQ_INT4_FP6: the
+ *              svdq_pack_weight_fp6 form (u8 [N, 3K/4])
  *   wgt_scales int4 bf16 [N, K/64]; nvfp4 u8 (E4M3) [N, K/16]
  *   alpha      scale of the 4-bit term (per-tensor; 1.0f for int4)
  *   lora_act   fp32 [M, rank]; lora_up bf16 [N, rank]; ignored when rank == 0
@@ -142,7 +159,7 @@ svdq_status svdq_gemm_w4a4(int32_t precision, int64_t M, int64_t N, int64_t K, i
  *   out_2i   = RNE_bf16( n_2i cos[m,i] - n_2i+1 sin[m,i] )
  *   out_2i+1 = RNE_bf16( n_2i+1 cos[m,i] + n_2i sin[m,i] ),   i < 64,
  * computed in fp32; V columns are y.  Arguments as for svdq_gemm_w4a4, plus:
- *   precision      SVDQ_INT4 or SVDQ_NVFP4
+ *   precision      SVDQ_INT4, SVDQ_NVFP4, SVDQ_INT4_PACKED or SVDQ_INT4_FP6
  *   N              a multiple of 384
  *   q_norm_weight  bf16 [128]; k_norm_weight bf16 [128]
  *   eps            finite, >= 0
@@ -276,6 +293,20 @@ svdq_status svdq_pack_weight_int4(int64_t N, int64_t K, const void *wgt_codes, c
                                   void *packed_weight, int32_t *invalid_codes, void *stream);
 
 /*
+ * svdq_pack_weight_fp6 -- offline re-encoding of an int4 weight for the
+ * SVDQ_INT4_FP6 GEMM: the codes in the FP6 layout (see the precision enum).
+ * gfx950's block-scaled matrix instruction takes E2M3 operands at twice its
+ * FP8 rate and returns fp32, and every int4 code is an exact E2M3 value
+ * (q/2), so the GEMM feeds both operands to the matrix cores as they are
+ * stored.  Every code, -8 included, has an exact form.
+ *   wgt_codes   u8 [N, K/2] two's complement int4 codes (svdq_gemm_w4a4's)
+ *   fp6_weight  out: u8 [N, 3K/4] = svdq_fp6_weight_bytes(N, K) bytes, device
+ * The weight's scales stay a separate argument of the GEMM.
+ */
+int64_t svdq_fp6_weight_bytes(int64_t N, int64_t K);   /* 3*N*K/4; -1 if invalid */
+svdq_status svdq_pack_weight_fp6(int64_t N, int64_t K, const void *wgt_codes, void *fp6_weight, void *stream);
+
+/*
  * svdq_debug_group_sums -- test hook on the int4 GEMM's own device code
  * path (operand unpacking and integer matrix-core products): writes the
  * exact integer group sums
@@ -293,6 +324,15 @@ svdq_status svdq_debug_group_sums(int64_t M, int64_t N, int64_t K, const void *a
  */
 svdq_status svdq_debug_group_sums_packed(int64_t M, int64_t N, int64_t K, const void *act_codes,
                                          const void *packed_weight, int32_t *G, void *stream);
+
+/*
+ * svdq_debug_group_sums_fp6 -- the same integer group sums G [M, N, K/64]
+ * from the main loop of the SVDQ_INT4_FP6 GEMM (E2M3 matrix-core products):
+ * act_codes in the FP6 layout (svdq_quantize_act with SVDQ_INT4_FP6),
+ * fp6_weight from svdq_pack_weight_fp6.
+ */
+svdq_status svdq_debug_group_sums_fp6(int64_t M, int64_t N, int64_t K, const void *act_codes,
+                                      const void *fp6_weight, int32_t *G, void *stream);
 
 /*
  * svdq_debug_gelu_bf16 -- test hook on the GELU of svdq_gelu_quantize_act
@@ -323,12 +363,14 @@ const char *svdq_status_string(svdq_status s);
 /* Text of the last argument-check failure on the calling thread ("" if none). */
 const char *svdq_last_error(void);
 
-/* ABI version of this header: 8 (1 plus svdq_gelu_quantize_act, svdq_debug_gelu_bf16,
+/* ABI version of this header: 9 (1 plus svdq_gelu_quantize_act, svdq_debug_gelu_bf16,
  * svdq_gemm_w4a4_qk_norm_rope, svdq_smooth_factors, svdq_quantize_weight,
  * svdq_lowrank_workspace_bytes, svdq_lowrank_factors,
  * svdq_lowrank_factors_noalloc, then SVDQ_INT4_PACKED with
  * svdq_packed_weight_bytes, svdq_pack_weight_int4 and
- * svdq_debug_group_sums_packed, then svdq_debug_stream_read). */
+ * svdq_debug_group_sums_packed, then svdq_debug_stream_read, then
+ * SVDQ_INT4_FP6 with svdq_fp6_weight_bytes, svdq_pack_weight_fp6 and
+ * svdq_debug_group_sums_fp6). */
 int32_t svdq_abi_version(void);
 
 #ifdef __cplusplus

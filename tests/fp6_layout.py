@@ -1,0 +1,91 @@
+"""Host-side FP6 layout of int4 codes, written from its definition in
+include/svdq.h (the precision enum): per row and group of 64 a 48-byte
+block of two 192-bit strings, one per half h of the group; field j (bits
+6j .. 6j+5) is the E2M3 encoding of q/2 for channel 64g + 32h + j; the
+block's 32-bit words are [h0 0-3 | h1 0-3 | h0 4-5 | h1 4-5].
+
+E2M3 (the OCP microscaling FP6 format): sign bit 5, exponent bits 3-4 with
+bias 1, mantissa bits 0-2; exponent 0 encodes the subnormals m/8, exponent
+e > 0 the value 2^(e-1) * (1 + m/8).  This module is test infrastructure:
+the tests compare the library's FP6 encoders (the activation step's and the
+weight packer's) with it, and feed the FP6 GEMM from it."""
+from __future__ import annotations
+
+import numpy as np
+
+
+def e2m3_value(f):
+    """Value of 6-bit E2M3 codes (array of ints)."""
+    f = np.asarray(f, np.int64)
+    s = np.where(f & 32, -1.0, 1.0)
+    e, m = (f >> 3) & 3, f & 7
+    mag = np.where(e == 0, m / 8.0, np.ldexp(1.0 + m / 8.0, e - 1))
+    return s * mag
+
+
+def e2m3_encode(v):
+    """E2M3 code of values that the format holds exactly (raises otherwise)."""
+    v = np.asarray(v, np.float64)
+    table = {float(e2m3_value(f)): f for f in range(64) if not (f == 32)}   # -0 -> +0
+    out = np.empty(v.shape, np.int64)
+    for idx, x in np.ndenumerate(v):
+        if float(x) not in table:
+            raise ValueError(f"{x} is not an E2M3 value")
+        out[idx] = table[float(x)]
+    return out
+
+
+def _strings_to_block(fields):
+    """fields [..., 2, 32] (half, field) -> 48 bytes per block [..., 48]."""
+    lead = fields.shape[:-2]
+    words = np.zeros(lead + (2, 6), np.uint64)
+    for j in range(32):
+        b = 6 * j
+        f = fields[..., j].astype(np.uint64)
+        w, o = b // 32, b % 32
+        words[..., w] |= (f << np.uint64(o)) & np.uint64(0xFFFFFFFF)
+        if o > 26:
+            words[..., w + 1] |= f >> np.uint64(32 - o)
+    words = words.astype(np.uint32)
+    order = np.concatenate([words[..., 0, 0:4], words[..., 1, 0:4], words[..., 0, 4:6], words[..., 1, 4:6]],
+                           axis=-1)
+    return order.view(np.uint8).reshape(lead + (48,))
+
+
+def fp6_layout_from_q(q):
+    """Integer codes q [R, K] in [-8, 7] -> FP6 layout bytes [R, 3K/4]."""
+    q = np.asarray(q, np.int64)
+    R, K = q.shape
+    fields = e2m3_encode(q / 2.0).reshape(R, K // 64, 2, 32)
+    return _strings_to_block(fields).reshape(R, 3 * K // 4)
+
+
+def q_from_fp6_layout(b, K):
+    """FP6 layout bytes [R, 3K/4] -> integer codes [R, K] (2 * the E2M3 values)."""
+    b = np.ascontiguousarray(b, np.uint8)
+    R = b.shape[0]
+    words = b.reshape(R, K // 64, 12, 4).view(np.uint32)[..., 0].astype(np.uint64)
+    halves = [np.concatenate([words[..., 0:4], words[..., 8:10]], axis=-1),
+              np.concatenate([words[..., 4:8], words[..., 10:12]], axis=-1)]
+    out = np.empty((R, K // 64, 2, 32), np.int64)
+    for h, wd in enumerate(halves):
+        for j in range(32):
+            bit = 6 * j
+            w, o = bit // 32, bit % 32
+            v = wd[..., w] >> np.uint64(o)
+            if o > 26:
+                v |= wd[..., w + 1] << np.uint64(32 - o)
+            out[..., h, j] = (v & np.uint64(63)).astype(np.int64)
+    vals = e2m3_value(out) * 2.0
+    return vals.reshape(R, K).astype(np.int64)
+
+
+def fp6_layout_from_nibbles(codes, K):
+    """Packed two's-complement nibbles [R, K/2] -> FP6 layout [R, 3K/4]."""
+    c = np.asarray(codes, np.uint8)
+    lo = (c & 15).astype(np.int64)
+    hi = (c >> 4).astype(np.int64)
+    q = np.empty((c.shape[0], K), np.int64)
+    q[:, 0::2] = np.where(lo >= 8, lo - 16, lo)
+    q[:, 1::2] = np.where(hi >= 8, hi - 16, hi)
+    return fp6_layout_from_q(q)

@@ -124,17 +124,29 @@ def svdq_case(cfg: synth.LinearConfig, with_bias=False, M=None, x=None):
 
 
 def gpu_quantize(prec, x, smooth, lora_down, K, gelu=False):
+    """The activation step on the GPU.  prec 3 (SVDQ_INT4_FP6): int4 codes in
+    the FP6 layout [M, 3K/4] with int4's bf16 scales."""
     from bit_w4a4_quantized_svdq_amd import capi
     M = x.shape[0]
     rank = 0 if lora_down is None else lora_down.shape[0]
-    codes = poison(empty((M, K // 2), "u8"))
-    scales = poison(empty((M, K // 64), "bf16") if prec == 0 else empty((M, K // 16), "u8"))
+    int4 = prec in (0, 3)
+    codes = poison(empty((M, 3 * K // 4 if prec == 3 else K // 2), "u8"))
+    scales = poison(empty((M, K // 64), "bf16") if int4 else empty((M, K // 16), "u8"))
     lact = poison(empty((M, rank), "f32")) if rank else None
     fn = capi.svdq_gelu_quantize_act if gelu else capi.svdq_quantize_act
     fn(prec, to_dev(x, "bf16"), to_dev(smooth, "bf16"), to_dev(lora_down, "bf16"), codes, scales, lact)
     torch.cuda.synchronize()
-    return (to_host(codes, "u8"), to_host(scales, "bf16" if prec == 0 else "u8"),
+    return (to_host(codes, "u8"), to_host(scales, "bf16" if int4 else "u8"),
             None if lact is None else to_host(lact, "f32"))
+
+
+def gpu_pack_weight_fp6(wgt_codes_dev):
+    """The FP6 layout [N, 3K/4] of device int4 codes (svdq_pack_weight_fp6)."""
+    from bit_w4a4_quantized_svdq_amd import capi
+    N, Kh = wgt_codes_dev.shape
+    out = poison(empty((N, 3 * Kh // 2), "u8"))
+    capi.svdq_pack_weight_fp6(wgt_codes_dev, out)
+    return out
 
 
 def gpu_pack_weight(wgt_codes_dev, wgt_scales_dev):
@@ -151,9 +163,13 @@ def gpu_pack_weight(wgt_codes_dev, wgt_scales_dev):
 
 
 def gpu_gemm(prec, act_codes, act_scales, wgt_codes, wgt_scales, lora_act, lora_up, bias, alpha=1.0,
-             zero_weight_ok=False, packed=False):
-    """The W4A4 GEMM on the GPU; packed (int4 only): through the packed weight
-    blob and the SVDQ_INT4_PACKED path."""
+             zero_weight_ok=False, packed=False, fp6=False, act_fp6=None):
+    """The W4A4 GEMM on the GPU (act_codes and wgt_codes: packed nibbles).
+    int4 only: packed -- through the packed weight blob and the
+    SVDQ_INT4_PACKED path; fp6 -- the SVDQ_INT4_FP6 path, the activation
+    codes put in the FP6 layout on the host (tests/fp6_layout.py), the
+    weight by svdq_pack_weight_fp6; act_fp6 (optional, with fp6): activation
+    codes already in the FP6 layout (e.g. the GPU activation step's)."""
     from bit_w4a4_quantized_svdq_amd import capi
     M, N = act_codes.shape[0], wgt_codes.shape[0]
     # a layer whose weight scales are all zero tests only the bias and low-rank
@@ -165,6 +181,15 @@ def gpu_gemm(prec, act_codes, act_scales, wgt_codes, wgt_scales, lora_act, lora_
     if packed:
         assert prec == 0
         wc, prec = gpu_pack_weight(wc, ws), capi.SVDQ_INT4_PACKED
+    if fp6:
+        from tests.fp6_layout import fp6_layout_from_nibbles
+        assert prec == 0
+        K = 2 * act_codes.shape[1]
+        if act_fp6 is not None:
+            act_codes = act_fp6
+        else:
+            act_codes = fp6_layout_from_nibbles(act_codes, K) if K else np.zeros((M, 0), np.uint8)
+        wc, prec = gpu_pack_weight_fp6(wc), capi.SVDQ_INT4_FP6
     capi.svdq_gemm_w4a4(prec, to_dev(act_codes, "u8"), to_dev(act_scales, skind), wc, ws, alpha,
                         to_dev(lora_act, "f32"), to_dev(lora_up, "bf16"), to_dev(bias, "bf16"), out)
     torch.cuda.synchronize()

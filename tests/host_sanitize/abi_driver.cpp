@@ -62,6 +62,9 @@ int main() {
         expect_launch(qa(SVDQ_NVFP4, 33, 4160, 0, P, nullptr, nullptr, P, P, nullptr, nullptr), name, 33, 4160, 1000);
         expect_noop(qa(SVDQ_INT4, 0, 64, 16, P, P, P, P, P, F, nullptr), "quantize M=0");
         expect_reject(qa(2, 4, 64, 16, P, P, P, P, P, F, nullptr), UNS, "precision 2");
+        expect_launch(qa(SVDQ_INT4_FP6, 4096, 3072, 32, P, P, P, P, P, F, nullptr), name, 4096, 3072, 2032);
+        expect_reject(qa(SVDQ_INT4_FP6, 4, 96, 16, P, P, P, P, P, F, nullptr), INV, "fp6 K % 64");
+        expect_reject(qa(4, 4, 64, 16, P, P, P, P, P, F, nullptr), UNS, "precision 4");
         expect_reject(qa(SVDQ_INT4, -1, 64, 16, P, P, P, P, P, F, nullptr), INV, "M < 0");
         expect_reject(qa(SVDQ_INT4, (1ll << 24) + 1, 64, 16, P, P, P, P, P, F, nullptr), INV, "M > 2^24");
         expect_reject(qa(SVDQ_INT4, 4, 96, 16, P, P, P, P, P, F, nullptr), INV, "K % 64");
@@ -105,8 +108,23 @@ int main() {
 
     expect_launch(svdq_gemm_w4a4(SVDQ_INT4_PACKED, 4096, 12288, 3072, 32, P, P, P, P, 1.0f, F, P, P, P, nullptr),
                   "gemm_int4_packed", 4096, 12288, 3072);
-    expect_reject(svdq_gemm_w4a4(3, 4, 64, 64, 0, P, P, P, P, 1.0f, nullptr, nullptr, nullptr, P, nullptr), UNS,
-                  "gemm precision 3");
+    expect_launch(svdq_gemm_w4a4(SVDQ_INT4_FP6, 4096, 12288, 3072, 32, P, P, P, P, 1.0f, F, P, P, P, nullptr),
+                  "gemm_fp6", 4096, 12288, 3072);
+    expect_reject(svdq_gemm_w4a4(SVDQ_INT4_FP6, 4, 64, 64, 16, P, P, P, P, 1.0f, nullptr, P, nullptr, P, nullptr),
+                  INV, "gemm fp6 lora_act NULL");
+    expect_reject(svdq_gemm_w4a4(4, 4, 64, 64, 0, P, P, P, P, 1.0f, nullptr, nullptr, nullptr, P, nullptr), UNS,
+                  "gemm precision 4");
+
+    // ---- FP6 layout of int4 weights
+    EXPECT(svdq_fp6_weight_bytes(12288, 3072) == 12288ll * 3072 * 3 / 4, "fp6 bytes");
+    EXPECT(svdq_fp6_weight_bytes(8, 100) == -1, "fp6 bytes, K % 64");
+    expect_launch(svdq_pack_weight_fp6(12288, 3072, P, P, nullptr), "pack_weight_fp6", 12288, 3072, 0);
+    expect_noop(svdq_pack_weight_fp6(0, 64, P, P, nullptr), "pack fp6 N=0");
+    expect_reject(svdq_pack_weight_fp6(5, 64, nullptr, P, nullptr), INV, "pack fp6 codes NULL");
+    expect_reject(svdq_pack_weight_fp6(5, 64, P, MIS, nullptr), INV, "pack fp6 out misaligned");
+    expect_launch(svdq_debug_group_sums_fp6(130, 384, 3072, P, P, I, nullptr), "group_sums_fp6", 130, 384, 3072);
+    expect_reject(svdq_debug_group_sums_fp6(130, 384, 3072, P, nullptr, I, nullptr), INV,
+                  "group sums fp6 weight NULL");
 
     // ---- packed int4 weights
     EXPECT(svdq_packed_weight_bytes(12288, 3072) == 12288ll * 1536 + 12288ll * 4 * 48, "packed bytes");
@@ -131,6 +149,9 @@ int main() {
     expect_launch(svdq_gemm_w4a4_qk_norm_rope(SVDQ_INT4_PACKED, 4096, 9216, 3072, 32, P, P, P, P, 1.0f, Fc, P, P, P,
                                               P, 1e-6f, Fc, Fc, P, nullptr),
                   "gemm_int4_packed_qk", 4096, 9216, 6144);
+    expect_launch(svdq_gemm_w4a4_qk_norm_rope(SVDQ_INT4_FP6, 4096, 9216, 3072, 32, P, P, P, P, 1.0f, Fc, P, P, P,
+                                              P, 1e-6f, Fc, Fc, P, nullptr),
+                  "gemm_fp6_qk", 4096, 9216, 6144);
     expect_launch(svdq_gemm_w4a4_qk_norm_rope(SVDQ_NVFP4, 3, 384, 256, 0, P, P, P, P, 1.0f, nullptr, nullptr,
                                               nullptr, P, P, 0.0f, Fc, Fc, P, nullptr),
                   "gemm_nvfp4_qk", 3, 384, 256);

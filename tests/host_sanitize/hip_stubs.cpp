@@ -84,6 +84,22 @@ hipError_t launch_awq_gemv(int M, int N, int K, const void *, const void *, cons
                            const void *, void *, hipStream_t) {
     return rec("awq_gemv", M, N, K);
 }
+size_t fp6_weight_bytes(int N, int K) { return (size_t)N * (K / 64) * 48; }
+hipError_t launch_pack_weight_fp6(int N, int K, const void *, void *, hipStream_t) {
+    return rec("pack_weight_fp6", N, K, 0);
+}
+hipError_t launch_gemm_w4a4_fp6(int M, int N, int K, int, const void *, const void *, const void *, const void *,
+                                float, const float *, const void *, const void *, void *, hipStream_t) {
+    return rec("gemm_fp6", M, N, K);
+}
+hipError_t launch_gemm_w4a4_fp6_qk(int M, int N, int, int, const void *, const void *, const void *, const void *,
+                                   float, const float *, const void *, const void *, const QkNormRope &qk, void *,
+                                   hipStream_t) {
+    return rec("gemm_fp6_qk", M, N, qk.qk_cols);
+}
+hipError_t launch_group_sums_fp6(int M, int N, int K, const void *, const void *, int32_t *, hipStream_t) {
+    return rec("group_sums_fp6", M, N, K);
+}
 hipError_t launch_stream_read(const void *, int64_t bytes, bool lines, uint32_t *, hipStream_t) {
     return rec("stream_read", (int)(bytes >> 20), lines, 0);
 }

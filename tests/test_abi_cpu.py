@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(capi.LIB_PATH)
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert capi.svdq_abi_version() == 8
+    assert capi.svdq_abi_version() == 9
     for s in range(4):
         assert capi.svdq_status_string(s).startswith(("SVDQ_OK", "SVDQ_ERR"))
     assert "unknown" in capi.svdq_status_string(99)
@@ -60,7 +60,7 @@ INV, UNS = capi.SVDQ_ERR_INVALID_ARG, capi.SVDQ_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("kw,want,msg", [
-    (dict(prec=2), UNS, "precision"),
+    (dict(prec=2), UNS, "precision"), (dict(prec=4), UNS, "precision"),
     (dict(K=0), INV, "K must"), (dict(K=96), INV, "K must"), (dict(K=1 << 17), INV, "K must"),
     (dict(M=-1), INV, "M and N"), (dict(M=(1 << 24) + 1), INV, "M and N"),
     (dict(rank=8), INV, "rank"), (dict(rank=144), INV, "rank"), (dict(rank=-16), INV, "rank"),
@@ -139,7 +139,8 @@ def test_newer_entry_points_reject_bad_arguments_on_the_host():
     # QKV epilogue: int4 only, N = 3 * heads * 128, finite eps >= 0
     qk = lambda prec=0, N=384, eps=1e-6, cos=A: L.svdq_gemm_w4a4_qk_norm_rope(
         prec, 4, N, 64, 16, A, A, A, A, 1.0, A, A, A, A, A, eps, cos, A, A, None)
-    assert qk(prec=3) == UNS
+    assert qk(prec=4) == UNS
+    assert qk(prec=capi.SVDQ_INT4_FP6, N=256) == INV
     assert qk(N=256) == INV
     assert qk(eps=-1.0) == INV
     assert qk(eps=float("inf")) == INV
@@ -206,7 +207,34 @@ def test_packed_weight_entry_points_host_checks():
     assert gs(w=0) == INV
     assert gs(K=100) == INV
     assert gs(M=0) == capi.SVDQ_OK
-    # the GEMM accepts precision 2 (checks as for int4) and rejects 3
-    assert gm(prec=3) == UNS
+    # the GEMM accepts precisions 2 and 3 (checks as for int4) and rejects 4
+    assert gm(prec=4) == UNS
     assert gm(prec=capi.SVDQ_INT4_PACKED, wc=0) == INV
     assert gm(prec=capi.SVDQ_INT4_PACKED, M=0) == capi.SVDQ_OK
+
+
+def test_fp6_entry_points_host_checks():
+    """svdq_fp6_weight_bytes and the host-side checks of the FP6-layout entry
+    points (every rejection happens before a launch)."""
+    L = capi.lib()
+    assert capi.svdq_fp6_weight_bytes(12288, 3072) == 12288 * 3072 * 3 // 4
+    assert capi.svdq_fp6_weight_bytes(1, 64) == 48
+    assert capi.svdq_fp6_weight_bytes(8, 100) == -1
+    assert capi.svdq_fp6_weight_bytes(-1, 64) == -1
+    pk = lambda N=64, K=128, c=A, out=A: L.svdq_pack_weight_fp6(N, K, c, out, None)
+    assert pk(K=96) == INV
+    assert pk(c=0) == INV
+    assert pk(out=MIS) == INV
+    assert pk(N=0) == capi.SVDQ_OK
+    gs = lambda M=4, N=64, K=128, ac=A, w=A, G=A: L.svdq_debug_group_sums_fp6(M, N, K, ac, w, G, None)
+    assert gs(w=0) == INV
+    assert gs(ac=MIS) == INV
+    assert gs(K=100) == INV
+    assert gs(N=0) == capi.SVDQ_OK
+    # the activation steps and the GEMM take SVDQ_INT4_FP6 with int4's checks
+    assert qa(prec=capi.SVDQ_INT4_FP6, K=96) == INV
+    assert qa(prec=capi.SVDQ_INT4_FP6, M=0) == capi.SVDQ_OK
+    assert L.svdq_gelu_quantize_act(capi.SVDQ_INT4_FP6, 4, 64, 8, A, A, A, A, A, A, None) == INV
+    assert gm(prec=capi.SVDQ_INT4_FP6, wsc=0) == INV
+    assert gm(prec=capi.SVDQ_INT4_FP6, rank=8) == INV
+    assert gm(prec=capi.SVDQ_INT4_FP6, M=0) == capi.SVDQ_OK

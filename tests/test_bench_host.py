@@ -22,18 +22,19 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 
 
 def test_algorithmic_bytes_of_the_dit_shapes():
-    # MLP up, int4 g64, rank 32: codes of both operands (half a byte per
-    # element), one bf16 scale per 64 codes, fp32 lora_act, bf16 lora_up, bf16 out
+    # MLP up, int4 g64, rank 32: codes of both operands in the FP6 layout (48
+    # bytes per 64 codes), one bf16 scale per 64 codes, fp32 lora_act, bf16
+    # lora_up, bf16 out
     M, N, K, r = 4096, 12288, 3072, 32
-    want = (M + N) * K // 2 + (M + N) * (K // 64) * 2 + M * r * 4 + N * r * 2 + M * N * 2
-    assert want == 128712704
+    want = (M + N) * K * 3 // 4 + (M + N) * (K // 64) * 2 + M * r * 4 + N * r * 2 + M * N * 2
+    assert want == 141295616
     assert bench.algorithmic_bytes_gemm(M, N, K, r, "int4") == want
     # NVFP4: one E4M3 byte per 16 codes instead
     assert bench.algorithmic_bytes_gemm(4096, 3072, 3072, 32, "nvfp4") == \
         7168 * 1536 + 7168 * 192 + 4096 * 128 + 3072 * 64 + 4096 * 3072 * 2
     # quantize: bf16 x in, codes + scales + fp32 t out, smooth and L1 read once
     assert bench.algorithmic_bytes_quantize(4096, 3072, 32, "int4") == \
-        4096 * 3072 * 2 + 3072 * 2 + 32 * 3072 * 2 + 4096 * 1536 + 4096 * 48 * 2 + 4096 * 32 * 4
+        4096 * 3072 * 2 + 3072 * 2 + 32 * 3072 * 2 + 4096 * 2304 + 4096 * 48 * 2 + 4096 * 32 * 4
     # adaLN GEMV at M = 1: 18432 x 3072 int4 codes, bf16 scales and zero points per 64
     assert bench.algorithmic_bytes_gemv(1, 18432, 3072) == 31893504
 
@@ -64,7 +65,7 @@ def test_counter_means_sum_dimensions_and_average_dispatches(tmp_path):
 
 def test_utilisation_and_gemv_traffic_summaries(tmp_path, monkeypatch):
     run = tmp_path / "run"
-    g = "void svdq::gemm_w4a4_int4_kernel<false, true, false>(int, ...)"
+    g = "void svdq::gemm_w4a4_fp6_kernel<false, true, false>(int, ...)"
     v = "void svdq::awq_gemv_kernel<2, true>(int, ...)"
     c = "__amd_rocclr_copyBuffer"
     _write_counters(str(run / "pmc_gemm_util"), [(1, g, "MfmaUtil", 35.5), (1, g, "VALUBusy", 72.0)])
@@ -77,16 +78,21 @@ def test_utilisation_and_gemv_traffic_summaries(tmp_path, monkeypatch):
     _write_counters(str(run / "pmc_copy_WRITE_SIZE"), [(1, c, "WRITE_SIZE", 256 * 1024)])
     _write_counters(str(run / "pmc_gemv_FETCH_SIZE"), [(1, v, "FETCH_SIZE", 15625.0), (2, v, "FETCH_SIZE", 15625.0)])
     _write_counters(str(run / "pmc_gemv_WRITE_SIZE"), [(1, v, "WRITE_SIZE", 36.0)])
+    # GRBM_GUI_ACTIVE comes once per XCD: their mean, not their sum
+    _write_counters(str(run / "pmc_gemm_clock"), [(1, g, "GRBM_GUI_ACTIVE", 300000.0), (1, g, "GRBM_GUI_ACTIVE", 300000.0),
+                                                  (1, g, "SQ_BUSY_CYCLES", 1)])
     util, traffic = tmp_path / "util.txt", tmp_path / "gemv.txt"
     monkeypatch.setattr(bench, "UTIL_FILE", str(util))
     monkeypatch.setattr(bench, "GEMV_TRAFFIC_FILE", str(traffic))
-    bench.summarize_utilisation(str(run), {"adaln.awq_gemv": 12.5})
+    bench.summarize_utilisation(str(run), {"adaln.awq_gemv": 12.5, "mlp_up.gemm_w4a4": 200.0})
     u = dict(l.split(": ", 1) for l in util.read_text().splitlines() if not l.startswith("#"))
     assert u["MfmaUtil_percent"].startswith("35.5")
     assert u["VALUBusy_percent"].startswith("72.0")
     assert u["valu_insts_per_wave_group"].startswith("200.0")
     assert u["mfma_insts_per_wave_group"].startswith("10.00")
     assert u["source_sha256"] == bench.gemm_int4_source_hash()
+    assert u["effective_clock_MHz"].startswith("1500")          # 300000 cycles in 200 us
+    assert u["cycles_per_wave_group_per_SIMD"].startswith(f"{300000 / (wg / 1024):.0f}")
     t = dict(l.split(": ", 1) for l in traffic.read_text().splitlines() if not l.startswith("#"))
     fetch = 15625.0 * 1024 * 2          # KiB -> bytes, times the copy factor 2
     assert int(t["fetch_bytes_per_launch"]) == int(fetch)

@@ -15,6 +15,7 @@ import torch
 
 import oracle
 from bit_w4a4_quantized_svdq_amd import synth
+from tests.fp6_layout import fp6_layout_from_nibbles
 from tests.gpu_helpers import announce, assert_bf16_close, assert_f32_close, gpu_gemm, gpu_gemv, gpu_quantize, svdq_case
 
 pytestmark = [pytest.mark.gpu,
@@ -63,12 +64,24 @@ def _layer_parity(cfg, case, prec):
     stats = assert_bf16_close(y[rows], ref, cfg.name)
     assert np.isfinite(synth.bf16_bits_to_f32(y)).all()
     if prec == oracle.INT4:
-        # the production path: the packed weight (fp8 matrix-core formulation)
+        # the packed weight (fp8 matrix-core formulation)
         announce("fullsize gemm_w4a4 packed", cfg.name)
         yp = gpu_gemm(prec, oc, os_, case["wgt_codes"], case["wgt_scales"], ot, case["lora_up"], case["bias"],
                       packed=True)
         stats = assert_bf16_close(yp[rows], ref, cfg.name + " packed")
         assert np.isfinite(synth.bf16_bits_to_f32(yp)).all()
+        # the production path: the activation step's FP6 output (whole tensor
+        # against the oracle's codes in that layout) into the FP6 GEMM
+        announce("fullsize quantize_act fp6", cfg.name)
+        fc, fs, ft = gpu_quantize(3, case["x"], case["smooth"], case["lora_down"], K)
+        assert np.array_equal(fs, os_), f"{cfg.name} fp6: scales differ"
+        assert np.array_equal(fc, fp6_layout_from_nibbles(oc, K)), f"{cfg.name} fp6: code bytes differ"
+        assert np.array_equal(ft, gt), f"{cfg.name} fp6: lora_act differs from the nibble output's"
+        announce("fullsize gemm_w4a4 fp6", cfg.name)
+        yf = gpu_gemm(prec, oc, os_, case["wgt_codes"], case["wgt_scales"], ft, case["lora_up"], case["bias"],
+                      fp6=True, act_fp6=fc)
+        stats = assert_bf16_close(yf[rows], ref, cfg.name + " fp6")
+        assert np.isfinite(synth.bf16_bits_to_f32(yf)).all()
     return stats
 
 

@@ -9,6 +9,7 @@ import torch
 
 import oracle
 from bit_w4a4_quantized_svdq_amd import capi, synth
+from tests.fp6_layout import fp6_layout_from_nibbles
 from tests.gpu_helpers import announce, assert_f32_close, gpu_quantize
 
 pytestmark = pytest.mark.gpu
@@ -23,6 +24,13 @@ def _check(prec, x, smooth, down, what):
     assert np.array_equal(gc, oc), f"{what}: codes differ at {np.argwhere(gc != oc)[:5].tolist()}"
     if down is not None:
         assert_f32_close(gt, ot, 1e-5, what)
+    if prec == 0:
+        # the same step with the codes in the FP6 layout
+        fc, fs, ft = gpu_quantize(3, x, smooth, down, K, gelu=True)
+        assert np.array_equal(fs, os_), f"{what} fp6: scales differ"
+        assert np.array_equal(fc, fp6_layout_from_nibbles(oc, K)), f"{what} fp6: code bytes differ"
+        if down is not None:
+            assert np.array_equal(ft, gt), f"{what} fp6: lora_act differs from the nibble output's"
 
 
 def test_gelu_every_bf16():

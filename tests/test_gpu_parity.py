@@ -8,8 +8,9 @@ import torch
 
 import oracle
 from bit_w4a4_quantized_svdq_amd import capi, synth
+from tests.fp6_layout import fp6_layout_from_nibbles, fp6_layout_from_q
 from tests.gpu_helpers import (announce, assert_bf16_close, assert_f32_close, gpu_gemm, gpu_gemv,
-                               gpu_quantize, svdq_case, to_dev, to_host, empty, poison)
+                               gpu_pack_weight_fp6, gpu_quantize, svdq_case, to_dev, to_host, empty, poison)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -31,7 +32,23 @@ def _check_quantize(prec, x, smooth, down, what):
     assert np.array_equal(gc, oc), f"{what}: codes differ at {np.argwhere(gc != oc)[:5].tolist()}"
     if down is not None:
         assert_f32_close(gt, ot, 1e-5, what)
+    if prec == 0:
+        _check_fp6_codes(x, smooth, down, oc, os_, gt, what)
     return oc, os_, ot
+
+
+def _check_fp6_codes(x, smooth, down, oc, os_, gt_int4, what, gelu=False):
+    """The SVDQ_INT4_FP6 activation step: the oracle's int4 codes in the FP6
+    layout (host reference encoder), int4's scales, and the same lora_act as
+    the nibble output."""
+    K = x.shape[1]
+    announce("quantize_act fp6", what, "shape", x.shape, "gelu", gelu)
+    fc, fs, ft = gpu_quantize(3, x, smooth, down, K, gelu=gelu)
+    assert np.array_equal(fs, os_), f"{what} fp6: scales differ"
+    want = fp6_layout_from_nibbles(oc, K)
+    assert np.array_equal(fc, want), f"{what} fp6: code bytes differ at {np.argwhere(fc != want)[:5].tolist()}"
+    if down is not None:
+        assert np.array_equal(ft, gt_int4), f"{what} fp6: lora_act differs from the nibble output's"
 
 
 # ------------------------------------------------------------ quantize_act
@@ -137,6 +154,10 @@ def _random_gemm_case(prec, M, N, K, rank, with_bias, seed):
     # NVFP4 staging paths: K % 512 == 0 (two-slice stages, several 8-slice scale
     # chunks, ragged M and N) and K % 512 == 256 (single-slice ring, 4-slice scales)
     (1, 67, 200, 1024, 32, True, 1.0), (1, 130, 192, 2560, 16, False, 0.5), (1, 200, 320, 768, 32, True, 1.0),
+    # FP6 main loops: K/64 = 3 (odd: a last stage with one group), 6 (pairs, 2-byte scales),
+    # 12 and 48 (4-group scale loads), ragged M and N
+    (0, 70, 200, 192, 16, True, 1.0), (0, 129, 130, 384, 32, False, 1.0), (0, 200, 256, 768, 32, True, 2.0),
+    (0, 131, 384, 3072, 32, True, 1.0),
 ])
 def test_gemm_shapes(prec, M, N, K, rank, with_bias, alpha):
     ac, asc, t, w, bias = _random_gemm_case(prec, M, N, K, rank, with_bias, 2000 + M + N + K + prec)
@@ -148,6 +169,9 @@ def test_gemm_shapes(prec, M, N, K, rank, with_bias, alpha):
         announce("gemm_w4a4 packed", "M,N,K,r", M, N, K, rank, "alpha", alpha)
         yp = gpu_gemm(prec, ac, asc, w["wgt_codes"], w["wgt_scales"], t, w["lora_up"], bias, alpha, packed=True)
         assert_bf16_close(yp, ref, f"gemm packed {M}x{N}x{K} r{rank}")
+        announce("gemm_w4a4 fp6", "M,N,K,r", M, N, K, rank, "alpha", alpha)
+        yf = gpu_gemm(prec, ac, asc, w["wgt_codes"], w["wgt_scales"], t, w["lora_up"], bias, alpha, fp6=True)
+        assert_bf16_close(yf, ref, f"gemm fp6 {M}x{N}x{K} r{rank}")
 
 
 # ------------------------------------------------------- packed int4 weights
@@ -223,6 +247,46 @@ def test_debug_group_sums_packed_exact(M, N, K):
     assert np.array_equal(got, ref), f"group sums differ at {np.argwhere(got != ref)[:5].tolist()}"
 
 
+# ------------------------------------------------------ FP6 layout of int4
+
+@pytest.mark.parametrize("N,K", [(64, 64), (130, 192), (257, 4160), (1000, 3072), (40, 512)])
+def test_pack_weight_fp6_layout_exact(N, K):
+    """svdq_pack_weight_fp6 against the host encoder of the documented layout;
+    every code in [-8, 7] (the FP6 form holds -8 too)."""
+    rng = np.random.default_rng(6300 + N + K)
+    q = rng.integers(-8, 8, (N, K))
+    q[0, :16] = np.arange(-8, 8)
+    codes = synth.pack_nibbles(q)
+    announce("pack_weight_fp6", N, K)
+    got = to_host(gpu_pack_weight_fp6(to_dev(codes, "u8")), "u8")
+    assert np.array_equal(got, fp6_layout_from_q(q)), "FP6 weight bytes differ"
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (64, 64, 64), (33, 130, 4160), (1, 1, 128), (65, 200, 192),
+    # K/64 a multiple of 4: the chunked loop with 4-group scale loads that the
+    # DiT shapes run (K = 3072, 12288); odd K/64 (4160, 192): a one-group last stage
+    (200, 320, 512), (130, 384, 3072), (130, 384, 12288), (257, 129, 1024),
+])
+def test_debug_group_sums_fp6_exact(M, N, K):
+    """Exact int32 group sums from the main loop of the FP6 GEMM, codes
+    anywhere in [-8, 7] on both sides."""
+    rng = np.random.default_rng(3700 + M + N + K)
+    qa = rng.integers(-8, 8, (M, K))
+    qw = rng.integers(-8, 8, (N, K))
+    qa[0, :64] = -8
+    qw[0, :64] = -8                                          # extreme group: 64 * 64 = 4096
+    ac, wc = synth.pack_nibbles(qa), synth.pack_nibbles(qw)
+    announce("debug_group_sums_fp6", M, N, K)
+    wf = gpu_pack_weight_fp6(to_dev(wc, "u8"))
+    G = poison(empty((M, N, K // 64), "i32"))
+    capi.svdq_debug_group_sums_fp6(to_dev(fp6_layout_from_q(qa), "u8"), wf, N, G)
+    torch.cuda.synchronize()
+    got = to_host(G, "i32")
+    ref = oracle.group_sums_int4(ac, wc, K)
+    assert np.array_equal(got, ref), f"group sums differ at {np.argwhere(got != ref)[:5].tolist()}"
+
+
 @pytest.mark.parametrize("M,N,K", [
     (64, 64, 64), (33, 130, 4160), (1, 1, 128), (65, 200, 4160),
     # K/64 a multiple of 8: the chunked main loop that every DiT-shaped GEMM
@@ -260,7 +324,8 @@ def test_zero_residual_layer_on_gpu():
     gc, gs, gt = gpu_quantize(0, x, None, down, K)
     y = gpu_gemm(0, gc, gs, zc, zs, gt, up, bias, zero_weight_ok=True)
     yp = gpu_gemm(0, gc, gs, zc, zs, gt, up, bias, zero_weight_ok=True, packed=True)
-    assert np.array_equal(y, yp)
+    yf = gpu_gemm(0, gc, gs, zc, zs, gt, up, bias, zero_weight_ok=True, fp6=True)
+    assert np.array_equal(y, yp) and np.array_equal(y, yf)
     ref_t = (synth.bf16_bits_to_f32(x).astype(np.float64) @ synth.bf16_bits_to_f32(down).astype(np.float64).T)
     ref = oracle.f64_to_bf16(ref_t @ synth.bf16_bits_to_f32(up).astype(np.float64).T +
                              synth.bf16_bits_to_f32(bias).astype(np.float64)[None, :])

@@ -12,8 +12,9 @@ import torch
 
 import oracle
 from bit_w4a4_quantized_svdq_amd import capi, synth
-from tests.gpu_helpers import (announce, assert_bf16_close, empty, gpu_gemm, gpu_pack_weight, poison, to_dev,
-                               to_host)
+from tests.fp6_layout import fp6_layout_from_nibbles
+from tests.gpu_helpers import (announce, assert_bf16_close, empty, gpu_gemm, gpu_pack_weight, gpu_pack_weight_fp6,
+                               poison, to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -25,13 +26,16 @@ def _norm_rope_inputs(rng, M):
     return qw, kw, np.cos(th).astype(np.float32), np.sin(th).astype(np.float32)
 
 
-def _gpu_qk(ac, asc, w, t, bias, qw, kw, eps, cs, sn, alpha=1.0, prec=0, packed=False):
+def _gpu_qk(ac, asc, w, t, bias, qw, kw, eps, cs, sn, alpha=1.0, prec=0, packed=False, fp6=False):
     M, N = ac.shape[0], w["wgt_codes"].shape[0]
     out = poison(empty((M, N), "bf16"))
     sk = "bf16" if prec == 0 else "u8"
     wc, ws = to_dev(w["wgt_codes"], "u8"), to_dev(w["wgt_scales"], sk)
     if packed:
         wc, prec = gpu_pack_weight(wc, ws), capi.SVDQ_INT4_PACKED
+    if fp6:
+        wc, prec = gpu_pack_weight_fp6(wc), capi.SVDQ_INT4_FP6
+        ac = fp6_layout_from_nibbles(ac, 2 * ac.shape[1])
     capi.svdq_gemm_w4a4_qk_norm_rope(prec, to_dev(ac, "u8"), to_dev(asc, sk), wc, ws, alpha, to_dev(t, "f32"),
                                      to_dev(w["lora_up"], "bf16"), to_dev(bias, "bf16"), to_dev(qw, "bf16"),
                                      to_dev(kw, "bf16"), eps, to_dev(cs, "f32"), to_dev(sn, "f32"), out)
@@ -83,6 +87,14 @@ def test_qk_norm_rope_shapes(prec, M, H, K, rank, with_bias, alpha):
         ulp = np.abs(yp.view(np.int16).astype(np.int32) - ep_p.view(np.int16).astype(np.int32))
         assert np.mean(ulp <= 1) >= 0.999, f"packed epilogue: {np.mean(ulp <= 1):.5f} within 1 ulp"
         assert_bf16_close(yp, ref, f"qkv packed {M}x{H}x{K} r{rank}")
+        announce("gemm qk_norm_rope fp6", "M,H,K,r", M, H, K, rank)
+        yf = _gpu_qk(ac, asc, w, t, bias, qw, kw, eps, cs, sn, alpha, prec, fp6=True)
+        plain_f = gpu_gemm(prec, ac, asc, w["wgt_codes"], w["wgt_scales"], t, w["lora_up"], bias, alpha, fp6=True)
+        assert np.array_equal(yf[:, 2 * HD:], plain_f[:, 2 * HD:]), "fp6: V columns differ from its plain GEMM"
+        ep_f = oracle.qk_norm_rope(plain_f, qw, kw, eps, cs, sn)
+        ulp = np.abs(yf.view(np.int16).astype(np.int32) - ep_f.view(np.int16).astype(np.int32))
+        assert np.mean(ulp <= 1) >= 0.999, f"fp6 epilogue: {np.mean(ulp <= 1):.5f} within 1 ulp"
+        assert_bf16_close(yf, ref, f"qkv fp6 {M}x{H}x{K} r{rank}")
 
 
 def test_qk_norm_rope_zero_and_tiny_heads():
@@ -117,3 +129,7 @@ def test_qk_norm_rope_fullsize_qkv():
     yp = _gpu_qk(ac, asc, w, t, None, qw, kw, 1e-6, cs, sn, packed=True)
     assert_bf16_close(yp[rows], ref, "fullsize qkv packed")
     assert np.isfinite(synth.bf16_bits_to_f32(yp)).all()
+    announce("fullsize qkv qk_norm_rope fp6")
+    yf = _gpu_qk(ac, asc, w, t, None, qw, kw, 1e-6, cs, sn, fp6=True)
+    assert_bf16_close(yf[rows], ref, "fullsize qkv fp6")
+    assert np.isfinite(synth.bf16_bits_to_f32(yf)).all()

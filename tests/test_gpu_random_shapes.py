@@ -10,6 +10,7 @@ import torch
 
 import oracle
 from bit_w4a4_quantized_svdq_amd import synth
+from tests.fp6_layout import fp6_layout_from_nibbles
 from tests.gpu_helpers import (announce, assert_bf16_close, assert_f32_close, gpu_gemm, gpu_gemv,
                                gpu_quantize)
 
@@ -73,6 +74,13 @@ def test_random_layer_shapes(i, prec, M, N, K, rank, with_bias, gelu):
         yp = gpu_gemm(prec, gc, gs, w["wgt_codes"], w["wgt_scales"], gt if rank else None, w["lora_up"], bias,
                       packed=True)
         assert_bf16_close(yp, ref, f"case {i} packed out")
+        # the FP6 chain: the activation step's FP6 output into the FP6 GEMM
+        fc, fs, ft = gpu_quantize(3, xb, smooth, w["lora_down"], K, gelu=gelu)
+        assert np.array_equal(fs, os_), f"case {i} fp6: scales differ"
+        assert np.array_equal(fc, fp6_layout_from_nibbles(oc, K)), f"case {i} fp6: code bytes differ"
+        yf = gpu_gemm(prec, gc, gs, w["wgt_codes"], w["wgt_scales"], ft if rank else None, w["lora_up"], bias,
+                      fp6=True, act_fp6=fc)
+        assert_bf16_close(yf, ref, f"case {i} fp6 out")
 
 
 @pytest.mark.parametrize("i,M,N,K,with_bias", _awq_cases())
