@@ -563,12 +563,18 @@ def summarize_utilisation(run_dir, trace_us):
             for r in _csv_rows(f):
                 if DOM_KERNEL in r["Kernel_Name"] and r["Counter_Name"] == "GRBM_GUI_ACTIVE":
                     per.setdefault(r["Dispatch_Id"], []).append(float(r["Counter_Value"]))
-        # one value per XCD (each counts the same GPU-active cycles): their mean
-        ga = float(np.mean([np.mean(v) for v in per.values()]))
-        inst = int(np.mean([len(v) for v in per.values()]))
+        # the counter sums the XCDs' GPU-active cycles (rows per dispatch are
+        # summed too); the agent record gives the XCD count
+        xcc = 1
+        for f in glob.glob(os.path.join(clk_dir, "**", "*agent_info.csv"), recursive=True):
+            for r in _csv_rows(f):
+                if r.get("Agent_Type") == "GPU":
+                    xcc = int(r.get("Num_Xcc", 1) or 1)
+        ga = float(np.mean([sum(v) for v in per.values()])) / xcc
         us = trace_us["mlp_up.gemm_w4a4"]
-        t.append(f"GRBM_GUI_ACTIVE_per_launch: {int(ga)}  (mean of {inst} per-XCD values, {len(per)} launches)")
-        t.append(f"effective_clock_MHz: {ga / us:.0f}  (GRBM_GUI_ACTIVE / the trace's {us:.2f} us)")
+        t.append(f"GRBM_GUI_ACTIVE_per_launch_per_XCD: {int(ga)}  (the counter / {xcc} XCDs, mean of {len(per)} "
+                 "launches)")
+        t.append(f"effective_clock_MHz: {ga / us:.0f}  (per-XCD active cycles / the trace's {us:.2f} us)")
         t.append(f"cycles_per_wave_group_per_SIMD: {ga / (wave_groups / 1024):.0f}  "
                  "(active cycles x 1024 SIMDs / wave-groups)")
     open(UTIL_FILE, "w").write("\n".join(t) + "\n")

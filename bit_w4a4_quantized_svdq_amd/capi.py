@@ -26,7 +26,7 @@ EXPORTED = ("svdq_quantize_act", "svdq_gelu_quantize_act", "svdq_gemm_w4a4", "sv
             "svdq_smooth_factors", "svdq_quantize_weight", "svdq_lowrank_workspace_bytes",
             "svdq_lowrank_factors", "svdq_lowrank_factors_noalloc",
             "svdq_packed_weight_bytes", "svdq_pack_weight_int4", "svdq_debug_group_sums_packed",
-            "svdq_fp6_weight_bytes", "svdq_pack_weight_fp6", "svdq_debug_group_sums_fp6",
+            "svdq_fp6_codes_bytes", "svdq_pack_weight_fp6", "svdq_debug_group_sums_fp6",
             "svdq_debug_group_sums", "svdq_debug_gelu_bf16", "svdq_debug_stream_read",
             "svdq_status_string", "svdq_last_error",
             "svdq_abi_version")
@@ -63,8 +63,8 @@ def lib() -> ctypes.CDLL:
         L.svdq_packed_weight_bytes.restype = _I64
         L.svdq_pack_weight_int4.argtypes = [_I64, _I64, _P, _P, _P, _P, _P]
         L.svdq_debug_group_sums_fp6.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P]
-        L.svdq_fp6_weight_bytes.argtypes = [_I64, _I64]
-        L.svdq_fp6_weight_bytes.restype = _I64
+        L.svdq_fp6_codes_bytes.argtypes = [_I64, _I64]
+        L.svdq_fp6_codes_bytes.restype = _I64
         L.svdq_pack_weight_fp6.argtypes = [_I64, _I64, _P, _P, _P]
         L.svdq_debug_gelu_bf16.argtypes = [_I64, _P, _P, _P]
         L.svdq_debug_stream_read.argtypes = [_P, _I64, _I32, _P, _P]
@@ -172,30 +172,32 @@ def svdq_debug_group_sums_packed(act_codes, packed_weight, N, G, stream=None):
                                               _stream(stream)), "svdq_debug_group_sums_packed")
 
 
-def svdq_fp6_weight_bytes(N, K) -> int:
-    return int(lib().svdq_fp6_weight_bytes(N, K))
+def svdq_fp6_codes_bytes(rows, K) -> int:
+    """Bytes of int4 codes of [rows, K] in the FP6 tiled layout (activations
+    of the SVDQ_INT4_FP6 path, or its weight)."""
+    return int(lib().svdq_fp6_codes_bytes(rows, K))
 
 
 def svdq_pack_weight_fp6(wgt_codes, fp6_weight, stream=None):
-    """Offline re-encoding of int4 weight codes [N, K/2] into the FP6 layout
-    [N, 3K/4] of the SVDQ_INT4_FP6 GEMM."""
+    """Offline re-encoding of int4 weight codes [N, K/2] into the FP6 tiled
+    layout (svdq_fp6_codes_bytes(N, K) bytes) of the SVDQ_INT4_FP6 GEMM."""
     N, Kh = wgt_codes.shape
     _check(lib().svdq_pack_weight_fp6(N, 2 * Kh, _ptr(wgt_codes), _ptr(fp6_weight), _stream(stream)),
            "svdq_pack_weight_fp6")
 
 
-def svdq_debug_group_sums_fp6(act_codes, fp6_weight, N, G, stream=None):
+def svdq_debug_group_sums_fp6(act_codes, fp6_weight, M, N, K, G, stream=None):
     """Exact int32 group sums [M,N,K/64] on the FP6 GEMM's device path
-    (act_codes in the FP6 layout [M, 3K/4])."""
-    M, Kf = act_codes.shape
-    _check(lib().svdq_debug_group_sums_fp6(M, N, Kf * 4 // 3, _ptr(act_codes), _ptr(fp6_weight), _ptr(G),
-                                           _stream(stream)), "svdq_debug_group_sums_fp6")
+    (both operands in the FP6 tiled layout)."""
+    _check(lib().svdq_debug_group_sums_fp6(M, N, K, _ptr(act_codes), _ptr(fp6_weight), _ptr(G), _stream(stream)),
+           "svdq_debug_group_sums_fp6")
 
 
 def svdq_gemm_w4a4(precision, act_codes, act_scales, wgt_codes, wgt_scales, alpha, lora_act,
                    lora_up, bias, out, stream=None):
-    """4-bit GEMM with the low-rank up-projection and bias; out is [M,N] bf16."""
-    M = act_codes.shape[0]
+    """4-bit GEMM with the low-rank up-projection and bias; out is [M,N] bf16
+    (M from out: the FP6 layout is one-dimensional)."""
+    M = out.shape[0]
     N, K = _weight_shape(precision, wgt_codes, wgt_scales)
     rank = 0 if lora_up is None else lora_up.shape[1]
     _check(lib().svdq_gemm_w4a4(precision, M, N, K, rank, _ptr(act_codes), _ptr(act_scales),
@@ -209,7 +211,7 @@ def svdq_gemm_w4a4_qk_norm_rope(precision, act_codes, act_scales, wgt_codes, wgt
                                 rope_sin, out, stream=None):
     """4-bit GEMM of a grouped QKV layer with per-head RMSNorm + rotary embedding
     of Q and K in the epilogue; out is [M, 3*H*128] bf16."""
-    M = act_codes.shape[0]
+    M = out.shape[0]
     N, K = _weight_shape(precision, wgt_codes, wgt_scales)
     rank = 0 if lora_up is None else lora_up.shape[1]
     _check(lib().svdq_gemm_w4a4_qk_norm_rope(precision, M, N, K, rank, _ptr(act_codes),

@@ -101,4 +101,21 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
     return (c & 0x80u) ? -v : v;
 }
 
+// FP6 tiled layout of int4 codes (the FP6 GEMM's operands): byte offset of
+// 16-byte chunk c (0..2: [h0 dwords 0-3 | h1 dwords 0-3 | h0 dwords 4-5,
+// h1 dwords 4-5]) of group g of row r.  Rows form tiles of 128, groups
+// pairs; (tile, pair) is a contiguous 12 KB block of 128 rows x 96 bytes,
+// and a row's six chunks sit rotated by (row % 128 >> 2) & 1 positions, the
+// GEMM's LDS stage image.  NP = pairs per row (ceil(K/128)).
+constexpr int FP6_TILE_ROWS = 128;
+constexpr int FP6_PAIR_BYTES = FP6_TILE_ROWS * 96;      // 12 KB
+__host__ __device__ __forceinline__ size_t fp6_tiled_chunk(int row, int g, int c, int NP) {
+    const int t = row >> 7, rho = row & 127, s = g >> 1;
+    const int slot = (3 * (g & 1) + c + ((rho >> 2) & 1)) % 6;
+    return ((size_t)t * NP + s) * FP6_PAIR_BYTES + (size_t)rho * 96 + 16 * slot;
+}
+__host__ __device__ __forceinline__ size_t fp6_tiled_bytes(int rows, int K) {
+    return (size_t)((rows + FP6_TILE_ROWS - 1) / FP6_TILE_ROWS) * (size_t)((K / 64 + 1) / 2) * FP6_PAIR_BYTES;
+}
+
 }  // namespace svdq

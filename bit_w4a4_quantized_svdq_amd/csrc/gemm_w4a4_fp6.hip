@@ -7,11 +7,11 @@
 // "Hugging Face integrates Nunchaku 4-bit diffusion inference into
 // Diffusers", "SVDQuant and the Nunchaku engine").
 //
-// Operands.  Both sides arrive in the FP6 layout (activation step with the
-// FP6 output, weights re-encoded once by svdq_pack_weight_fp6): per row and
-// group a 48-byte block of two 192-bit strings, one per K-half, field j =
-// E2M3 code of q/2 for channel 32h + j; block bytes [h0 dw0-3 | h1 dw0-3 |
-// h0 dw4-5 | h1 dw4-5].  Every int4 code is exact in E2M3 (q/2 in
+// Operands.  Both sides arrive in the FP6 tiled layout (activation step
+// with the FP6 output, weights re-encoded once by svdq_pack_weight_fp6;
+// fp6_tiled_chunk): per row and group two 192-bit strings, one per K-half,
+// field j = E2M3 code of q/2 for channel 32h + j, as 16-byte chunks [h0
+// dw0-3 | h1 dw0-3 | h0 dw4-5, h1 dw4-5].  Every int4 code is exact in E2M3 (q/2 in
 // {0, +-0.5, ..., +-4}), so v_mfma_scale_f32_32x32x64_f8f6f4 in its FP6 form
 // with E8M0 block scales 2^1 on both sides returns X_g exactly in fp32, at
 // the FP6/FP4 rate (half the cycles of the FP8 form) and with no conversion
@@ -35,18 +35,18 @@
 // Data movement.  256 threads own a 128x128 output tile (4 waves of 64x64,
 // each 2x2 tiles of 32x32).  Stages hold two groups: 96 bytes of each of the
 // tile's 128 A rows and 128 B rows (24 KB), written by buffer loads straight
-// into LDS; two stages alternate (48 KB, three blocks per CU).  A stage's
-// 12 KB per operand is filled by 12 copies of 1 KB; copy q, lane i writes
-// LDS chunk p = 64q + i (16 bytes) = slot p % 6 of row p / 6, which receives
-// the row's chunk (slot - rot) mod 6, rot = (row >> 2) & 1: the rotation
-// moves rows r+4 .. r+7 by 16 bytes against rows r .. r+3, so the eight rows
-// that one LDS cycle of a 16-byte fragment read serves fall on distinct
-// banks.  One barrier per stage; the copies of stage s+1 go out right after
-// it and land while stage s is computed.  Rows past M (columns past N) lie
-// beyond the buffer descriptor's range and read as zeros.  When K/64 is odd
-// the last stage's second group reads past the row (the next row's codes, or
-// zeros past the operand): its scales are taken as zero, and since E2M3
-// values are finite, X * 0 adds nothing.
+// into LDS; two stages alternate (48 KB, three blocks per CU).  In the tiled
+// layout a stage's 12 KB of one operand is one contiguous block already in
+// the LDS arrangement, so 12 copies of 1 KB (whole cache lines, lane i at
+// byte 16i) fill it: row r's chunk c sits in slot (c + rot) mod 6 of its 96
+// bytes, rot = (r >> 2) & 1, which moves rows r+4 .. r+7 by 16 bytes against
+// rows r .. r+3, so the eight rows that one LDS cycle of a 16-byte fragment
+// read serves fall on distinct banks.  One barrier per stage; the copies of
+// stage s+1 go out right after it and land while stage s is computed.  Rows
+// past M (columns past N) of the last tile, and the second group of the last
+// pair when K/64 is odd, are padding the producers never write: they hold
+// some E2M3 values, all finite, which only feed outputs that are not stored,
+// or are multiplied by a zero scale.
 // Blocks are mapped to tiles so that each XCD walks a contiguous band of
 // tiles in groups of 8 M-tiles (tile_of_block).
 //
@@ -117,31 +117,25 @@ void gemm_w4a4_fp6_kernel(int M, int N, int K, int rank,
     const int m0 = bm * F6_BM, n0 = bn * F6_BN;
     const int NG = K >> 6;
     const int NP = (NG + 1) >> 1;                           // stages (pairs of groups)
-    const int rowbytes = NG * F6_GB;
+    const int tile_bytes = NP * FP6_PAIR_BYTES;             // one 128-row tile of an operand
 
-    // ---- producer: copy q = wave + 4u (u = 0, 1, 2) of each operand; its
-    // lane writes LDS chunk p = 64q + lane of the operand's 12 KB
+    // ---- producer: copy q = wave + 4u (u = 0, 1, 2) of each operand moves
+    // bytes 1024q .. 1024q + 1023 of the stage's 12 KB block (lane i: 16i)
+    static_assert(F6_OPER == FP6_PAIR_BYTES, "a stage holds one pair of the tiled layout");
     const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(act_codes + (size_t)m0 * rowbytes), (short)0, min(F6_BM, M - m0) * rowbytes, 0x00020000);
+        (void *)(act_codes + (size_t)bm * tile_bytes), (short)0, tile_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(wgt_codes + (size_t)n0 * rowbytes), (short)0, min(F6_BN, N - n0) * rowbytes, 0x00020000);
-    uint32_t c_off[F6_COPIES / 4];
-#pragma unroll
-    for (int u = 0; u < F6_COPIES / 4; ++u) {
-        const int p = 64 * (wave + 4 * u) + lane;
-        const int row = p / 6, slot = p % 6;
-        const int c = (slot + 6 - ((row >> 2) & 1)) % 6;
-        c_off[u] = (uint32_t)(row * rowbytes + 16 * c);
-    }
+        (void *)(wgt_codes + (size_t)bn * tile_bytes), (short)0, tile_bytes, 0x00020000);
+    const uint32_t c_off = (uint32_t)(1024 * wave + 16 * lane);
     // groups 2s, 2s+1 into stage `buf`
     auto issue_pair = [&](int s, int buf) {
         uint8_t *st = smem + buf * F6_STAGE;
 #pragma unroll
         for (int u = 0; u < F6_COPIES / 4; ++u) {
             const int q = wave + 4 * u;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lptr_t)(st + q * 1024), 16, c_off[u], s * F6_ROWB, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lptr_t)(st + F6_OPER + q * 1024), 16, c_off[u],
-                                                     s * F6_ROWB, 0, 0);
+            const int soff = s * F6_OPER + 4096 * u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lptr_t)(st + q * 1024), 16, c_off, soff, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lptr_t)(st + F6_OPER + q * 1024), 16, c_off, soff, 0, 0);
         }
     };
 

@@ -38,19 +38,22 @@
 //    nearest value with ties to the even code.  v comes from the same Newton
 //    step; ties are exact and non-ties stay 2^-11 (relative) away.
 //
-// FP6 layout (PREC 2, int4 codes for the FP6 GEMM): the same codes q in
-// [-8, 7], written as E2M3 values q/2 (exact: every integer up to 8 has at
-// most three significant bits) in the operand layout of the gfx950 block-
-// scaled matrix instruction.  Per row and group of 64 a 48-byte block holds
-// two 192-bit strings, one per K-half h: field j (bits 6j .. 6j+5) is the
-// code of channel 32h + j.  Byte layout of the block: [h0 dwords 0-3 |
-// h1 dwords 0-3 | h0 dwords 4-5 | h1 dwords 4-5], so a GEMM lane reads its
-// 24 bytes as one 16-byte and one 8-byte piece.  A lane converts its 16
-// codes with one v_cvt_scalef32_2xpk16_fp6_f32 (two 16-value sources whose
-// fields interleave: field 2i from the first, 2i+1 from the second; the
-// scale divides, so 2.0 turns q into q/2), giving its 48 bits of each half;
-// two lane swaps (v_permlane16_swap, v_permlane32_swap) gather a whole half
-// string in each lane, and one store per lane writes a 16- or 8-byte piece.
+// FP6 tiled layout (PREC 2, int4 codes for the FP6 GEMM): the same codes q
+// in [-8, 7], written as E2M3 values q/2 (exact: every integer up to 8 has
+// at most three significant bits) in the operand layout of the gfx950
+// block-scaled matrix instruction.  Per row and group of 64, two 192-bit
+// strings, one per K-half h: field j (bits 6j .. 6j+5) is the code of
+// channel 32h + j; as three 16-byte chunks [h0 dwords 0-3 | h1 dwords 0-3 |
+// h0 dwords 4-5, h1 dwords 4-5], so a GEMM lane reads its 24 bytes as one
+// 16-byte and one 8-byte piece.  Rows are stored in tiles of 128 and groups
+// in pairs, each (tile, pair) a contiguous 12 KB image of the GEMM's LDS
+// stage (fp6_tiled_chunk): the GEMM copies it with whole-line loads.
+// A lane converts its 16 codes with one v_cvt_scalef32_2xpk16_fp6_f32 (two
+// 16-value sources whose fields interleave: field 2i from the first, 2i+1
+// from the second; the scale divides, so 2.0 turns q into q/2), giving its
+// 48 bits of each half; two lane swaps (v_permlane16_swap,
+// v_permlane32_swap) gather a whole half string in each lane, and one store
+// per lane writes a 16- or 8-byte piece.
 //
 // GELU variant (a layer fed by a GELU MLP's up projection): x is first
 // mapped through GELU (tanh form) of bf16 to bf16, exact by construction
@@ -154,12 +157,14 @@ __device__ __noinline__ F16 int4_q_exact(F16 xh, float sb) {
 
 typedef float v16f_q __attribute__((ext_vector_type(16)));
 
-// The 16 codes of one lane (q[0..7]: channels 8kq..8kq+7 of the group's
+// The 16 codes of one lane (q[0..7]: channels 8kq..8kq+7 of group g's
 // first K-half, q[8..15]: the same of the second), integers in [-8, 7] held
-// as floats, into the group's 48-byte FP6 block.  Lanes kq = 0..3 of a row
-// are lanes r + 16 kq; every lane of the wave takes part (the swaps are
+// as floats, into the group's three chunks of the FP6 tiled layout (codes:
+// the tensor, NP = pairs of groups per row).  Lanes kq = 0..3 of a row are
+// lanes r + 16 kq; every lane of the wave takes part (the swaps are
 // wave-wide), only lanes with store set write.
-__device__ __forceinline__ void store_fp6_group(const float (&q)[16], uint8_t *blk, bool store, int kq) {
+__device__ __forceinline__ void store_fp6_group(const float (&q)[16], uint8_t *codes, int row, int g, int NP,
+                                                bool store, int kq) {
     v16f_q a, b;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -196,8 +201,8 @@ __device__ __forceinline__ void store_fp6_group(const float (&q)[16], uint8_t *b
     }
     if (store) {
         const int half = kq & 1;
-        if (kq < 2) *(v4u *)(blk + 16 * half) = v4u{d[0], d[1], d[2], sr[0]};
-        else *(v2u *)(blk + 32 + 8 * half) = v2u{sr[1], sr[2]};
+        if (kq < 2) *(v4u *)(codes + fp6_tiled_chunk(row, g, half, NP)) = v4u{d[0], d[1], d[2], sr[0]};
+        else *(v2u *)(codes + fp6_tiled_chunk(row, g, 2, NP) + 8 * half) = v2u{sr[1], sr[2]};
     }
 }
 
@@ -346,7 +351,7 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
                 // a zero code is +0 in the layout (rint keeps the sign of -0.4)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) q[e] += 0.0f;
-                store_fp6_group(q, codes + (size_t)min(row, M - 1) * (size_t)(48 * NG) + g * 48, row_ok, kq);
+                store_fp6_group(q, codes, row, g, (NG + 1) >> 1, row_ok, kq);
                 if (row_ok && kq == 0) ((uint16_t *)scales)[(size_t)row * NG + g] = (uint16_t)sbits;
             } else if constexpr (PREC == 0) {
                 // ---- int4, group 64: absmax over the row's 4 lanes

@@ -374,10 +374,10 @@ svdq_status svdq_debug_group_sums_fp6(int64_t M, int64_t N, int64_t K, const voi
     return group_sums_common(2, "svdq_debug_group_sums_fp6", M, N, K, act_codes, fp6_weight, G, stream);
 }
 
-int64_t svdq_fp6_weight_bytes(int64_t N, int64_t K)
+int64_t svdq_fp6_codes_bytes(int64_t rows, int64_t K)
 {
-    if (check_shape(1, N, K, 0) != SVDQ_OK) return -1;
-    return (int64_t)svdq::fp6_weight_bytes((int)N, (int)K);
+    if (check_shape(rows, 1, K, 0) != SVDQ_OK) return -1;
+    return (int64_t)svdq::fp6_weight_bytes((int)rows, (int)K);
 }
 
 svdq_status svdq_pack_weight_fp6(int64_t N, int64_t K, const void *wgt_codes, void *fp6_weight, void *stream)
@@ -437,6 +437,6 @@ const char *svdq_status_string(svdq_status s)
 
 const char *svdq_last_error(void) { return g_last_error; }
 
-int32_t svdq_abi_version(void) { return 9; }
+int32_t svdq_abi_version(void) { return 10; }
 
 }  // extern "C"

@@ -40,10 +40,10 @@ def pack_weight_int4(wgt_codes, wgt_scales):
 
 
 def pack_weight_fp6(wgt_codes):
-    """Device int4 codes [N, K/2] -> their FP6 layout [N, 3K/4] (the weight
+    """Device int4 codes [N, K/2] -> their FP6 tiled layout (the weight
     operand of the SVDQ_INT4_FP6 GEMM)."""
     N, Kh = wgt_codes.shape
-    out = torch.empty((N, 3 * Kh // 2), dtype=torch.uint8, device=wgt_codes.device)
+    out = torch.empty((capi.svdq_fp6_codes_bytes(N, 2 * Kh),), dtype=torch.uint8, device=wgt_codes.device)
     capi.svdq_pack_weight_fp6(wgt_codes, out)
     return out
 
@@ -94,8 +94,9 @@ class SVDQW4A4Linear:
         if b is None:
             d = self.device
             sdt = torch.bfloat16 if self.prec == capi.SVDQ_INT4 else torch.uint8
-            cb = 3 * self.K // 4 if self.act_prec == capi.SVDQ_INT4_FP6 else self.K // 2
-            b = {"codes": torch.empty((M, cb), dtype=torch.uint8, device=d),
+            shape = ((capi.svdq_fp6_codes_bytes(M, self.K),) if self.act_prec == capi.SVDQ_INT4_FP6
+                     else (M, self.K // 2))
+            b = {"codes": torch.empty(shape, dtype=torch.uint8, device=d),
                  "scales": torch.empty((M, self.K // self.group), dtype=sdt, device=d),
                  "lora_act": torch.empty((M, max(self.rank, 1)), dtype=torch.float32, device=d),
                  "out": torch.empty((M, self.N), dtype=torch.bfloat16, device=d)}

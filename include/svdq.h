@@ -57,23 +57,31 @@ typedef enum svdq_status {
 /* precision of the W4A4 layer ("Supported quantization types" table).
  * SVDQ_INT4_PACKED is int4 with the weight in the packed form written by
  * svdq_pack_weight_int4; its activations are int4's.  SVDQ_INT4_FP6 is int4
- * (the same codes and scales) with both operands' codes in the FP6 layout:
+ * (the same codes and scales) with both operands' codes in the FP6 tiled layout:
  * the activations from svdq_quantize_act / svdq_gelu_quantize_act called
  * with SVDQ_INT4_FP6, the weight from svdq_pack_weight_fp6 (the GEMM's
  * fastest path).
  *
- * FP6 layout of int4 codes ([rows, 3K/4] bytes): per row and group of 64 a
- * 48-byte block (group g at byte 48g of the row) holding two 192-bit strings,
- * one per half h of the group; field j of a string (bits 6j .. 6j+5) is the
- * E2M3 encoding (sign bit 5, two exponent bits with bias 1, three mantissa
- * bits) of q/2 for channel 64g + 32h + j, exact for every q in [-8, 7].  The
- * block's 32-bit words are [h0 words 0-3 | h1 words 0-3 | h0 words 4-5 |
- * h1 words 4-5], bits numbered from the least significant bit of word 0. */
+ * FP6 tiled layout of int4 codes [rows, K] (svdq_fp6_codes_bytes(rows, K)
+ * bytes): per row and group of 64, two 192-bit strings, one per half h of
+ * the group; field j of a string (bits 6j .. 6j+5) is the E2M3 encoding (sign
+ * bit 5, two exponent bits with bias 1, three mantissa bits) of q/2 for
+ * channel 64g + 32h + j, exact for every q in [-8, 7] (a zero code is +0).
+ * Bits are numbered from the least significant bit of word 0 of a string.
+ * A row's group g is three 16-byte chunks: c = 0: words 0-3 of h0, c = 1:
+ * words 0-3 of h1, c = 2: words 4-5 of h0 then words 4-5 of h1.  Rows are
+ * stored in tiles of 128 (the last one padded) and groups in pairs (the last
+ * one padded when K/64 is odd); chunk c of group g of row r is at byte
+ *   ((r / 128) * ceil(K/128) + g / 2) * 12288 + (r % 128) * 96
+ *     + 16 * ((3 * (g % 2) + c + ((r % 128) / 4) % 2) mod 6),
+ * so each (tile, pair) is one contiguous 12 KB block: the GEMM's LDS stage,
+ * copied with whole cache lines.  Padding is never written or needed: the
+ * GEMM only multiplies it into outputs it does not store, or by a zero scale. */
 enum {
     SVDQ_INT4 = 0 /* group 64, bf16 scales */,
     SVDQ_NVFP4 = 1 /* group 16, E4M3 scales */,
     SVDQ_INT4_PACKED = 2 /* int4, weight from svdq_pack_weight_int4 (GEMM calls only) */,
-    SVDQ_INT4_FP6 = 3 /* int4, codes of both operands in the FP6 layout */
+    SVDQ_INT4_FP6 = 3 /* int4, codes of both operands in the FP6 tiled layout */
 };
 
 /*
@@ -89,11 +97,12 @@ enum {
  * against the rule above; lora_act is an fp32 sum in unspecified order.
  *
  *   precision  SVDQ_INT4, SVDQ_NVFP4 or SVDQ_INT4_FP6 (int4's codes and
- *              scales, the codes written in the FP6 layout)
+ *              scales, the codes written in the FP6 tiled layout)
  *   x          bf16 [M, K]
  *   smooth     bf16 [K] smoothing factors; NULL means 1
  *   lora_down  bf16 [rank, K]; ignored (may be NULL) when rank == 0
- *   act_codes  out: u8 [M, K/2]; SVDQ_INT4_FP6: u8 [M, 3K/4] (FP6 layout)
+ *   act_codes  out: u8 [M, K/2]; SVDQ_INT4_FP6: the FP6 tiled layout,
+ *              svdq_fp6_codes_bytes(M, K) bytes
  *   act_scales out: int4 bf16 [M, K/64]; nvfp4 u8 (E4M3) [M, K/16]
  *   lora_act   out: fp32 [M, rank]; ignored (may be NULL) when rank == 0
  */
@@ -134,7 +143,7 @@ svdq_status svdq_gelu_quantize_act(int32_t precision, int64_t M, int64_t K, int3
  *   wgt_codes  u8 [N, K/2] (int4 or E2M1 codes of the 4-bit residual);
  *              SVDQ_INT4_PACKED: the svdq_pack_weight_int4 blob of them
  *              (svdq_packed_weight_bytes(N, K) bytes); SVDQ_INT4_FP6: the
- *              svdq_pack_weight_fp6 form (u8 [N, 3K/4])
+ *              svdq_pack_weight_fp6 form (svdq_fp6_codes_bytes(N, K) bytes)
  *   wgt_scales int4 bf16 [N, K/64]; nvfp4 u8 (E4M3) [N, K/16]
  *   alpha      scale of the 4-bit term (per-tensor; 1.0f for int4)
  *   lora_act   fp32 [M, rank]; lora_up bf16 [N, rank]; ignored when rank == 0
@@ -294,16 +303,19 @@ svdq_status svdq_pack_weight_int4(int64_t N, int64_t K, const void *wgt_codes, c
 
 /*
  * svdq_pack_weight_fp6 -- offline re-encoding of an int4 weight for the
- * SVDQ_INT4_FP6 GEMM: the codes in the FP6 layout (see the precision enum).
+ * SVDQ_INT4_FP6 GEMM: the codes in the FP6 tiled layout (see the
+ * precision enum).
  * gfx950's block-scaled matrix instruction takes E2M3 operands at twice its
  * FP8 rate and returns fp32, and every int4 code is an exact E2M3 value
  * (q/2), so the GEMM feeds both operands to the matrix cores as they are
  * stored.  Every code, -8 included, has an exact form.
  *   wgt_codes   u8 [N, K/2] two's complement int4 codes (svdq_gemm_w4a4's)
- *   fp6_weight  out: u8 [N, 3K/4] = svdq_fp6_weight_bytes(N, K) bytes, device
+ *   fp6_weight  out: u8 [svdq_fp6_codes_bytes(N, K)], device
  * The weight's scales stay a separate argument of the GEMM.
  */
-int64_t svdq_fp6_weight_bytes(int64_t N, int64_t K);   /* 3*N*K/4; -1 if invalid */
+/* bytes of [rows, K] int4 codes in the FP6 tiled layout:
+ * ceil(rows/128) * ceil(K/128) * 12288; -1 if rows or K is invalid */
+int64_t svdq_fp6_codes_bytes(int64_t rows, int64_t K);
 svdq_status svdq_pack_weight_fp6(int64_t N, int64_t K, const void *wgt_codes, void *fp6_weight, void *stream);
 
 /*
@@ -328,7 +340,7 @@ svdq_status svdq_debug_group_sums_packed(int64_t M, int64_t N, int64_t K, const 
 /*
  * svdq_debug_group_sums_fp6 -- the same integer group sums G [M, N, K/64]
  * from the main loop of the SVDQ_INT4_FP6 GEMM (E2M3 matrix-core products):
- * act_codes in the FP6 layout (svdq_quantize_act with SVDQ_INT4_FP6),
+ * act_codes in the FP6 tiled layout (svdq_quantize_act with SVDQ_INT4_FP6),
  * fp6_weight from svdq_pack_weight_fp6.
  */
 svdq_status svdq_debug_group_sums_fp6(int64_t M, int64_t N, int64_t K, const void *act_codes,
@@ -363,14 +375,14 @@ const char *svdq_status_string(svdq_status s);
 /* Text of the last argument-check failure on the calling thread ("" if none). */
 const char *svdq_last_error(void);
 
-/* ABI version of this header: 9 (1 plus svdq_gelu_quantize_act, svdq_debug_gelu_bf16,
+/* ABI version of this header: 10 (1 plus svdq_gelu_quantize_act, svdq_debug_gelu_bf16,
  * svdq_gemm_w4a4_qk_norm_rope, svdq_smooth_factors, svdq_quantize_weight,
  * svdq_lowrank_workspace_bytes, svdq_lowrank_factors,
  * svdq_lowrank_factors_noalloc, then SVDQ_INT4_PACKED with
  * svdq_packed_weight_bytes, svdq_pack_weight_int4 and
  * svdq_debug_group_sums_packed, then svdq_debug_stream_read, then
- * SVDQ_INT4_FP6 with svdq_fp6_weight_bytes, svdq_pack_weight_fp6 and
- * svdq_debug_group_sums_fp6). */
+ * SVDQ_INT4_FP6 with svdq_fp6_codes_bytes, svdq_pack_weight_fp6 and
+ * svdq_debug_group_sums_fp6, in the FP6 tiled layout). */
 int32_t svdq_abi_version(void);
 
 #ifdef __cplusplus

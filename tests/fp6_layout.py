@@ -1,14 +1,18 @@
-"""Host-side FP6 layout of int4 codes, written from its definition in
-include/svdq.h (the precision enum): per row and group of 64 a 48-byte
-block of two 192-bit strings, one per half h of the group; field j (bits
-6j .. 6j+5) is the E2M3 encoding of q/2 for channel 64g + 32h + j; the
-block's 32-bit words are [h0 0-3 | h1 0-3 | h0 4-5 | h1 4-5].
+"""Host-side FP6 tiled layout of int4 codes, written from its definition in
+include/svdq.h (the precision enum): per row and group of 64, two 192-bit
+strings, one per half h of the group; field j (bits 6j .. 6j+5) is the E2M3
+encoding of q/2 for channel 64g + 32h + j; the group is three 16-byte chunks
+[h0 words 0-3 | h1 words 0-3 | h0 words 4-5, h1 words 4-5]; chunk c of group
+g of row r sits at
+  ((r / 128) * ceil(K/128) + g / 2) * 12288 + (r % 128) * 96
+    + 16 * ((3 * (g % 2) + c + ((r % 128) / 4) % 2) mod 6).
 
 E2M3 (the OCP microscaling FP6 format): sign bit 5, exponent bits 3-4 with
 bias 1, mantissa bits 0-2; exponent 0 encodes the subnormals m/8, exponent
 e > 0 the value 2^(e-1) * (1 + m/8).  This module is test infrastructure:
 the tests compare the library's FP6 encoders (the activation step's and the
-weight packer's) with it, and feed the FP6 GEMM from it."""
+weight packer's) with it, and feed the FP6 GEMM from it.  Bytes the layout
+leaves as padding are given a fill value (the GPU tests' 0xFF poison)."""
 from __future__ import annotations
 
 import numpy as np
@@ -52,22 +56,48 @@ def _strings_to_block(fields):
     return order.view(np.uint8).reshape(lead + (48,))
 
 
-def fp6_layout_from_q(q):
-    """Integer codes q [R, K] in [-8, 7] -> FP6 layout bytes [R, 3K/4]."""
+def fp6_codes_bytes(R, K):
+    return -(-R // 128) * -(-K // 128) * 12288
+
+
+def chunk_offset(r, g, c, K):
+    """Byte offset of chunk c (0..2) of group g of row r (the documented formula)."""
+    NP = -(-K // 128)
+    rho = r % 128
+    slot = (3 * (g % 2) + c + (rho // 4) % 2) % 6
+    return ((r // 128) * NP + g // 2) * 12288 + rho * 96 + 16 * slot
+
+
+def fp6_layout_from_q(q, fill=0xFF):
+    """Integer codes q [R, K] in [-8, 7] -> the FP6 tiled layout (uint8, 1-D)."""
     q = np.asarray(q, np.int64)
     R, K = q.shape
-    fields = e2m3_encode(q / 2.0).reshape(R, K // 64, 2, 32)
-    return _strings_to_block(fields).reshape(R, 3 * K // 4)
+    NG = K // 64
+    blocks = _strings_to_block(e2m3_encode(q / 2.0).reshape(R, NG, 2, 32))      # [R, NG, 48]
+    out = np.full(fp6_codes_bytes(R, K), fill, np.uint8)
+    r = np.arange(R)[:, None]
+    g = np.arange(NG)[None, :]
+    for c in range(3):
+        off = np.vectorize(chunk_offset)(r, g, c, K)                              # [R, NG]
+        idx = off[..., None] + np.arange(16)
+        out[idx] = blocks[..., 16 * c:16 * c + 16]
+    return out
 
 
-def q_from_fp6_layout(b, K):
-    """FP6 layout bytes [R, 3K/4] -> integer codes [R, K] (2 * the E2M3 values)."""
-    b = np.ascontiguousarray(b, np.uint8)
-    R = b.shape[0]
-    words = b.reshape(R, K // 64, 12, 4).view(np.uint32)[..., 0].astype(np.uint64)
+def q_from_fp6_layout(b, R, K):
+    """The FP6 tiled layout -> integer codes [R, K] (2 * the E2M3 values)."""
+    b = np.asarray(b, np.uint8)
+    NG = K // 64
+    r = np.arange(R)[:, None]
+    g = np.arange(NG)[None, :]
+    blocks = np.empty((R, NG, 48), np.uint8)
+    for c in range(3):
+        off = np.vectorize(chunk_offset)(r, g, c, K)
+        blocks[..., 16 * c:16 * c + 16] = b[off[..., None] + np.arange(16)]
+    words = blocks.view(np.uint32).astype(np.uint64)                             # [R, NG, 12]
     halves = [np.concatenate([words[..., 0:4], words[..., 8:10]], axis=-1),
               np.concatenate([words[..., 4:8], words[..., 10:12]], axis=-1)]
-    out = np.empty((R, K // 64, 2, 32), np.int64)
+    out = np.empty((R, NG, 2, 32), np.int64)
     for h, wd in enumerate(halves):
         for j in range(32):
             bit = 6 * j
@@ -76,16 +106,19 @@ def q_from_fp6_layout(b, K):
             if o > 26:
                 v |= wd[..., w + 1] << np.uint64(32 - o)
             out[..., h, j] = (v & np.uint64(63)).astype(np.int64)
-    vals = e2m3_value(out) * 2.0
-    return vals.reshape(R, K).astype(np.int64)
+    return (e2m3_value(out) * 2.0).reshape(R, K).astype(np.int64)
 
 
-def fp6_layout_from_nibbles(codes, K):
-    """Packed two's-complement nibbles [R, K/2] -> FP6 layout [R, 3K/4]."""
+def nibbles_to_q(codes, K):
     c = np.asarray(codes, np.uint8)
     lo = (c & 15).astype(np.int64)
     hi = (c >> 4).astype(np.int64)
     q = np.empty((c.shape[0], K), np.int64)
     q[:, 0::2] = np.where(lo >= 8, lo - 16, lo)
     q[:, 1::2] = np.where(hi >= 8, hi - 16, hi)
-    return fp6_layout_from_q(q)
+    return q
+
+
+def fp6_layout_from_nibbles(codes, K, fill=0xFF):
+    """Packed two's-complement nibbles [R, K/2] -> the FP6 tiled layout."""
+    return fp6_layout_from_q(nibbles_to_q(codes, K), fill)

@@ -130,7 +130,7 @@ def gpu_quantize(prec, x, smooth, lora_down, K, gelu=False):
     M = x.shape[0]
     rank = 0 if lora_down is None else lora_down.shape[0]
     int4 = prec in (0, 3)
-    codes = poison(empty((M, 3 * K // 4 if prec == 3 else K // 2), "u8"))
+    codes = poison(empty((capi.svdq_fp6_codes_bytes(M, K),) if prec == 3 else (M, K // 2), "u8"))
     scales = poison(empty((M, K // 64), "bf16") if int4 else empty((M, K // 16), "u8"))
     lact = poison(empty((M, rank), "f32")) if rank else None
     fn = capi.svdq_gelu_quantize_act if gelu else capi.svdq_quantize_act
@@ -141,10 +141,11 @@ def gpu_quantize(prec, x, smooth, lora_down, K, gelu=False):
 
 
 def gpu_pack_weight_fp6(wgt_codes_dev):
-    """The FP6 layout [N, 3K/4] of device int4 codes (svdq_pack_weight_fp6)."""
+    """The FP6 tiled layout of device int4 codes (svdq_pack_weight_fp6), in a
+    poisoned buffer: padding the packer must not write stays 0xFF."""
     from bit_w4a4_quantized_svdq_amd import capi
     N, Kh = wgt_codes_dev.shape
-    out = poison(empty((N, 3 * Kh // 2), "u8"))
+    out = poison(empty((capi.svdq_fp6_codes_bytes(N, 2 * Kh),), "u8"))
     capi.svdq_pack_weight_fp6(wgt_codes_dev, out)
     return out
 
@@ -188,7 +189,7 @@ def gpu_gemm(prec, act_codes, act_scales, wgt_codes, wgt_scales, lora_act, lora_
         if act_fp6 is not None:
             act_codes = act_fp6
         else:
-            act_codes = fp6_layout_from_nibbles(act_codes, K) if K else np.zeros((M, 0), np.uint8)
+            act_codes = fp6_layout_from_nibbles(act_codes, K)
         wc, prec = gpu_pack_weight_fp6(wc), capi.SVDQ_INT4_FP6
     capi.svdq_gemm_w4a4(prec, to_dev(act_codes, "u8"), to_dev(act_scales, skind), wc, ws, alpha,
                         to_dev(lora_act, "f32"), to_dev(lora_up, "bf16"), to_dev(bias, "bf16"), out)

@@ -116,8 +116,9 @@ int main() {
                   "gemm precision 4");
 
     // ---- FP6 layout of int4 weights
-    EXPECT(svdq_fp6_weight_bytes(12288, 3072) == 12288ll * 3072 * 3 / 4, "fp6 bytes");
-    EXPECT(svdq_fp6_weight_bytes(8, 100) == -1, "fp6 bytes, K % 64");
+    EXPECT(svdq_fp6_codes_bytes(12288, 3072) == 12288ll * 3072 * 3 / 4, "fp6 bytes");
+    EXPECT(svdq_fp6_codes_bytes(130, 4160) == 2ll * 33 * 12288, "fp6 bytes, padded tile and pair");
+    EXPECT(svdq_fp6_codes_bytes(8, 100) == -1, "fp6 bytes, K % 64");
     expect_launch(svdq_pack_weight_fp6(12288, 3072, P, P, nullptr), "pack_weight_fp6", 12288, 3072, 0);
     expect_noop(svdq_pack_weight_fp6(0, 64, P, P, nullptr), "pack fp6 N=0");
     expect_reject(svdq_pack_weight_fp6(5, 64, nullptr, P, nullptr), INV, "pack fp6 codes NULL");

@@ -84,7 +84,7 @@ hipError_t launch_awq_gemv(int M, int N, int K, const void *, const void *, cons
                            const void *, void *, hipStream_t) {
     return rec("awq_gemv", M, N, K);
 }
-size_t fp6_weight_bytes(int N, int K) { return (size_t)N * (K / 64) * 48; }
+size_t fp6_weight_bytes(int N, int K) { return (size_t)((N + 127) / 128) * (size_t)((K / 64 + 1) / 2) * 12288u; }
 hipError_t launch_pack_weight_fp6(int N, int K, const void *, void *, hipStream_t) {
     return rec("pack_weight_fp6", N, K, 0);
 }

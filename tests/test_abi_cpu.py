@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(capi.LIB_PATH)
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert capi.svdq_abi_version() == 9
+    assert capi.svdq_abi_version() == 10
     for s in range(4):
         assert capi.svdq_status_string(s).startswith(("SVDQ_OK", "SVDQ_ERR"))
     assert "unknown" in capi.svdq_status_string(99)
@@ -214,13 +214,15 @@ def test_packed_weight_entry_points_host_checks():
 
 
 def test_fp6_entry_points_host_checks():
-    """svdq_fp6_weight_bytes and the host-side checks of the FP6-layout entry
+    """svdq_fp6_codes_bytes and the host-side checks of the FP6-layout entry
     points (every rejection happens before a launch)."""
     L = capi.lib()
-    assert capi.svdq_fp6_weight_bytes(12288, 3072) == 12288 * 3072 * 3 // 4
-    assert capi.svdq_fp6_weight_bytes(1, 64) == 48
-    assert capi.svdq_fp6_weight_bytes(8, 100) == -1
-    assert capi.svdq_fp6_weight_bytes(-1, 64) == -1
+    # tiles of 128 rows x pairs of groups, 12 KB each (padded)
+    assert capi.svdq_fp6_codes_bytes(12288, 3072) == 12288 * 3072 * 3 // 4
+    assert capi.svdq_fp6_codes_bytes(1, 64) == 12288
+    assert capi.svdq_fp6_codes_bytes(130, 4160) == 2 * 33 * 12288
+    assert capi.svdq_fp6_codes_bytes(8, 100) == -1
+    assert capi.svdq_fp6_codes_bytes(-1, 64) == -1
     pk = lambda N=64, K=128, c=A, out=A: L.svdq_pack_weight_fp6(N, K, c, out, None)
     assert pk(K=96) == INV
     assert pk(c=0) == INV

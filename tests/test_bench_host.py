@@ -78,9 +78,13 @@ def test_utilisation_and_gemv_traffic_summaries(tmp_path, monkeypatch):
     _write_counters(str(run / "pmc_copy_WRITE_SIZE"), [(1, c, "WRITE_SIZE", 256 * 1024)])
     _write_counters(str(run / "pmc_gemv_FETCH_SIZE"), [(1, v, "FETCH_SIZE", 15625.0), (2, v, "FETCH_SIZE", 15625.0)])
     _write_counters(str(run / "pmc_gemv_WRITE_SIZE"), [(1, v, "WRITE_SIZE", 36.0)])
-    # GRBM_GUI_ACTIVE comes once per XCD: their mean, not their sum
-    _write_counters(str(run / "pmc_gemm_clock"), [(1, g, "GRBM_GUI_ACTIVE", 300000.0), (1, g, "GRBM_GUI_ACTIVE", 300000.0),
-                                                  (1, g, "SQ_BUSY_CYCLES", 1)])
+    # GRBM_GUI_ACTIVE sums the XCDs' active cycles: divided by the agent's XCD count
+    _write_counters(str(run / "pmc_gemm_clock"), [(1, g, "GRBM_GUI_ACTIVE", 2400000.0), (1, g, "SQ_BUSY_CYCLES", 1)])
+    with open(run / "pmc_gemm_clock" / "run_agent_info.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Node_Id", "Agent_Type", "Num_Xcc"])
+        w.writeheader()
+        w.writerow({"Node_Id": 0, "Agent_Type": "CPU", "Num_Xcc": 1})
+        w.writerow({"Node_Id": 1, "Agent_Type": "GPU", "Num_Xcc": 8})
     util, traffic = tmp_path / "util.txt", tmp_path / "gemv.txt"
     monkeypatch.setattr(bench, "UTIL_FILE", str(util))
     monkeypatch.setattr(bench, "GEMV_TRAFFIC_FILE", str(traffic))

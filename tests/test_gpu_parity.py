@@ -280,7 +280,7 @@ def test_debug_group_sums_fp6_exact(M, N, K):
     announce("debug_group_sums_fp6", M, N, K)
     wf = gpu_pack_weight_fp6(to_dev(wc, "u8"))
     G = poison(empty((M, N, K // 64), "i32"))
-    capi.svdq_debug_group_sums_fp6(to_dev(fp6_layout_from_q(qa), "u8"), wf, N, G)
+    capi.svdq_debug_group_sums_fp6(to_dev(fp6_layout_from_q(qa), "u8"), wf, M, N, K, G)
     torch.cuda.synchronize()
     got = to_host(G, "i32")
     ref = oracle.group_sums_int4(ac, wc, K)
