@@ -144,11 +144,16 @@ def capture_step(torch, layers, xs):
     return g
 
 
-def gemv_sweep(torch, synth, reps=160):
+def gemv_sweep(torch, synth, rounds=12):
     """The W4A16 layer alone on the adaptive-norm weights (3072 -> 18432),
     rotating 16 weight copies (512 MB): M in {1,2,8} (the GEMV, GB/s against
-    HBM) and M in {256,1024,4096} (the library's GEMM regime, TFLOP/s against
-    the bf16 matrix-core peak)."""
+    HBM) next to a plain read of the M = 1 GEMV's bytes (contiguous and in
+    the GEMV's row pattern, svdq_debug_stream_read), all taking turns in each
+    round so that clock drift affects them alike; then M in {256,1024,4096}
+    (the library's GEMM regime, TFLOP/s against the bf16 matrix-core peak).
+    Each timing is a batch of 16 back-to-back launches (one per weight copy)
+    between two HIP events: a single launch bracketed by events would add the
+    launch gap (several us) to a kernel of ~10 us."""
     from bit_w4a4_quantized_svdq_amd import capi
     name, K, N, seed = ADALN
     copies = []
@@ -159,72 +164,64 @@ def gemv_sweep(torch, synth, reps=160):
                        torch.from_numpy(aw["wgt_zeros"].view(np.int16)).view(torch.bfloat16).cuda()])
     rng = np.random.default_rng(seed)
     x = torch.from_numpy(synth.to_bf16_bits(rng.standard_normal((4096, K))).view(np.int16)).view(torch.bfloat16).cuda()
-    out = {}
-    for M in (1, 2, 8, 256, 1024, 4096):
-        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-        for i in range(20):
-            c = copies[i % 16]
-            capi.awq_gemv_w4a16(x[:M], c[0], c[1], c[2], None, y)
-        torch.cuda.synchronize()
-        # batches of 16 back-to-back launches (one per weight copy) between two
-        # events: a single launch bracketed by events would add the launch gap
-        # (several us) to a kernel of ~10 us
-        ev = []
-        for i in range(reps // 16 if M <= 8 else 3):
-            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s.record()
-            for c in copies:
-                capi.awq_gemv_w4a16(x[:M], c[0], c[1], c[2], None, y)
-            e.record()
-            ev.append((s, e))
-        torch.cuda.synchronize()
-        us = float(np.median([s.elapsed_time(e) for s, e in ev])) * 1e3 / 16
-        if M <= 8:
-            gbps = algorithmic_bytes_gemv(M, N, K) / (us * 1e-6) / 1e9
-            out[f"M={M}"] = {"us": round(us, 3), "GB/s": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4)}
-        else:
-            tf = 2.0 * M * N * K / (us * 1e-6) / 1e12
-            out[f"M={M}"] = {"us": round(us, 3), "TFLOP/s": round(tf, 1),
-                             "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
-        print(f"[bench] awq M={M}: {us:.1f} us", file=sys.stderr, flush=True)
-    out["read_ceiling"] = read_ceiling(torch, algorithmic_bytes_gemv(1, N, K), reps)
-    m1 = out["M=1"]
-    for pat in ("contiguous", "gemv_rows"):
-        m1[f"frac_of_{pat}_read"] = round(out["read_ceiling"][pat]["us"] / m1["us"], 4)
-    return out
-
-
-def read_ceiling(torch, nbytes, reps=160):
-    """A plain read of ``nbytes`` (the M = 1 GEMV's algorithmic bytes) from 16
-    rotating 16-byte-aligned slices of one buffer (more than the Infinity
-    Cache), in batches of 16 launches between HIP events: contiguous, and in
-    the GEMV's row pattern (svdq_debug_stream_read)."""
-    from bit_w4a4_quantized_svdq_amd import capi
+    nbytes = algorithmic_bytes_gemv(1, N, K)
     span = (nbytes + 4095) // 4096 * 4096
     buf = torch.randint(0, 255, (16 * span,), dtype=torch.uint8, device="cuda")
     acc = torch.zeros((nbytes + capi.STREAM_READ_SPAN - 1) // capi.STREAM_READ_SPAN, dtype=torch.int32,
                       device="cuda")
-    res = {}
-    for pat, key in ((0, "contiguous"), (1, "gemv_rows")):
-        fn = lambda i: capi.svdq_debug_stream_read(buf[i * span:], acc, pat, nbytes)
-        for i in range(32):
-            fn(i % 16)
-        torch.cuda.synchronize()
-        ev = []
-        for _ in range(reps // 16):
+    ys = {M: torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for M in (1, 2, 8, 256, 1024, 4096)}
+
+    def gemv_batch(M):
+        return lambda: [capi.awq_gemv_w4a16(x[:M], c[0], c[1], c[2], None, ys[M]) for c in copies]
+
+    def read_batch(pat):
+        return lambda: [capi.svdq_debug_stream_read(buf[i * span:], acc, pat, nbytes) for i in range(16)]
+
+    kinds = {"M=1": gemv_batch(1), "M=2": gemv_batch(2), "M=8": gemv_batch(8),
+             "contiguous": read_batch(0), "gemv_rows": read_batch(1)}
+    for fn in kinds.values():
+        fn()
+        fn()
+    torch.cuda.synchronize()
+    ev = {k: [] for k in kinds}
+    for _ in range(rounds):
+        for k, fn in kinds.items():
             s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             s.record()
-            for i in range(16):
-                fn(i)
+            fn()
             e.record()
-            ev.append((s, e))
+            ev[k].append((s, e))
+    torch.cuda.synchronize()
+    us = {k: float(np.median([s.elapsed_time(e) for s, e in v])) * 1e3 / 16 for k, v in ev.items()}
+    out = {}
+    for M in (1, 2, 8):
+        gbps = algorithmic_bytes_gemv(M, N, K) / (us[f"M={M}"] * 1e-6) / 1e9
+        out[f"M={M}"] = {"us": round(us[f"M={M}"], 3), "GB/s": round(gbps, 1),
+                         "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4)}
+        print(f"[bench] awq M={M}: {us[f'M={M}']:.2f} us", file=sys.stderr, flush=True)
+    out["read_ceiling"] = {"bytes": int(nbytes)}
+    for k in ("contiguous", "gemv_rows"):
+        gbps = nbytes / (us[k] * 1e-6) / 1e9
+        out["read_ceiling"][k] = {"us": round(us[k], 3), "GB/s": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4)}
+        out["M=1"][f"frac_of_{k}_read"] = round(us[k] / us["M=1"], 4)
+        print(f"[bench] read ceiling {k}: {us[k]:.2f} us", file=sys.stderr, flush=True)
+    for M in (256, 1024, 4096):
+        fn = gemv_batch(M)
+        fn()
         torch.cuda.synchronize()
-        us = float(np.median([s.elapsed_time(e) for s, e in ev])) * 1e3 / 16
-        gbps = nbytes / (us * 1e-6) / 1e9
-        res[key] = {"us": round(us, 3), "GB/s": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4)}
-        print(f"[bench] read ceiling {key}: {us:.2f} us", file=sys.stderr, flush=True)
-    res["bytes"] = int(nbytes)
-    return res
+        evs = []
+        for _ in range(3):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            fn()
+            e.record()
+            evs.append((s, e))
+        torch.cuda.synchronize()
+        t = float(np.median([s.elapsed_time(e) for s, e in evs])) * 1e3 / 16
+        tf = 2.0 * M * N * K / (t * 1e-6) / 1e12
+        out[f"M={M}"] = {"us": round(t, 3), "TFLOP/s": round(tf, 1), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        print(f"[bench] awq M={M}: {t:.1f} us", file=sys.stderr, flush=True)
+    return out
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_int4_mlp_up_traffic.txt")

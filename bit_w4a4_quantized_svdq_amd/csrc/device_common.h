@@ -70,6 +70,23 @@ __device__ __forceinline__ float shfl_xor_f(float v, int mask) {
     return __shfl_xor(v, mask, kWave);
 }
 
+// max(v, v of lane l ^ 16) and max(v, v of lane l ^ 32) on the vector ALU:
+// v_permlane16_swap exchanges rows 1 and 3 of 16 lanes of its first operand
+// with rows 0 and 2 of its second, v_permlane32_swap the upper 32 lanes of
+// the first with the lower 32 of the second; with v in both operands every
+// lane ends up with its own value in one result and its partner's in the
+// other (no LDS round trip, as a cross-lane shuffle would take).
+__device__ __forceinline__ float max_xor16(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const auto s = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const auto s = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+
 // E4M3 ("FN") encode of a non-negative finite fp32, round to nearest even,
 // saturating at 448 (the format has no infinity).
 __device__ __forceinline__ uint32_t e4m3_encode_nonneg(float v) {

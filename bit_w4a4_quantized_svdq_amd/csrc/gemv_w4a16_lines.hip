@@ -14,7 +14,7 @@
 // products per instruction), which at one or two rows of x costs less than
 // the stream.
 //
-// Order of work in a block (3 waves, 24 weight rows):
+// Order of work in a block (4 waves, 32 weight rows):
 //   1. each thread issues its loads of x and of the block's scales and zero
 //      points, then all of its weight chunks;
 //   2. it waits for the first two only (loads complete in order), stores x
@@ -31,7 +31,7 @@
 
 namespace svdq {
 
-constexpr int AL_WAVES = 3, AL_THREADS = AL_WAVES * 64;
+constexpr int AL_WAVES = 4, AL_THREADS = AL_WAVES * 64;   // 3 and 6 measured slower at K = 3072
 constexpr int AL_ROWS = AL_WAVES * 8;               // weight rows per block
 constexpr int AL_MAX_K = 4096;                      // K / 256 <= 16 chunk loads per lane
 

@@ -159,12 +159,14 @@ typedef float v16f_q __attribute__((ext_vector_type(16)));
 
 // The 16 codes of one lane (q[0..7]: channels 8kq..8kq+7 of group g's
 // first K-half, q[8..15]: the same of the second), integers in [-8, 7] held
-// as floats, into the group's three chunks of the FP6 tiled layout (codes:
-// the tensor, NP = pairs of groups per row).  Lanes kq = 0..3 of a row are
+// as floats, into the group's three chunks of the FP6 tiled layout, here in
+// the block's LDS image of it: [pair][16 rows][96 bytes], row r's chunk c of
+// group g (g even: chunks 0-2, odd: 3-5) at slot (c + ((r >> 2) & 1)) mod 6
+// (a block's 16 rows start at a multiple of 16 in their 128-row tile, so
+// this is the rotation of the tiled layout).  Lanes kq = 0..3 of a row are
 // lanes r + 16 kq; every lane of the wave takes part (the swaps are
-// wave-wide), only lanes with store set write.
-__device__ __forceinline__ void store_fp6_group(const float (&q)[16], uint8_t *codes, int row, int g, int NP,
-                                                bool store, int kq) {
+// wave-wide).
+__device__ __forceinline__ void store_fp6_group(const float (&q)[16], uint8_t *img, int r, int g_local, int kq) {
     v16f_q a, b;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -199,11 +201,11 @@ __device__ __forceinline__ void store_fp6_group(const float (&q)[16], uint8_t *c
         d[i] = w[0];
         sr[i] = w[1];
     }
-    if (store) {
-        const int half = kq & 1;
-        if (kq < 2) *(v4u *)(codes + fp6_tiled_chunk(row, g, half, NP)) = v4u{d[0], d[1], d[2], sr[0]};
-        else *(v2u *)(codes + fp6_tiled_chunk(row, g, 2, NP) + 8 * half) = v2u{sr[1], sr[2]};
-    }
+    const int half = kq & 1, rot = (r >> 2) & 1;
+    uint8_t *rowimg = img + (g_local >> 1) * (16 * 96) + r * 96;
+    const int c0 = 3 * (g_local & 1);
+    if (kq < 2) *(v4u *)(rowimg + 16 * ((c0 + half + rot) % 6)) = v4u{d[0], d[1], d[2], sr[0]};
+    else *(v2u *)(rowimg + 16 * ((c0 + 2 + rot) % 6) + 8 * half) = v2u{sr[1], sr[2]};
 }
 
 template <int PREC, int RT, bool GELU>
@@ -222,13 +224,24 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
     __shared__ float s_inv[QA_CHUNK * 64];
     __shared__ float s_part[RT > 0 ? QA_WAVES * QA_ROWS * RT * 16 : 1];
     __shared__ uint16_t s_gelu[GELU ? GELU_TAB : 2];
+    // The chunk's codes and scales are staged in LDS and written out once per
+    // chunk with whole-line stores: storing each lane's 2 to 16 bytes as the
+    // groups are done costs one memory request per piece, and the vector
+    // memory path is what this kernel waits on.
+    //   PREC 2: [pair][16 rows][96 B], the FP6 tiled layout of these rows;
+    //   PREC 0/1: [16 rows][QA_OROW bytes] packed nibbles, row-major;
+    //   scales: [16 rows][QA_SROW bytes] (bf16 per group; NVFP4 4 E4M3 bytes).
+    constexpr int QA_OROW = QA_CHUNK * 32 + 16;        // +16: rows 0 and 8 share banks only
+    constexpr int QA_OUT = PREC == 2 ? QA_CHUNK / 2 * 16 * 96 : QA_ROWS * QA_OROW;
+    constexpr int QA_SROW = QA_CHUNK * (PREC == 1 ? 4 : 2) + 4;
+    __shared__ __attribute__((aligned(16))) uint8_t s_out[QA_OUT];
+    __shared__ __attribute__((aligned(16))) uint8_t s_osc[QA_ROWS * QA_SROW];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int r = lane & 15;
     const int kq = lane >> 4;
     const int row = blockIdx.x * QA_ROWS + r;
-    const bool row_ok = row < M;
     const int NG = K >> 6;
     const size_t xrow_off = (size_t)min(row, M - 1) * (size_t)K;   // rows past M: clamped, results not stored
 
@@ -324,8 +337,7 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
             if constexpr (PREC == 2) {
                 // ---- int4 codes in the FP6 layout: the same scale and codes
                 amax = fmaxf(amax_j[0], amax_j[1]);
-                amax = fmaxf(amax, shfl_xor_f(amax, 16));
-                amax = fmaxf(amax, shfl_xor_f(amax, 32));
+                amax = max_xor32(max_xor16(amax));
                 const float s_f = amax * (1.0f / 7.0f);
                 const uint32_t sbits = f32_to_bf16_rne(s_f);
                 const float sb = __uint_as_float(sbits << 16);
@@ -351,13 +363,12 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
                 // a zero code is +0 in the layout (rint keeps the sign of -0.4)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) q[e] += 0.0f;
-                store_fp6_group(q, codes, row, g, (NG + 1) >> 1, row_ok, kq);
-                if (row_ok && kq == 0) ((uint16_t *)scales)[(size_t)row * NG + g] = (uint16_t)sbits;
+                store_fp6_group(q, s_out, r, g - c0, kq);
+                if (kq == 0) *(uint16_t *)(s_osc + r * QA_SROW + 2 * (g - c0)) = (uint16_t)sbits;
             } else if constexpr (PREC == 0) {
                 // ---- int4, group 64: absmax over the row's 4 lanes
                 amax = fmaxf(amax_j[0], amax_j[1]);
-                amax = fmaxf(amax, shfl_xor_f(amax, 16));
-                amax = fmaxf(amax, shfl_xor_f(amax, 32));
+                amax = max_xor32(max_xor16(amax));
                 // fl32(amax / 7) and fl32(amax * fl32(1/7)) round to the same bf16
                 // for every bf16 amax (checked exhaustively)
                 const float s_f = amax * (1.0f / 7.0f);
@@ -390,11 +401,11 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
                         word[w] = pack_int4_word(qv);
                     }
                 }
-                if (row_ok) {
-                    uint8_t *cp = codes + (size_t)row * (size_t)(K >> 1) + g * 32 + 4 * kq;
+                {
+                    uint8_t *cp = s_out + r * QA_OROW + (g - c0) * 32 + 4 * kq;
                     *(uint32_t *)cp = word[0];
                     *(uint32_t *)(cp + 16) = word[1];
-                    if (kq == 0) ((uint16_t *)scales)[(size_t)row * NG + g] = (uint16_t)sbits;
+                    if (kq == 0) *(uint16_t *)(s_osc + r * QA_SROW + 2 * (g - c0)) = (uint16_t)sbits;
                 }
             } else {
                 // ---- NVFP4, group 16: lanes kq and kq^1 share a group within step j
@@ -402,7 +413,7 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
                 uint32_t sc[2];
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    float a = fmaxf(amax_j[j], shfl_xor_f(amax_j[j], 16));
+                    float a = max_xor16(amax_j[j]);
                     const float s_f = a * (1.0f / 6.0f);   // same E4M3 code as fl32(a / 6) for every bf16 a
                     const uint32_t se = e4m3_encode_nonneg(s_f);
                     const float d = e4m3_decode_nonneg(se);
@@ -423,12 +434,12 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
                         }
                     }
                 }
-                if (row_ok) {
-                    uint8_t *cp = codes + (size_t)row * (size_t)(K >> 1) + g * 32 + 4 * kq;
+                {
+                    uint8_t *cp = s_out + r * QA_OROW + (g - c0) * 32 + 4 * kq;
                     *(uint32_t *)cp = word[0];
                     *(uint32_t *)(cp + 16) = word[1];
                     if ((kq & 1) == 0) {
-                        uint8_t *sp = (uint8_t *)scales + (size_t)row * (size_t)(K >> 4) + g * 4 + (kq >> 1);
+                        uint8_t *sp = s_osc + r * QA_SROW + (g - c0) * 4 + (kq >> 1);
                         sp[0] = (uint8_t)sc[0];
                         sp[2] = (uint8_t)sc[1];
                     }
@@ -495,6 +506,46 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
                 }(std::make_integer_sequence<int, QA_PERIOD>{});
         }
         __syncthreads();
+
+        // ---- the chunk's codes and scales: LDS -> global, consecutive threads
+        // on consecutive bytes (rows past M are not written, and neither is
+        // the second group of a last pair when K/64 is odd: FP6 padding)
+        const int T = QA_WAVES * 64;
+        const int row0 = blockIdx.x * QA_ROWS;
+        const int rows = min(QA_ROWS, M - row0);
+        if constexpr (PREC == 2) {
+            const int NP = (NG + 1) >> 1, np = (cg + 1) >> 1;
+            for (int idx = threadIdx.x; idx < np * 96; idx += T) {
+                const int pl = idx / 96, rem = idx - pl * 96, rr = rem / 6, slot = rem - rr * 6;
+                const int c = (slot + 6 - ((rr >> 2) & 1)) % 6;          // the chunk held in this slot
+                if (rr < rows && c0 + 2 * pl + c / 3 < NG) {
+                    const int grow = row0 + rr;
+                    const size_t off = ((size_t)(grow >> 7) * NP + (c0 >> 1) + pl) * FP6_PAIR_BYTES +
+                                       (size_t)(grow & 127) * 96 + 16 * slot;
+                    *(v4u *)(codes + off) = *(const v4u *)(s_out + idx * 16);
+                }
+            }
+        } else {
+            const int per_row = cg * 2;                                    // 16-byte pieces of a row
+            for (int idx = threadIdx.x; idx < rows * per_row; idx += T) {
+                const int rr = idx / per_row, pc = idx - rr * per_row;
+                *(v4u *)(codes + (size_t)(row0 + rr) * (size_t)(K >> 1) + (size_t)c0 * 32 + 16 * pc) =
+                    *(const v4u *)(s_out + rr * QA_OROW + 16 * pc);
+            }
+        }
+        if constexpr (PREC == 1) {
+            for (int idx = threadIdx.x; idx < rows * cg; idx += T) {
+                const int rr = idx / cg, gl = idx - rr * cg;
+                *(uint32_t *)((uint8_t *)scales + (size_t)(row0 + rr) * (size_t)(K >> 4) + (size_t)(c0 + gl) * 4) =
+                    *(const uint32_t *)(s_osc + rr * QA_SROW + 4 * gl);
+            }
+        } else {
+            for (int idx = threadIdx.x; idx < rows * cg; idx += T) {
+                const int rr = idx / cg, gl = idx - rr * cg;
+                ((uint16_t *)scales)[(size_t)(row0 + rr) * NG + c0 + gl] =
+                    *(const uint16_t *)(s_osc + rr * QA_SROW + 2 * gl);
+            }
+        }
     }
 
     if constexpr (RT > 0) {
