@@ -748,7 +748,7 @@ def cpu_threads():
     return max(1, min(n, CPU_THREADS_MAX))
 
 
-def cpu_baseline(synth, rows_per_thread=32):
+def cpu_baseline(synth, rows_per_thread=64):
     """The CPU oracle (plain C, as it stands) on a bounded sample of the same
     step, on every host core this process may use: each W4A4 layer's first
     ``rows_per_thread`` x threads rows (quantize + GEMM; rows are independent,
