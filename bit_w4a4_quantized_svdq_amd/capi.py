@@ -112,8 +112,60 @@ def _check(status: int, func: str):
         raise SvdqError(status, func, svdq_last_error())
 
 
+_gpu = None
+
+
+def _gpu_present() -> bool:
+    global _gpu
+    if _gpu is None:
+        import torch
+        _gpu = bool(torch.cuda.is_available())
+    return _gpu
+
+
 def _ptr(t):
-    return None if t is None else t.data_ptr()
+    """Device pointer of a tensor handed to the library: it must be
+    contiguous (the C ABI takes flat buffers) and, where a GPU is present,
+    in device memory (a host pointer would reach the kernels)."""
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("libsvdq takes contiguous tensors")
+    if not t.is_cuda and _gpu_present():
+        raise ValueError("libsvdq takes device tensors")
+    return t.data_ptr()
+
+
+def _need(t, nbytes, what, func):
+    """Raise unless tensor t (if given) holds at least nbytes."""
+    if t is not None and t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{func}: {what} holds {t.numel() * t.element_size()} bytes, "
+                         f"{int(nbytes)} are needed")
+
+
+def _code_bytes(precision, rows, K, weight=False):
+    """Bytes of a [rows, K] operand's codes in the given precision's layout."""
+    if precision == SVDQ_INT4_FP6:
+        return svdq_fp6_codes_bytes(rows, K)
+    if precision == SVDQ_INT4_PACKED and weight:
+        return svdq_packed_weight_bytes(rows, K)
+    return rows * K // 2
+
+
+def _scale_bytes(precision, rows, K):
+    return rows * K // 16 if precision == SVDQ_NVFP4 else rows * (K // 64) * 2
+
+
+def _check_layer_buffers(func, precision, M, N, K, rank, act_codes, act_scales, wgt_codes, wgt_scales,
+                         lora_act, lora_up, bias, out):
+    _need(act_codes, _code_bytes(precision, M, K), "act_codes", func)
+    _need(act_scales, _scale_bytes(precision, M, K), "act_scales", func)
+    _need(wgt_codes, _code_bytes(precision, N, K, weight=True), "wgt_codes", func)
+    _need(wgt_scales, _scale_bytes(precision, N, K), "wgt_scales", func)
+    _need(lora_act, 4 * M * rank, "lora_act", func)
+    _need(lora_up, 2 * N * rank, "lora_up", func)
+    _need(bias, 2 * N, "bias", func)
+    _need(out, 2 * M * N, "out", func)
 
 
 def _stream(stream):
@@ -123,11 +175,21 @@ def _stream(stream):
     return torch.cuda.current_stream().cuda_stream
 
 
+def _check_act_buffers(func, precision, M, K, rank, smooth, lora_down, act_codes, act_scales, lora_act):
+    _need(smooth, 2 * K, "smooth", func)
+    _need(lora_down, 2 * rank * K, "lora_down", func)
+    _need(act_codes, _code_bytes(precision, M, K), "act_codes", func)
+    _need(act_scales, _scale_bytes(precision, M, K), "act_scales", func)
+    _need(lora_act, 4 * M * rank, "lora_act", func)
+
+
 def svdq_quantize_act(precision, x, smooth, lora_down, act_codes, act_scales, lora_act,
                       stream=None):
     """Smooth, low-rank down-projection and group quantization of x [M,K]."""
     M, K = x.shape
     rank = 0 if lora_down is None else lora_down.shape[0]
+    _check_act_buffers("svdq_quantize_act", precision, M, K, rank, smooth, lora_down, act_codes, act_scales,
+                       lora_act)
     _check(lib().svdq_quantize_act(precision, M, K, rank, _ptr(x), _ptr(smooth), _ptr(lora_down),
                                    _ptr(act_codes), _ptr(act_scales), _ptr(lora_act),
                                    _stream(stream)), "svdq_quantize_act")
@@ -138,6 +200,8 @@ def svdq_gelu_quantize_act(precision, x, smooth, lora_down, act_codes, act_scale
     """svdq_quantize_act of GELU(x) (tanh form), x being a GELU MLP's up-projection output."""
     M, K = x.shape
     rank = 0 if lora_down is None else lora_down.shape[0]
+    _check_act_buffers("svdq_gelu_quantize_act", precision, M, K, rank, smooth, lora_down, act_codes,
+                       act_scales, lora_act)
     _check(lib().svdq_gelu_quantize_act(precision, M, K, rank, _ptr(x), _ptr(smooth), _ptr(lora_down),
                                         _ptr(act_codes), _ptr(act_scales), _ptr(lora_act),
                                         _stream(stream)), "svdq_gelu_quantize_act")
@@ -200,6 +264,8 @@ def svdq_gemm_w4a4(precision, act_codes, act_scales, wgt_codes, wgt_scales, alph
     M = out.shape[0]
     N, K = _weight_shape(precision, wgt_codes, wgt_scales)
     rank = 0 if lora_up is None else lora_up.shape[1]
+    _check_layer_buffers("svdq_gemm_w4a4", precision, M, N, K, rank, act_codes, act_scales, wgt_codes,
+                         wgt_scales, lora_act, lora_up, bias, out)
     _check(lib().svdq_gemm_w4a4(precision, M, N, K, rank, _ptr(act_codes), _ptr(act_scales),
                                 _ptr(wgt_codes), _ptr(wgt_scales), float(alpha), _ptr(lora_act),
                                 _ptr(lora_up), _ptr(bias), _ptr(out), _stream(stream)),
@@ -214,6 +280,10 @@ def svdq_gemm_w4a4_qk_norm_rope(precision, act_codes, act_scales, wgt_codes, wgt
     M = out.shape[0]
     N, K = _weight_shape(precision, wgt_codes, wgt_scales)
     rank = 0 if lora_up is None else lora_up.shape[1]
+    _check_layer_buffers("svdq_gemm_w4a4_qk_norm_rope", precision, M, N, K, rank, act_codes, act_scales,
+                         wgt_codes, wgt_scales, lora_act, lora_up, bias, out)
+    _need(rope_cos, 4 * M * 64, "rope_cos", "svdq_gemm_w4a4_qk_norm_rope")
+    _need(rope_sin, 4 * M * 64, "rope_sin", "svdq_gemm_w4a4_qk_norm_rope")
     _check(lib().svdq_gemm_w4a4_qk_norm_rope(precision, M, N, K, rank, _ptr(act_codes),
                                              _ptr(act_scales), _ptr(wgt_codes), _ptr(wgt_scales),
                                              float(alpha), _ptr(lora_act), _ptr(lora_up), _ptr(bias),
@@ -226,6 +296,11 @@ def awq_gemv_w4a16(x, wgt_codes, wgt_scales, wgt_zeros, bias, out, group_size=64
     """int4 weight-only layer: out[M,N] = x . dequant(W)^T + bias."""
     M, K = x.shape
     N = wgt_codes.shape[0]
+    if group_size == 64:
+        for t, nb, what in ((wgt_codes, N * K // 2, "wgt_codes"), (wgt_scales, 2 * N * (K // 64), "wgt_scales"),
+                            (wgt_zeros, 2 * N * (K // 64), "wgt_zeros"), (bias, 2 * N, "bias"),
+                            (out, 2 * M * N, "out")):
+            _need(t, nb, what, "awq_gemv_w4a16")
     _check(lib().awq_gemv_w4a16(M, N, K, group_size, _ptr(x), _ptr(wgt_codes), _ptr(wgt_scales),
                                 _ptr(wgt_zeros), _ptr(bias), _ptr(out), _stream(stream)),
            "awq_gemv_w4a16")

@@ -76,6 +76,19 @@ template <int RT, bool GELU> constexpr int qa_waves() { return RT <= 1 && !GELU 
 // K-groups whose 1/s is staged in LDS at a time: 8 channels per thread
 template <int RT, bool GELU> constexpr int qa_chunk() { return qa_waves<RT, GELU>() * 8; }
 constexpr int QA_XDEPTH = 2;         // x slices in flight per wave (groups ahead)
+// Whole-line x loads (8-wave blocks): a group's 16 rows x 128 bytes are
+// loaded as 8 rows x 128 B per instruction (lane i: row 8j + i/8, 16-byte
+// chunk i % 8), so every load instruction moves whole cache lines, and one
+// LDS pass per wave puts them into the MFMA layout (lane l: row l % 16,
+// chunks l/16 and l/16 + 4).  Loading the MFMA layout directly touches each
+// line with two instructions (64 of its 128 bytes each); the vector memory
+// path is what this kernel waits on.  Measured against the direct loads
+// (same outputs byte for byte): 14.2 against 15.5 us at K = 3072 and 43.8
+// against 50.1 us at K = 12288 (4096 rows, rank 32, FP6 codes); the
+// GELU-fed step was 2 % slower with it and keeps the direct loads, as do
+// ranks above 64 (whose three-slot low-rank ring would spill).
+template <int RT, bool GELU> constexpr bool qa_lds_x() { return qa_waves<RT, GELU>() == 8 && RT <= 4 && !GELU; }
+constexpr int QA_XSLOT = QA_ROWS * 128;      // bytes of one group's x slice
 constexpr int QA_PERIOD = 3;         // unroll period: a multiple of both ring sizes (3, and 3 or 1)
 
 __device__ __forceinline__ float v4u_elem(const v4u &v, int e) {
@@ -217,7 +230,11 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
                          float *__restrict__ lora_act)
 {
     constexpr int QA_WAVES = qa_waves<RT, GELU>();
-    constexpr int LSLOTS = 1;                 // low-rank slices (L2 resident): loaded per group
+    constexpr bool LDSX = qa_lds_x<RT, GELU>();
+    // low-rank slices (L2 resident): loaded per group, or one group ahead
+    // when x comes through LDS (so that waiting for them never waits for
+    // the newest x copies)
+    constexpr int LSLOTS = LDSX ? 3 : 1;
     constexpr int QA_CHUNK = qa_chunk<RT, GELU>();
     constexpr int SINV = QA_CHUNK * 64 / (QA_WAVES * 64);   // 1/s channels per thread per chunk
     static_assert(SINV == 4 || SINV == 8, "1/s staging: 8 or 16 bytes of bf16 per thread");
@@ -236,14 +253,30 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
     constexpr int QA_SROW = QA_CHUNK * (PREC == 1 ? 4 : 2) + 4;
     __shared__ __attribute__((aligned(16))) uint8_t s_out[QA_OUT];
     __shared__ __attribute__((aligned(16))) uint8_t s_osc[QA_ROWS * QA_SROW];
+    // per wave one [16 rows][128 B] slice; row rl's 16-byte chunk c at
+    // position c ^ ((rl >> 1) & 7), so that the 16 rows one LDS cycle
+    // serves fall on distinct banks
+    __shared__ __attribute__((aligned(16))) uint8_t s_xr[LDSX ? QA_WAVES * QA_XSLOT : 16];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar)
     const int r = lane & 15;
     const int kq = lane >> 4;
     const int row = blockIdx.x * QA_ROWS + r;
     const int NG = K >> 6;
     const size_t xrow_off = (size_t)min(row, M - 1) * (size_t)K;   // rows past M: clamped, results not stored
+    // whole-line loads of x: lane i of load j takes chunk i % 8 of row
+    // 8j + i/8 (clamped to a valid row) and puts it at its LDS position
+    size_t xl_off[2] = {0, 0};
+    int xl_pos[2] = {0, 0};
+    if constexpr (LDSX) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int rl = 8 * j + (lane >> 3);
+            xl_off[j] = (size_t)min(blockIdx.x * QA_ROWS + rl, M - 1) * (size_t)K + 8 * (lane & 7);
+            xl_pos[j] = rl * 128 + 16 * ((lane & 7) ^ ((rl >> 1) & 7));
+        }
+    }
 
     v4f acc[RT > 0 ? RT : 1];
 #pragma unroll
@@ -266,9 +299,15 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
         v4u lring[LSLOTS][RT > 0 ? RT : 1][2];
         auto load_x = [&](int i, auto slot_c) __attribute__((always_inline)) {
             constexpr int S = decltype(slot_c)::value;
-            const int kb = (c0 + wave + i * QA_WAVES) * 64 + 8 * kq;
-            xring[S][0] = *(const v4u *)(x + xrow_off + kb);
-            xring[S][1] = *(const v4u *)(x + xrow_off + kb + 32);
+            if constexpr (LDSX) {
+                const int kg = (c0 + wave + i * QA_WAVES) * 64;
+                xring[S][0] = *(const v4u *)(x + xl_off[0] + kg);
+                xring[S][1] = *(const v4u *)(x + xl_off[1] + kg);
+            } else {
+                const int kb = (c0 + wave + i * QA_WAVES) * 64 + 8 * kq;
+                xring[S][0] = *(const v4u *)(x + xrow_off + kb);
+                xring[S][1] = *(const v4u *)(x + xrow_off + kb + 32);
+            }
             asm volatile("" ::: "memory");   // keep the loads here, ahead of their use
             __builtin_amdgcn_sched_barrier(0);
         };
@@ -454,6 +493,24 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
         auto step = [&](int i, auto q_c) __attribute__((always_inline)) {
             constexpr int Q = decltype(q_c)::value;       // i % QA_PERIOD
             constexpr int XS = Q % XR, LS = Q % LSLOTS;
+            if constexpr (LDSX) {
+                // issue order per step: the low-rank slices of group i+1, then
+                // the x slice of group i+2, so that waiting for group i's slices
+                // (issued before the x slice of group i+1) never waits for the
+                // newest x loads
+                load_l(min(i + 1, i_last), std::integral_constant<int, (LS + 1) % 3>{});
+                load_x(min(i + QA_XDEPTH, i_last), std::integral_constant<int, (XS + QA_XDEPTH) % XR>{});
+                // into the MFMA layout through this wave's LDS slice (a wave's LDS
+                // accesses run in order: the previous group's reads are done)
+                uint8_t *sw = s_xr + wave * QA_XSLOT;
+                *(v4u *)(sw + xl_pos[0]) = xring[XS][0];
+                *(v4u *)(sw + xl_pos[1]) = xring[XS][1];
+                const uint8_t *sl = sw + r * 128;
+                const int fr = (r >> 1) & 7;
+                const v4u xl[2] = {*(const v4u *)(sl + 16 * (kq ^ fr)), *(const v4u *)(sl + 16 * ((kq + 4) ^ fr))};
+                process(i, xl, lring[LS]);
+                return;
+            }
             load_x(min(i + QA_XDEPTH, i_last), std::integral_constant<int, (XS + QA_XDEPTH) % XR>{});
             if constexpr (LSLOTS == 3) {
                 load_l(min(i + 1, i_last), std::integral_constant<int, (LS + 1) % 3>{});
@@ -464,10 +521,17 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
             }
         };
         if (n_w > 0) {
-            [&]<int... P>(std::integer_sequence<int, P...>) __attribute__((always_inline)) {
-                (load_x(min(P, i_last), std::integral_constant<int, P>{}), ...);
-            }(std::make_integer_sequence<int, QA_XDEPTH>{});
-            if constexpr (LSLOTS == 3) load_l(0, std::integral_constant<int, 0>{});
+            if constexpr (LDSX) {
+                static_assert(QA_XDEPTH == 2, "the wait count assumes two x slices ahead");
+                load_x(0, std::integral_constant<int, 0>{});
+                load_l(0, std::integral_constant<int, 0>{});
+                load_x(min(1, i_last), std::integral_constant<int, 1>{});
+            } else {
+                [&]<int... P>(std::integer_sequence<int, P...>) __attribute__((always_inline)) {
+                    (load_x(min(P, i_last), std::integral_constant<int, P>{}), ...);
+                }(std::make_integer_sequence<int, QA_XDEPTH>{});
+                if constexpr (LSLOTS == 3) load_l(0, std::integral_constant<int, 0>{});
+            }
         }
         // 1/s of the chunk's channels (IEEE division), staged in LDS: thread t
         // takes channels SINV*t .. +SINV-1 with one load, issued after the

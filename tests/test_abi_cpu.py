@@ -240,3 +240,24 @@ def test_fp6_entry_points_host_checks():
     assert gm(prec=capi.SVDQ_INT4_FP6, wsc=0) == INV
     assert gm(prec=capi.SVDQ_INT4_FP6, rank=8) == INV
     assert gm(prec=capi.SVDQ_INT4_FP6, M=0) == capi.SVDQ_OK
+
+
+def test_python_binding_checks_buffers_before_the_call():
+    import torch
+    x = torch.zeros((4, 128), dtype=torch.bfloat16)
+    codes = torch.zeros((4, 64), dtype=torch.uint8)
+    scales = torch.zeros((4, 2), dtype=torch.bfloat16)
+    # a transposed view is not a flat buffer
+    with pytest.raises(ValueError, match="contiguous"):
+        capi.svdq_quantize_act(0, x, None, None, codes.t(), scales, None, stream=0)
+    # codes too small for [4, 128] nibbles, scales too small for two groups per row
+    with pytest.raises(ValueError, match="act_codes"):
+        capi.svdq_quantize_act(0, x, None, None, codes[:3], scales, None, stream=0)
+    with pytest.raises(ValueError, match="act_scales"):
+        capi.svdq_quantize_act(0, x, None, None, codes, scales[:, :1].contiguous(), None, stream=0)
+    # GEMM: an output smaller than [M, N] bf16
+    out = torch.zeros((4, 63), dtype=torch.bfloat16)
+    w = torch.zeros((64, 64), dtype=torch.uint8)
+    ws = torch.zeros((64, 2), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="out"):
+        capi.svdq_gemm_w4a4(0, codes, scales, w, ws, 1.0, None, None, None, out, stream=0)
