@@ -120,15 +120,22 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
 
 // FP6 tiled layout of int4 codes (the FP6 GEMM's operands): byte offset of
 // 16-byte chunk c (0..2: [h0 dwords 0-3 | h1 dwords 0-3 | h0 dwords 4-5,
-// h1 dwords 4-5]) of group g of row r.  Rows form tiles of 128, groups
-// pairs; (tile, pair) is a contiguous 12 KB block of 128 rows x 96 bytes,
-// and a row's six chunks sit rotated by (row % 128 >> 2) & 1 positions, the
-// GEMM's LDS stage image.  NP = pairs per row (ceil(K/128)).
+// h1 dwords 4-5], the halves of chunk 2 swapped when fp6_half_swap(row)) of
+// group g of row r.  Rows form tiles of 128, groups pairs; (tile, pair) is
+// a contiguous 12 KB block of 128 rows x 96 bytes, the GEMM's LDS stage
+// image, and a row's six chunks sit rotated by fp6_rot(row) positions.  With
+// 64 LDS banks of 4 bytes, one LDS cycle serves 16 lanes' 16-byte fragments
+// (16 consecutive rows, 96 bytes apart) or 32 lanes' 8-byte pieces; the
+// rotation puts those 16 rows on distinct banks (rows r and r + 8 would
+// share them with a rotation by bit 2 alone), and the swap does the same for
+// the 8-byte pieces of 32 rows.  NP = pairs per row (ceil(K/128)).
 constexpr int FP6_TILE_ROWS = 128;
 constexpr int FP6_PAIR_BYTES = FP6_TILE_ROWS * 96;      // 12 KB
+__host__ __device__ __forceinline__ int fp6_rot(int row) { return ((row >> 2) ^ (row >> 3)) & 1; }
+__host__ __device__ __forceinline__ int fp6_half_swap(int row) { return ((row >> 3) ^ (row >> 4)) & 1; }
 __host__ __device__ __forceinline__ size_t fp6_tiled_chunk(int row, int g, int c, int NP) {
     const int t = row >> 7, rho = row & 127, s = g >> 1;
-    const int slot = (3 * (g & 1) + c + ((rho >> 2) & 1)) % 6;
+    const int slot = (3 * (g & 1) + c + fp6_rot(rho)) % 6;
     return ((size_t)t * NP + s) * FP6_PAIR_BYTES + (size_t)rho * 96 + 16 * slot;
 }
 __host__ __device__ __forceinline__ size_t fp6_tiled_bytes(int rows, int K) {

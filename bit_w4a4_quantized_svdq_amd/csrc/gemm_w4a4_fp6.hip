@@ -38,10 +38,11 @@
 // into LDS; two stages alternate (48 KB, three blocks per CU).  In the tiled
 // layout a stage's 12 KB of one operand is one contiguous block already in
 // the LDS arrangement, so 12 copies of 1 KB (whole cache lines, lane i at
-// byte 16i) fill it: row r's chunk c sits in slot (c + rot) mod 6 of its 96
-// bytes, rot = (r >> 2) & 1, which moves rows r+4 .. r+7 by 16 bytes against
-// rows r .. r+3, so the eight rows that one LDS cycle of a 16-byte fragment
-// read serves fall on distinct banks.  One barrier per stage; the copies of
+// byte 16i) fill it: row r's chunk c sits in slot (c + fp6_rot(r)) mod 6 of
+// its 96 bytes and the two 8-byte halves of its last chunk are swapped when
+// fp6_half_swap(r), so the 16 rows whose 16-byte fragments one LDS cycle
+// serves, and the 32 rows whose 8-byte pieces it serves, fall on distinct
+// banks (64 banks of 4 bytes).  One barrier per stage; the copies of
 // stage s+1 go out right after it and land while stage s is computed.  Rows
 // past M (columns past N) of the last tile, and the second group of the last
 // pair when K/64 is odd, are padding the producers never write: they hold
@@ -74,7 +75,7 @@ static_assert(F6_SMEM >= QK_SMEM, "the QK epilogue stages a 128-row tile in the 
 static_assert(F6_COPIES % 4 == 0, "every wave issues the same number of copies");
 
 // LDS slot (16-byte unit within a row's 96 bytes) of the row's chunk c
-__device__ __forceinline__ int f6_slot(int row, int c) { return (c + ((row >> 2) & 1)) % 6; }
+__device__ __forceinline__ int f6_slot(int row, int c) { return (c + fp6_rot(row)) % 6; }
 
 // X = sum_k qa_k * qw_k over one group: FP6 (E2M3) operands holding q/2,
 // block scales 2^1 * 2^1 (E8M0 128): exact integers in fp32
@@ -140,13 +141,15 @@ void gemm_w4a4_fp6_kernel(int M, int N, int K, int rank,
     };
 
     // ---- consumer: fragment offsets of group gg of a stage (tile t adds 32
-    // rows = 3072 bytes; B adds a wave-uniform delta).  The row's rotation is
-    // (row >> 2) & 1 = (l32 >> 2) & 1; the 16-byte piece of group 1 sits 48
-    // bytes after that of group 0, the 8-byte piece wraps for rotated rows.
+    // rows = 3072 bytes; B adds a wave-uniform delta: rotation and swap
+    // depend on row bits 2-4 only).  The 16-byte piece of group 1 sits 48
+    // bytes after that of group 0 (the rotation is at most 1), the 8-byte
+    // piece wraps for rotated rows and is the second half of its chunk for
+    // h = 1, or for h = 0 in swapped rows.
     const int ra = wm * 64 + l32;
     const int a16 = ra * F6_ROWB + 16 * f6_slot(ra, h);
-    const int a8_0 = ra * F6_ROWB + 16 * f6_slot(ra, 2) + 8 * h;
-    const int a8_1 = ra * F6_ROWB + 16 * f6_slot(ra, 5) + 8 * h;
+    const int a8_0 = ra * F6_ROWB + 16 * f6_slot(ra, 2) + 8 * (h ^ fp6_half_swap(ra));
+    const int a8_1 = ra * F6_ROWB + 16 * f6_slot(ra, 5) + 8 * (h ^ fp6_half_swap(ra));
     const int bdelta = F6_OPER + (wn - wm) * 64 * F6_ROWB;
 
     // ---- scales: lanes 0-31 the A row l of the first tile, 32-63 of the

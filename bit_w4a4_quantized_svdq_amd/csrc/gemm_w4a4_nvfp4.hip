@@ -245,8 +245,12 @@ void gemm_w4a4_nvfp4_kernel(int M, int N, int K, int rank,
 // Main path (K a multiple of 512): a stage holds two slices, 64 bytes of
 // every row, so each copy instruction reads 16 rows x 64 B (four lanes per
 // row).  Within a row's 64 bytes the four 16-byte chunks are stored in the
-// order c ^ ((row >> 1) & 3), so that the 8 consecutive rows that a fragment
-// load serves per LDS cycle fall on distinct banks.
+// order c ^ co_swz(row), co_swz(row) = ((row >> 1) & 3) ^ ((row >> 3) & 1):
+// the 16 consecutive rows whose 16-byte fragments one LDS cycle serves (64
+// banks of 4 bytes) then fall on distinct banks, and so do any 8 of them
+// that are consecutive.  (The swizzle (row >> 1) & 3 alone leaves rows r
+// and r + 8 on the same banks: the LDS bank-conflict counter read 74 % of
+// the LDS-active cycles with it.)
 constexpr int CO_ROWB = 64;                               // bytes per row and stage
 constexpr int CO_CODES = NV_BM * CO_ROWB;                 // 8 KB of A (or B) codes per stage
 constexpr int CO_STAGE = 2 * CO_CODES;                    // 16 KB
@@ -255,7 +259,8 @@ constexpr int CO_SC_SLOT = (NV_BM + NV_BN) * CO_SC_ROWB;  // 8 KB
 constexpr int CO_SC = 2 * CO_STAGE;
 constexpr int CO_SMEM = CO_SC + 2 * CO_SC_SLOT;           // 48 KB
 
-__device__ __forceinline__ int co_chunk_slot(int row, int c) { return c ^ ((row >> 1) & 3); }
+__device__ __forceinline__ int co_swz(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int co_chunk_slot(int row, int c) { return c ^ co_swz(row); }
 
 template <bool QK = false>
 __global__ __launch_bounds__(NV_THREADS, 2)
@@ -341,8 +346,8 @@ void gemm_w4a4_nvfp4_co_kernel(int M, int N, int K, int rank,
     for (int t = 0; t < 2; ++t) {
         a_row[t] = wm * 64 + t * 32 + l32;
         b_row[t] = wn * 64 + t * 32 + l32;
-        a_sw[t] = (a_row[t] >> 1) & 3;
-        b_sw[t] = (b_row[t] >> 1) & 3;
+        a_sw[t] = co_swz(a_row[t]);
+        b_sw[t] = co_swz(b_row[t]);
     }
 
     auto deq = [](uint32_t c, v2h sc2, int s) {

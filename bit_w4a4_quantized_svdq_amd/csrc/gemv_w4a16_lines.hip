@@ -8,19 +8,25 @@
 // the shape of its loads: a lane there owns one weight row, so each load
 // instruction touches 32 rows x 32 bytes.  Here a wave owns 8 weight rows
 // and lane l reads 16-byte chunk l%8 + 8j of row l/8: every load instruction
-// covers 8 whole 128-byte lines, and all of a lane's chunks (K/256 loads)
-// are issued before anything waits, so the whole weight matrix is requested
-// at once.  The dot products run on the vector ALU (v_dot2_f32_bf16, two
-// products per instruction), which at one or two rows of x costs less than
-// the stream.
+// covers 8 whole 128-byte lines, and each lane keeps AL_AHEAD chunk loads in
+// flight ahead of the chunk it works on (about 7 MB over the whole grid at
+// this shape, enough to keep HBM streaming).  The dot products run on the
+// vector ALU (v_dot2_f32_bf16, two products per instruction): about 75
+// vector instructions per chunk and lane, which the stream has to hide.
+// Measured at 3072 -> 18432 over 16 rotating weight copies: with all of a
+// lane's loads issued at once (the whole matrix requested at the start)
+// 9.6 us, since most chunks then land near the end and their arithmetic
+// runs after the stream; 3 ahead 8.6 us (1 ahead 9.3, 2 ahead 8.65, 4
+// ahead 8.7); the same kernel without the arithmetic 7.4 us.
 //
 // Order of work in a block (4 waves, 32 weight rows):
 //   1. each thread issues its loads of x and of the block's scales and zero
-//      points, then all of its weight chunks;
+//      points, then its first AL_AHEAD weight chunks;
 //   2. it waits for the first two only (loads complete in order), stores x
 //      into LDS in the pair order of the unpacked codes together with the
 //      sums of x over every 32-code chunk, and the scales and zero points;
-//   3. after one barrier, each weight chunk is used as soon as it lands.
+//   3. after one barrier, chunk j is used as soon as it lands, after the
+//      load of chunk j + AL_AHEAD has gone out.
 // Arithmetic (as in the matrix-core GEMV): a code q in 0..15 becomes the bf16
 // value 128 + q by placing it under the byte 0x43 (v_perm_b32), so
 // sum (q - z) x = sum (128 + q) x - (128 + z) sum x per chunk, and the group
@@ -34,6 +40,7 @@ namespace svdq {
 constexpr int AL_WAVES = 4, AL_THREADS = AL_WAVES * 64;   // 3 and 6 measured slower at K = 3072
 constexpr int AL_ROWS = AL_WAVES * 8;               // weight rows per block
 constexpr int AL_MAX_K = 4096;                      // K / 256 <= 16 chunk loads per lane
+constexpr int AL_AHEAD = 3;                         // chunk loads in flight ahead of the one in use
 
 bool awq_gemv_lines_applies(int M, int N, int K) {
     return M >= 1 && M <= 2 && N >= 1 && K % 512 == 0 && K <= AL_MAX_K;
@@ -88,11 +95,12 @@ void awq_gemv_lines_kernel(int N, int K, const uint16_t *__restrict__ x, const u
     const int c0 = lane & 7;
     const uint8_t *wrow = codes + (size_t)row * (size_t)(K >> 1) + 16 * c0;
     v4u wr[NL];
+    constexpr int AH = AL_AHEAD < NL ? AL_AHEAD : NL;
 #pragma unroll
-    for (int j = 0; j < NL; ++j) wr[j] = *(const v4u *)(wrow + 128 * j);
+    for (int j = 0; j < AH; ++j) wr[j] = *(const v4u *)(wrow + 128 * j);
 
     // ---- 2. wait for x and the scales (issued first), stage them in LDS
-    __builtin_amdgcn_s_waitcnt((NL & 15) | ((NL >> 4) << 14) | 0x0F70);   // vmcnt(NL)
+    __builtin_amdgcn_s_waitcnt((AH & 15) | ((AH >> 4) << 14) | 0x0F70);   // vmcnt(AH)
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
@@ -135,7 +143,10 @@ void awq_gemv_lines_kernel(int N, int K, const uint16_t *__restrict__ x, const u
     auto chunk = [&](auto jc) {
         constexpr int j = decltype(jc)::value;
         __builtin_amdgcn_sched_barrier(0);           // chunks stay in order (registers: one chunk's x at a time)
-        __builtin_amdgcn_s_waitcnt(((NL - 1 - j) & 15) | (((NL - 1 - j) >> 4) << 14) | 0x0F70);   // vmcnt
+        if constexpr (j + AH < NL) wr[j + AH] = *(const v4u *)(wrow + 128 * (j + AH));
+        // loads issued after chunk j's: up to chunk j + AH
+        constexpr int newer = (j + AH < NL ? j + AH : NL - 1) - j;
+        __builtin_amdgcn_s_waitcnt((newer & 15) | ((newer >> 4) << 14) | 0x0F70);   // vmcnt(newer)
         asm volatile("" ::: "memory");
         const int c = c0 + 8 * j;                    // chunk of the row: codes 32c .. 32c+31
         v2bf pq[16];

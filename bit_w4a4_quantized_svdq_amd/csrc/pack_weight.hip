@@ -72,8 +72,9 @@ __global__ __launch_bounds__(256) void pack_int4_kernel(int N, int NG, const uin
 // layout as the FP6 output of the activation step; fp6_tiled_chunk): per row
 // n and group g two 192-bit strings, one per K-half h, field j (bits 6j ..
 // 6j+5) = E2M3 code of q[n, 64g + 32h + j] / 2, as three 16-byte chunks
-// [h0 dwords 0-3 | h1 dwords 0-3 | h0 dwords 4-5, h1 dwords 4-5] placed by
-// row tile, group pair and rotation.  Every code in [-8, 7] has an exact
+// [h0 dwords 0-3 | h1 dwords 0-3 | h0 dwords 4-5, h1 dwords 4-5] (the last
+// chunk's halves swapped when fp6_half_swap(n)) placed by row tile, group
+// pair and rotation.  Every code in [-8, 7] has an exact
 // form: |q|/2 = 0, 0.5 (E2M3 subnormal 4/8), then 1 .. 4 in steps of 0.5
 // (normal, three mantissa bits).
 size_t fp6_weight_bytes(int N, int K) { return fp6_tiled_bytes(N, K); }
@@ -113,7 +114,8 @@ __global__ __launch_bounds__(256) void pack_fp6_kernel(int N, int NG, const uint
     const int NP = (NG + 1) >> 1;
     *(v4u *)(blob + fp6_tiled_chunk(n, g, 0, NP)) = v4u{dw[0][0], dw[0][1], dw[0][2], dw[0][3]};
     *(v4u *)(blob + fp6_tiled_chunk(n, g, 1, NP)) = v4u{dw[1][0], dw[1][1], dw[1][2], dw[1][3]};
-    *(v4u *)(blob + fp6_tiled_chunk(n, g, 2, NP)) = v4u{dw[0][4], dw[0][5], dw[1][4], dw[1][5]};
+    const int sw = fp6_half_swap(n);
+    *(v4u *)(blob + fp6_tiled_chunk(n, g, 2, NP)) = v4u{dw[sw][4], dw[sw][5], dw[sw ^ 1][4], dw[sw ^ 1][5]};
 }
 
 hipError_t launch_pack_weight_fp6(int N, int K, const void *wgt_codes, void *blob, hipStream_t stream)

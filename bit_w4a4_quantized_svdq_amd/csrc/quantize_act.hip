@@ -174,12 +174,14 @@ typedef float v16f_q __attribute__((ext_vector_type(16)));
 // first K-half, q[8..15]: the same of the second), integers in [-8, 7] held
 // as floats, into the group's three chunks of the FP6 tiled layout, here in
 // the block's LDS image of it: [pair][16 rows][96 bytes], row r's chunk c of
-// group g (g even: chunks 0-2, odd: 3-5) at slot (c + ((r >> 2) & 1)) mod 6
-// (a block's 16 rows start at a multiple of 16 in their 128-row tile, so
-// this is the rotation of the tiled layout).  Lanes kq = 0..3 of a row are
+// group g (g even: chunks 0-2, odd: 3-5) at slot (c + fp6_rot(rho)) mod 6,
+// the halves of its last chunk swapped when fp6_half_swap(rho); rho = the
+// row's index in its 128-row tile (a block's 16 rows start at a multiple of
+// 16 there, so rho = 16 * (block % 8) + r).  Lanes kq = 0..3 of a row are
 // lanes r + 16 kq; every lane of the wave takes part (the swaps are
 // wave-wide).
-__device__ __forceinline__ void store_fp6_group(const float (&q)[16], uint8_t *img, int r, int g_local, int kq) {
+__device__ __forceinline__ void store_fp6_group(const float (&q)[16], uint8_t *img, int r, int rho, int g_local,
+                                                int kq) {
     v16f_q a, b;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -214,11 +216,11 @@ __device__ __forceinline__ void store_fp6_group(const float (&q)[16], uint8_t *i
         d[i] = w[0];
         sr[i] = w[1];
     }
-    const int half = kq & 1, rot = (r >> 2) & 1;
+    const int half = kq & 1, rot = fp6_rot(rho), sw = fp6_half_swap(rho);
     uint8_t *rowimg = img + (g_local >> 1) * (16 * 96) + r * 96;
     const int c0 = 3 * (g_local & 1);
     if (kq < 2) *(v4u *)(rowimg + 16 * ((c0 + half + rot) % 6)) = v4u{d[0], d[1], d[2], sr[0]};
-    else *(v2u *)(rowimg + 16 * ((c0 + 2 + rot) % 6) + 8 * half) = v2u{sr[1], sr[2]};
+    else *(v2u *)(rowimg + 16 * ((c0 + 2 + rot) % 6) + 8 * (half ^ sw)) = v2u{sr[1], sr[2]};
 }
 
 template <int PREC, int RT, bool GELU>
@@ -402,7 +404,7 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
                 // a zero code is +0 in the layout (rint keeps the sign of -0.4)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) q[e] += 0.0f;
-                store_fp6_group(q, s_out, r, g - c0, kq);
+                store_fp6_group(q, s_out, r, 16 * (blockIdx.x & 7) + r, g - c0, kq);
                 if (kq == 0) *(uint16_t *)(s_osc + r * QA_SROW + 2 * (g - c0)) = (uint16_t)sbits;
             } else if constexpr (PREC == 0) {
                 // ---- int4, group 64: absmax over the row's 4 lanes
@@ -581,7 +583,7 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
             const int NP = (NG + 1) >> 1, np = (cg + 1) >> 1;
             for (int idx = threadIdx.x; idx < np * 96; idx += T) {
                 const int pl = idx / 96, rem = idx - pl * 96, rr = rem / 6, slot = rem - rr * 6;
-                const int c = (slot + 6 - ((rr >> 2) & 1)) % 6;          // the chunk held in this slot
+                const int c = (slot + 6 - fp6_rot(rr)) % 6;              // the chunk held in this slot
                 if (rr < rows && c0 + 2 * pl + c / 3 < NG) {
                     const int grow = row0 + rr;
                     const size_t off = ((size_t)(grow >> 7) * NP + (c0 >> 1) + pl) * FP6_PAIR_BYTES +

@@ -69,13 +69,17 @@ typedef enum svdq_status {
  * channel 64g + 32h + j, exact for every q in [-8, 7] (a zero code is +0).
  * Bits are numbered from the least significant bit of word 0 of a string.
  * A row's group g is three 16-byte chunks: c = 0: words 0-3 of h0, c = 1:
- * words 0-3 of h1, c = 2: words 4-5 of h0 then words 4-5 of h1.  Rows are
+ * words 0-3 of h1, c = 2: words 4-5 of h0 then words 4-5 of h1, the two
+ * halves of chunk 2 swapped (h1's words first) when s(r) = 1.  Rows are
  * stored in tiles of 128 (the last one padded) and groups in pairs (the last
- * one padded when K/64 is odd); chunk c of group g of row r is at byte
- *   ((r / 128) * ceil(K/128) + g / 2) * 12288 + (r % 128) * 96
- *     + 16 * ((3 * (g % 2) + c + ((r % 128) / 4) % 2) mod 6),
+ * one padded when K/64 is odd); with p = r % 128, rot(r) = ((p >> 2) xor
+ * (p >> 3)) & 1 and s(r) = ((p >> 3) xor (p >> 4)) & 1, chunk c of group g
+ * of row r is at byte
+ *   ((r / 128) * ceil(K/128) + g / 2) * 12288 + p * 96
+ *     + 16 * ((3 * (g % 2) + c + rot(r)) mod 6),
  * so each (tile, pair) is one contiguous 12 KB block: the GEMM's LDS stage,
- * copied with whole cache lines.  Padding is never written or needed: the
+ * copied with whole cache lines (rot and s place the 16 rows whose
+ * fragments one LDS cycle serves on distinct banks).  Padding is never written or needed: the
  * GEMM only multiplies it into outputs it does not store, or by a zero scale. */
 enum {
     SVDQ_INT4 = 0 /* group 64, bf16 scales */,

@@ -2,10 +2,12 @@
 include/svdq.h (the precision enum): per row and group of 64, two 192-bit
 strings, one per half h of the group; field j (bits 6j .. 6j+5) is the E2M3
 encoding of q/2 for channel 64g + 32h + j; the group is three 16-byte chunks
-[h0 words 0-3 | h1 words 0-3 | h0 words 4-5, h1 words 4-5]; chunk c of group
-g of row r sits at
-  ((r / 128) * ceil(K/128) + g / 2) * 12288 + (r % 128) * 96
-    + 16 * ((3 * (g % 2) + c + ((r % 128) / 4) % 2) mod 6).
+[h0 words 0-3 | h1 words 0-3 | h0 words 4-5, h1 words 4-5], the two halves of
+the last chunk swapped when s(r) = 1; with p = r % 128,
+rot(r) = ((p >> 2) xor (p >> 3)) & 1 and s(r) = ((p >> 3) xor (p >> 4)) & 1,
+chunk c of group g of row r sits at
+  ((r / 128) * ceil(K/128) + g / 2) * 12288 + p * 96
+    + 16 * ((3 * (g % 2) + c + rot(r)) mod 6).
 
 E2M3 (the OCP microscaling FP6 format): sign bit 5, exponent bits 3-4 with
 bias 1, mantissa bits 0-2; exponent 0 encodes the subnormals m/8, exponent
@@ -60,12 +62,31 @@ def fp6_codes_bytes(R, K):
     return -(-R // 128) * -(-K // 128) * 12288
 
 
+def rot(r):
+    p = r % 128
+    return ((p >> 2) ^ (p >> 3)) & 1
+
+
+def half_swap(r):
+    p = r % 128
+    return ((p >> 3) ^ (p >> 4)) & 1
+
+
 def chunk_offset(r, g, c, K):
     """Byte offset of chunk c (0..2) of group g of row r (the documented formula)."""
     NP = -(-K // 128)
-    rho = r % 128
-    slot = (3 * (g % 2) + c + (rho // 4) % 2) % 6
-    return ((r // 128) * NP + g // 2) * 12288 + rho * 96 + 16 * slot
+    slot = (3 * (g % 2) + c + rot(r)) % 6
+    return ((r // 128) * NP + g // 2) * 12288 + (r % 128) * 96 + 16 * slot
+
+
+def _swap_last_chunk(blocks, R):
+    """Swap the two 8-byte halves of chunk 2 in the rows with s(r) = 1
+    (blocks [R, NG, 48]; an involution)."""
+    out = blocks.copy()
+    rows = np.array([half_swap(r) for r in range(R)], bool)
+    out[rows, :, 32:40] = blocks[rows, :, 40:48]
+    out[rows, :, 40:48] = blocks[rows, :, 32:40]
+    return out
 
 
 def fp6_layout_from_q(q, fill=0xFF):
@@ -73,7 +94,7 @@ def fp6_layout_from_q(q, fill=0xFF):
     q = np.asarray(q, np.int64)
     R, K = q.shape
     NG = K // 64
-    blocks = _strings_to_block(e2m3_encode(q / 2.0).reshape(R, NG, 2, 32))      # [R, NG, 48]
+    blocks = _swap_last_chunk(_strings_to_block(e2m3_encode(q / 2.0).reshape(R, NG, 2, 32)), R)   # [R, NG, 48]
     out = np.full(fp6_codes_bytes(R, K), fill, np.uint8)
     r = np.arange(R)[:, None]
     g = np.arange(NG)[None, :]
@@ -94,6 +115,7 @@ def q_from_fp6_layout(b, R, K):
     for c in range(3):
         off = np.vectorize(chunk_offset)(r, g, c, K)
         blocks[..., 16 * c:16 * c + 16] = b[off[..., None] + np.arange(16)]
+    blocks = _swap_last_chunk(blocks, R)
     words = blocks.view(np.uint32).astype(np.uint64)                             # [R, NG, 12]
     halves = [np.concatenate([words[..., 0:4], words[..., 8:10]], axis=-1),
               np.concatenate([words[..., 4:8], words[..., 10:12]], axis=-1)]

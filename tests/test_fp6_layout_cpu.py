@@ -66,6 +66,26 @@ def test_tiled_addressing_hand_cases():
     assert len(offs) == 128 * 4 * 3 and min(offs) == 0 and max(offs) == 2 * 12288 - 16
 
 
+def test_rotation_and_half_swap_hand_cases():
+    # p = row % 128: rot = ((p >> 2) ^ (p >> 3)) & 1, swap = ((p >> 3) ^ (p >> 4)) & 1
+    assert [f6.rot(r) for r in (0, 4, 8, 12, 16, 24, 132)] == [0, 1, 1, 0, 0, 1, 1]
+    assert [f6.half_swap(r) for r in (0, 8, 16, 24, 136)] == [0, 1, 1, 0, 1]
+    # row 8: rotated by one chunk, so group 0's chunk 2 sits in slot 3 and
+    # group 1's chunk 2 (slot 5 + 1) wraps to slot 0
+    assert f6.chunk_offset(8, 0, 2, 128) == 8 * 96 + 48
+    assert f6.chunk_offset(8, 1, 2, 128) == 8 * 96 + 0
+    # row 8 is swapped: chunk 2 holds words 4-5 of half 1 first.  Channel 63
+    # (half 1, field 31) lives in bits 26..31 of that half's word 5.
+    q = np.zeros((9, 128), np.int64)
+    q[8, 63] = 3                                          # 1.5 -> code 12
+    q[8, 31] = -2                                         # half 0, field 31: -1 -> code 32 | 8 = 40
+    b = f6.fp6_layout_from_q(q, fill=0)
+    w = b[8 * 96 + 48: 8 * 96 + 64].view(np.uint32)      # the chunk in slot 3
+    assert (w[1] >> 26) & 63 == 12                        # half 1 first ...
+    assert (w[3] >> 26) & 63 == 40                        # ... then half 0
+    assert np.array_equal(f6.q_from_fp6_layout(b, 9, 128), q)
+
+
 def test_layout_round_trip_and_nibbles():
     rng = np.random.default_rng(3)
     for R, K in ((5, 192), (130, 256)):
