@@ -574,6 +574,15 @@ def summarize_utilisation(run_dir, trace_us):
         t.append(f"effective_clock_MHz: {ga / us:.0f}  (per-XCD active cycles / the trace's {us:.2f} us)")
         t.append(f"cycles_per_wave_group_per_SIMD: {ga / (wave_groups / 1024):.0f}  "
                  "(active cycles x 1024 SIMDs / wave-groups)")
+    lds_dir = os.path.join(run_dir, "pmc_gemm_lds")
+    if os.path.isdir(lds_dir):
+        lds = _counter_means(lds_dir, DOM_KERNEL)
+        t.append(f"# LDS: rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE -f csv -d {run_dir}/pmc_gemm_lds "
+                 f"-o run -- {cmd} --profile-kernel mlp_up.gemm_w4a4 --steps 5")
+        bc, act = lds["SQ_LDS_BANK_CONFLICT"][0], lds["SQ_LDS_IDX_ACTIVE"][0]
+        t.append(f"SQ_LDS_BANK_CONFLICT_per_launch: {int(bc)}")
+        t.append(f"SQ_LDS_IDX_ACTIVE_per_launch: {int(act)}")
+        t.append(f"lds_bank_conflict_fraction: {bc / act:.4f}  (conflict cycles / LDS-active cycles)")
     open(UTIL_FILE, "w").write("\n".join(t) + "\n")
 
     cf, _ = _counter_mean_kib(os.path.join(run_dir, "pmc_copy_FETCH_SIZE"), "copyBuffer")
