@@ -110,10 +110,10 @@ class SVDQW4A4Linear:
         fn(self.act_prec, x, self.smooth, self.lora_down, b["codes"], b["scales"],
            b["lora_act"] if self.rank else None)
 
-    def gemm(self, b):
+    def gemm(self, b, out=None):
         capi.svdq_gemm_w4a4(self.gemm_prec, b["codes"], b["scales"], self.wgt_codes, self.wgt_scales,
                             self.alpha, b["lora_act"] if self.rank else None, self.lora_up,
-                            self.bias, b["out"])
+                            self.bias, b["out"] if out is None else out)
 
     def gemm_qk_norm_rope(self, b, q_norm_weight, k_norm_weight, eps, rope_cos, rope_sin):
         """The GEMM step of a grouped QKV layer (N = 3 * heads * 128) with
@@ -123,12 +123,15 @@ class SVDQW4A4Linear:
                                          b["lora_act"] if self.rank else None, self.lora_up, self.bias,
                                          q_norm_weight, k_norm_weight, eps, rope_cos, rope_sin, b["out"])
 
-    def forward(self, x):
-        """x: bf16 [M,K] device tensor -> bf16 [M,N] (a reused buffer)."""
+    def forward(self, x, out=None):
+        """x: bf16 [M,K] device tensor -> bf16 [M,N].  Without ``out`` the
+        result is the layer's own buffer for this M, which the next call with
+        the same M overwrites; pass ``out`` (bf16 [M,N], contiguous, on the
+        device) to keep results apart."""
         b = self.buffers(x.shape[0])
         self.quantize(x, b)
-        self.gemm(b)
-        return b["out"]
+        self.gemm(b, out)
+        return b["out"] if out is None else out
 
     __call__ = forward
 
@@ -148,11 +151,14 @@ class AWQW4A16Linear:
         self.device = device
         self._out = {}
 
-    def forward(self, x):
+    def forward(self, x, out=None):
+        """x: bf16 [M,K] -> bf16 [M,N]; without ``out`` the result is a buffer
+        of the layer's own, reused by the next call with the same M."""
         M = x.shape[0]
-        out = self._out.get(M)
         if out is None:
-            out = self._out[M] = torch.empty((M, self.N), dtype=torch.bfloat16, device=self.device)
+            out = self._out.get(M)
+            if out is None:
+                out = self._out[M] = torch.empty((M, self.N), dtype=torch.bfloat16, device=self.device)
         capi.awq_gemv_w4a16(x, self.wgt_codes, self.wgt_scales, self.wgt_zeros, self.bias, out)
         return out
 

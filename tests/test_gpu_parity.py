@@ -344,8 +344,11 @@ def test_layer_end_to_end_and_determinism():
     announce("layer end to end", cfg.name)
     y1 = to_host(layer(xd).clone(), "bf16")
     y2 = to_host(layer(xd).clone(), "bf16")
+    own = torch.empty((xd.shape[0], layer.N), dtype=torch.bfloat16, device="cuda")
+    y3 = to_host(layer(xd, out=own), "bf16")
     torch.cuda.synchronize()
     assert np.array_equal(y1, y2)
+    assert np.array_equal(y1, y3)                 # a caller's output buffer: the same bits
     ac, asc, t = oracle.quantize_act(0, c["x"], c["smooth"], c["lora_down"])
     ref = oracle.gemm_w4a4(0, ac, asc, c["wgt_codes"], c["wgt_scales"], t, c["lora_up"], c["bias"])
     assert_bf16_close(y1, ref, "layer")
