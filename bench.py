@@ -624,8 +624,8 @@ def summarize_gemv_trace(run_dir):
     trace = glob.glob(os.path.join(run_dir, "gemv_trace", "**", "*kernel_trace.csv"), recursive=True)[0]
     _, K, N, _ = ADALN
     kinds = [("awq_gemv_lines_kernel<1,", "AWQ GEMV M=1", algorithmic_bytes_gemv(1, N, K)),
-             ("awq_gemv_lines_kernel<2,", "AWQ GEMV M=2", algorithmic_bytes_gemv(2, N, K)),
-             ("awq_gemv_kernel", "AWQ GEMV M=8", algorithmic_bytes_gemv(8, N, K)),
+             ("awq_gemv_lines_mfma_kernel<4,2,", "AWQ GEMV M=2", algorithmic_bytes_gemv(2, N, K)),
+             ("awq_gemv_lines_mfma_kernel<8,8,", "AWQ GEMV M=8", algorithmic_bytes_gemv(8, N, K)),
              ("stream_read_kernel<false>", "plain read, contiguous", algorithmic_bytes_gemv(1, N, K)),
              ("stream_read_kernel<true>", "plain read, GEMV row pattern", algorithmic_bytes_gemv(1, N, K))]
     durs = {k: [] for k, _, _ in kinds}

@@ -335,9 +335,11 @@ hipError_t launch_awq_gemv(int M, int N, int K, const void *x, const void *codes
                            const void *scales, const void *zeros, const void *bias, void *out,
                            hipStream_t stream)
 {
-    // one or two rows of x: the whole-line stream of gemv_w4a16_lines.hip
+    // up to 8 rows of x: the whole-line streams of gemv_w4a16_lines.hip
     if (awq_gemv_lines_applies(M, N, K))
         return launch_awq_gemv_lines(M, N, K, x, codes, scales, zeros, bias, out, stream);
+    if (awq_gemv_lines_mfma_applies(M, N, K))
+        return launch_awq_gemv_lines_mfma(M, N, K, x, codes, scales, zeros, bias, out, stream);
     const int MR = M <= 2 ? 2 : (M <= 8 ? 8 : (M <= 16 ? 16 : 32));
     const int nmt = (M + MR - 1) / MR;
     const int Mt = M < MR ? M : MR;   // rows of the largest M-tile

@@ -80,11 +80,16 @@ hipError_t launch_gemm_w4a4_nvfp4(int M, int N, int K, int rank, const void *act
 hipError_t launch_group_sums_int4(bool packed, int M, int N, int K, const void *act_codes,
                                   const void *wgt_codes, int32_t *G, hipStream_t stream);
 
-// The AWQ layer for one or two rows of x (K a multiple of 512, at most 4096):
+// The AWQ layer for one row of x (K a multiple of 512, at most 4096):
 // whole-line weight loads, dot products on the vector ALU.
 bool awq_gemv_lines_applies(int M, int N, int K);
 hipError_t launch_awq_gemv_lines(int M, int N, int K, const void *x, const void *codes, const void *scales,
                                  const void *zeros, const void *bias, void *out, hipStream_t stream);
+// The same whole-line stream for up to 8 rows of x with the products on the
+// matrix cores (K a multiple of 512, at most 4096, x within the LDS budget).
+bool awq_gemv_lines_mfma_applies(int M, int N, int K);
+hipError_t launch_awq_gemv_lines_mfma(int M, int N, int K, const void *x, const void *codes, const void *scales,
+                                      const void *zeros, const void *bias, void *out, hipStream_t stream);
 // plain read, contiguous or in the GEMV's access pattern (a measurement hook)
 int64_t stream_read_spans(int64_t bytes);
 hipError_t launch_stream_read(const void *src, int64_t bytes, bool lines, uint32_t *out, hipStream_t stream);

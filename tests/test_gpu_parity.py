@@ -376,6 +376,14 @@ def test_layer_end_to_end_and_determinism():
     # stream (8 rows per wave, 24 per block), ragged N, every chunk count
     (1, 5, 512, True), (2, 33, 1024, False), (1, 25, 1536, False), (2, 48, 2048, True),
     (1, 71, 2560, True), (2, 24, 3584, False), (1, 49, 4096, True), (2, 100, 4096, True),
+    # two to eight rows with K a multiple of 512 up to 4096: the whole-line
+    # matrix-core stream (8 weight rows per wave; 4 waves per block up to 4
+    # rows of x, 8 beyond), ragged N, every line count; the last two need more
+    # than its LDS budget and take the one-row-per-lane GEMV
+    (3, 7, 512, True), (4, 33, 1024, False), (5, 65, 1536, True), (6, 24, 2048, False),
+    (7, 100, 2560, True), (8, 57, 3072, True), (3, 40, 3584, False), (4, 64, 4096, True),
+    (5, 70, 4096, False), (2, 1, 512, False), (8, 200, 512, False),
+    (8, 33, 4096, True), (8, 40, 3584, False),
 ])
 def test_awq_gemv_shapes(M, N, K, with_bias):
     rng = np.random.default_rng(4000 + M + N + K)
