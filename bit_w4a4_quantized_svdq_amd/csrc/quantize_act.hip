@@ -283,8 +283,6 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
     v4f acc[RT > 0 ? RT : 1];
 #pragma unroll
     for (int t = 0; t < (RT > 0 ? RT : 1); ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
-    // the GELU table: published by the barrier before the first group is processed
-    if constexpr (GELU) gelu_table_fill(s_gelu, threadIdx.x, QA_WAVES * 64);
 
     for (int c0 = 0; c0 < NG; c0 += QA_CHUNK) {
         const int cg = min(QA_CHUNK, NG - c0);
@@ -535,6 +533,11 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
                 if constexpr (LSLOTS == 3) load_l(0, std::integral_constant<int, 0>{});
             }
         }
+        // the GELU table, computed while the first slices are on their way
+        // (published by the barrier below, before the first group is processed)
+        if constexpr (GELU) {
+            if (c0 == 0) gelu_table_fill(s_gelu, threadIdx.x, QA_WAVES * 64);
+        }
         // 1/s of the chunk's channels (IEEE division), staged in LDS: thread t
         // takes channels SINV*t .. +SINV-1 with one load, issued after the
         // first x slices so that both latencies overlap.
@@ -575,41 +578,71 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
 
         // ---- the chunk's codes and scales: LDS -> global, consecutive threads
         // on consecutive bytes (rows past M are not written, and neither is
-        // the second group of a last pair when K/64 is odd: FP6 padding)
+        // the second group of a last pair when K/64 is odd: FP6 padding).
+        // Every LDS read of a thread goes out before its first store (reads
+        // from a clamped, valid position; only the stores are guarded), so the
+        // pass waits for LDS once instead of once per piece.
         const int T = QA_WAVES * 64;
         const int row0 = blockIdx.x * QA_ROWS;
         const int rows = min(QA_ROWS, M - row0);
         if constexpr (PREC == 2) {
             const int NP = (NG + 1) >> 1, np = (cg + 1) >> 1;
-            for (int idx = threadIdx.x; idx < np * 96; idx += T) {
+            constexpr int FN = (QA_CHUNK / 2 * 96 + T - 1) / T;          // pieces per thread, at most
+            v4u fv[FN];
+#pragma unroll
+            for (int f = 0; f < FN; ++f)
+                fv[f] = *(const v4u *)(s_out + min((int)threadIdx.x + f * T, np * 96 - 1) * 16);
+#pragma unroll
+            for (int f = 0; f < FN; ++f) {
+                const int idx = threadIdx.x + f * T;
                 const int pl = idx / 96, rem = idx - pl * 96, rr = rem / 6, slot = rem - rr * 6;
                 const int c = (slot + 6 - fp6_rot(rr)) % 6;              // the chunk held in this slot
-                if (rr < rows && c0 + 2 * pl + c / 3 < NG) {
+                if (idx < np * 96 && rr < rows && c0 + 2 * pl + c / 3 < NG) {
                     const int grow = row0 + rr;
                     const size_t off = ((size_t)(grow >> 7) * NP + (c0 >> 1) + pl) * FP6_PAIR_BYTES +
                                        (size_t)(grow & 127) * 96 + 16 * slot;
-                    *(v4u *)(codes + off) = *(const v4u *)(s_out + idx * 16);
+                    *(v4u *)(codes + off) = fv[f];
                 }
             }
         } else {
             const int per_row = cg * 2;                                    // 16-byte pieces of a row
-            for (int idx = threadIdx.x; idx < rows * per_row; idx += T) {
+            constexpr int FN = (QA_ROWS * QA_CHUNK * 2 + T - 1) / T;
+            v4u fv[FN];
+#pragma unroll
+            for (int f = 0; f < FN; ++f) {
+                const int idx = min((int)threadIdx.x + f * T, rows * per_row - 1);
                 const int rr = idx / per_row, pc = idx - rr * per_row;
-                *(v4u *)(codes + (size_t)(row0 + rr) * (size_t)(K >> 1) + (size_t)c0 * 32 + 16 * pc) =
-                    *(const v4u *)(s_out + rr * QA_OROW + 16 * pc);
+                fv[f] = *(const v4u *)(s_out + rr * QA_OROW + 16 * pc);
+            }
+#pragma unroll
+            for (int f = 0; f < FN; ++f) {
+                const int idx = threadIdx.x + f * T;
+                const int rr = idx / per_row, pc = idx - rr * per_row;
+                if (idx < rows * per_row)
+                    *(v4u *)(codes + (size_t)(row0 + rr) * (size_t)(K >> 1) + (size_t)c0 * 32 + 16 * pc) = fv[f];
             }
         }
-        if constexpr (PREC == 1) {
-            for (int idx = threadIdx.x; idx < rows * cg; idx += T) {
+        {
+            constexpr int FN = (QA_ROWS * QA_CHUNK + T - 1) / T;
+            constexpr int SB = PREC == 1 ? 4 : 2;                          // bytes of one group's scale
+            uint32_t sv[FN];
+#pragma unroll
+            for (int f = 0; f < FN; ++f) {
+                const int idx = min((int)threadIdx.x + f * T, rows * cg - 1);
                 const int rr = idx / cg, gl = idx - rr * cg;
-                *(uint32_t *)((uint8_t *)scales + (size_t)(row0 + rr) * (size_t)(K >> 4) + (size_t)(c0 + gl) * 4) =
-                    *(const uint32_t *)(s_osc + rr * QA_SROW + 4 * gl);
+                const uint8_t *sp = s_osc + rr * QA_SROW + SB * gl;
+                sv[f] = SB == 4 ? *(const uint32_t *)sp : (uint32_t)*(const uint16_t *)sp;
             }
-        } else {
-            for (int idx = threadIdx.x; idx < rows * cg; idx += T) {
+#pragma unroll
+            for (int f = 0; f < FN; ++f) {
+                const int idx = threadIdx.x + f * T;
                 const int rr = idx / cg, gl = idx - rr * cg;
-                ((uint16_t *)scales)[(size_t)(row0 + rr) * NG + c0 + gl] =
-                    *(const uint16_t *)(s_osc + rr * QA_SROW + 2 * gl);
+                if (idx < rows * cg) {
+                    if constexpr (PREC == 1)
+                        *(uint32_t *)((uint8_t *)scales + (size_t)(row0 + rr) * (size_t)(K >> 4) + (size_t)(c0 + gl) * 4) = sv[f];
+                    else
+                        ((uint16_t *)scales)[(size_t)(row0 + rr) * NG + c0 + gl] = (uint16_t)sv[f];
+                }
             }
         }
     }
