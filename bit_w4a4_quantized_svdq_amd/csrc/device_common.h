@@ -15,7 +15,6 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
-typedef short v4s16 __attribute__((ext_vector_type(4)));
 
 // address-space-qualified pointers for global_load_lds (global -> LDS copies)
 typedef __attribute__((address_space(1))) const void *gptr_t;
