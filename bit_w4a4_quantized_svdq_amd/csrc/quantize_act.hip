@@ -69,10 +69,19 @@ namespace svdq {
 
 constexpr int QA_ROWS = 16;          // rows per block (one MFMA row tile)
 // waves per block: 16 (four per SIMD) for ranks up to 16, else 8 (the
-// low-rank partials of all waves are reduced in LDS).  At rank 32, 8 waves
-// were measured 2-4 % faster than 16 (whose 128-register budget also
-// spilled), and the GELU variants need more than 128 registers.
-template <int RT, bool GELU> constexpr int qa_waves() { return RT <= 1 && !GELU ? 16 : 8; }
+// low-rank partials of all waves are reduced in LDS), and 12 for the GELU
+// variants at rank 17-32.  A block's time is the latency of its waves' group
+// sequences (one block per CU), so more waves per block shorten it where the
+// registers allow: at rank 32 the GELU variants fit 12 waves (3 per SIMD,
+// 168 registers) without spilling.  Measured at 4096 rows against 8 waves
+// (int4 nibbles / NVFP4 / FP6 codes): K = 12288 51.1 / 56.0 / 52.2 against
+// 53.0 / 63.0 / 57.1 us, K = 3072 18.4 / 19.9 / 18.8 against 19.2 / 21.6 /
+// 19.8 us.  Without GELU, 12 waves lose the whole-line x loads (more
+// registers) and were slower for every precision (int4 at K = 3072: 14.6
+// against 12.8 us; FP6 spilled); 16 waves at rank 32 (128 registers) spill.
+template <int RT, bool GELU> constexpr int qa_waves() {
+    return RT <= 1 && !GELU ? 16 : (RT == 2 && GELU ? 12 : 8);
+}
 // K-groups whose 1/s is staged in LDS at a time: 8 channels per thread
 template <int RT, bool GELU> constexpr int qa_chunk() { return qa_waves<RT, GELU>() * 8; }
 constexpr int QA_XDEPTH = 2;         // x slices in flight per wave (groups ahead)
@@ -578,71 +587,41 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
 
         // ---- the chunk's codes and scales: LDS -> global, consecutive threads
         // on consecutive bytes (rows past M are not written, and neither is
-        // the second group of a last pair when K/64 is odd: FP6 padding).
-        // Every LDS read of a thread goes out before its first store (reads
-        // from a clamped, valid position; only the stores are guarded), so the
-        // pass waits for LDS once instead of once per piece.
+        // the second group of a last pair when K/64 is odd: FP6 padding)
         const int T = QA_WAVES * 64;
         const int row0 = blockIdx.x * QA_ROWS;
         const int rows = min(QA_ROWS, M - row0);
         if constexpr (PREC == 2) {
             const int NP = (NG + 1) >> 1, np = (cg + 1) >> 1;
-            constexpr int FN = (QA_CHUNK / 2 * 96 + T - 1) / T;          // pieces per thread, at most
-            v4u fv[FN];
-#pragma unroll
-            for (int f = 0; f < FN; ++f)
-                fv[f] = *(const v4u *)(s_out + min((int)threadIdx.x + f * T, np * 96 - 1) * 16);
-#pragma unroll
-            for (int f = 0; f < FN; ++f) {
-                const int idx = threadIdx.x + f * T;
+            for (int idx = threadIdx.x; idx < np * 96; idx += T) {
                 const int pl = idx / 96, rem = idx - pl * 96, rr = rem / 6, slot = rem - rr * 6;
                 const int c = (slot + 6 - fp6_rot(rr)) % 6;              // the chunk held in this slot
-                if (idx < np * 96 && rr < rows && c0 + 2 * pl + c / 3 < NG) {
+                if (rr < rows && c0 + 2 * pl + c / 3 < NG) {
                     const int grow = row0 + rr;
                     const size_t off = ((size_t)(grow >> 7) * NP + (c0 >> 1) + pl) * FP6_PAIR_BYTES +
                                        (size_t)(grow & 127) * 96 + 16 * slot;
-                    *(v4u *)(codes + off) = fv[f];
+                    *(v4u *)(codes + off) = *(const v4u *)(s_out + idx * 16);
                 }
             }
         } else {
             const int per_row = cg * 2;                                    // 16-byte pieces of a row
-            constexpr int FN = (QA_ROWS * QA_CHUNK * 2 + T - 1) / T;
-            v4u fv[FN];
-#pragma unroll
-            for (int f = 0; f < FN; ++f) {
-                const int idx = min((int)threadIdx.x + f * T, rows * per_row - 1);
+            for (int idx = threadIdx.x; idx < rows * per_row; idx += T) {
                 const int rr = idx / per_row, pc = idx - rr * per_row;
-                fv[f] = *(const v4u *)(s_out + rr * QA_OROW + 16 * pc);
-            }
-#pragma unroll
-            for (int f = 0; f < FN; ++f) {
-                const int idx = threadIdx.x + f * T;
-                const int rr = idx / per_row, pc = idx - rr * per_row;
-                if (idx < rows * per_row)
-                    *(v4u *)(codes + (size_t)(row0 + rr) * (size_t)(K >> 1) + (size_t)c0 * 32 + 16 * pc) = fv[f];
+                *(v4u *)(codes + (size_t)(row0 + rr) * (size_t)(K >> 1) + (size_t)c0 * 32 + 16 * pc) =
+                    *(const v4u *)(s_out + rr * QA_OROW + 16 * pc);
             }
         }
-        {
-            constexpr int FN = (QA_ROWS * QA_CHUNK + T - 1) / T;
-            constexpr int SB = PREC == 1 ? 4 : 2;                          // bytes of one group's scale
-            uint32_t sv[FN];
-#pragma unroll
-            for (int f = 0; f < FN; ++f) {
-                const int idx = min((int)threadIdx.x + f * T, rows * cg - 1);
+        if constexpr (PREC == 1) {
+            for (int idx = threadIdx.x; idx < rows * cg; idx += T) {
                 const int rr = idx / cg, gl = idx - rr * cg;
-                const uint8_t *sp = s_osc + rr * QA_SROW + SB * gl;
-                sv[f] = SB == 4 ? *(const uint32_t *)sp : (uint32_t)*(const uint16_t *)sp;
+                *(uint32_t *)((uint8_t *)scales + (size_t)(row0 + rr) * (size_t)(K >> 4) + (size_t)(c0 + gl) * 4) =
+                    *(const uint32_t *)(s_osc + rr * QA_SROW + 4 * gl);
             }
-#pragma unroll
-            for (int f = 0; f < FN; ++f) {
-                const int idx = threadIdx.x + f * T;
+        } else {
+            for (int idx = threadIdx.x; idx < rows * cg; idx += T) {
                 const int rr = idx / cg, gl = idx - rr * cg;
-                if (idx < rows * cg) {
-                    if constexpr (PREC == 1)
-                        *(uint32_t *)((uint8_t *)scales + (size_t)(row0 + rr) * (size_t)(K >> 4) + (size_t)(c0 + gl) * 4) = sv[f];
-                    else
-                        ((uint16_t *)scales)[(size_t)(row0 + rr) * NG + c0 + gl] = (uint16_t)sv[f];
-                }
+                ((uint16_t *)scales)[(size_t)(row0 + rr) * NG + c0 + gl] =
+                    *(const uint16_t *)(s_osc + rr * QA_SROW + 2 * gl);
             }
         }
     }
