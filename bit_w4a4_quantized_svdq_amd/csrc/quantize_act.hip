@@ -69,23 +69,26 @@ namespace svdq {
 
 constexpr int QA_ROWS = 16;          // rows per block (one MFMA row tile)
 // waves per block: 16 (four per SIMD) for ranks up to 16, else 8 (the
-// low-rank partials of all waves are reduced in LDS), and 12 for the GELU
-// variants at rank 17-32.  A block's time is the latency of its waves' group
+// low-rank partials of all waves are reduced in LDS), and 12 at rank 17-32
+// for the GELU variants and NVFP4.  Both int4 outputs (nibbles and the FP6
+// layout) take the same count, so that their low-rank sums agree bit for bit.  A block's time is the latency of its waves' group
 // sequences (one block per CU), so more waves per block shorten it where the
 // registers allow: at rank 32 the GELU variants fit 12 waves (3 per SIMD,
 // 168 registers) without spilling.  Measured at 4096 rows against 8 waves
 // (int4 nibbles / NVFP4 / FP6 codes): K = 12288 51.1 / 56.0 / 52.2 against
 // 53.0 / 63.0 / 57.1 us, K = 3072 18.4 / 19.9 / 18.8 against 19.2 / 21.6 /
-// 19.8 us.  Without GELU, 12 waves lose the whole-line x loads (more
-// registers) and were slower for every precision (int4 at K = 3072: 14.6
-// against 12.8 us; FP6 spilled); 16 waves at rank 32 (128 registers) spill.
-template <int RT, bool GELU> constexpr int qa_waves() {
-    return RT <= 1 && !GELU ? 16 : (RT == 2 && GELU ? 12 : 8);
+// 19.8 us.  Without GELU, with the whole-line x loads: NVFP4 at K = 3072
+// 14.0 against 14.7 us, at K = 12288 43.0 against 45.5 us; the FP6 variant
+// spilled at 12 waves (14.6 against 13.7 us), so both int4 variants keep 8
+// (nibbles: 12.7 either way at K = 3072, 40.8 against 41.7 at K = 12288).
+// 16 waves at rank 32 (128 registers) spill.
+template <int PREC, int RT, bool GELU> constexpr int qa_waves() {
+    return RT <= 1 && !GELU ? 16 : (RT == 2 && (GELU || PREC == 1) ? 12 : 8);
 }
 // K-groups whose 1/s is staged in LDS at a time: 8 channels per thread
-template <int RT, bool GELU> constexpr int qa_chunk() { return qa_waves<RT, GELU>() * 8; }
+template <int PREC, int RT, bool GELU> constexpr int qa_chunk() { return qa_waves<PREC, RT, GELU>() * 8; }
 constexpr int QA_XDEPTH = 2;         // x slices in flight per wave (groups ahead)
-// Whole-line x loads (8-wave blocks): a group's 16 rows x 128 bytes are
+// Whole-line x loads (8- and 12-wave blocks): a group's 16 rows x 128 bytes are
 // loaded as 8 rows x 128 B per instruction (lane i: row 8j + i/8, 16-byte
 // chunk i % 8), so every load instruction moves whole cache lines, and one
 // LDS pass per wave puts them into the MFMA layout (lane l: row l % 16,
@@ -96,7 +99,9 @@ constexpr int QA_XDEPTH = 2;         // x slices in flight per wave (groups ahea
 // against 50.1 us at K = 12288 (4096 rows, rank 32, FP6 codes); the
 // GELU-fed step was 2 % slower with it and keeps the direct loads, as do
 // ranks above 64 (whose three-slot low-rank ring would spill).
-template <int RT, bool GELU> constexpr bool qa_lds_x() { return qa_waves<RT, GELU>() == 8 && RT <= 4 && !GELU; }
+template <int PREC, int RT, bool GELU> constexpr bool qa_lds_x() {
+    return (qa_waves<PREC, RT, GELU>() == 8 || qa_waves<PREC, RT, GELU>() == 12) && RT <= 4 && !GELU;
+}
 constexpr int QA_XSLOT = QA_ROWS * 128;      // bytes of one group's x slice
 constexpr int QA_PERIOD = 3;         // unroll period: a multiple of both ring sizes (3, and 3 or 1)
 
@@ -233,20 +238,20 @@ __device__ __forceinline__ void store_fp6_group(const float (&q)[16], uint8_t *i
 }
 
 template <int PREC, int RT, bool GELU>
-__global__ __launch_bounds__((qa_waves<RT, GELU>() * 64))
+__global__ __launch_bounds__((qa_waves<PREC, RT, GELU>() * 64))
 void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
                          const uint16_t *__restrict__ smooth,
                          const uint16_t *__restrict__ lora_down,
                          uint8_t *__restrict__ codes, void *__restrict__ scales,
                          float *__restrict__ lora_act)
 {
-    constexpr int QA_WAVES = qa_waves<RT, GELU>();
-    constexpr bool LDSX = qa_lds_x<RT, GELU>();
+    constexpr int QA_WAVES = qa_waves<PREC, RT, GELU>();
+    constexpr bool LDSX = qa_lds_x<PREC, RT, GELU>();
     // low-rank slices (L2 resident): loaded per group, or one group ahead
     // when x comes through LDS (so that waiting for them never waits for
     // the newest x copies)
     constexpr int LSLOTS = LDSX ? 3 : 1;
-    constexpr int QA_CHUNK = qa_chunk<RT, GELU>();
+    constexpr int QA_CHUNK = qa_chunk<PREC, RT, GELU>();
     constexpr int SINV = QA_CHUNK * 64 / (QA_WAVES * 64);   // 1/s channels per thread per chunk
     static_assert(SINV == 4 || SINV == 8, "1/s staging: 8 or 16 bytes of bf16 per thread");
     __shared__ float s_inv[QA_CHUNK * 64];
@@ -659,7 +664,7 @@ static hipError_t launch_prec(int M, int K, int rank, const void *x, const void 
     uint8_t *cp = (uint8_t *)codes;
 #define QA_CASE(RTV)                                                                            \
     case RTV:                                                                                   \
-        hipLaunchKernelGGL((quantize_act_kernel<PREC, RTV, GELU>), grid, dim3((qa_waves<RTV, GELU>() * 64)), 0, st, \
+        hipLaunchKernelGGL((quantize_act_kernel<PREC, RTV, GELU>), grid, dim3((qa_waves<PREC, RTV, GELU>() * 64)), 0, st, \
                            M, K, xp, sp, lp, cp, scales, lora_act);                             \
         break;
     switch (rank / 16) {
