@@ -326,6 +326,31 @@ def gelu_fusion(torch, synth, layers, batches=3, per=10):
     return out
 
 
+def mlp_fusion(torch, layers, xs, rounds=9, per=5):
+    """The GELU MLP's up GEMM and the down layer's activation step (4096 x
+    3072 -> 12288 -> activation step of 4096 x 12288, int4 FP6 layout, ranks
+    32): two calls (svdq_gemm_w4a4, then svdq_gelu_quantize_act reading the
+    written intermediate) beside svdq_gemm_w4a4_gelu_quantize (the activation
+    step in the up GEMM's epilogue, intermediate not written).  Timed by
+    ``interleaved_us``; both produce the same codes and scales."""
+    up, down = layers["mlp_up"], layers["mlp_down"]
+    M = xs["mlp_up"].shape[0]
+    bu, bd = up.buffers(M), down.buffers(M)
+    up.quantize(xs["mlp_up"], bu)
+
+    def two_calls():
+        up.gemm(bu)
+        down.quantize(bu["out"], bd, gelu=True)
+
+    fns = {"two_calls": two_calls, "fused": lambda: up.gemm_gelu_quantize(bu, down, bd)}
+    t = interleaved_us(torch, fns, rounds=rounds, per=per)
+    out = {k: {"us": round(v, 3)} for k, v in t.items()}
+    out["saved_us"] = round(t["two_calls"] - t["fused"], 3)
+    print(f"[bench] mlp fusion: {t['fused']:.1f} us fused, {t['two_calls']:.1f} us in two calls",
+          file=sys.stderr, flush=True)
+    return out
+
+
 def qk_fusion(torch, synth, layers, xs, per=5):
     """The grouped QKV layer's GEMM (4096 x 3072 -> 9216, 24 heads of 128)
     with per-head RMSNorm + rotary embedding of Q and K in its epilogue,
@@ -932,6 +957,7 @@ def main():
     gemv = None if args.no_gemv_sweep else gemv_sweep(torch, synth)
     fusion = None if args.no_gemv_sweep else gelu_fusion(torch, synth, layers)
     qk = None if args.no_gemv_sweep else qk_fusion(torch, synth, layers, xs)
+    mlp = None if args.no_gemv_sweep else mlp_fusion(torch, layers, xs)
     prep = None if args.no_gemv_sweep else prepare_timing(torch, synth)
     cpu = None if args.no_cpu_baseline else cpu_baseline(synth)
 
@@ -945,6 +971,7 @@ def main():
                       "layers": {n: f"{p} {M}x{K}->{N} rank {r}" for n, p, M, K, N, r, _ in LAYERS} |
                                 {"adaln": f"awq_w4a16 1x{K}->{N} g64"}},
            "roofline": roofline, "kernels": kernels, "gemv": gemv, "gelu_fusion": fusion, "qk_fusion": qk,
+           "mlp_fusion": mlp,
            "weight_preparation": prep,
            "cpu_baseline": cpu}
     print(json.dumps(rec))

@@ -22,6 +22,7 @@ SVDQ_OK, SVDQ_ERR_INVALID_ARG, SVDQ_ERR_UNSUPPORTED, SVDQ_ERR_HIP = 0, 1, 2, 3
 SVDQ_INT4, SVDQ_NVFP4, SVDQ_INT4_PACKED, SVDQ_INT4_FP6 = 0, 1, 2, 3
 
 EXPORTED = ("svdq_quantize_act", "svdq_gelu_quantize_act", "svdq_gemm_w4a4", "svdq_gemm_w4a4_qk_norm_rope",
+            "svdq_gelu_quantize_workspace_bytes", "svdq_gemm_w4a4_gelu_quantize",
             "awq_gemv_w4a16",
             "svdq_smooth_factors", "svdq_quantize_weight", "svdq_lowrank_workspace_bytes",
             "svdq_lowrank_factors", "svdq_lowrank_factors_noalloc",
@@ -56,6 +57,10 @@ def lib() -> ctypes.CDLL:
                                      _P, _P]
         L.svdq_gemm_w4a4_qk_norm_rope.argtypes = [_I32, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _F32, _P, _P,
                                                   _P, _P, _P, _F32, _P, _P, _P, _P]
+        L.svdq_gelu_quantize_workspace_bytes.argtypes = [_I64, _I64, _I32]
+        L.svdq_gelu_quantize_workspace_bytes.restype = _I64
+        L.svdq_gemm_w4a4_gelu_quantize.argtypes = [_I32, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _F32, _P, _P, _P,
+                                                   _I32, _P, _P, _P, _P, _P, _P, _I64, _P, _P]
         L.awq_gemv_w4a16.argtypes = [_I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P]
         L.svdq_debug_group_sums.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P]
         L.svdq_debug_group_sums_packed.argtypes = [_I64, _I64, _I64, _P, _P, _P, _P]
@@ -75,7 +80,7 @@ def lib() -> ctypes.CDLL:
         L.svdq_lowrank_factors.argtypes = [_I64, _I64, _I32, _P, _P, ctypes.c_uint64, _P, _I64, _P, _P, _P]
         L.svdq_lowrank_factors_noalloc.argtypes = [_I64, _I64, _I32, _P, _P, ctypes.c_uint64, _P, _P, _P]
         for f in ("svdq_quantize_act", "svdq_gelu_quantize_act", "svdq_gemm_w4a4",
-                  "svdq_gemm_w4a4_qk_norm_rope", "awq_gemv_w4a16",
+                  "svdq_gemm_w4a4_qk_norm_rope", "svdq_gemm_w4a4_gelu_quantize", "awq_gemv_w4a16",
                   "svdq_debug_group_sums", "svdq_debug_group_sums_packed", "svdq_pack_weight_int4",
                   "svdq_debug_group_sums_fp6", "svdq_pack_weight_fp6",
                   "svdq_debug_gelu_bf16", "svdq_debug_stream_read", "svdq_smooth_factors",
@@ -290,6 +295,38 @@ def svdq_gemm_w4a4_qk_norm_rope(precision, act_codes, act_scales, wgt_codes, wgt
                                              _ptr(q_norm_weight), _ptr(k_norm_weight), float(eps),
                                              _ptr(rope_cos), _ptr(rope_sin), _ptr(out), _stream(stream)),
            "svdq_gemm_w4a4_qk_norm_rope")
+
+
+def svdq_gelu_quantize_workspace_bytes(M, N, rank_next) -> int:
+    """Workspace bytes of svdq_gemm_w4a4_gelu_quantize (-1 if the sizes are invalid)."""
+    return int(lib().svdq_gelu_quantize_workspace_bytes(M, N, rank_next))
+
+
+def svdq_gemm_w4a4_gelu_quantize(act_codes, act_scales, wgt_codes, wgt_scales, alpha, lora_act, lora_up,
+                                 bias, smooth_next, lora_down_next, next_codes, next_scales, next_lora_act,
+                                 workspace, out=None, stream=None):
+    """Up projection of a GELU MLP (int4, FP6 layout) with the down layer's
+    activation step in its epilogue: writes the down layer's FP6 codes,
+    scales [M, N/64] and lora_act [M, rank_next] (M from next_scales), and
+    the up layer's output into out [M, N] when given; workspace: a uint8
+    device tensor of svdq_gelu_quantize_workspace_bytes(M, N, rank_next)."""
+    func = "svdq_gemm_w4a4_gelu_quantize"
+    prec = SVDQ_INT4_FP6
+    M = next_scales.shape[0]
+    N, K = _weight_shape(prec, wgt_codes, wgt_scales)
+    rank = 0 if lora_up is None else lora_up.shape[1]
+    rank_next = 0 if lora_down_next is None else lora_down_next.shape[0]
+    _check_layer_buffers(func, prec, M, N, K, rank, act_codes, act_scales, wgt_codes, wgt_scales, lora_act,
+                         lora_up, bias, out)
+    _check_act_buffers(func, prec, M, N, rank_next, smooth_next, lora_down_next, next_codes, next_scales,
+                       next_lora_act)
+    _check(lib().svdq_gemm_w4a4_gelu_quantize(prec, M, N, K, rank, _ptr(act_codes), _ptr(act_scales),
+                                              _ptr(wgt_codes), _ptr(wgt_scales), float(alpha), _ptr(lora_act),
+                                              _ptr(lora_up), _ptr(bias), rank_next, _ptr(smooth_next),
+                                              _ptr(lora_down_next), _ptr(next_codes), _ptr(next_scales),
+                                              _ptr(next_lora_act), _ptr(workspace),
+                                              workspace.numel() * workspace.element_size(), _ptr(out),
+                                              _stream(stream)), func)
 
 
 def awq_gemv_w4a16(x, wgt_codes, wgt_scales, wgt_zeros, bias, out, group_size=64, stream=None):

@@ -87,6 +87,18 @@ __device__ __forceinline__ float max_xor32(float v) {
     return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
 }
 
+// max(m, |a|, |b|) in one v_max3_f32 (the values are finite; fp32 denormals
+// are preserved by the kernels' float mode)
+__device__ __forceinline__ float max3_abs(float m, float a, float b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    float r;
+    asm("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(r) : "v"(m), "v"(a), "v"(b));
+    return r;
+#else
+    return fmaxf(m, fmaxf(fabsf(a), fabsf(b)));
+#endif
+}
+
 // E4M3 ("FN") encode of a non-negative finite fp32, round to nearest even,
 // saturating at 448 (the format has no infinity).
 __device__ __forceinline__ uint32_t e4m3_encode_nonneg(float v) {

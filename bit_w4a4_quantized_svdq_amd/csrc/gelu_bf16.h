@@ -23,9 +23,11 @@
 //
 // Fast path: two values per dword, their table slots formed with packed
 // 16-bit integer operations.  Inputs outside the table's range land on a
-// sentinel slot (0x7FFF: bits 14 and 13 both set, which no result below 32
-// in magnitude has); when any lane of the wave meets one, the whole group is
-// redone with the exact rules (a wave-uniform branch).
+// sentinel slot (0x7FFF) and raise a tracked slot maximum (one packed max per
+// pair); when any lane of the wave has an input of 32 or more in magnitude,
+// the pairs get the |y| >= 32 rule by selects, and when any has a NaN or an
+// input below 2^-14, the whole group is redone with the exact rules
+// (wave-uniform branches).
 #pragma once
 
 #include <stdint.h>
@@ -75,42 +77,76 @@ __device__ inline uint32_t gelu_bf16_exact(uint32_t h, const uint16_t *tab)
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-// Table lookups of two packed bf16 (sentinels for inputs outside the range).
-__device__ __forceinline__ uint32_t gelu_lookup2(uint32_t w, const uint16_t *tab)
+// Table lookups of two packed bf16 (the sentinel for inputs outside the
+// range), keeping in tmax the largest unclamped slot index seen (one packed
+// max): a half of tmax at or above GELU_SPAN means an input outside the
+// table's range.
+__device__ __forceinline__ uint32_t gelu_lookup2_track(uint32_t w, const uint16_t *tab, u16x2 &tmax)
 {
     const u16x2 m = __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu);
-    u16x2 ti = m - (u16x2)(unsigned short)(GELU_E_LO << 7);                  // wraps below the range
-    ti = __builtin_elementwise_min(ti, (u16x2)(unsigned short)GELU_SPAN);    // the sentinel slot
+    u16x2 ti = m - (u16x2)(unsigned short)(GELU_E_LO << 7);
+    tmax = __builtin_elementwise_max(tmax, ti);
+    ti = __builtin_elementwise_min(ti, (u16x2)(unsigned short)GELU_SPAN);
     const u16x2 s = __builtin_bit_cast(u16x2, w) >> (unsigned short)15;
     const u16x2 idx = s * (u16x2)(unsigned short)GELU_STRIDE + ti;
     const uint32_t id = __builtin_bit_cast(uint32_t, idx);
     return (uint32_t)tab[id & 0xFFFFu] | ((uint32_t)tab[id >> 16] << 16);
 }
 
+// Unclamped slot index of +-infinity: inputs whose index lies in
+// [GELU_SPAN, GELU_TI_INF] are 32 <= |y| <= infinity; above it lie NaNs and,
+// wrapped around, the inputs below 2^-14.
+constexpr uint32_t GELU_TI_INF = 0x7F80u - (uint32_t)(GELU_E_LO << 7);
+
+// The exact rule for |y| >= 32 applied to a looked-up pair: y for y >= 32
+// (+infinity included), -0 for y <= -32; other halves keep the table's
+// result.  Valid when no input of the pair is a NaN or below 2^-14.
+__device__ __forceinline__ uint32_t gelu_fix_big2(uint32_t g, uint32_t w)
+{
+    const float y0 = bf16_lo(w), y1 = bf16_hi(w);
+    uint32_t lo = g & 0xFFFFu, hi = g >> 16;
+    lo = y0 >= 32.0f ? (w & 0xFFFFu) : (y0 <= -32.0f ? 0x8000u : lo);
+    hi = y1 >= 32.0f ? (w >> 16) : (y1 <= -32.0f ? 0x8000u : hi);
+    return lo | (hi << 16);
+}
+
+// GELU of n packed pairs in place after gelu_lookup2_track (g: looked-up
+// results, w: inputs, tmax: the tracked slot maximum; every lane of the wave
+// takes part, the branches are wave-uniform): inputs of 32 and above in
+// magnitude take gelu_fix_big2, a NaN or an input below 2^-14 anywhere in
+// the wave sends all n pairs through the exact rules.
+template <int n>
+__device__ __forceinline__ void gelu_resolve(uint32_t (&g)[n], const uint32_t (&w)[n], u16x2 tmax,
+                                             const uint16_t *tab)
+{
+    const uint32_t tm = tmax[0] > tmax[1] ? tmax[0] : tmax[1];
+    if (__builtin_expect(__any(tm > GELU_TI_INF), 0)) {
+#pragma unroll
+        for (int p = 0; p < n; ++p)
+            g[p] = gelu_bf16_exact(w[p] & 0xFFFFu, tab) | (gelu_bf16_exact(w[p] >> 16, tab) << 16);
+    } else if (__any(tm >= (uint32_t)GELU_SPAN)) {
+#pragma unroll
+        for (int p = 0; p < n; ++p) g[p] = gelu_fix_big2(g[p], w[p]);
+    }
+}
+
 // GELU of 16 packed bf16 in place (the quantize kernel's slice of a group).
 __device__ __forceinline__ void gelu_bf16x16(v4u (&x)[2], const uint16_t *tab)
 {
-    v4u r[2];
-    uint32_t flag = 0;
+    uint32_t w[8], r[8];
+    u16x2 tmax = (u16x2)(unsigned short)0;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            const uint32_t v = gelu_lookup2(x[j][p], tab);
-            r[j][p] = v;
-            flag |= v & (v << 1);   // bits 14 and 13 of a half both set: a sentinel
+            w[4 * j + p] = x[j][p];
+            r[4 * j + p] = gelu_lookup2_track(x[j][p], tab, tmax);
         }
-    if (__builtin_expect(__any((flag & 0x40004000u) != 0u), 0)) {
+    gelu_resolve(r, w, tmax, tab);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const uint32_t w = x[j][p];
-                r[j][p] = gelu_bf16_exact(w & 0xFFFFu, tab) | (gelu_bf16_exact(w >> 16, tab) << 16);
-            }
-    }
-    x[0] = r[0];
-    x[1] = r[1];
+        for (int p = 0; p < 4; ++p) x[j][p] = r[4 * j + p];
 }
 
 }  // namespace svdq

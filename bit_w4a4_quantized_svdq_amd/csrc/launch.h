@@ -60,6 +60,15 @@ hipError_t launch_gemm_w4a4_fp6_qk(int M, int N, int K, int rank, const void *ac
                                    const QkNormRope &qk, void *out, hipStream_t stream);
 hipError_t launch_group_sums_fp6(int M, int N, int K, const void *act_codes, const void *wgt_codes, int32_t *G,
                                  hipStream_t stream);
+// the FP6 GEMM of a GELU MLP's up projection with the down layer's activation
+// step in its epilogue (workspace: gelu_quant_workspace_bytes)
+size_t gelu_quant_workspace_bytes(int M, int N, int rank_next);
+hipError_t launch_gemm_w4a4_fp6_gelu_quant(int M, int N, int K, int rank, const void *act_codes,
+                                           const void *act_scales, const void *wgt_codes, const void *wgt_scales,
+                                           float alpha, const float *lora_act, const void *lora_up,
+                                           const void *bias, int rank_next, const void *smooth_next,
+                                           const void *lora_down_next, void *next_codes, void *next_scales,
+                                           float *next_lora_act, void *workspace, void *out, hipStream_t stream);
 hipError_t launch_gemm_w4a4_nvfp4_qk(int M, int N, int K, int rank, const void *act_codes,
                                      const void *act_scales, const void *wgt_codes,
                                      const void *wgt_scales, float alpha, const float *lora_act,

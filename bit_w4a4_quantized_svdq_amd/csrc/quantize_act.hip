@@ -113,18 +113,6 @@ __device__ __forceinline__ float v4u_elem(const v4u &v, int e) {
 
 struct F16 { float v[16]; };
 
-// max(m, |a|, |b|) in one v_max3_f32 (the values are finite; fp32 denormals
-// are preserved by the kernel's float mode)
-__device__ __forceinline__ float max3_abs(float m, float a, float b) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    float r;
-    asm("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(r) : "v"(m), "v"(a), "v"(b));
-    return r;
-#else
-    return fmaxf(m, fmaxf(fabsf(a), fabsf(b)));
-#endif
-}
-
 // Eight quotients clamped to [-8, 7], rounded to the nearest integer (ties
 // to even) and packed as two's-complement nibbles, element e in nibble e.
 // Even elements: the fp32 add of 2^23 + 8 rounds and leaves q + 8 in the low

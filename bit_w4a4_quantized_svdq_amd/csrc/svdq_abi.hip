@@ -281,6 +281,57 @@ svdq_status svdq_gemm_w4a4_qk_norm_rope(int32_t precision, int64_t M, int64_t N,
     return launched(e, "svdq_gemm_w4a4_qk_norm_rope");
 }
 
+int64_t svdq_gelu_quantize_workspace_bytes(int64_t M, int64_t N, int32_t rank_next)
+{
+    if (check_shape(M, 1, N, rank_next) != SVDQ_OK) return -1;
+    return (int64_t)svdq::gelu_quant_workspace_bytes((int)M, (int)N, rank_next);
+}
+
+svdq_status svdq_gemm_w4a4_gelu_quantize(int32_t precision, int64_t M, int64_t N, int64_t K, int32_t rank,
+                                         const void *act_codes, const void *act_scales,
+                                         const void *wgt_codes, const void *wgt_scales, float alpha,
+                                         const float *lora_act, const void *lora_up, const void *bias,
+                                         int32_t rank_next, const void *smooth_next, const void *lora_down_next,
+                                         void *next_codes, void *next_scales, float *next_lora_act,
+                                         void *workspace, int64_t workspace_bytes, void *out, void *stream)
+{
+    if (precision != SVDQ_INT4_FP6)
+        return fail(SVDQ_ERR_UNSUPPORTED, "svdq_gemm_w4a4_gelu_quantize takes SVDQ_INT4_FP6 only (got %d)",
+                    precision);
+    SVDQ_TRY(check_shape(M, N, K, rank));
+    if (N == 0 || N % 64 != 0 || N > kMaxK || rank_next < 0 || rank_next > 128 || rank_next % 16 != 0)
+        return fail(SVDQ_ERR_INVALID_ARG,
+                    "N must be a positive multiple of 64 up to 2^16 and rank_next a multiple of 16 in [0, 128] "
+                    "(N=%lld rank_next=%d)", (long long)N, rank_next);
+    SVDQ_TRY(check_ptr(act_codes, "act_codes", false));
+    SVDQ_TRY(check_ptr(act_scales, "act_scales", false));
+    SVDQ_TRY(check_ptr(wgt_codes, "wgt_codes", false));
+    SVDQ_TRY(check_ptr(wgt_scales, "wgt_scales", false));
+    SVDQ_TRY(check_ptr(lora_act, "lora_act", rank == 0));
+    SVDQ_TRY(check_ptr(lora_up, "lora_up", rank == 0));
+    SVDQ_TRY(check_ptr(bias, "bias", true));
+    SVDQ_TRY(check_ptr(smooth_next, "smooth_next", true));
+    SVDQ_TRY(check_ptr(lora_down_next, "lora_down_next", rank_next == 0));
+    SVDQ_TRY(check_ptr(next_codes, "next_codes", false));
+    SVDQ_TRY(check_ptr(next_scales, "next_scales", false));
+    SVDQ_TRY(check_ptr(next_lora_act, "next_lora_act", rank_next == 0));
+    SVDQ_TRY(check_ptr(workspace, "workspace", false));
+    SVDQ_TRY(check_ptr(out, "out", true));
+    const int64_t need = (int64_t)svdq::gelu_quant_workspace_bytes((int)M, (int)N, rank_next);
+    if (workspace_bytes < need)
+        return fail(SVDQ_ERR_INVALID_ARG, "workspace too small: %lld bytes, %lld needed", (long long)workspace_bytes,
+                    (long long)need);
+    if (M == 0) return SVDQ_OK;
+    SVDQ_TRY(check_grid(M, N, 128, 128));
+    SVDQ_TRY(check_device());
+    return launched(svdq::launch_gemm_w4a4_fp6_gelu_quant((int)M, (int)N, (int)K, rank, act_codes, act_scales,
+                                                          wgt_codes, wgt_scales, alpha, lora_act, lora_up, bias,
+                                                          rank_next, smooth_next, lora_down_next, next_codes,
+                                                          next_scales, next_lora_act, workspace, out,
+                                                          (hipStream_t)stream),
+                    "svdq_gemm_w4a4_gelu_quantize");
+}
+
 svdq_status svdq_gemm_w4a4(int32_t precision, int64_t M, int64_t N, int64_t K, int32_t rank,
                            const void *act_codes, const void *act_scales, const void *wgt_codes,
                            const void *wgt_scales, float alpha, const float *lora_act,
@@ -437,6 +488,6 @@ const char *svdq_status_string(svdq_status s)
 
 const char *svdq_last_error(void) { return g_last_error; }
 
-int32_t svdq_abi_version(void) { return 10; }
+int32_t svdq_abi_version(void) { return 11; }
 
 }  // extern "C"

@@ -123,6 +123,23 @@ class SVDQW4A4Linear:
                                          b["lora_act"] if self.rank else None, self.lora_up, self.bias,
                                          q_norm_weight, k_norm_weight, eps, rope_cos, rope_sin, b["out"])
 
+    def gemm_gelu_quantize(self, b, nxt, nb, out=None):
+        """The GEMM step of a GELU MLP's up projection with the down layer
+        ``nxt``'s activation step in its epilogue: writes nxt's codes, scales
+        and lora_act into its buffers ``nb`` (and this layer's output into
+        ``out`` when given).  Both layers int4 in the FP6 layout."""
+        if self.gemm_prec != capi.SVDQ_INT4_FP6 or nxt.act_prec != capi.SVDQ_INT4_FP6 or nxt.K != self.N:
+            raise ValueError("gemm_gelu_quantize: both layers int4 in the FP6 layout, nxt.K == N")
+        M = nb["scales"].shape[0]
+        ws = b.get("gq_workspace")
+        need = capi.svdq_gelu_quantize_workspace_bytes(M, self.N, nxt.rank)
+        if ws is None or ws.numel() < need:
+            ws = b["gq_workspace"] = torch.empty((need,), dtype=torch.uint8, device=self.device)
+        capi.svdq_gemm_w4a4_gelu_quantize(b["codes"], b["scales"], self.wgt_codes, self.wgt_scales, self.alpha,
+                                          b["lora_act"] if self.rank else None, self.lora_up, self.bias,
+                                          nxt.smooth, nxt.lora_down, nb["codes"], nb["scales"],
+                                          nb["lora_act"] if nxt.rank else None, ws, out)
+
     def forward(self, x, out=None):
         """x: bf16 [M,K] device tensor -> bf16 [M,N].  Without ``out`` the
         result is the layer's own buffer for this M, which the next call with

@@ -187,6 +187,42 @@ svdq_status svdq_gemm_w4a4_qk_norm_rope(int32_t precision, int64_t M, int64_t N,
                                         void *stream);
 
 /*
+ * svdq_gemm_w4a4_gelu_quantize -- the up projection of a GELU MLP with the
+ * down layer's activation step in its epilogue, so that the [M, N] bf16
+ * intermediate is not written ("Nunchaku Lite" docs, "Fused kernels": the
+ * original engine runs the MLP's GELU fused into its kernels).  Int4 in the
+ * FP6 layout only.  With y the bf16 output svdq_gemm_w4a4(SVDQ_INT4_FP6, ...)
+ * would write, the outputs are exactly what svdq_gelu_quantize_act(
+ * SVDQ_INT4_FP6, y, smooth_next, lora_down_next, ...) writes: the same codes
+ * and scales bit for bit; next_lora_act equal up to fp32 summation order
+ * (here: partial sums over 128-column tiles, added in tile order, so a given
+ * shape gives the same bits on every run).
+ *   precision       SVDQ_INT4_FP6 (input operands and output codes)
+ *   M, N, K, rank, act_codes ... bias   as for svdq_gemm_w4a4; N <= 65536
+ *   rank_next       rank of the down layer (0 or a multiple of 16 up to 128)
+ *   smooth_next     bf16 [N] or NULL (s = 1): the down layer's smoothing
+ *   lora_down_next  bf16 [rank_next, N]; NULL iff rank_next == 0
+ *   next_codes      out: the FP6 tiled layout of [M, N] (svdq_fp6_codes_bytes(M, N))
+ *   next_scales     out: bf16 [M, N/64]
+ *   next_lora_act   out: fp32 [M, rank_next]; NULL iff rank_next == 0
+ *   workspace       device memory of at least
+ *                   svdq_gelu_quantize_workspace_bytes(M, N, rank_next) bytes,
+ *                   owned by the caller; its contents need no initialisation
+ *                   and are scratch (calls that share a workspace must be
+ *                   ordered, e.g. on one stream)
+ *   out             bf16 [M, N], or NULL: where given, also receives y
+ * Two kernels and a small table fill are enqueued on `stream`.
+ */
+int64_t svdq_gelu_quantize_workspace_bytes(int64_t M, int64_t N, int32_t rank_next);   /* -1 if invalid */
+svdq_status svdq_gemm_w4a4_gelu_quantize(int32_t precision, int64_t M, int64_t N, int64_t K, int32_t rank,
+                                         const void *act_codes, const void *act_scales,
+                                         const void *wgt_codes, const void *wgt_scales, float alpha,
+                                         const float *lora_act, const void *lora_up, const void *bias,
+                                         int32_t rank_next, const void *smooth_next, const void *lora_down_next,
+                                         void *next_codes, void *next_scales, float *next_lora_act,
+                                         void *workspace, int64_t workspace_bytes, void *out, void *stream);
+
+/*
  * awq_gemv_w4a16 -- int4 weight-only layer with bf16 activations, for the
  * memory-bound, precision-sensitive layers (adaptive-norm modulation;
  * "Nunchaku Lite" docs, awq_w4a16 int4 group 64).

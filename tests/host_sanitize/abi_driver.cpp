@@ -127,6 +127,23 @@ int main() {
     expect_reject(svdq_debug_group_sums_fp6(130, 384, 3072, P, nullptr, I, nullptr), INV,
                   "group sums fp6 weight NULL");
 
+    // ---- the up GEMM with the next layer's activation step (FP6 only)
+    {
+        const int64_t need = svdq_gelu_quantize_workspace_bytes(4096, 12288, 32);
+        EXPECT(need == 16384 + 96ll * 4096 * 32 * 4, "gelu-quantize workspace bytes");
+        EXPECT(svdq_gelu_quantize_workspace_bytes(4, 100, 32) == -1, "gelu-quantize workspace, N % 64");
+        auto gq = [&](int32_t prec, int64_t N, int32_t rn, int64_t wb, void *work) {
+            return svdq_gemm_w4a4_gelu_quantize(prec, 4096, N, 3072, 32, P, P, P, P, 1.0f, F, P, P, rn, P,
+                                                rn ? P : nullptr, P, P, rn ? F : nullptr, work, wb, nullptr, nullptr);
+        };
+        expect_launch(gq(SVDQ_INT4_FP6, 12288, 32, need, P), "gemm_fp6_gelu_quant", 4096, 12288, 3072 + 32);
+        expect_reject(gq(SVDQ_INT4, 12288, 32, need, P), UNS, "gelu-quantize int4 nibbles");
+        expect_reject(gq(SVDQ_INT4_FP6, 12288, 32, need - 1, P), INV, "gelu-quantize workspace too small");
+        expect_reject(gq(SVDQ_INT4_FP6, 12288, 32, need, nullptr), INV, "gelu-quantize workspace NULL");
+        expect_reject(gq(SVDQ_INT4_FP6, 12300, 32, need, P), INV, "gelu-quantize N % 64");
+        expect_reject(gq(SVDQ_INT4_FP6, 12288, 24, need, P), INV, "gelu-quantize rank_next 24");
+    }
+
     // ---- packed int4 weights
     EXPECT(svdq_packed_weight_bytes(12288, 3072) == 12288ll * 1536 + 12288ll * 4 * 48, "packed bytes");
     EXPECT(svdq_packed_weight_bytes(8, 100) == -1, "packed bytes, K % 64");

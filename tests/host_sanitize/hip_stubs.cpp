@@ -97,6 +97,15 @@ hipError_t launch_gemm_w4a4_fp6_qk(int M, int N, int, int, const void *, const v
                                    hipStream_t) {
     return rec("gemm_fp6_qk", M, N, qk.qk_cols);
 }
+size_t gelu_quant_workspace_bytes(int M, int N, int rank_next) {
+    return 16384u + (size_t)((N + 127) / 128) * (size_t)M * (size_t)rank_next * 4u;
+}
+hipError_t launch_gemm_w4a4_fp6_gelu_quant(int M, int N, int K, int, const void *, const void *, const void *,
+                                           const void *, float, const float *, const void *, const void *,
+                                           int rank_next, const void *, const void *, void *, void *, float *,
+                                           void *, void *, hipStream_t) {
+    return rec("gemm_fp6_gelu_quant", M, N, K + rank_next);
+}
 hipError_t launch_group_sums_fp6(int M, int N, int K, const void *, const void *, int32_t *, hipStream_t) {
     return rec("group_sums_fp6", M, N, K);
 }

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(capi.LIB_PATH)
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert capi.svdq_abi_version() == 10
+    assert capi.svdq_abi_version() == 11
     for s in range(4):
         assert capi.svdq_status_string(s).startswith(("SVDQ_OK", "SVDQ_ERR"))
     assert "unknown" in capi.svdq_status_string(99)
@@ -261,3 +261,39 @@ def test_python_binding_checks_buffers_before_the_call():
     ws = torch.zeros((64, 2), dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="out"):
         capi.svdq_gemm_w4a4(0, codes, scales, w, ws, 1.0, None, None, None, out, stream=0)
+
+
+def test_gelu_quantize_entry_point_host_checks():
+    """The up-GEMM with the next layer's activation step: FP6 layout only, N
+    a multiple of 64 (the next layer's K), rank_next a multiple of 16 up to
+    128, a workspace of at least the queried size; all checked on the host."""
+    L = capi.lib()
+    ws = capi.svdq_gelu_quantize_workspace_bytes
+    # the GELU table slot plus fp32 partials [ceil(N/128)][M][rank_next]
+    assert ws(4, 192, 32) == 16384 + 2 * 4 * 32 * 4
+    assert ws(4, 192, 0) == 16384
+    assert ws(4, 100, 32) == -1
+    assert ws(4, 192, 8) == -1
+    FP6 = capi.SVDQ_INT4_FP6
+
+    def f(prec=FP6, M=4, N=192, K=64, rank=16, rank_next=32, smooth=A, down=A, codes=A, scales=A, lact=A,
+          work=A, wb=None, out=A):
+        wb = ws(M, N, rank_next) if wb is None else wb
+        return L.svdq_gemm_w4a4_gelu_quantize(prec, M, N, K, rank, A, A, A, A, 1.0, A, A, A, rank_next, smooth,
+                                              down, codes, scales, lact, work, wb, out, None)
+    assert f(prec=capi.SVDQ_INT4) == UNS
+    assert f(prec=capi.SVDQ_NVFP4) == UNS
+    assert f(N=100) == INV
+    assert f(N=0) == INV
+    assert f(N=1 << 17) == INV
+    assert f(K=100) == INV
+    assert f(rank_next=8) == INV
+    assert f(rank_next=144) == INV
+    assert f(down=0) == INV
+    assert f(lact=0) == INV
+    assert f(codes=0) == INV
+    assert f(scales=MIS) == INV
+    assert f(work=0) == INV
+    assert f(wb=ws(4, 192, 32) - 1) == INV
+    assert f(M=0) == capi.SVDQ_OK
+    assert f(M=0, rank_next=0, down=0, lact=0, smooth=0, out=0) == capi.SVDQ_OK

@@ -1,0 +1,209 @@
+"""The GELU MLP's up projection with the down layer's activation step in its
+epilogue (svdq_gemm_w4a4_gelu_quantize), against the oracle and against the
+two-call chain it replaces (svdq_gemm_w4a4 then svdq_gelu_quantize_act, both
+in the FP6 layout).
+
+Its outputs are those of the activation step applied to the up layer's bf16
+output y ("Nunchaku Lite" docs, "Fused kernels": GELU fused into the MLP's
+kernels).  Codes and scales are decided from y, so they match the oracle bit
+for bit wherever the GPU's y equals the oracle's y:
+  * exact cases: the up layer's inputs are dyadic (power-of-two scales, small
+    integer codes, dyadic low-rank factors and bias), so every sum is exact in
+    fp32 and y is the same on both sides: y, codes and scales must match
+    exactly, lora_act to 1e-5;
+  * seeded DiT-like cases: y within the output bar; codes and scales exact on
+    every (row, group) whose 64 y values equal the oracle's, elsewhere within
+    one code and four scale ulps; lora_act to max(1e-5, 3 * 2^-8 * sqrt(p)),
+    p the share of y values that differ (each by at most 2 ulp, so x_hat by
+    at most ~3 ulp of 2^-8 on a share p of its entries);
+  * against the two-call chain on the same GPU: y, codes and scales identical
+    byte for byte, lora_act to 1e-6 (summation order only);
+and the down layer fed with the fused outputs is compared with the oracle's
+MLP output.  Shapes cover ragged M, N not a multiple of 128 (a last tile with
+one group), K with an odd group count, next-layer ranks 0/16/32/48 and no
+smoothing; canaries around every output and poisoned buffers show any byte
+written out of place."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_w4a4_quantized_svdq_amd import synth
+from tests.fp6_layout import fp6_layout_from_nibbles, fp6_layout_from_q, nibbles_to_q, q_from_fp6_layout
+from tests.gpu_helpers import (announce, assert_bf16_close, assert_f32_close, empty, gpu_gemm,
+                               gpu_pack_weight_fp6, poison, to_dev, to_host, ulp_dist)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def _run_fused(act_fp6, act_scales, w_nib, w_scales, lora_act, lora_up, bias, smooth_next, down_next, M,
+               with_out=True):
+    """The fused call; returns (y or None, codes bytes, scales, lora_act or None)."""
+    from bit_w4a4_quantized_svdq_amd import capi
+    N, K = w_nib.shape[0], 2 * w_nib.shape[1]
+    rn = 0 if down_next is None else down_next.shape[0]
+    wc = gpu_pack_weight_fp6(to_dev(w_nib, "u8"))
+    codes = poison(empty((capi.svdq_fp6_codes_bytes(M, N),), "u8"))
+    scales = poison(empty((M, N // 64), "bf16"))
+    lact = poison(empty((M, rn), "f32")) if rn else None
+    out = poison(empty((M, N), "bf16")) if with_out else None
+    work = poison(empty((capi.svdq_gelu_quantize_workspace_bytes(M, N, rn),), "u8"))
+    capi.svdq_gemm_w4a4_gelu_quantize(to_dev(act_fp6, "u8"), to_dev(act_scales, "bf16"), wc,
+                                      to_dev(w_scales, "bf16"), 1.0, to_dev(lora_act, "f32"),
+                                      to_dev(lora_up, "bf16"), to_dev(bias, "bf16"), to_dev(smooth_next, "bf16"),
+                                      to_dev(down_next, "bf16"), codes, scales, lact, work, out)
+    torch.cuda.synchronize()
+    return (to_host(out, "bf16") if with_out else None, to_host(codes, "u8"), to_host(scales, "bf16"),
+            None if lact is None else to_host(lact, "f32"))
+
+
+def _next_layer(rng, N, rank_next, smooth=True):
+    sm = synth.to_bf16_bits(np.exp(rng.standard_normal(N) * 0.5)) if smooth else None
+    dn = synth.to_bf16_bits(rng.standard_normal((rank_next, N)) * 0.05) if rank_next else None
+    return sm, dn
+
+
+# (M, N, K, rank of the up layer, rank of the down layer, smoothing)
+EXACT_CASES = [(130, 192, 192, 16, 16, True), (64, 256, 256, 0, 32, True), (257, 384, 640, 32, 48, False),
+               (33, 64, 64, 16, 0, True), (128, 128, 3072, 32, 32, True)]
+
+
+@pytest.mark.parametrize("M,N,K,rank,rank_next,smooth", EXACT_CASES)
+def test_fused_exact_inputs_match_oracle_bit_for_bit(M, N, K, rank, rank_next, smooth):
+    """Dyadic up-layer inputs: y is exact on both sides, so y, the next
+    layer's codes and scales equal the oracle's exactly."""
+    rng = np.random.default_rng(1000 * M + N + K + rank_next)
+    NG = K // 64
+    # activation codes in [-7, 7] with a +-7 in every group and scale 2^-5:
+    # what the activation step gives for x = q * 2^-5
+    qa = rng.integers(-7, 8, size=(M, K))
+    qa[:, ::64] = np.where(rng.integers(0, 2, size=(M, NG)) == 1, 7, -7)
+    a_nib = synth.pack_nibbles(qa)
+    a_sc = np.full((M, NG), 0x3D00, np.uint16)                        # bf16 2^-5
+    w_nib = synth.pack_nibbles(rng.integers(-7, 8, size=(N, K)))
+    w_sc = np.full((N, NG), 0x3D00, np.uint16)
+    # low-rank factors and bias: small dyadic values (products and sums exact)
+    t = (rng.integers(-16, 17, size=(M, rank)) / 8.0).astype(np.float32) if rank else None
+    up = synth.to_bf16_bits(rng.integers(-8, 9, size=(N, rank)) / 64.0) if rank else None
+    bias = synth.to_bf16_bits(rng.integers(-8, 9, size=N) / 4.0)
+    sm, dn = _next_layer(rng, N, rank_next, smooth)
+    announce("gelu-quantize exact", "M,N,K", M, N, K, "rank", rank, "rank_next", rank_next, "smooth", smooth)
+    y, codes, scales, lact = _run_fused(fp6_layout_from_q(qa), a_sc, w_nib, w_sc, t, up, bias, sm, dn, M)
+
+    y_ref = oracle.gemm_w4a4(oracle.INT4, a_nib, a_sc, w_nib, w_sc, t, up, bias)
+    assert np.array_equal(y, y_ref), f"y differs at {np.argwhere(y != y_ref)[:5].tolist()}"
+    g = synth.bf16_bits_to_f32(y_ref)
+    assert (g < 0).mean() > 0.2 and (g > 0).mean() > 0.2, "y should take both signs"
+    oc, os_, ot = oracle.gelu_quantize_act(oracle.INT4, y_ref, sm, dn)
+    assert np.any(os_ != 0)
+    assert np.array_equal(scales, os_), f"scales differ at {np.argwhere(scales != os_)[:5].tolist()}"
+    assert np.array_equal(codes, fp6_layout_from_nibbles(oc, N)), "code bytes differ (or padding was written)"
+    if rank_next:
+        assert_f32_close(lact, ot, 1e-5, "lora_act")
+
+
+# (M, N, K, rank, rank_next)
+RANDOM_CASES = [(130, 384, 320, 32, 32), (257, 192, 192, 16, 16), (64, 640, 1024, 0, 48), (200, 320, 512, 32, 0)]
+
+
+def _random_up_layer(rng, M, N, K, rank):
+    x = rng.standard_normal((M, K))
+    x[:, rng.choice(K, max(1, K // 100), replace=False)] *= 50.0
+    xb = synth.to_bf16_bits(x)
+    smooth = synth.to_bf16_bits(np.exp(rng.standard_normal(K) * 0.5))
+    w = synth.synthetic_w4a4_weights(int(rng.integers(1 << 30)), N, K, rank, "int4")
+    bias = synth.to_bf16_bits(rng.standard_normal(N) * 0.5)
+    oc, os_, ot = oracle.quantize_act(oracle.INT4, xb, smooth, w["lora_down"])
+    return oc, os_, (ot if rank else None), w, bias
+
+
+@pytest.mark.parametrize("M,N,K,rank,rank_next", RANDOM_CASES)
+def test_fused_seeded_layers_against_oracle_and_two_call_chain(M, N, K, rank, rank_next):
+    rng = np.random.default_rng(7 * M + 3 * N + K + rank_next)
+    oc, os_, ot, w, bias = _random_up_layer(rng, M, N, K, rank)
+    sm, dn = _next_layer(rng, N, rank_next)
+    announce("gelu-quantize seeded", "M,N,K", M, N, K, "rank", rank, "rank_next", rank_next)
+    y, codes, scales, lact = _run_fused(fp6_layout_from_nibbles(oc, K), os_, w["wgt_codes"], w["wgt_scales"], ot,
+                                        w["lora_up"], bias, sm, dn, M)
+
+    # the oracle: the up layer's y, then the down layer's activation step
+    y_ref = oracle.gemm_w4a4(oracle.INT4, oc, os_, w["wgt_codes"], w["wgt_scales"], ot, w["lora_up"], bias)
+    assert_bf16_close(y, y_ref, "y")
+    rc, rs, rt = oracle.gelu_quantize_act(oracle.INT4, y_ref, sm, dn)
+    NG = N // 64
+    same = (y == y_ref).reshape(M, NG, 64).all(axis=2)            # (row, group) with identical y
+    share = (y != y_ref).mean()
+    assert share < 0.02, f"{share:.4%} of y differ from the oracle's"
+    q = q_from_fp6_layout(codes, M, N).reshape(M, NG, 64)
+    rq = nibbles_to_q(rc, N).reshape(M, NG, 64)
+    assert np.array_equal(scales[same], rs[same]), "scales differ on groups with identical y"
+    assert np.array_equal(q[same], rq[same]), "codes differ on groups with identical y"
+    assert (ulp_dist(scales, rs) <= 4).all(), "a scale differs by more than four ulp"
+    assert (np.abs(q - rq) <= 1).all(), "a code differs by more than one"
+    if rank_next:
+        assert_f32_close(lact, rt, max(1e-5, 3 * 2.0 ** -8 * np.sqrt(share)), "lora_act vs oracle")
+
+    # the two-call chain on the GPU: identical bytes
+    y2 = gpu_gemm(0, oc, os_, w["wgt_codes"], w["wgt_scales"], ot, w["lora_up"], bias, fp6=True)
+    assert np.array_equal(y, y2), "y differs from svdq_gemm_w4a4's"
+    from tests.gpu_helpers import gpu_quantize
+    c2, s2, t2 = gpu_quantize(3, y2, sm, dn, N, gelu=True)
+    assert np.array_equal(scales, s2) and np.array_equal(codes, c2), "codes/scales differ from the two-call chain"
+    if rank_next:
+        assert_f32_close(lact, t2.astype(np.float64), 1e-6, "lora_act vs the two-call chain")
+
+    # the MLP's down layer on the fused outputs against the oracle's MLP
+    if rank_next:
+        wd = synth.synthetic_w4a4_weights(int(rng.integers(1 << 30)), 192, N, rank_next, "int4")
+        out = gpu_gemm(0, rc, scales, wd["wgt_codes"], wd["wgt_scales"], lact, wd["lora_up"], None, fp6=True,
+                       act_fp6=codes)
+        ref = oracle.gemm_w4a4(oracle.INT4, rc, rs, wd["wgt_codes"], wd["wgt_scales"], rt, wd["lora_up"], None)
+        assert_bf16_close(out, ref, "down layer on the fused outputs")
+
+
+def test_fused_without_output_buffer_and_repeat_calls_agree():
+    """out = NULL writes only the next layer's tensors; two calls give the
+    same bytes (the partial sums are added in a fixed order)."""
+    M, N, K, rank, rank_next = 96, 256, 256, 16, 32
+    rng = np.random.default_rng(99)
+    oc, os_, ot, w, bias = _random_up_layer(rng, M, N, K, rank)
+    sm, dn = _next_layer(rng, N, rank_next)
+    args = (fp6_layout_from_nibbles(oc, K), os_, w["wgt_codes"], w["wgt_scales"], ot, w["lora_up"], bias, sm, dn, M)
+    announce("gelu-quantize out=NULL", "M,N,K", M, N, K)
+    _, c1, s1, t1 = _run_fused(*args, with_out=False)
+    _, c2, s2, t2 = _run_fused(*args, with_out=True)
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+    assert np.array_equal(t1.view(np.uint32), t2.view(np.uint32)), "lora_act differs between two runs"
+
+
+def test_fused_full_size_mlp_up():
+    """The MLP up shape the benchmark times (4096 x 3072 -> 12288, rank 32,
+    down rank 32): identical bytes to the two-call chain over the whole
+    tensor, and the oracle on rows sampled in every 128-row tile."""
+    cfg = synth.MLP_UP
+    M, N, K, rank = cfg.M, cfg.N, cfg.K, cfg.rank
+    rng = np.random.default_rng(2027)
+    oc, os_, ot, w, bias = _random_up_layer(rng, M, N, K, rank)
+    sm, dn = _next_layer(rng, N, 32)
+    announce("gelu-quantize full size", "M,N,K", M, N, K)
+    y, codes, scales, lact = _run_fused(fp6_layout_from_nibbles(oc, K), os_, w["wgt_codes"], w["wgt_scales"], ot,
+                                        w["lora_up"], bias, sm, dn, M)
+    from tests.gpu_helpers import gpu_quantize
+    c2, s2, t2 = gpu_quantize(3, y, sm, dn, N, gelu=True)
+    assert np.array_equal(scales, s2), "scales differ from the two-call chain"
+    assert np.array_equal(codes, c2), "code bytes differ from the two-call chain"
+    assert_f32_close(lact, t2.astype(np.float64), 1e-6, "lora_act vs the two-call chain")
+    rows = np.unique(np.concatenate([[0, M - 1], np.arange(0, M, 128) + (np.arange(M // 128) * 37) % 128]))
+    y_ref = oracle.gemm_w4a4(oracle.INT4, oc, os_, w["wgt_codes"], w["wgt_scales"], ot, w["lora_up"], bias,
+                             rows=rows)
+    assert_bf16_close(y[rows], y_ref, "y on sampled rows")
+    rc, rs, rt = oracle.gelu_quantize_act(oracle.INT4, y_ref, sm, dn)
+    same = (y[rows] == y_ref).reshape(len(rows), N // 64, 64).all(axis=2)
+    assert same.mean() > 0.9
+    q = q_from_fp6_layout(codes, M, N)[rows].reshape(len(rows), N // 64, 64)
+    rq = nibbles_to_q(rc, N).reshape(len(rows), N // 64, 64)
+    assert np.array_equal(scales[rows].reshape(len(rows), -1)[same], rs[same])
+    assert np.array_equal(q[same], rq[same])
+    share = (y[rows] != y_ref).mean()
+    assert_f32_close(lact[rows], rt, max(1e-5, 3 * 2.0 ** -8 * np.sqrt(share)), "lora_act on sampled rows")
