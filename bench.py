@@ -682,6 +682,48 @@ def summarize_gemv_trace(run_dir):
     print(f"wrote {GEMV_TRACE_FILE}")
 
 
+MLP_FUSION_FILE = os.path.join(ROOT, "profiles", "mlp_pair_gelu_fusion_kernel_trace.txt")
+
+
+def summarize_mlp_fusion(run_dir):
+    """Per-kernel durations of `bench.py --mlp-fusion-only` from a rocprofv3
+    kernel trace (<run_dir>/mlp_trace, its JSON line in
+    <run_dir>/mlp_trace_bench.json)."""
+    import glob
+    stats = glob.glob(os.path.join(run_dir, "mlp_trace", "**", "*kernel_stats.csv"), recursive=True)[0]
+    rows = {r["Name"].split("(")[0].replace("void ", ""): r for r in _csv_rows(stats)}
+    res = None
+    for line in open(os.path.join(run_dir, "mlp_trace_bench.json")):
+        if line.startswith("{"):
+            res = json.loads(line)["mlp_fusion"]
+    roles = [("svdq::gemm_w4a4_fp6_kernel<false, true, 2>", "fused: up GEMM with the down layer's activation step"),
+             ("svdq::gq_partial_sum_kernel", "fused: fixed-order sum of the low-rank partials"),
+             ("svdq::gelu_table_kernel", "fused: GELU table fill"),
+             ("svdq::gemm_w4a4_fp6_kernel<false, true, 0>", "two calls: up GEMM writing y"),
+             ("svdq::quantize_act_kernel<2, 2, true>", "two calls: GELU-fed activation step reading y")]
+    lines = ["# The GELU MLP pair's up GEMM + the down layer's activation step, DiT MLP 4096x3072 -> 12288",
+             "# (int4 FP6 layout, ranks 32): fused (svdq_gemm_w4a4_gelu_quantize) against two calls",
+             "# (svdq_gemm_w4a4, then svdq_gelu_quantize_act on the written intermediate), rocprofv3 kernel trace",
+             "# Command (paths relative to the repository root; run with TMPDIR=/tmp):",
+             f"#   rocprofv3 --kernel-trace --stats -f csv -d {run_dir}/mlp_trace -o mlp -- "
+             "python3 bench.py --mlp-fusion-only",
+             f"# Same-run interleaved HIP events per pass: fused {res['fused']['us']} us, "
+             f"two calls {res['two_calls']['us']} us.",
+             "# source_sha256 covers gemm_w4a4_fp6.hip, gemm_common.h and device_common.h (in that order).",
+             f"source_sha256: {gemm_int4_source_hash()}",
+             "#",
+             f"{'kernel':46s} {'calls':>5s} {'avg_us':>8s} {'min_us':>8s}  role"]
+    for name, role in roles:
+        r = rows[name]
+        lines.append(f"{name[:46]:46s} {r['Calls']:>5s} {float(r['AverageNs']) / 1e3:8.2f} "
+                     f"{float(r['MinNs']) / 1e3:8.2f}  {role}")
+    f = sum(float(rows[n]["AverageNs"]) for n, _ in roles[:3]) / 1e3
+    t = sum(float(rows[n]["AverageNs"]) for n, _ in roles[3:]) / 1e3
+    lines.append(f"# sum of kernel averages: fused {f:.2f} us, two calls {t:.2f} us")
+    open(MLP_FUSION_FILE, "w").write("\n".join(lines) + "\n")
+    print(f"wrote {MLP_FUSION_FILE}")
+
+
 def summarize_profiles(run_dir, warmup, steps):
     """Write the committed profile summaries from a rocprofv3 run directory:
     <run_dir>/trace (kernel trace of `bench.py --steps S --warmup W`, whose
@@ -770,6 +812,8 @@ def summarize_profiles(run_dir, warmup, steps):
         summarize_gemv_trace(run_dir)
     if os.path.isdir(os.path.join(run_dir, "pmc_gemm_util")):
         summarize_utilisation(run_dir, {k: sum(a["us"]) / len(a["us"]) for k, a in agg.items()})
+    if os.path.isdir(os.path.join(run_dir, "mlp_trace")):
+        summarize_mlp_fusion(run_dir)
 
 
 def cpu_threads():
@@ -845,6 +889,8 @@ def main():
                     help="run only a plain copy of this many MiB --steps times (counter calibration)")
     ap.add_argument("--gemv-only", action="store_true",
                     help="run only the AWQ sweep and the plain-read ceiling, print them as JSON (for rocprofv3)")
+    ap.add_argument("--mlp-fusion-only", action="store_true",
+                    help="run only the GELU-MLP fusion comparison, print it as JSON (for rocprofv3)")
     ap.add_argument("--summarize", default=None, metavar="RUN_DIR",
                     help="write the profiles/ summaries from a rocprofv3 run directory (no GPU needed)")
     args = ap.parse_args()
@@ -865,6 +911,10 @@ def main():
         return
     if args.profile_kernel:
         profile_kernel(torch, synth, args.profile_kernel, args.steps)
+        return
+    if args.mlp_fusion_only:
+        layers, xs = build_inputs(torch, synth)
+        print(json.dumps({"mlp_fusion": mlp_fusion(torch, layers, xs)}))
         return
     if args.gemv_only:
         print(json.dumps({"gemv": gemv_sweep(torch, synth)}))
