@@ -117,3 +117,54 @@ def test_graph_replay_matches_eager_fused_paths():
         torch.cuda.synchronize()
         for o, r in zip(eager, ref):
             assert torch.equal(o.view(torch.int16), r.view(torch.int16))
+
+
+def test_graph_replay_matches_eager_mlp_in_the_up_epilogue():
+    """A GELU MLP whose up GEMM runs the down layer's activation step in its
+    epilogue (svdq_gemm_w4a4_gelu_quantize: table fill, GEMM, fixed-order
+    partial sum), then the down GEMM, in one graph: every replay gives the
+    eager bytes of the down layer's codes, scales, lora_act and output."""
+    from bit_w4a4_quantized_svdq_amd.layer import SVDQW4A4Linear
+    announce("graph replay", "mlp 130x256->320 (up epilogue gelu-quantize) ->192")
+    rng = np.random.default_rng(43)
+    wu = synth.synthetic_w4a4_weights(44, 320, 256, 32, "int4")
+    U = SVDQW4A4Linear("int4", wu["wgt_codes"], wu["wgt_scales"], wu["lora_down"], wu["lora_up"], wu["smooth"],
+                       synth.to_bf16_bits(rng.standard_normal(320)))
+    wd = synth.synthetic_w4a4_weights(45, 192, 320, 16, "int4")
+    D = SVDQW4A4Linear("int4", wd["wgt_codes"], wd["wgt_scales"], wd["lora_down"], wd["lora_up"], wd["smooth"], None)
+    x, _ = synth.draw_activations(rng, 130, 256, 3, 30.0)
+    xt = torch.from_numpy(synth.to_bf16_bits(x).view(np.int16)).view(torch.bfloat16).cuda()
+    bu, bd = U.buffers(130), D.buffers(130)
+
+    def step():
+        U.quantize(xt, bu)
+        U.gemm_gelu_quantize(bu, D, bd)
+        D.gemm(bd)
+        return [bd["codes"], bd["scales"], bd["lora_act"], bd["out"]]
+
+    for o in (bd["codes"], bd["scales"], bd["lora_act"], bd["out"]):
+        o.zero_()                                            # the FP6 layout's padding rows stay 0
+    ref = [o.clone() for o in step()]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        outs = step()
+    for rep in range(3):
+        for o in outs:
+            o.zero_()
+        bu["gq_workspace"].zero_()                           # the workspace needs no initialisation
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (o, r) in enumerate(zip(outs, ref)):
+            assert torch.equal(o.view(torch.uint8), r.view(torch.uint8)), f"replay {rep}, output {i}"
+        eager = step()
+        torch.cuda.synchronize()
+        for o, r in zip(eager, ref):
+            assert torch.equal(o.view(torch.uint8), r.view(torch.uint8))
