@@ -7,15 +7,18 @@
 //
 // A bf16 input has 65536 possible values, so the rounded result is made
 // exact by construction rather than by a careful fp32 evaluation:
-//  * |y| in [2^-14, 32): a table of 2 x 19 x 128 results in LDS, computed by
-//    each block in fp64 as y / (1 + exp(-2u)) -- the same function, free of
-//    the cancellation in 1 + tanh u.  Over the whole input range no exact
+//  * |y| in [2^-14, 128): a table of 2 x 21 x 128 results in LDS, computed
+//    in fp64 as y / (1 + exp(-2u)) -- the same function, free of the
+//    cancellation in 1 + tanh u.  Over the whole input range no exact
 //    result comes within 2^-13 of a bf16 spacing of a rounding midpoint,
 //    while the fp64 error stays below 2^-36 spacings, so the fp64 value
-//    rounds to the correctly rounded result.
+//    rounds to the correctly rounded result (from 32 on, exp(-2u) is 0 or
+//    infinity in fp64 and the entries are exactly y and -0, as below).
 //  * |y| >= 32: y for y > 0 (the correction is below 1e-400 relative) and -0
 //    for y < 0 (|gelu(y)| far under half the least subnormal); +inf -> +inf,
 //    -inf -> -0 (the limit), NaN -> the quiet NaN 0x7FC0 with the sign.
+//    The table covers this rule up to 128, the range a GELU MLP's
+//    pre-activations reach, so the selects below are rarely needed.
 //  * |y| < 2^-14: gelu(y) = y/2 + y tanh(u)/2, and the second term is
 //    positive and below 2^-14 of the first, under half a spacing: the result
 //    is y/2 -- exact (an exponent decrement) while y/2 is normal, and for the
@@ -24,7 +27,7 @@
 // Fast path: two values per dword, their table slots formed with packed
 // 16-bit integer operations.  Inputs outside the table's range land on a
 // sentinel slot (0x7FFF) and raise a tracked slot maximum (one packed max per
-// pair); when any lane of the wave has an input of 32 or more in magnitude,
+// pair); when any lane of the wave has an input of 128 or more in magnitude,
 // the pairs get the |y| >= 32 rule by selects, and when any has a NaN or an
 // input below 2^-14, the whole group is redone with the exact rules
 // (wave-uniform branches).
@@ -37,10 +40,10 @@
 namespace svdq {
 
 constexpr int GELU_E_LO = 113;                                // 2^-14
-constexpr int GELU_E_HI = 131;                                // [16, 32)
+constexpr int GELU_E_HI = 133;                                // [64, 128)
 constexpr int GELU_SPAN = (GELU_E_HI - GELU_E_LO + 1) * 128;  // results per sign
 constexpr int GELU_STRIDE = GELU_SPAN + 1;                    // plus the sentinel slot
-constexpr int GELU_TAB = 2 * GELU_STRIDE;                     // 4866 entries, 9.5 KB
+constexpr int GELU_TAB = 2 * GELU_STRIDE;                     // 5378 entries, 10.5 KB
 constexpr uint32_t GELU_SENTINEL = 0x7FFFu;
 
 // Table slot i: sign i / GELU_STRIDE; slot GELU_SPAN of each sign is the
@@ -94,7 +97,7 @@ __device__ __forceinline__ uint32_t gelu_lookup2_track(uint32_t w, const uint16_
 }
 
 // Unclamped slot index of +-infinity: inputs whose index lies in
-// [GELU_SPAN, GELU_TI_INF] are 32 <= |y| <= infinity; above it lie NaNs and,
+// [GELU_SPAN, GELU_TI_INF] are 128 <= |y| <= infinity; above it lie NaNs and,
 // wrapped around, the inputs below 2^-14.
 constexpr uint32_t GELU_TI_INF = 0x7F80u - (uint32_t)(GELU_E_LO << 7);
 
@@ -112,7 +115,7 @@ __device__ __forceinline__ uint32_t gelu_fix_big2(uint32_t g, uint32_t w)
 
 // GELU of n packed pairs in place after gelu_lookup2_track (g: looked-up
 // results, w: inputs, tmax: the tracked slot maximum; every lane of the wave
-// takes part, the branches are wave-uniform): inputs of 32 and above in
+// takes part, the branches are wave-uniform): inputs of 128 and above in
 // magnitude take gelu_fix_big2, a NaN or an input below 2^-14 anywhere in
 // the wave sends all n pairs through the exact rules.
 template <int n>

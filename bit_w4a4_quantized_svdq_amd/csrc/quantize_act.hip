@@ -57,7 +57,7 @@
 //
 // GELU variant (a layer fed by a GELU MLP's up projection): x is first
 // mapped through GELU (tanh form) of bf16 to bf16, exact by construction
-// (gelu_bf16.h: a 9.5 KB LDS table each block fills in fp64, plus exact rules
+// (gelu_bf16.h: a 10.5 KB LDS table each block fills in fp64, plus exact rules
 // outside the table's range); everything after it is unchanged.
 #include <type_traits>
 

@@ -66,13 +66,16 @@ def test_gelu_quantize_act_shapes(prec, M, K, rank):
 @pytest.mark.parametrize("prec", [0, 1])
 def test_gelu_quantize_act_range_edges(prec):
     """Inputs at every boundary of the GELU's table and rules: just below and
-    above 2^-10 and 16 in magnitude, the two lowest binades (subnormal and
-    least-normal ties), negative values whose GELU underflows, +-0, and
-    large magnitudes (kept finite after the smoothing: an overflowing value
-    is outside the step's contract)."""
+    above 2^-14 and 128 in magnitude (the table's edges), 32 (where the
+    |y| >= 32 rule starts inside the table), 2^-10 and 16, the two lowest
+    binades (subnormal and least-normal ties), negative values whose GELU
+    underflows, +-0, and large magnitudes (kept finite after the smoothing:
+    an overflowing value is outside the step's contract)."""
     K = 256
     edges = [2.0 ** -10, 2.0 ** -10 * (1 - 2 ** -8), 16.0, 16.0 * (1 - 2 ** -8), 8.0, 2.0 ** -126,
-             3 * 2.0 ** -133, 2.0 ** -133, 10.3, 10.5, 13.0, 21.5, 1.0e36, 0.75, 0.5234, 1.0]
+             3 * 2.0 ** -133, 2.0 ** -133, 10.3, 10.5, 13.0, 21.5, 1.0e36, 0.75, 0.5234, 1.0,
+             2.0 ** -14, 2.0 ** -14 * (1 - 2 ** -8), 32.0, 32.0 * (1 - 2 ** -8), 128.0, 128.0 * (1 - 2 ** -8),
+             100.0]
     vals = np.array(edges + [-e for e in edges])
     x = synth.to_bf16_bits(np.resize(vals, (6, K)) * np.array([[1.0], [1.0], [-1.0], [0.5], [2.0], [1.0]]))
     x[5, :] = 0
