@@ -7,8 +7,9 @@
 //
 // A bf16 input has 65536 possible values, so the rounded result is made
 // exact by construction rather than by a careful fp32 evaluation:
-//  * |y| in [2^-14, 128): a table of 2 x 21 x 128 results in LDS, computed
-//    in fp64 as y / (1 + exp(-2u)) -- the same function, free of the
+//  * |y| in [2^-14, 128): a table of 2 x 21 x 128 results (gelu_table.h:
+//    built at compile time, copied into LDS by each block), computed in fp64
+//    as y / (1 + exp(-2u)) -- the same function, free of the
 //    cancellation in 1 + tanh u.  Over the whole input range no exact
 //    result comes within 2^-13 of a bf16 spacing of a rounding midpoint,
 //    while the fp64 error stays below 2^-36 spacings, so the fp64 value
@@ -36,35 +37,22 @@
 #include <stdint.h>
 
 #include "device_common.h"
+#include "gelu_table.h"
 
 namespace svdq {
 
-constexpr int GELU_E_LO = 113;                                // 2^-14
-constexpr int GELU_E_HI = 133;                                // [64, 128)
-constexpr int GELU_SPAN = (GELU_E_HI - GELU_E_LO + 1) * 128;  // results per sign
-constexpr int GELU_STRIDE = GELU_SPAN + 1;                    // plus the sentinel slot
-constexpr int GELU_TAB = 2 * GELU_STRIDE;                     // 5378 entries, 10.5 KB
-constexpr uint32_t GELU_SENTINEL = 0x7FFFu;
+// The table (gelu_table.h) as constant device data, built by the compiler;
+// each translation unit that includes this header holds its own copy.
+static __device__ const std::array<uint16_t, GELU_TAB_PAD> g_gelu_table __attribute__((aligned(16))) =
+    make_gelu_table();
 
-// Table slot i: sign i / GELU_STRIDE; slot GELU_SPAN of each sign is the
-// sentinel, the others hold magnitude bits (GELU_E_LO << 7) + i % GELU_STRIDE.
-__device__ inline uint16_t gelu_table_entry(int i)
-{
-    const int j = i % GELU_STRIDE;
-    if (j == GELU_SPAN) return (uint16_t)GELU_SENTINEL;
-    const uint32_t neg = i >= GELU_STRIDE ? 0x8000u : 0u;
-    const uint32_t mag = (uint32_t)(GELU_E_LO << 7) + (uint32_t)j;
-    const double y = (double)__uint_as_float((neg | mag) << 16);
-    const double u = 0.79788456080286535588 * (y + 0.044715 * y * y * y);   // sqrt(2/pi)
-    const double v = y / (1.0 + exp(-2.0 * u));
-    return (uint16_t)f64_to_bf16_rne(v);   // the sign comes from the bits: v may be -0
-}
-
-// Fill a block's table (tid, nthreads: the block's threads); the caller's
-// next barrier publishes it.
+// Copy the table into a block's LDS (16-byte aligned, GELU_TAB_PAD entries;
+// tid, nthreads: the block's threads, 16 bytes per thread and step); the
+// caller's next barrier publishes it.
 __device__ inline void gelu_table_fill(uint16_t *tab, int tid, int nthreads)
 {
-    for (int i = tid; i < GELU_TAB; i += nthreads) tab[i] = gelu_table_entry(i);
+    const v4u *src = (const v4u *)g_gelu_table.data();
+    for (int i = tid; i < GELU_TAB_PAD / 8; i += nthreads) ((v4u *)tab)[i] = src[i];
 }
 
 // GELU of one bf16 by the exact rules (bits in the low half of h, high half 0).

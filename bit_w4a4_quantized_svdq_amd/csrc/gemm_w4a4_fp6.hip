@@ -116,7 +116,6 @@ __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F7
 // group) -- and wave w runs rows 32w..32w+31 of the low-rank partial on the
 // matrix core.  Rows past M and groups past N are not written.
 struct GeluQuantNext {
-    const uint16_t *gelu_tab;    // GELU_TAB results (gelu_table_kernel), 16-byte aligned
     const uint16_t *smooth;      // bf16 [N] or NULL (s = 1)
     const uint16_t *lora_down;   // bf16 [rank, N]
     int rank;                    // 0 or a multiple of 16 up to 128
@@ -124,19 +123,13 @@ struct GeluQuantNext {
     uint16_t *scales;            // bf16 [M, N/64]
     float *partial;              // fp32 [ceil(N/128)][M][rank]
 };
-constexpr int GQ_TAB_BYTES = (GELU_TAB * 2 + 15) / 16 * 16;
+constexpr int GQ_TAB_BYTES = GELU_TAB_PAD * 2;
 constexpr int GQ_INV_OFF = GQ_TAB_BYTES;                 // float [128]: 1/s of the tile's columns
 constexpr int GQ_ROWB = 128 * 2 + 16;                    // x_hat tile row (bf16, padded)
 constexpr int GQ_TILE_OFF = GQ_INV_OFF + 128 * 4;
 constexpr int GQ_SMEM = GQ_TILE_OFF + 128 * GQ_ROWB;
 static_assert(F6_SMEM >= GQ_SMEM, "the GELU-quantize epilogue uses the operand LDS");
 static_assert(GQ_TILE_OFF % 16 == 0, "16-byte LDS rows");
-
-// fills the GELU table the epilogue copies into each block's LDS
-__global__ __launch_bounds__(256) void gelu_table_kernel(uint16_t *__restrict__ tab) {
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i < GELU_TAB) tab[i] = gelu_table_entry(i);
-}
 
 // lora_act[i] = sum over column tiles b of partial[b][i], in a fixed order:
 // four threads share 4 consecutive values, thread j summing the tiles
@@ -186,7 +179,7 @@ __device__ __forceinline__ void gq_prefetch(GqPrefetch &pf, const GeluQuantNext 
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
         const int i = tid + u * F6_THREADS;
-        if (i < GQ_TAB_CHUNKS) pf.tab[u] = ((const v4u *)gq.gelu_tab)[i];
+        if (i < GQ_TAB_CHUNKS) pf.tab[u] = ((const v4u *)g_gelu_table.data())[i];
     }
     pf.smooth = 0x3F80u;                                  // bf16 1.0
     if (tid < 128 && gq.smooth && n0 + tid < N) pf.smooth = gq.smooth[n0 + tid];
@@ -634,14 +627,11 @@ hipError_t launch_gemm_w4a4_fp6_qk(int M, int N, int K, int rank, const void *ac
                                      lora_up, bias, out, nullptr, qk, no_gq, stream);
 }
 
-// Workspace of the GELU-quantize form: the GELU table, then the low-rank
-// partials [ceil(N/128)][M][rank_next] (fp32).
-constexpr size_t GQ_WS_TABLE = 16384;
-static_assert(GQ_WS_TABLE >= (size_t)GQ_TAB_BYTES, "the table fits its slot");
-
+// Workspace of the GELU-quantize form: the low-rank partials
+// [ceil(N/128)][M][rank_next] (fp32).
 size_t gelu_quant_workspace_bytes(int M, int N, int rank_next)
 {
-    return GQ_WS_TABLE + (size_t)((N + F6_BN - 1) / F6_BN) * (size_t)M * (size_t)rank_next * 4u;
+    return (size_t)((N + F6_BN - 1) / F6_BN) * (size_t)M * (size_t)rank_next * 4u;
 }
 
 hipError_t launch_gemm_w4a4_fp6_gelu_quant(int M, int N, int K, int rank, const void *act_codes,
@@ -651,13 +641,8 @@ hipError_t launch_gemm_w4a4_fp6_gelu_quant(int M, int N, int K, int rank, const 
                                            const void *lora_down_next, void *next_codes, void *next_scales,
                                            float *next_lora_act, void *workspace, void *out, hipStream_t stream)
 {
-    uint16_t *tab = (uint16_t *)workspace;
-    float *partial = (float *)((uint8_t *)workspace + GQ_WS_TABLE);
-    hipLaunchKernelGGL(gelu_table_kernel, dim3((GELU_TAB + 255) / 256), dim3(256), 0, stream, tab);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    float *partial = (float *)workspace;
     GeluQuantNext gq;
-    gq.gelu_tab = tab;
     gq.smooth = (const uint16_t *)smooth_next;
     gq.lora_down = (const uint16_t *)lora_down_next;
     gq.rank = rank_next;
@@ -665,7 +650,7 @@ hipError_t launch_gemm_w4a4_fp6_gelu_quant(int M, int N, int K, int rank, const 
     gq.scales = (uint16_t *)next_scales;
     gq.partial = partial;
     const QkNormRope none{};
-    e = launch_fp6<false, EPI_GQ>(M, N, K, rank, act_codes, act_scales, wgt_codes, wgt_scales, alpha, lora_act,
+    const hipError_t e = launch_fp6<false, EPI_GQ>(M, N, K, rank, act_codes, act_scales, wgt_codes, wgt_scales, alpha, lora_act,
                                   lora_up, bias, out, nullptr, none, gq, stream);
     if (e != hipSuccess || rank_next == 0) return e;
     const int64_t n = (int64_t)M * rank_next;

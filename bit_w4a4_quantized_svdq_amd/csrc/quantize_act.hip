@@ -57,8 +57,9 @@
 //
 // GELU variant (a layer fed by a GELU MLP's up projection): x is first
 // mapped through GELU (tanh form) of bf16 to bf16, exact by construction
-// (gelu_bf16.h: a 10.5 KB LDS table each block fills in fp64, plus exact rules
-// outside the table's range); everything after it is unchanged.
+// (gelu_bf16.h: a 10.5 KB table built at compile time, which each block
+// copies into LDS, plus exact rules outside the table's range); everything
+// after it is unchanged.
 #include <type_traits>
 
 #include "device_common.h"
@@ -244,7 +245,7 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
     static_assert(SINV == 4 || SINV == 8, "1/s staging: 8 or 16 bytes of bf16 per thread");
     __shared__ float s_inv[QA_CHUNK * 64];
     __shared__ float s_part[RT > 0 ? QA_WAVES * QA_ROWS * RT * 16 : 1];
-    __shared__ uint16_t s_gelu[GELU ? GELU_TAB : 2];
+    __shared__ __attribute__((aligned(16))) uint16_t s_gelu[GELU ? GELU_TAB_PAD : 8];
     // The chunk's codes and scales are staged in LDS and written out once per
     // chunk with whole-line stores: storing each lane's 2 to 16 bytes as the
     // groups are done costs one memory request per piece, and the vector
@@ -535,8 +536,8 @@ void quantize_act_kernel(int M, int K, const uint16_t *__restrict__ x,
                 if constexpr (LSLOTS == 3) load_l(0, std::integral_constant<int, 0>{});
             }
         }
-        // the GELU table, computed while the first slices are on their way
-        // (published by the barrier below, before the first group is processed)
+        // the GELU table, copied into LDS while the first slices are on their
+        // way (published by the barrier below, before the first group is processed)
         if constexpr (GELU) {
             if (c0 == 0) gelu_table_fill(s_gelu, threadIdx.x, QA_WAVES * 64);
         }
@@ -684,7 +685,7 @@ hipError_t launch_quantize_act(int precision, bool gelu, int M, int K, int rank,
 __global__ __launch_bounds__(256) void gelu_bf16_kernel(int64_t n, const uint16_t *__restrict__ in,
                                                         uint16_t *__restrict__ out)
 {
-    __shared__ uint16_t tab[GELU_TAB];
+    __shared__ __attribute__((aligned(16))) uint16_t tab[GELU_TAB_PAD];
     gelu_table_fill(tab, threadIdx.x, 256);
     __syncthreads();
     const int64_t base = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 16;

@@ -315,9 +315,9 @@ svdq_status svdq_gemm_w4a4_gelu_quantize(int32_t precision, int64_t M, int64_t N
     SVDQ_TRY(check_ptr(next_codes, "next_codes", false));
     SVDQ_TRY(check_ptr(next_scales, "next_scales", false));
     SVDQ_TRY(check_ptr(next_lora_act, "next_lora_act", rank_next == 0));
-    SVDQ_TRY(check_ptr(workspace, "workspace", false));
-    SVDQ_TRY(check_ptr(out, "out", true));
     const int64_t need = (int64_t)svdq::gelu_quant_workspace_bytes((int)M, (int)N, rank_next);
+    SVDQ_TRY(check_ptr(workspace, "workspace", need == 0));
+    SVDQ_TRY(check_ptr(out, "out", true));
     if (workspace_bytes < need)
         return fail(SVDQ_ERR_INVALID_ARG, "workspace too small: %lld bytes, %lld needed", (long long)workspace_bytes,
                     (long long)need);

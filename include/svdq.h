@@ -206,12 +206,14 @@ svdq_status svdq_gemm_w4a4_qk_norm_rope(int32_t precision, int64_t M, int64_t N,
  *   next_scales     out: bf16 [M, N/64]
  *   next_lora_act   out: fp32 [M, rank_next]; NULL iff rank_next == 0
  *   workspace       device memory of at least
- *                   svdq_gelu_quantize_workspace_bytes(M, N, rank_next) bytes,
- *                   owned by the caller; its contents need no initialisation
- *                   and are scratch (calls that share a workspace must be
- *                   ordered, e.g. on one stream)
+ *                   svdq_gelu_quantize_workspace_bytes(M, N, rank_next) bytes
+ *                   (ceil(N/128) * M * rank_next * 4: the fp32 low-rank
+ *                   partials of the 128-column tiles), owned by the caller;
+ *                   its contents need no initialisation and are scratch
+ *                   (calls that share a workspace must be ordered, e.g. on
+ *                   one stream); may be NULL when that size is 0
  *   out             bf16 [M, N], or NULL: where given, also receives y
- * Two kernels and a small table fill are enqueued on `stream`.
+ * Two kernels are enqueued on `stream` (one when rank_next is 0).
  */
 int64_t svdq_gelu_quantize_workspace_bytes(int64_t M, int64_t N, int32_t rank_next);   /* -1 if invalid */
 svdq_status svdq_gemm_w4a4_gelu_quantize(int32_t precision, int64_t M, int64_t N, int64_t K, int32_t rank,

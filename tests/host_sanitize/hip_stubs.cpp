@@ -98,7 +98,7 @@ hipError_t launch_gemm_w4a4_fp6_qk(int M, int N, int, int, const void *, const v
     return rec("gemm_fp6_qk", M, N, qk.qk_cols);
 }
 size_t gelu_quant_workspace_bytes(int M, int N, int rank_next) {
-    return 16384u + (size_t)((N + 127) / 128) * (size_t)M * (size_t)rank_next * 4u;
+    return (size_t)((N + 127) / 128) * (size_t)M * (size_t)rank_next * 4u;
 }
 hipError_t launch_gemm_w4a4_fp6_gelu_quant(int M, int N, int K, int, const void *, const void *, const void *,
                                            const void *, float, const float *, const void *, const void *,

@@ -269,9 +269,9 @@ def test_gelu_quantize_entry_point_host_checks():
     128, a workspace of at least the queried size; all checked on the host."""
     L = capi.lib()
     ws = capi.svdq_gelu_quantize_workspace_bytes
-    # the GELU table slot plus fp32 partials [ceil(N/128)][M][rank_next]
-    assert ws(4, 192, 32) == 16384 + 2 * 4 * 32 * 4
-    assert ws(4, 192, 0) == 16384
+    # the fp32 low-rank partials [ceil(N/128)][M][rank_next]
+    assert ws(4, 192, 32) == 2 * 4 * 32 * 4
+    assert ws(4, 192, 0) == 0
     assert ws(4, 100, 32) == -1
     assert ws(4, 192, 8) == -1
     FP6 = capi.SVDQ_INT4_FP6
@@ -297,3 +297,4 @@ def test_gelu_quantize_entry_point_host_checks():
     assert f(wb=ws(4, 192, 32) - 1) == INV
     assert f(M=0) == capi.SVDQ_OK
     assert f(M=0, rank_next=0, down=0, lact=0, smooth=0, out=0) == capi.SVDQ_OK
+    assert f(M=0, rank_next=0, down=0, lact=0, work=0) == capi.SVDQ_OK      # nothing to hold
