@@ -38,7 +38,7 @@ pytestmark = [pytest.mark.gpu,
 
 
 def _run_fused(act_fp6, act_scales, w_nib, w_scales, lora_act, lora_up, bias, smooth_next, down_next, M,
-               with_out=True):
+               with_out=True, alpha=1.0):
     """The fused call; returns (y or None, codes bytes, scales, lora_act or None)."""
     from bit_w4a4_quantized_svdq_amd import capi
     N, K = w_nib.shape[0], 2 * w_nib.shape[1]
@@ -50,7 +50,7 @@ def _run_fused(act_fp6, act_scales, w_nib, w_scales, lora_act, lora_up, bias, sm
     out = poison(empty((M, N), "bf16")) if with_out else None
     work = poison(empty((capi.svdq_gelu_quantize_workspace_bytes(M, N, rn),), "u8"))
     capi.svdq_gemm_w4a4_gelu_quantize(to_dev(act_fp6, "u8"), to_dev(act_scales, "bf16"), wc,
-                                      to_dev(w_scales, "bf16"), 1.0, to_dev(lora_act, "f32"),
+                                      to_dev(w_scales, "bf16"), alpha, to_dev(lora_act, "f32"),
                                       to_dev(lora_up, "bf16"), to_dev(bias, "bf16"), to_dev(smooth_next, "bf16"),
                                       to_dev(down_next, "bf16"), codes, scales, lact, work, out)
     torch.cuda.synchronize()
@@ -103,32 +103,38 @@ def test_fused_exact_inputs_match_oracle_bit_for_bit(M, N, K, rank, rank_next, s
         assert_f32_close(lact, ot, 1e-5, "lora_act")
 
 
-# (M, N, K, rank, rank_next)
-RANDOM_CASES = [(130, 384, 320, 32, 32), (257, 192, 192, 16, 16), (64, 640, 1024, 0, 48), (200, 320, 512, 32, 0)]
+# (M, N, K, rank, rank_next, alpha, bias)
+RANDOM_CASES = [(130, 384, 320, 32, 32, 1.0, True), (257, 192, 192, 16, 16, 1.0, True),
+                (64, 640, 1024, 0, 48, 1.0, True), (200, 320, 512, 32, 0, 1.0, True),
+                (96, 256, 256, 16, 128, 1.0, True),          # the largest next-layer rank: four rank chunks
+                (130, 192, 448, 32, 32, 0.5, False),         # alpha scales the 4-bit term only; no bias
+                (40, 128, 3072, 48, 16, 2.0, True)]
 
 
-def _random_up_layer(rng, M, N, K, rank):
+def _random_up_layer(rng, M, N, K, rank, with_bias=True):
     x = rng.standard_normal((M, K))
     x[:, rng.choice(K, max(1, K // 100), replace=False)] *= 50.0
     xb = synth.to_bf16_bits(x)
     smooth = synth.to_bf16_bits(np.exp(rng.standard_normal(K) * 0.5))
     w = synth.synthetic_w4a4_weights(int(rng.integers(1 << 30)), N, K, rank, "int4")
-    bias = synth.to_bf16_bits(rng.standard_normal(N) * 0.5)
+    bias = synth.to_bf16_bits(rng.standard_normal(N) * 0.5) if with_bias else None
     oc, os_, ot = oracle.quantize_act(oracle.INT4, xb, smooth, w["lora_down"])
     return oc, os_, (ot if rank else None), w, bias
 
 
-@pytest.mark.parametrize("M,N,K,rank,rank_next", RANDOM_CASES)
-def test_fused_seeded_layers_against_oracle_and_two_call_chain(M, N, K, rank, rank_next):
+@pytest.mark.parametrize("M,N,K,rank,rank_next,alpha,with_bias", RANDOM_CASES)
+def test_fused_seeded_layers_against_oracle_and_two_call_chain(M, N, K, rank, rank_next, alpha, with_bias):
     rng = np.random.default_rng(7 * M + 3 * N + K + rank_next)
-    oc, os_, ot, w, bias = _random_up_layer(rng, M, N, K, rank)
+    oc, os_, ot, w, bias = _random_up_layer(rng, M, N, K, rank, with_bias)
     sm, dn = _next_layer(rng, N, rank_next)
-    announce("gelu-quantize seeded", "M,N,K", M, N, K, "rank", rank, "rank_next", rank_next)
+    announce("gelu-quantize seeded", "M,N,K", M, N, K, "rank", rank, "rank_next", rank_next, "alpha", alpha,
+             "bias", with_bias)
     y, codes, scales, lact = _run_fused(fp6_layout_from_nibbles(oc, K), os_, w["wgt_codes"], w["wgt_scales"], ot,
-                                        w["lora_up"], bias, sm, dn, M)
+                                        w["lora_up"], bias, sm, dn, M, alpha=alpha)
 
     # the oracle: the up layer's y, then the down layer's activation step
-    y_ref = oracle.gemm_w4a4(oracle.INT4, oc, os_, w["wgt_codes"], w["wgt_scales"], ot, w["lora_up"], bias)
+    y_ref = oracle.gemm_w4a4(oracle.INT4, oc, os_, w["wgt_codes"], w["wgt_scales"], ot, w["lora_up"], bias,
+                             alpha=alpha)
     assert_bf16_close(y, y_ref, "y")
     rc, rs, rt = oracle.gelu_quantize_act(oracle.INT4, y_ref, sm, dn)
     NG = N // 64
@@ -145,7 +151,7 @@ def test_fused_seeded_layers_against_oracle_and_two_call_chain(M, N, K, rank, ra
         assert_f32_close(lact, rt, max(1e-5, 3 * 2.0 ** -8 * np.sqrt(share)), "lora_act vs oracle")
 
     # the two-call chain on the GPU: identical bytes
-    y2 = gpu_gemm(0, oc, os_, w["wgt_codes"], w["wgt_scales"], ot, w["lora_up"], bias, fp6=True)
+    y2 = gpu_gemm(0, oc, os_, w["wgt_codes"], w["wgt_scales"], ot, w["lora_up"], bias, alpha=alpha, fp6=True)
     assert np.array_equal(y, y2), "y differs from svdq_gemm_w4a4's"
     from tests.gpu_helpers import gpu_quantize
     c2, s2, t2 = gpu_quantize(3, y2, sm, dn, N, gelu=True)
