@@ -66,7 +66,7 @@ def _next_layer(rng, N, rank_next, smooth=True):
 
 # (M, N, K, rank of the up layer, rank of the down layer, smoothing)
 EXACT_CASES = [(130, 192, 192, 16, 16, True), (64, 256, 256, 0, 32, True), (257, 384, 640, 32, 48, False),
-               (33, 64, 64, 16, 0, True), (128, 128, 3072, 32, 32, True)]
+               (33, 64, 64, 16, 0, True), (128, 128, 3072, 32, 32, True), (1, 128, 128, 16, 16, True)]
 
 
 @pytest.mark.parametrize("M,N,K,rank,rank_next,smooth", EXACT_CASES)
