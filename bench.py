@@ -719,6 +719,22 @@ def summarize_mlp_fusion(run_dir):
     f = sum(float(rows[n]["AverageNs"]) for n, _ in roles[:2]) / 1e3
     t = sum(float(rows[n]["AverageNs"]) for n, _ in roles[2:]) / 1e3
     lines.append(f"# sum of kernel averages: fused {f:.2f} us, two calls {t:.2f} us")
+    pmc = os.path.join(run_dir, "mlp_insts")
+    if os.path.isdir(pmc):
+        # instruction counts of the two up GEMMs from one --pmc run
+        lines += ["#", "# Instruction counts per launch (all waves), from:",
+                  f"#   rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_WAVES -f csv -d {pmc} -o run -- "
+                  "python3 bench.py --mlp-fusion-only"]
+        per = {}
+        for key, sub in (("fused", "fp6_kernel<false, true, 2>"), ("plain", "fp6_kernel<false, true, 0>")):
+            per[key] = {k: v[0] for k, v in _counter_means(pmc, sub).items()}
+            c = per[key]
+            lines.append(f"{key:6s} VALU {c['SQ_INSTS_VALU']:.0f}  MFMA {c['SQ_INSTS_MFMA']:.0f}  "
+                         f"LDS {c['SQ_INSTS_LDS']:.0f}  waves {c['SQ_WAVES']:.0f}  "
+                         f"VALU per wave {c['SQ_INSTS_VALU'] / c['SQ_WAVES']:.1f}")
+        d = (per["fused"]["SQ_INSTS_VALU"] - per["plain"]["SQ_INSTS_VALU"]) / per["fused"]["SQ_WAVES"]
+        lines.append(f"# the epilogue's extra vector instructions per wave: {d:.1f} "
+                     f"({100 * d / (per['plain']['SQ_INSTS_VALU'] / per['plain']['SQ_WAVES']):.1f} % of the plain GEMM's)")
     open(MLP_FUSION_FILE, "w").write("\n".join(lines) + "\n")
     print(f"wrote {MLP_FUSION_FILE}")
 
