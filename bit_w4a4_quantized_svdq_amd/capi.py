@@ -309,7 +309,8 @@ def svdq_gemm_w4a4_gelu_quantize(act_codes, act_scales, wgt_codes, wgt_scales, a
     activation step in its epilogue: writes the down layer's FP6 codes,
     scales [M, N/64] and lora_act [M, rank_next] (M from next_scales), and
     the up layer's output into out [M, N] when given; workspace: a uint8
-    device tensor of svdq_gelu_quantize_workspace_bytes(M, N, rank_next)."""
+    device tensor of svdq_gelu_quantize_workspace_bytes(M, N, rank_next)
+    bytes (None when that is 0, i.e. rank_next == 0)."""
     func = "svdq_gemm_w4a4_gelu_quantize"
     prec = SVDQ_INT4_FP6
     M = next_scales.shape[0]
@@ -325,8 +326,8 @@ def svdq_gemm_w4a4_gelu_quantize(act_codes, act_scales, wgt_codes, wgt_scales, a
                                               _ptr(lora_up), _ptr(bias), rank_next, _ptr(smooth_next),
                                               _ptr(lora_down_next), _ptr(next_codes), _ptr(next_scales),
                                               _ptr(next_lora_act), _ptr(workspace),
-                                              workspace.numel() * workspace.element_size(), _ptr(out),
-                                              _stream(stream)), func)
+                                              0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                              _ptr(out), _stream(stream)), func)
 
 
 def awq_gemv_w4a16(x, wgt_codes, wgt_scales, wgt_zeros, bias, out, group_size=64, stream=None):

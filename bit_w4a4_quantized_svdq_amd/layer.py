@@ -133,8 +133,10 @@ class SVDQW4A4Linear:
         M = nb["scales"].shape[0]
         ws = b.get("gq_workspace")
         need = capi.svdq_gelu_quantize_workspace_bytes(M, self.N, nxt.rank)
-        if ws is None or ws.numel() < need:
+        if need > 0 and (ws is None or ws.numel() < need):
             ws = b["gq_workspace"] = torch.empty((need,), dtype=torch.uint8, device=self.device)
+        if need == 0:
+            ws = None
         capi.svdq_gemm_w4a4_gelu_quantize(b["codes"], b["scales"], self.wgt_codes, self.wgt_scales, self.alpha,
                                           b["lora_act"] if self.rank else None, self.lora_up, self.bias,
                                           nxt.smooth, nxt.lora_down, nb["codes"], nb["scales"],

@@ -298,3 +298,4 @@ def test_gelu_quantize_entry_point_host_checks():
     assert f(M=0) == capi.SVDQ_OK
     assert f(M=0, rank_next=0, down=0, lact=0, smooth=0, out=0) == capi.SVDQ_OK
     assert f(M=0, rank_next=0, down=0, lact=0, work=0) == capi.SVDQ_OK      # nothing to hold
+

@@ -48,7 +48,8 @@ def _run_fused(act_fp6, act_scales, w_nib, w_scales, lora_act, lora_up, bias, sm
     scales = poison(empty((M, N // 64), "bf16"))
     lact = poison(empty((M, rn), "f32")) if rn else None
     out = poison(empty((M, N), "bf16")) if with_out else None
-    work = poison(empty((capi.svdq_gelu_quantize_workspace_bytes(M, N, rn),), "u8"))
+    # no workspace at all when the next layer has no low-rank branch (size 0)
+    work = poison(empty((capi.svdq_gelu_quantize_workspace_bytes(M, N, rn),), "u8")) if rn else None
     capi.svdq_gemm_w4a4_gelu_quantize(to_dev(act_fp6, "u8"), to_dev(act_scales, "bf16"), wc,
                                       to_dev(w_scales, "bf16"), alpha, to_dev(lora_act, "f32"),
                                       to_dev(lora_up, "bf16"), to_dev(bias, "bf16"), to_dev(smooth_next, "bf16"),
