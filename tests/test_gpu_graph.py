@@ -121,7 +121,7 @@ def test_graph_replay_matches_eager_fused_paths():
 
 def test_graph_replay_matches_eager_mlp_in_the_up_epilogue():
     """A GELU MLP whose up GEMM runs the down layer's activation step in its
-    epilogue (svdq_gemm_w4a4_gelu_quantize: table fill, GEMM, fixed-order
+    epilogue (svdq_gemm_w4a4_gelu_quantize: GEMM and fixed-order
     partial sum), then the down GEMM, in one graph: every replay gives the
     eager bytes of the down layer's codes, scales, lora_act and output."""
     from bit_w4a4_quantized_svdq_amd.layer import SVDQW4A4Linear
